@@ -1,0 +1,431 @@
+/*
+ * kia_oracle.c -- the oracle for K-interval attention: a plain, slow,
+ * double-precision CPU implementation of the forward and backward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load or call this code; the product path
+ * (the HIP library and its Python binding) never does, and shares no code,
+ * header, table or helper with it.
+ *
+ * Source of every step: "Pretraining Transformers with Quantized Softmax in
+ * Attention" (Zhu, Hu, Kozlowski), §3 "Objects and calibration" and
+ * "Reconstruction", App. A "Edge cases and conventions", App. B (normalization
+ * Jacobian, LERP own-score slope, full calibration gradient (MinMax) = eq. (1),
+ * detach (legacy), Weight-STE, Prob-STE, FWM), App. C.2 (iii) (strict hard
+ * forward).  Steps follow the pages' order and notation: calibration ->
+ * interval index r_j and local position t_j -> LERP / Nearest weights ->
+ * normalization -> P V; backward: gamma (normalization Jacobian) -> Delta
+ * (secant slope) -> calibration terms through the row extrema -> dS -> dQ, dK, dV.
+ *
+ * Readings taken where the pages are silent or lost in extraction:
+ *  - eq. (1) (lost): differentiating w^L = (1-t)e^{b_r} + t e^{b_{r+1}} through
+ *    t, b_r, b_{r+1} and h gives dw/dM = X - w - rho*Delta and
+ *    dw/dm = w - X - (1-rho)*Delta, with rho and X as App. B defines them; these
+ *    satisfy the stated identity Delta + dw/dM + dw/dm = 0.
+ *  - Weight-STE body (lost): w = w^L + sg(w^N - w^L), P = w / sum(w); the
+ *    normalization Jacobian is taken at the forward point (P^N, W^N) and the
+ *    weight Jacobian is that of w^L (calibration terms included).
+ *  - degenerate MinMax rows (M - m <= 1e-12): h is the constant 1 (no gradient
+ *    through h); b_r = (1 - r/K)(m - M) keeps its dependence on M and m.
+ *  - the clamp of t passes the gradient at its bounds (so the argmax / argmin
+ *    keys keep their own-score term, as the zero-sum identity requires).
+ *  - interval index r = clamp(floor(u), 0, K-1); Nearest rounds t = 1/2 up.
+ *  - FWM: z = -tau is inside the window; only z < -tau is tail (weight 0).
+ *  - tied extrema: the extremum's gradient is split evenly among tied keys.
+ *
+ * Flip list: a test may ask the oracle to take, at named (row, key) positions,
+ * the other valid decision at a bin boundary (the other interval at an integer
+ * u, the other rounding at u = k + 1/2, the other side of the FWM tail edge).
+ * The positions come from the oracle's own list of near-boundary positions;
+ * this is how a test checks that a result computed in fp32 is one of the
+ * answers that are correct within the boundary guard.
+ *
+ * Mutations: cfg.mutation != 0 plants one known mistake; tests use this to
+ * show that the pins catch such mistakes.  Zero in every other use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { KO_MINMAX = 0, KO_FWM = 1 };
+enum { KO_LERP = 0, KO_NEAREST = 1 };
+enum { KO_WEIGHT_STE = 0, KO_PROB_STE = 1 };
+enum { KO_FULL = 0, KO_DETACHED = 1 };
+
+enum { FLIP_INTERVAL = 1, FLIP_NEAREST = 2, FLIP_TAIL = 4 };
+
+enum {
+  MUT_NONE = 0,
+  MUT_DROP_RHO_DELTA = 1,   /* dw/dM without the -rho*Delta term */
+  MUT_SIGN_DM = 2,          /* dw/dm with the wrong sign */
+  MUT_DELTA_TIMES_H = 3,    /* secant slope multiplied by h instead of divided */
+  MUT_NEAREST_STRICT = 4,   /* Nearest rounds t = 1/2 down */
+  MUT_WSTE_USES_LERP = 5,   /* Weight-STE gamma taken at (P^L, W^L) */
+  MUT_DK_WITH_DO = 6,       /* dK accumulates dO instead of Q */
+  MUT_TAIL_INCLUSIVE = 7,   /* FWM tail includes z = -tau */
+  MUT_NO_TIE_SPLIT = 8,     /* extremum gradient given whole to the first tied key */
+  MUT_NEAREST_FWD_LERP = 9, /* Nearest forward returns P^L */
+  MUT_EXTREMA_ALL_KEYS = 10,/* row extrema over all keys, ignoring the causal set */
+  MUT_DQ_NO_SCALE = 11,     /* dQ without the score scale */
+  MUT_NO_HSAFE = 12,        /* degenerate rows divide by span/K */
+  MUT_INTERVAL_ROUND = 13,  /* interval index by rounding instead of floor */
+  MUT_GAMMA_SIGN = 14,      /* gamma = (D - g)/W */
+  MUT_DV_WITH_PL = 15,      /* Nearest dV uses P^L instead of the forward P^N */
+  MUT_FWM_GRID_SHIFT = 16,  /* FWM grid b_r = -tau + (r+1)h */
+  MUT_X_INDEX = 17,         /* X uses r instead of r+1 in its second term */
+  MUT_DETACH_KEEPS_M = 18   /* detached mode keeps the M channel */
+};
+
+typedef struct {
+  int32_t calib, recon, ste, grad, K, mutation;
+  double tau;
+} ko_cfg_t;
+
+/* per-row record: doubles */
+enum { RD_M = 0, RD_m, RD_h, RD_WL, RD_WN, RD_a, RD_b, RD_gapM, RD_gapm, RD_D, RD_N };
+/* per-row record: ints */
+enum { RI_amax = 0, RI_amin, RI_nA, RI_nC, RI_degenerate, RI_N };
+
+#define DEGENERATE_EPS 1e-12
+
+int ko_rowd_n(void) { return RD_N; }
+int ko_rowi_n(void) { return RI_N; }
+
+typedef struct {
+  double guard;
+  int64_t cap;
+  int64_t count;      /* may exceed cap; only the first cap entries are stored */
+  int32_t *pos;       /* cap x 3: row, key, kind */
+  double *dist;       /* cap */
+} ko_flags_t;
+
+static void flag_push(ko_flags_t *f, int row, int key, int kind, double dist) {
+  if (!f) return;
+  int64_t idx;
+#ifdef _OPENMP
+#pragma omp atomic capture
+#endif
+  idx = f->count++;
+  if (idx < f->cap) {
+    f->pos[3 * idx] = row; f->pos[3 * idx + 1] = key; f->pos[3 * idx + 2] = kind;
+    f->dist[idx] = dist;
+  }
+}
+
+/*
+ * One attention row.  s[0..n) are the scaled scores of the row's visible keys,
+ * g[0..n) the upstream gradient dL/dP_j (may be NULL: forward only).
+ * Outputs P (forward probabilities), dS (score gradient, if g != NULL), and
+ * optional per-key diagnostics.  row_id is used only for flag reporting.
+ */
+static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const double *g,
+                        const uint8_t *flip, double *P, double *dS, double *PL_out,
+                        double *u_out, int32_t *r_out, double *t_out, int32_t *ell_out, uint8_t *tail_out,
+                        double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags) {
+  const int K = cfg->K;
+  const int mut = cfg->mutation;
+  double *E = (double *)malloc(sizeof(double) * (K + 1));
+  double *bgrid = (double *)malloc(sizeof(double) * (K + 1));
+  double *u = (double *)malloc(sizeof(double) * n);
+  double *t = (double *)malloc(sizeof(double) * n);
+  double *wL = (double *)malloc(sizeof(double) * n);
+  double *wN = (double *)malloc(sizeof(double) * n);
+  double *Delta = (double *)malloc(sizeof(double) * n);
+  double *gam = (double *)malloc(sizeof(double) * n);
+  int *r = (int *)malloc(sizeof(int) * n);
+  int *ell = (int *)malloc(sizeof(int) * n);
+  uint8_t *tail = (uint8_t *)malloc(n);
+
+  /* --- calibration (§3 Objects and calibration; App. A) --- */
+  /* row extrema over the visible keys, and the sets of keys attaining them */
+  double M = -INFINITY, m = INFINITY;
+  for (int j = 0; j < n; ++j) {
+    if (s[j] > M) M = s[j];
+    if (s[j] < m) m = s[j];
+  }
+  int amax = -1, amin = -1, nA = 0, nC = 0;
+  double belowM = -INFINITY, abovem = INFINITY;
+  for (int j = 0; j < n; ++j) {
+    if (s[j] == M) { if (amax < 0) amax = j; nA++; } else if (s[j] > belowM) belowM = s[j];
+    if (s[j] == m) { if (amin < 0) amin = j; nC++; } else if (s[j] < abovem) abovem = s[j];
+  }
+  double h;
+  int degenerate = 0;
+  if (cfg->calib == KO_MINMAX) {
+    /* MinMax: grid on the observed range, h = (M - m)/K, b_r = (1 - r/K)(m - M).
+       Degenerate rows (M - m <= eps) use the safe width 1 before any division. */
+    double span = M - m;
+    degenerate = !(span > DEGENERATE_EPS);
+    h = (degenerate && mut != MUT_NO_HSAFE) ? 1.0 : span / K;
+    for (int q = 0; q <= K; ++q) bgrid[q] = (1.0 - (double)q / K) * (m - M);
+  } else {
+    /* FWM: fixed window [M - tau, M], h = tau/K, b_r = -tau + r h. */
+    h = cfg->tau / K;
+    for (int q = 0; q <= K; ++q)
+      bgrid[q] = -cfg->tau + (mut == MUT_FWM_GRID_SHIFT ? q + 1 : q) * h;
+  }
+  for (int q = 0; q <= K; ++q) E[q] = exp(bgrid[q]);
+
+  /* --- interval index and local position (§3) --- */
+  for (int j = 0; j < n; ++j) {
+    double uj;
+    int tj = 0;
+    if (cfg->calib == KO_MINMAX) {
+      uj = (s[j] - m) / h;
+    } else {
+      double z = s[j] - M;
+      tj = (mut == MUT_TAIL_INCLUSIVE) ? (z <= -cfg->tau) : (z < -cfg->tau);
+      double zc = z < -cfg->tau ? -cfg->tau : (z > 0.0 ? 0.0 : z);   /* clip(z, -tau, 0) */
+      uj = (zc + cfg->tau) / h;
+      if (flags && fabs(z + cfg->tau) / h < flags->guard)
+        flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_TAIL, fabs(z + cfg->tau) / h);
+    }
+    if (flags) {
+      double kint = floor(uj + 0.5);
+      if (K >= 2 && kint >= 1 && kint <= K - 1 && fabs(uj - kint) < flags->guard)
+        flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_INTERVAL, fabs(uj - kint));
+      double khalf = floor(uj) + 0.5;
+      if (cfg->recon == KO_NEAREST && khalf < K && fabs(uj - khalf) < flags->guard)
+        flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_NEAREST, fabs(uj - khalf));
+    }
+    int rj = (mut == MUT_INTERVAL_ROUND) ? (int)floor(uj + 0.5) : (int)floor(uj);
+    if (rj < 0) rj = 0;
+    if (rj > K - 1) rj = K - 1;
+    double tt = uj - rj;
+    if (tt < 0.0) tt = 0.0;
+    if (tt > 1.0) tt = 1.0;
+    uint8_t fl = flip ? flip[j] : 0;
+    if (fl & FLIP_TAIL) {
+      tj = !tj;
+      if (!tj && uj > 0.0 && (s[j] - M) < -cfg->tau + 0.5 * h) { /* leaving the tail: onto the edge */
+        uj = 0.0; rj = 0; tt = 0.0;
+      }
+      if (!tj && uj == 0.0) { rj = 0; tt = 0.0; }
+    }
+    if (fl & FLIP_INTERVAL) {
+      int kint = (int)floor(uj + 0.5);
+      if (kint >= 1 && kint <= K - 1) {
+        rj = (rj == kint) ? kint - 1 : kint;
+        tt = uj - rj;
+        if (tt < 0.0) tt = 0.0;
+        if (tt > 1.0) tt = 1.0;
+      }
+    }
+    int lj = rj + ((mut == MUT_NEAREST_STRICT) ? (tt > 0.5) : (tt >= 0.5));
+    if (fl & FLIP_NEAREST) {
+      int k2 = (int)floor(uj);
+      if (k2 > K - 1) k2 = K - 1;
+      lj = (lj == k2 + 1) ? k2 : k2 + 1;
+    }
+    u[j] = uj; r[j] = rj; t[j] = tt; ell[j] = lj; tail[j] = (uint8_t)tj;
+  }
+
+  /* --- reconstruction (§3 Reconstruction) --- */
+  for (int j = 0; j < n; ++j) {
+    if (tail[j]) { wL[j] = 0.0; wN[j] = 0.0; continue; }
+    wL[j] = (1.0 - t[j]) * E[r[j]] + t[j] * E[r[j] + 1];   /* LERP between adjacent grid values */
+    wN[j] = E[ell[j]];                                       /* Nearest grid centre */
+  }
+
+  /* --- normalization (§3) and strict hard forward (App. C.2 (iii)) --- */
+  double WL = 0.0, WN = 0.0;
+  for (int j = 0; j < n; ++j) { WL += wL[j]; WN += wN[j]; }
+  int nearest_fwd = (cfg->recon == KO_NEAREST) && (mut != MUT_NEAREST_FWD_LERP);
+  for (int j = 0; j < n; ++j) {
+    P[j] = nearest_fwd ? wN[j] / WN : wL[j] / WL;
+    if (PL_out) PL_out[j] = (mut == MUT_DV_WITH_PL) ? wL[j] / WL : P[j];
+  }
+
+  double a = 0.0, b = 0.0, Dsum = 0.0;
+  if (g) {
+    /* --- normalization Jacobian (App. B): gamma_j = (g_j - sum_i P_i g_i)/W,
+       at (P^L, W^L) for LERP and Prob-STE, at (P^N, W^N) for Weight-STE --- */
+    int use_lerp_point = (cfg->recon == KO_LERP) || (cfg->ste == KO_PROB_STE) || (mut == MUT_WSTE_USES_LERP);
+    double Wg = use_lerp_point ? WL : WN;
+    for (int j = 0; j < n; ++j) Dsum += (use_lerp_point ? wL[j] / WL : wN[j] / WN) * g[j];
+    for (int j = 0; j < n; ++j) gam[j] = (mut == MUT_GAMMA_SIGN) ? (Dsum - g[j]) / Wg : (g[j] - Dsum) / Wg;
+
+    /* --- LERP own-score slope (App. B): Delta_j = (e^{b_{r+1}} - e^{b_r})/h --- */
+    for (int j = 0; j < n; ++j) {
+      if (tail[j]) { Delta[j] = 0.0; continue; }
+      Delta[j] = (mut == MUT_DELTA_TIMES_H) ? (E[r[j] + 1] - E[r[j]]) * h : (E[r[j] + 1] - E[r[j]]) / h;
+      dS[j] = gam[j] * Delta[j];
+    }
+    for (int j = 0; j < n; ++j) if (tail[j]) dS[j] = 0.0;
+
+    /* --- calibration gradient through the row extrema (App. B) --- */
+    int full = (cfg->grad == KO_FULL);
+    if (full || mut == MUT_DETACH_KEEPS_M) {
+      if (cfg->calib == KO_MINMAX) {
+        for (int j = 0; j < n; ++j) {
+          double rho = (r[j] + t[j]) / K;
+          double X = mut == MUT_X_INDEX
+                         ? ((1.0 - t[j]) * r[j] * E[r[j]] + t[j] * r[j] * E[r[j] + 1]) / K
+                         : ((1.0 - t[j]) * r[j] * E[r[j]] + t[j] * (r[j] + 1) * E[r[j] + 1]) / K;
+          double dM, dm;
+          if (!degenerate) {              /* eq. (1), regular branch */
+            dM = X - wL[j] - (mut == MUT_DROP_RHO_DELTA ? 0.0 : rho * Delta[j]);
+            dm = wL[j] - X - (1.0 - rho) * Delta[j];
+          } else {                        /* degenerate branch: h is a constant */
+            dM = X - wL[j];
+            dm = wL[j] - X - Delta[j];
+          }
+          if (mut == MUT_SIGN_DM) dm = -dm;
+          a += gam[j] * dM;
+          b += gam[j] * dm;
+        }
+        if (!full) b = 0.0;   /* only reachable under MUT_DETACH_KEEPS_M */
+      } else {
+        /* FWM: in-window keys have dw/dM = -Delta, tail keys contribute nothing */
+        for (int j = 0; j < n; ++j) if (!tail[j]) a += -gam[j] * Delta[j];
+      }
+      /* the extremum gradient is split evenly among tied keys */
+      for (int j = 0; j < n; ++j) {
+        if (s[j] == M) {
+          if (mut == MUT_NO_TIE_SPLIT) { if (j == amax) dS[j] += a; }
+          else dS[j] += a / nA;
+        }
+        if (cfg->calib == KO_MINMAX && s[j] == m) {
+          if (mut == MUT_NO_TIE_SPLIT) { if (j == amin) dS[j] += b; }
+          else dS[j] += b / nC;
+        }
+      }
+    }
+  }
+
+  if (u_out) for (int j = 0; j < n; ++j) {
+    u_out[j] = u[j]; r_out[j] = r[j]; t_out[j] = t[j]; ell_out[j] = ell[j]; tail_out[j] = tail[j];
+  }
+  if (rowd) {
+    rowd[RD_M] = M; rowd[RD_m] = m; rowd[RD_h] = h; rowd[RD_WL] = WL; rowd[RD_WN] = WN;
+    rowd[RD_a] = a; rowd[RD_b] = b; rowd[RD_gapM] = M - belowM; rowd[RD_gapm] = abovem - m; rowd[RD_D] = Dsum;
+  }
+  if (rowi) {
+    rowi[RI_amax] = amax; rowi[RI_amin] = amin; rowi[RI_nA] = nA; rowi[RI_nC] = nC; rowi[RI_degenerate] = degenerate;
+  }
+  free(E); free(bgrid); free(u); free(t); free(wL); free(wN); free(Delta); free(gam); free(r); free(ell); free(tail);
+}
+
+/* Row-level entry point (no flags).  g may be NULL for forward only. */
+int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const uint8_t *flip,
+           double *P, double *dS, double *u, int32_t *r, double *t, int32_t *ell, uint8_t *tail,
+           double *rowd, int32_t *rowi) {
+  if (!cfg || n < 1 || cfg->K < 1 || !s || !P || (g && !dS)) return -1;
+  if (cfg->calib == KO_FWM && !(cfg->tau > 0.0)) return -1;
+  if (u && !(r && t && ell && tail)) return -1;
+  ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL);
+  return 0;
+}
+
+/*
+ * One attention head: Q, K, V, dO are [T, D] row-major doubles.  Scores are
+ * s_ij = scale * Q_i . K_j over the visible keys (j <= i when causal).
+ * O = P V; dQ_i = scale * sum_j dS_ij K_j; dK_j = scale * sum_i dS_ij Q_i;
+ * dV_j = sum_i P_ij dO_i.  dO may be NULL (forward only; dQ/dK/dV untouched).
+ * flips: nflip triples (row, key, bits).  flags: optional near-boundary report.
+ */
+int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
+            const double *Q, const double *Kt, const double *V, const double *dO,
+            double *O, double *dQ, double *dK, double *dV, double *rowd, int32_t *rowi,
+            int64_t nflip, const int32_t *flips,
+            double guard, int64_t flag_cap, int32_t *flag_pos, double *flag_dist, int64_t *nflags,
+            int nthreads) {
+  if (!cfg || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
+  if (dO && !(dQ && dK && dV)) return -1;
+  if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
+  const int mut = cfg->mutation;
+  ko_flags_t fl_store, *fl = NULL;
+  if (flag_cap > 0 && flag_pos && flag_dist) {
+    fl_store.guard = guard; fl_store.cap = flag_cap; fl_store.count = 0;
+    fl_store.pos = flag_pos; fl_store.dist = flag_dist;
+    fl = &fl_store;
+  }
+  if (nthreads < 1) nthreads = 1;
+  memset(O, 0, sizeof(double) * (size_t)T * D);
+  if (dO) {
+    memset(dQ, 0, sizeof(double) * (size_t)T * D);
+    memset(dK, 0, sizeof(double) * (size_t)T * D);
+    memset(dV, 0, sizeof(double) * (size_t)T * D);
+  }
+  /* thread-private dK, dV accumulators, summed in thread order at the end */
+  double *accK = NULL, *accV = NULL;
+  if (dO) {
+    accK = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
+    accV = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
+    if (!accK || !accV) { free(accK); free(accV); return -2; }
+  }
+  const double dq_scale = (mut == MUT_DQ_NO_SCALE) ? 1.0 : scale;
+
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+#endif
+  for (int i = 0; i < T; ++i) {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    int n = (causal && mut != MUT_EXTREMA_ALL_KEYS) ? i + 1 : T;
+    double *s = (double *)malloc(sizeof(double) * n);
+    double *g = dO ? (double *)malloc(sizeof(double) * n) : NULL;
+    double *P = (double *)malloc(sizeof(double) * n);
+    double *Pv = (double *)malloc(sizeof(double) * n);
+    double *dS = dO ? (double *)malloc(sizeof(double) * n) : NULL;
+    int32_t *kid = (int32_t *)malloc(sizeof(int32_t) * n);
+    uint8_t *flip = NULL;
+    for (int j = 0; j < n; ++j) {
+      kid[j] = j;
+      double acc = 0.0;
+      for (int k = 0; k < D; ++k) acc += Q[(size_t)i * D + k] * Kt[(size_t)j * D + k];
+      s[j] = scale * acc;
+      if (dO) {
+        double ga = 0.0;
+        for (int k = 0; k < D; ++k) ga += dO[(size_t)i * D + k] * V[(size_t)j * D + k];
+        g[j] = ga;
+      }
+    }
+    for (int64_t f = 0; f < nflip; ++f) {
+      if (flips[3 * f] == i && flips[3 * f + 1] >= 0 && flips[3 * f + 1] < n) {
+        if (!flip) flip = (uint8_t *)calloc(n, 1);
+        flip[flips[3 * f + 1]] |= (uint8_t)flips[3 * f + 2];
+      }
+    }
+    ko_row_impl(cfg, n, s, g, flip, P, dS, Pv, NULL, NULL, NULL, NULL, NULL,
+                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl);
+    if (mut == MUT_EXTREMA_ALL_KEYS && causal) {
+      /* the planted mistake computed the extrema over all keys; keep the causal output shape */
+      double Wsum = 0.0;
+      for (int j = 0; j <= i; ++j) Wsum += P[j];
+      for (int j = 0; j <= i; ++j) { P[j] /= Wsum; Pv[j] = P[j]; }
+      n = i + 1;
+    }
+    /* O_i = sum_j P_ij V_j */
+    for (int j = 0; j < n; ++j)
+      for (int k = 0; k < D; ++k) O[(size_t)i * D + k] += P[j] * V[(size_t)j * D + k];
+    if (dO) {
+      double *aK = accK + (size_t)tid * T * D, *aV = accV + (size_t)tid * T * D;
+      for (int j = 0; j < n; ++j) {
+        for (int k = 0; k < D; ++k) {
+          dQ[(size_t)i * D + k] += dq_scale * dS[j] * Kt[(size_t)j * D + k];
+          double src = (mut == MUT_DK_WITH_DO) ? dO[(size_t)i * D + k] : Q[(size_t)i * D + k];
+          aK[(size_t)j * D + k] += scale * dS[j] * src;
+          aV[(size_t)j * D + k] += Pv[j] * dO[(size_t)i * D + k];
+        }
+      }
+    }
+    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip);
+  }
+  if (dO) {
+    for (int th = 0; th < nthreads; ++th)
+      for (size_t x = 0; x < (size_t)T * D; ++x) {
+        dK[x] += accK[(size_t)th * T * D + x];
+        dV[x] += accV[(size_t)th * T * D + x];
+      }
+    free(accK); free(accV);
+  }
+  if (nflags) *nflags = fl ? fl->count : 0;
+  return 0;
+}

@@ -1,0 +1,188 @@
+"""ctypes front end of the K-interval attention oracle (kia_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product path.  It imports
+nothing from the HIP package.
+
+Everything is double precision; inputs are widened from float32 (or from
+bf16-representable float32) values.  Every step follows "Pretraining
+Transformers with Quantized Softmax in Attention", §3 and App. A-C; the C file
+states the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kia_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkia_oracle.so")
+
+CALIB = {"minmax": 0, "fwm": 1}
+RECON = {"lerp": 0, "nearest": 1}
+STE = {"weight": 0, "prob": 1}
+GRAD = {"full": 0, "detached": 1}
+
+FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL = 1, 2, 4
+MUTATIONS = {
+    "drop_rho_delta": 1, "sign_dm": 2, "delta_times_h": 3, "nearest_strict": 4,
+    "wste_uses_lerp": 5, "dk_with_do": 6, "tail_inclusive": 7, "no_tie_split": 8,
+    "nearest_fwd_lerp": 9, "extrema_all_keys": 10, "dq_no_scale": 11, "no_hsafe": 12,
+    "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
+    "x_index": 17, "detach_keeps_m": 18,
+}
+ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D")
+ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("calib", ctypes.c_int32), ("recon", ctypes.c_int32), ("ste", ctypes.c_int32),
+                ("grad", ctypes.c_int32), ("K", ctypes.c_int32), ("mutation", ctypes.c_int32),
+                ("tau", ctypes.c_double)]
+
+
+@dataclass(frozen=True)
+class OracleConfig:
+    calib: str = "minmax"
+    recon: str = "lerp"
+    ste: str = "prob"
+    grad: str = "full"
+    K: int = 4
+    tau: float = 8.0
+    mutation: str | None = None
+
+    @classmethod
+    def of(cls, v, mutation=None):
+        """Build from any object with calib/recon/ste/grad/K/tau attributes."""
+        return cls(v.calib, v.recon, v.ste, v.grad, int(v.K), float(v.tau), mutation)
+
+    def _c(self) -> _Cfg:
+        return _Cfg(CALIB[self.calib], RECON[self.recon], STE[self.ste], GRAD[self.grad],
+                    int(self.K), MUTATIONS[self.mutation] if self.mutation else 0, float(self.tau))
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        up = ctypes.POINTER(ctypes.c_uint8)
+        lp = ctypes.POINTER(ctypes.c_int64)
+        lib.ko_row.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, dp, dp, up, dp, dp, dp, ip, dp, ip, up, dp, ip]
+        lib.ko_row.restype = ctypes.c_int
+        lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, ctypes.c_int]
+        lib.ko_head.restype = ctypes.c_int
+        assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
+        _lib = lib
+    return _lib
+
+
+def _p(a, ct):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def row(cfg: OracleConfig, s, g=None, flip=None):
+    """One row of visible scores s (already scaled) with upstream dL/dP g.
+
+    Returns a dict: P, dS (None if g is None), u, r, t, ell, tail and the row
+    record fields (M, m, h, WL, WN, a, b, gapM, gapm, D, amax, amin, nA, nC, degenerate).
+    """
+    lib = _load()
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    n = s.shape[0]
+    g = None if g is None else np.ascontiguousarray(g, dtype=np.float64)
+    flip = None if flip is None else np.ascontiguousarray(flip, dtype=np.uint8)
+    P = np.zeros(n); dS = np.zeros(n) if g is not None else None
+    u = np.zeros(n); r = np.zeros(n, np.int32); t = np.zeros(n); ell = np.zeros(n, np.int32)
+    tail = np.zeros(n, np.uint8)
+    rd = np.zeros(len(ROWD_FIELDS)); ri = np.zeros(len(ROWI_FIELDS), np.int32)
+    c = cfg._c()
+    rc = lib.ko_row(ctypes.byref(c), n, _p(s, ctypes.c_double), _p(g, ctypes.c_double), _p(flip, ctypes.c_uint8),
+                    _p(P, ctypes.c_double), _p(dS, ctypes.c_double), _p(u, ctypes.c_double),
+                    _p(r, ctypes.c_int32), _p(t, ctypes.c_double), _p(ell, ctypes.c_int32),
+                    _p(tail, ctypes.c_uint8), _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError(f"oracle row rejected its arguments (rc={rc})")
+    out = dict(P=P, dS=dS, u=u, r=r, t=t, ell=ell, tail=tail.astype(bool))
+    out.update({k: float(rd[i]) for i, k in enumerate(ROWD_FIELDS)})
+    out.update({k: int(ri[i]) for i, k in enumerate(ROWI_FIELDS)})
+    return out
+
+
+def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=None,
+         guard=0.0, flag_cap=0, nthreads=None):
+    """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags."""
+    lib = _load()
+    Q = np.ascontiguousarray(Q, dtype=np.float64)
+    K = np.ascontiguousarray(K, dtype=np.float64)
+    V = np.ascontiguousarray(V, dtype=np.float64)
+    T, D = Q.shape
+    dO = None if dO is None else np.ascontiguousarray(dO, dtype=np.float64)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    O = np.zeros((T, D))
+    dQ = np.zeros((T, D)) if dO is not None else None
+    dK = np.zeros((T, D)) if dO is not None else None
+    dV = np.zeros((T, D)) if dO is not None else None
+    rd = np.zeros((T, len(ROWD_FIELDS))); ri = np.zeros((T, len(ROWI_FIELDS)), np.int32)
+    fl = np.zeros((0, 3), np.int32) if flips is None else np.ascontiguousarray(flips, dtype=np.int32).reshape(-1, 3)
+    fpos = np.zeros((max(flag_cap, 1), 3), np.int32); fdist = np.zeros(max(flag_cap, 1))
+    nfl = ctypes.c_int64(0)
+    c = cfg._c()
+    rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
+                     _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
+                     _p(O, ctypes.c_double), _p(dQ, ctypes.c_double), _p(dK, ctypes.c_double), _p(dV, ctypes.c_double),
+                     _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32),
+                     fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
+                     _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
+                     int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle head rejected its arguments (rc={rc})")
+    nf = int(nfl.value)
+    kept = min(nf, flag_cap)
+    order = np.lexsort((fpos[:kept, 1], fpos[:kept, 0])) if kept else np.zeros(0, np.int64)
+    rowd = {k: rd[:, i].copy() for i, k in enumerate(ROWD_FIELDS)}
+    rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
+    return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
+                flags=fpos[:kept][order], flag_dist=fdist[:kept][order])
+
+
+def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):
+    """[B, H, T, D] arrays; runs the listed (b, h) heads (all by default).
+
+    Returns O, dQ, dK, dV as [n_heads, T, D] arrays in the order of `heads`.
+    """
+    B, H, T, D = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    outs = {key: np.zeros((len(heads), T, D)) for key in ("O", "dQ", "dK", "dV")}
+    for n, (b, h) in enumerate(heads):
+        r = head(cfg, q[b, h], k[b, h], v[b, h], None if do is None else do[b, h],
+                 causal=causal, scale=scale, nthreads=nthreads)
+        for key in outs:
+            if r[key] is not None:
+                outs[key][n] = r[key]
+    return outs

@@ -1,0 +1,96 @@
+"""Float64 torch-autograd reference of the K-interval attention forward.
+
+Used only as a pin for the oracle: the forward is written from the definitions
+in "Pretraining Transformers with Quantized Softmax in Attention" (§3 Objects
+and calibration, Reconstruction; App. A edge cases; App. B Weight-STE /
+Prob-STE / FWM; App. C.2 (iii) strict forward), and its backward comes from
+torch's automatic differentiation, a derivation route independent of the
+oracle's closed forms.  torch's amax/amin split an extremum's gradient evenly
+among tied entries, which is the tie convention the pages state.
+
+Readings shared with the oracle (each a reading of a silent point, not a
+formula copied from it): the clamp on t passes the gradient at its bounds;
+degenerate MinMax rows use the constant width 1; Nearest rounds t = 1/2 up.
+"""
+import torch
+
+DEGENERATE_EPS = 1e-12
+
+
+def _st_clamp01(x):
+    # value clamp(x, 0, 1); gradient of the identity (the bound is reached only by rounding)
+    return x + (x.clamp(0.0, 1.0) - x).detach()
+
+
+def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0):
+    """s: [R, n] float64, mask: [R, n] bool (visible keys).  Returns P [R, n]."""
+    dt = s.dtype
+    pos_inf = torch.tensor(float("inf"), dtype=dt)
+    M = torch.where(mask, s, -pos_inf).amax(dim=1, keepdim=True)
+    m = torch.where(mask, s, pos_inf).amin(dim=1, keepdim=True)
+    if grad == "detached":
+        M, m = M.detach(), m.detach()
+    rr = torch.arange(K + 1, dtype=dt)
+    R = s.shape[0]
+    if calib == "minmax":
+        span = M - m
+        deg = ~(span > DEGENERATE_EPS)
+        h = torch.where(deg, torch.ones_like(span), span / K)
+        b = (1.0 - rr / K) * (m - M)                        # [R, K+1]
+        u = (s - m) / h
+        tail = torch.zeros_like(mask)
+    else:
+        h = tau / K
+        b = (-tau + rr * h).expand(R, K + 1)
+        z = s - M
+        tail = (z < -tau).detach()
+        u = (torch.clamp(z, -tau, 0.0) + tau) / h
+    u_safe = torch.where(mask, u, torch.zeros_like(u))
+    r = torch.clamp(torch.floor(u_safe.detach()), 0, K - 1).long()
+    t = _st_clamp01(u_safe - r.to(dt))
+    E = torch.exp(b)
+    Er = torch.gather(E, 1, r)
+    Er1 = torch.gather(E, 1, r + 1)
+    wL = (1.0 - t) * Er + t * Er1
+    ell = r + (t.detach() >= 0.5).long()
+    wN = torch.gather(E, 1, ell)
+    keep = mask & ~tail
+    zero = torch.zeros_like(wL)
+    wL = torch.where(keep, wL, zero)
+    wN = torch.where(keep, wN, zero)
+    if recon == "lerp":
+        return wL / wL.sum(dim=1, keepdim=True)
+    if ste == "weight":
+        w = wL + (wN - wL).detach()
+        return w / w.sum(dim=1, keepdim=True)
+    PN = (wN / wN.sum(dim=1, keepdim=True)).detach()
+    PL = wL / wL.sum(dim=1, keepdim=True)
+    return PL + (PN - PL).detach()
+
+
+def row_grad(s, g, calib, recon, ste, grad, K, tau=8.0):
+    """Single row: returns (P, dS) as float64 tensors."""
+    s = torch.as_tensor(s, dtype=torch.float64).reshape(1, -1).clone().requires_grad_(True)
+    g = torch.as_tensor(g, dtype=torch.float64).reshape(1, -1)
+    mask = torch.ones_like(s, dtype=torch.bool)
+    P = row_probs(s, mask, calib, recon, ste, grad, K, tau)
+    (P * g).sum().backward()
+    return P.detach()[0], s.grad[0]
+
+
+def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, scale=None):
+    """One head, materialized T x T in float64: returns O, dQ, dK, dV."""
+    Q = torch.as_tensor(Q, dtype=torch.float64).clone().requires_grad_(True)
+    Kt = torch.as_tensor(K_, dtype=torch.float64).clone().requires_grad_(True)
+    V = torch.as_tensor(V, dtype=torch.float64).clone().requires_grad_(True)
+    dO = torch.as_tensor(dO, dtype=torch.float64)
+    T, D = Q.shape
+    c = (1.0 / D ** 0.5) if scale is None else scale
+    S = c * (Q @ Kt.T)
+    mask = torch.ones(T, T, dtype=torch.bool)
+    if causal:
+        mask = torch.tril(mask)
+    P = row_probs(S, mask, calib, recon, ste, grad, K, tau)
+    O = P @ V
+    (O * dO).sum().backward()
+    return O.detach(), Q.grad, Kt.grad, V.grad

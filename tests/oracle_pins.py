@@ -1,0 +1,340 @@
+"""Pins of the oracle against what the pages and the mathematics fix.
+
+Each pin takes an oracle configuration (possibly carrying a planted mutation)
+and raises AssertionError when the oracle disagrees with:
+  * float64 torch autograd of the literal forward definitions (independent
+    derivation route for every backward term, including ties);
+  * central finite differences of the oracle's own double forward (LERP, and
+    dV for Nearest);
+  * the zero-sum identity of the full calibration gradient and its violation
+    under detached extrema (App. B, §5.1);
+  * the two-key softmax identity (App. B, Verification);
+  * the interpolation bounds of a chord of exp and the K -> infinity limit;
+  * brute-force nearest grid centre in score coordinates;
+  * shift invariance of the output (and of dQ for the full gradient);
+  * degenerate rows, causal row 0, V = 1, tied extrema, K = 1 affine LERP;
+  * the hand-derived fixtures in tests/golden/.
+Source: "Pretraining Transformers with Quantized Softmax in Attention", §3,
+§5.1, App. A, App. B, App. C.2.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+import autograd_ref as AR
+import golden_io
+from oracle import oracle as ORC
+
+VARIANTS = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest")
+            for s in ("weight", "prob") for g in ("full", "detached")]
+
+
+def cfg_of(calib, recon, ste, grad, K=4, tau=8.0, mutation=None):
+    return ORC.OracleConfig(calib, recon, ste, grad, K, tau, mutation)
+
+
+def _near_boundary(res, cfg, guard=1e-6):
+    u = res["u"]
+    near_int = np.abs(u - np.round(u)) < guard
+    near_half = np.abs(u - (np.floor(u) + 0.5)) < guard
+    interior = (np.round(u) >= 1) & (np.round(u) <= cfg.K - 1)
+    bad = (near_int & interior) | near_half
+    return bool(bad.any())
+
+
+def _random_rows(seed, cfg, count=24):
+    """Random rows (n in 2..40) at several score scales, away from bin boundaries."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    scales = (0.7, 2.5, 6.0) if cfg.calib == "minmax" else (1.0, 3.0, 7.0)
+    tries = 0
+    while len(rows) < count and tries < 10 * count:
+        tries += 1
+        n = int(rng.integers(2, 41))
+        s = rng.standard_normal(n) * scales[len(rows) % 3]
+        g = rng.standard_normal(n)
+        res = ORC.row(dataclasses.replace(cfg, mutation=None), s, g)
+        if _near_boundary(res, cfg):
+            continue
+        if cfg.calib == "fwm" and np.any(np.abs(s - s.max() + cfg.tau) < 1e-6):
+            continue
+        rows.append((s, g))
+    return rows
+
+
+def _close(a, b, rtol, atol, what):
+    a = np.asarray(a, dtype=np.float64); b = np.asarray(b, dtype=np.float64)
+    err = np.abs(a - b)
+    lim = atol + rtol * np.abs(b)
+    if not np.all(err <= lim) or not np.all(np.isfinite(a)):
+        i = int(np.argmax(err - lim))
+        raise AssertionError(f"{what}: max excess at {i}: got {a.flat[i]!r}, want {b.flat[i]!r}")
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_autograd_rows(cfg):
+    for s, g in _random_rows(11, cfg):
+        res = ORC.row(cfg, s, g)
+        P, dS = AR.row_grad(s, g, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau)
+        _close(res["P"], P.numpy(), 1e-12, 1e-14, "row P vs autograd")
+        _close(res["dS"], dS.numpy(), 1e-9, 1e-12, "row dS vs autograd")
+
+
+def pin_autograd_ties(cfg):
+    rng = np.random.default_rng(5)
+    for n in (5, 9, 17):
+        s = rng.standard_normal(n) * 2.0
+        s[1] = s[3] = s.max() + 0.75        # tied maxima
+        s[0] = s[2] = s.min() - 0.4         # tied minima
+        if cfg.calib == "fwm":
+            s[0] = s[2] = s.max() - 0.6 * cfg.tau   # keep both in the window
+        g = rng.standard_normal(n)
+        res = ORC.row(dataclasses.replace(cfg, mutation=None), s, g)
+        if _near_boundary(res, cfg):
+            continue
+        res = ORC.row(cfg, s, g)
+        P, dS = AR.row_grad(s, g, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau)
+        _close(res["P"], P.numpy(), 1e-12, 1e-14, "tied row P vs autograd")
+        _close(res["dS"], dS.numpy(), 1e-9, 1e-12, "tied row dS vs autograd")
+
+
+def _head_inputs(seed, T, D, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((T, D)) * qscale
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    dO = rng.standard_normal((T, D))
+    return Q, K, V, dO
+
+
+def pin_autograd_head(cfg):
+    for seed, T, D, causal, qs in ((1, 24, 8, True, 1.5), (2, 10, 6, False, 3.0), (3, 33, 4, True, 4.0)):
+        Q, K, V, dO = _head_inputs(seed, T, D, qs)
+        res = ORC.head(cfg, Q, K, V, dO, causal=causal, nthreads=2)
+        O, dQ, dK, dV = AR.head_grad(Q, K, V, dO, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau,
+                                     causal=causal)
+        _close(res["O"], O.numpy(), 1e-11, 1e-13, "head O vs autograd")
+        _close(res["dV"], dV.numpy(), 1e-10, 1e-12, "head dV vs autograd")
+        _close(res["dQ"], dQ.numpy(), 1e-8, 1e-11, "head dQ vs autograd")
+        _close(res["dK"], dK.numpy(), 1e-8, 1e-11, "head dK vs autograd")
+
+
+def pin_zero_sum(cfg):
+    """Full gradient: every row's score gradient sums to zero; detached: it does not."""
+    nonzero = 0
+    rows = _random_rows(23, cfg)
+    for s, g in rows:
+        res = ORC.row(cfg, s, g)
+        tot, mag = abs(res["dS"].sum()), np.abs(res["dS"]).sum()
+        if cfg.grad == "full":
+            assert tot <= 1e-12 * mag + 1e-300, f"zero-sum violated: {tot} vs {mag}"
+        elif tot > 1e-6 * mag:
+            nonzero += 1
+    if cfg.grad == "detached":
+        assert nonzero >= len(rows) // 2, "detached gradient unexpectedly zero-sum"
+
+
+def pin_two_key(cfg):
+    """MinMax with two keys reproduces softmax and, with full gradients, its gradient."""
+    if cfg.calib != "minmax":
+        return
+    rng = np.random.default_rng(7)
+    for _ in range(12):
+        s = rng.standard_normal(2) * 3.0
+        g = rng.standard_normal(2)
+        res = ORC.row(cfg, s, g)
+        e = np.exp(s - s.max())
+        Pe = e / e.sum()
+        _close(res["P"], Pe, 1e-14, 1e-15, "two-key P vs softmax")
+        if cfg.grad == "full":
+            _close(res["dS"], Pe * (g - (Pe * g).sum()), 1e-12, 1e-15, "two-key dS vs softmax gradient")
+
+
+def _weights(res, recon):
+    return res["P"] * (res["WL"] if recon == "lerp" else res["WN"])
+
+
+def pin_reconstruction_bounds(cfg):
+    """LERP is a chord of the convex e^z: above it, by at most h^2/8 e^{z+h};
+    Nearest picks a grid value within h/2 of z in score coordinates."""
+    for s, g in _random_rows(31, cfg):
+        res = ORC.row(cfg, s, g)
+        if res["degenerate"]:
+            continue
+        z = s - res["M"]
+        w = _weights(res, cfg.recon)
+        h = res["h"]
+        tail = z < -cfg.tau if cfg.calib == "fwm" else np.zeros_like(z, dtype=bool)
+        assert np.all(w[tail] == 0.0), "tail weight not zero"
+        win = ~tail
+        if cfg.recon == "lerp":
+            ez = np.exp(z[win])
+            assert np.all(w[win] >= ez * (1 - 1e-12)), "LERP below exp"
+            assert np.all(w[win] - ez <= (h * h / 8.0) * np.exp(z[win] + h) * (1 + 1e-9) + 1e-300), \
+                "LERP chord error above h^2/8 bound"
+        else:
+            assert np.all(np.abs(np.log(w[win]) - z[win]) <= 0.5 * h * (1 + 1e-9) + 1e-12), \
+                "Nearest weight farther than h/2 from e^z"
+
+
+def pin_nearest_brute_force(cfg):
+    """The Nearest index is the grid point closest to z (ties upward), found by brute force."""
+    for s, g in _random_rows(41, cfg):
+        res = ORC.row(cfg, s, g)
+        if res["degenerate"]:
+            continue
+        M, m = s.max(), s.min()
+        K = cfg.K
+        if cfg.calib == "minmax":
+            grid = m + np.arange(K + 1) * (M - m) / K
+        else:
+            grid = M - cfg.tau + np.arange(K + 1) * (cfg.tau / K)
+        for j in range(len(s)):
+            if cfg.calib == "fwm" and s[j] - M < -cfg.tau:
+                continue
+            d = np.abs(s[j] - grid)
+            best = np.flatnonzero(d <= d.min() * (1 + 1e-12) + 1e-15)
+            assert res["ell"][j] == best.max(), f"nearest index {res['ell'][j]} vs brute force {best}"
+
+
+def pin_finite_differences(cfg):
+    """Central differences of the double forward: LERP full gradient in Q, K, V; dV for every variant."""
+    Q, K, V, dO = _head_inputs(13, 12, 6, 2.0)
+    base = ORC.head(cfg, Q, K, V, dO, nthreads=1)
+    clean = ORC.head(dataclasses.replace(cfg, mutation=None), Q, K, V, dO, guard=1e-4, flag_cap=64, nthreads=1)
+    if clean["nflags"]:
+        return
+    rng = np.random.default_rng(3)
+    eps = 1e-6
+
+    def loss(Qx, Kx, Vx):
+        return float((ORC.head(cfg, Qx, Kx, Vx, None, nthreads=1)["O"] * dO).sum())
+
+    targets = [("V", "dV")]
+    if cfg.recon == "lerp" and cfg.grad == "full":
+        targets += [("Q", "dQ"), ("K", "dK")]
+    for name, gname in targets:
+        for _ in range(8):
+            i, k = int(rng.integers(0, 12)), int(rng.integers(0, 6))
+            arrs = {"Q": Q.copy(), "K": K.copy(), "V": V.copy()}
+            arrs[name][i, k] += eps
+            lp = loss(arrs["Q"], arrs["K"], arrs["V"])
+            arrs[name][i, k] -= 2 * eps
+            lm = loss(arrs["Q"], arrs["K"], arrs["V"])
+            fd = (lp - lm) / (2 * eps)
+            an = base[gname][i, k]
+            assert abs(fd - an) <= 2e-7 * max(1.0, abs(an)), f"finite difference {name}[{i},{k}]: {fd} vs {an}"
+
+
+def pin_shift_invariance(cfg):
+    """K_j -> K_j + v adds a per-row constant to the scores: O, dK, dV unchanged;
+    dQ unchanged exactly when the row gradients sum to zero (full mode)."""
+    Q, K, V, dO = _head_inputs(17, 16, 8, 1.5)
+    v = np.random.default_rng(4).standard_normal(8) * 0.5
+    a = ORC.head(cfg, Q, K, V, dO, nthreads=1)
+    b = ORC.head(cfg, Q, K + v, V, dO, nthreads=1)
+    fl = ORC.head(dataclasses.replace(cfg, mutation=None), Q, K, V, dO, guard=1e-6, flag_cap=64, nthreads=1)
+    if fl["nflags"]:
+        return
+    _close(b["O"], a["O"], 1e-10, 1e-12, "O under key shift")
+    _close(b["dV"], a["dV"], 1e-10, 1e-12, "dV under key shift")
+    _close(b["dK"], a["dK"], 1e-8, 1e-11, "dK under key shift")
+    if cfg.grad == "full":
+        _close(b["dQ"], a["dQ"], 1e-8, 1e-11, "dQ under key shift (full)")
+    else:
+        assert np.max(np.abs(b["dQ"] - a["dQ"])) > 1e-8, "detached dQ unexpectedly shift-invariant"
+
+
+def pin_degenerate_and_causal_edges(cfg):
+    """All-equal scores: uniform P; MinMax gradient exactly zero.  Causal row 0 (one
+    key): O_0 = V_0 and dQ_0 = 0.  V = 1 gives O = 1."""
+    for n in (1, 3, 8):
+        s = np.full(n, 0.8125)
+        g = np.random.default_rng(n).standard_normal(n)
+        res = ORC.row(cfg, s, g)
+        _close(res["P"], np.full(n, 1.0 / n), 1e-15, 0.0, "degenerate P")
+        if cfg.calib == "minmax":
+            assert np.all(np.abs(res["dS"]) <= 1e-15), "degenerate MinMax row has a gradient"
+        assert abs(res["dS"].sum()) <= 1e-15 or cfg.grad == "detached", "degenerate row not zero-sum"
+    Q, K, V, dO = _head_inputs(19, 9, 5, 2.0)
+    r = ORC.head(cfg, Q, K, V, dO, nthreads=1)
+    assert np.array_equal(r["O"][0], V[0]), "causal row 0 must return V_0"
+    assert np.all(r["dQ"][0] == 0.0), "causal row 0 has a query gradient"
+    r1 = ORC.head(cfg, Q, K, np.ones_like(V), dO, nthreads=1)
+    _close(r1["O"], np.ones_like(V), 1e-14, 0.0, "V = 1 must give O = 1")
+
+
+def pin_special_cases(cfg):
+    """w at the argmax is e^0 = 1; MinMax w at the argmin is e^{m-M}; sum P = 1;
+    the STE flag does not change LERP; K = 1 LERP is affine in s."""
+    for s, g in _random_rows(53, cfg, count=10):
+        res = ORC.row(cfg, s, g)
+        w = _weights(res, cfg.recon)
+        assert abs(res["P"].sum() - 1.0) <= 1e-14, "probabilities do not sum to 1"
+        assert abs(w[res["amax"]] - 1.0) <= 1e-14, "weight at the argmax is not 1"
+        if cfg.calib == "minmax":
+            assert abs(w[res["amin"]] - math.exp(res["m"] - res["M"])) <= 1e-14, "weight at the argmin"
+        if cfg.recon == "lerp":
+            other = dataclasses.replace(cfg, ste="weight" if cfg.ste == "prob" else "prob")
+            assert np.array_equal(ORC.row(other, s, g)["dS"], res["dS"]), "STE flag changed LERP"
+    if cfg.calib == "minmax" and cfg.recon == "lerp":
+        c1 = dataclasses.replace(cfg, K=1)
+        s = np.random.default_rng(2).standard_normal(15) * 2.0
+        res = ORC.row(c1, s)
+        M, m = s.max(), s.min()
+        want = math.exp(m - M) + (s - m) / (M - m) * (1.0 - math.exp(m - M))
+        _close(res["P"] * res["WL"], want, 1e-13, 1e-15, "K=1 LERP is affine in s")
+
+
+def pin_k_limit(cfg):
+    """LERP -> softmax as K grows: forward error O(h^2), gradient error O(h) (full)."""
+    if cfg.recon != "lerp":
+        return
+    rng = np.random.default_rng(61)
+    s = rng.standard_normal(48) * 2.0
+    g = rng.standard_normal(48)
+    e = np.exp(s - s.max()); Pe = e / e.sum()
+    dSe = Pe * (g - (Pe * g).sum())
+    tau = float(s.max() - s.min() + 1.0)
+    errs, gerrs = [], []
+    for K in (16, 64, 256):
+        res = ORC.row(dataclasses.replace(cfg, K=K, tau=tau), s, g)
+        errs.append(np.max(np.abs(res["P"] - Pe)))
+        gerrs.append(np.max(np.abs(res["dS"] - dSe)))
+    assert errs[2] < errs[0] / 100.0 and errs[2] < 1e-4, f"LERP forward not converging: {errs}"
+    if cfg.grad == "full":
+        assert gerrs[2] < gerrs[0] / 6.0 and gerrs[2] < 5e-3, f"LERP gradient not converging: {gerrs}"
+
+
+def pin_golden(cfg):
+    """Hand-derived fixtures (tests/golden/hand_rows.txt)."""
+    for case in golden_io.load_cases():
+        if case["calib"] != cfg.calib:
+            continue
+        c = dataclasses.replace(cfg, K=int(case["K"]), tau=float(case.get("tau", cfg.tau)))
+        s = np.array(case["s"], dtype=np.float64)
+        g = np.linspace(-1.0, 1.0, len(s))
+        res = ORC.row(c, s, g)
+        name = case["case"]
+        _close(res["u"], case["u"], 0.0, 1e-15, f"{name}: u")
+        assert list(res["r"]) == [int(x) for x in case["r"]], f"{name}: r"
+        _close(res["t"], case["t"], 0.0, 1e-15, f"{name}: t")
+        assert list(res["tail"].astype(int)) == [int(x) for x in case["tail"]], f"{name}: tail"
+        if c.recon == "nearest":
+            assert list(res["ell"]) == [int(x) for x in case["ell"]], f"{name}: ell"
+        w = np.array(case["wL" if c.recon == "lerp" else "wN"])
+        _close(res["P"], w / w.sum(), 1e-14, 1e-16, f"{name}: P")
+        for key in ("M", "m", "h"):
+            assert abs(res[key] - case[key]) <= 1e-15, f"{name}: {key}"
+        for key in ("nA", "nC", "degenerate"):
+            assert res[key] == int(case[key]), f"{name}: {key}"
+
+
+PINS = [pin_golden, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_two_key,
+        pin_reconstruction_bounds, pin_nearest_brute_force, pin_finite_differences, pin_shift_invariance,
+        pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit]
