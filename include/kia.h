@@ -1,0 +1,139 @@
+/*
+ * kia.h -- C ABI of the K-interval attention library (libkia.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operator is the one defined in "Pretraining Transformers with Quantized
+ * Softmax in Attention" (Zhu, Hu, Kozlowski), §3 and App. A-C.  For one causal
+ * row of scores s_j = scale * Q_i . K_j (j <= i), a per-row calibration places
+ * K+1 grid values e^{b_r}:
+ *   MinMax (§3 "Objects and calibration"): h = (M-m)/K, b_r = (1-r/K)(m-M),
+ *     with the row maximum M and minimum m; rows with M - m <= 1e-12 use the
+ *     safe width h = 1 (App. A "Edge cases and conventions");
+ *   FWM: h = tau/K, b_r = -tau + r h, the score shifted by M is clipped to
+ *     [-tau, 0] and keys below the window get weight 0.
+ * Each key's weight is rebuilt from the grid (§3 "Reconstruction"): LERP
+ * interpolates between e^{b_r} and e^{b_{r+1}} at the key's local position t;
+ * Nearest takes the grid value of index r + 1[t >= 1/2].  Weights are
+ * normalized, P = w / sum(w), and O = P V.  The forward returns the hard value
+ * P^N exactly for Nearest (App. C.2 (iii), strict forward).
+ * The backward (App. B) applies the normalization Jacobian at the Weight-STE
+ * point (P^N, W^N) or the Prob-STE point (P^L, W^L), the LERP secant slope
+ * Delta_j = (e^{b_{r+1}} - e^{b_r})/h, and, in full mode, the calibration
+ * gradient through the row extrema (split evenly among tied keys) that makes
+ * every row's score gradient sum to zero.  Detached mode drops the extremum
+ * terms (the legacy ablation of §5.1).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors Q, K, V, dO are [B, H, T, D], C-contiguous, in device memory, of
+ *    the dtype given by params->dtype (KIA_F32 or KIA_BF16).  O, dQ, dK, dV are
+ *    float32 [B, H, T, D] for every input dtype.
+ *  - All buffers are owned and allocated by the caller; the library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    the call returns after the launch, without synchronizing.
+ *  - Arguments are checked before any launch; on failure nothing is enqueued,
+ *    a negative status is returned and kia_last_error() describes it.
+ *  - NaN and Inf inputs are not checked; they propagate.
+ *  - Calls that share output or record buffers and overlap on different
+ *    streams race; order them on one stream.
+ */
+#ifndef KIA_H
+#define KIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KIA_OK = 0,
+  KIA_ERR_INVALID_ARG = -1, /* null pointer, bad size or enum value, tau <= 0 under FWM */
+  KIA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
+  KIA_ERR_WORKSPACE = -3,   /* reserved: a buffer smaller than kia_workspace_size asks */
+  KIA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} kia_status_t;
+
+typedef enum { KIA_CALIB_MINMAX = 0, KIA_CALIB_FWM = 1 } kia_calib_t;
+typedef enum { KIA_RECON_LERP = 0, KIA_RECON_NEAREST = 1 } kia_recon_t;
+/* surrogate placement; ignored under LERP (both give the LERP Jacobian) */
+typedef enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 } kia_ste_t;
+/* full calibration gradient, or the detached-extrema ablation */
+typedef enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACHED = 1 } kia_grad_t;
+typedef enum { KIA_F32 = 0, KIA_BF16 = 1 } kia_dtype_t;
+
+typedef struct {
+  int64_t B, H, T, D;   /* batch, heads, sequence length, head dim; T >= 1, D in {64, 128} */
+  int32_t causal;       /* 1: query i sees keys j <= i; 0: every key */
+  int32_t K;            /* number of intervals, 1..64 */
+  float tau;            /* FWM window width in nats (> 0); ignored under MinMax */
+  float scale;          /* score scale; 0 selects 1/sqrt(D) */
+  int32_t calib;        /* kia_calib_t */
+  int32_t recon;        /* kia_recon_t */
+  int32_t ste;          /* kia_ste_t */
+  int32_t grad;         /* kia_grad_t */
+  int32_t dtype;        /* kia_dtype_t of Q, K, V and dO */
+} kia_params_t;
+
+/*
+ * Sizes of the two caller-owned buffers for `p` (host-only, no GPU needed).
+ *  rowrec_bytes: the per-row record written by kia_forward and read by
+ *    kia_backward (row extrema, their first index and tie counts, W^N, W^L,
+ *    and for Nearest with Prob-STE the LERP output O^L).  Layout (offsets are
+ *    multiples of 256 bytes), N = B*H*T:
+ *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N];
+ *      float OL[N*D] (Nearest + Prob-STE only).
+ *  bwd_ws_bytes: scratch for kia_backward (per-row D_i, alpha_i, beta_i).
+ * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
+ * KIA_ERR_UNSUPPORTED for parameters kia_forward would reject.
+ */
+kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, size_t* bwd_ws_bytes);
+
+/*
+ * Forward pass (§3; strict hard forward of App. C.2 (iii) for Nearest).
+ *  q, k, v: device, [B,H,T,D] of params->dtype.
+ *  o:       device float32 [B,H,T,D], written.
+ *  rowrec:  device, rowrec_bytes (kia_workspace_size), written; it must be
+ *           passed unchanged to kia_backward with identical params.
+ * Forwards under KIA_GRAD_FULL and KIA_GRAD_DETACHED are bit-identical.
+ */
+kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                         float* o, void* rowrec, void* stream);
+
+/*
+ * Backward pass (App. B): gradients of L = sum(dO * O) for the operator and
+ * surrogate selected by params.
+ *  q, k, v, d_o: device, [B,H,T,D] of params->dtype; d_o = dL/dO.
+ *  o:       device float32, the output of kia_forward.
+ *  rowrec:  the record written by kia_forward with the same params.
+ *  dq, dk, dv: device float32 [B,H,T,D], written (not accumulated).
+ *  workspace: device, bwd_ws_bytes (kia_workspace_size); contents on entry are ignored.
+ */
+kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                          const float* o, const void* d_o, const void* rowrec,
+                          float* dq, float* dk, float* dv, void* workspace, void* stream);
+
+/*
+ * Test hook: the reconstruction decision of every (query, key) pair as the
+ * kernels take it, for bit-exact comparison of bin decisions.
+ *  bins: device uint8 [B,H,T,T]: for visible keys the Nearest index l in 0..K
+ *        (recon = Nearest) or the interval index r in 0..K-1 (recon = LERP);
+ *        254 for FWM tail keys; 255 for keys the query does not see.
+ *  rowrec: the record written by kia_forward with the same params.
+ * Requires K <= 64 (always true) and costs O(B*H*T*T) bytes; meant for small T.
+ */
+kia_status_t kia_debug_bins(const kia_params_t* p, const void* q, const void* k, const void* rowrec,
+                            uint8_t* bins, void* stream);
+
+/* Static string naming a status code. */
+const char* kia_status_string(kia_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* kia_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIA_H */

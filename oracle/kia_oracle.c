@@ -327,13 +327,15 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
  * O = P V; dQ_i = scale * sum_j dS_ij K_j; dK_j = scale * sum_i dS_ij Q_i;
  * dV_j = sum_i P_ij dO_i.  dO may be NULL (forward only; dQ/dK/dV untouched).
  * flips: nflip triples (row, key, bits).  flags: optional near-boundary report.
+ * bins: optional [T, T] decision map: Nearest index l (Nearest) or interval index r
+ * (LERP) for visible keys, 254 for FWM tail keys, 255 for keys the query does not see.
  */
 int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
             const double *Q, const double *Kt, const double *V, const double *dO,
             double *O, double *dQ, double *dK, double *dV, double *rowd, int32_t *rowi,
             int64_t nflip, const int32_t *flips,
             double guard, int64_t flag_cap, int32_t *flag_pos, double *flag_dist, int64_t *nflags,
-            int nthreads) {
+            uint8_t *bins, int nthreads) {
   if (!cfg || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
   if (dO && !(dQ && dK && dV)) return -1;
   if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
@@ -393,8 +395,22 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
         flip[flips[3 * f + 1]] |= (uint8_t)flips[3 * f + 2];
       }
     }
-    ko_row_impl(cfg, n, s, g, flip, P, dS, Pv, NULL, NULL, NULL, NULL, NULL,
+    double *du = NULL, *dt = NULL;
+    int32_t *dr = NULL, *dl = NULL;
+    uint8_t *dtail = NULL;
+    if (bins) {
+      du = (double *)malloc(sizeof(double) * n); dt = (double *)malloc(sizeof(double) * n);
+      dr = (int32_t *)malloc(sizeof(int32_t) * n); dl = (int32_t *)malloc(sizeof(int32_t) * n);
+      dtail = (uint8_t *)malloc(n);
+    }
+    ko_row_impl(cfg, n, s, g, flip, P, dS, Pv, du, dr, dt, dl, dtail,
                 rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl);
+    if (bins) {
+      for (int j = 0; j < T; ++j) bins[(size_t)i * T + j] = 255;
+      for (int j = 0; j < n && j < T; ++j)
+        bins[(size_t)i * T + j] = dtail[j] ? 254 : (uint8_t)(cfg->recon == KO_NEAREST ? dl[j] : dr[j]);
+      free(du); free(dt); free(dr); free(dl); free(dtail);
+    }
     if (mut == MUT_EXTREMA_ALL_KEYS && causal) {
       /* the planted mistake computed the extrema over all keys; keep the causal output shape */
       double Wsum = 0.0;

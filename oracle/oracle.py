@@ -90,7 +90,7 @@ def _load():
         lib.ko_row.restype = ctypes.c_int
         lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                 dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
-                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, ctypes.c_int]
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, ctypes.c_int]
         lib.ko_head.restype = ctypes.c_int
         assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
         _lib = lib
@@ -135,8 +135,9 @@ def row(cfg: OracleConfig, s, g=None, flip=None):
 
 
 def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=None,
-         guard=0.0, flag_cap=0, nthreads=None):
-    """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags."""
+         guard=0.0, flag_cap=0, bins=False, nthreads=None):
+    """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags
+    (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible)."""
     lib = _load()
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
@@ -152,6 +153,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     fl = np.zeros((0, 3), np.int32) if flips is None else np.ascontiguousarray(flips, dtype=np.int32).reshape(-1, 3)
     fpos = np.zeros((max(flag_cap, 1), 3), np.int32); fdist = np.zeros(max(flag_cap, 1))
     nfl = ctypes.c_int64(0)
+    bmap = np.zeros((T, T), np.uint8) if bins else None
     c = cfg._c()
     rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
                      _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
@@ -159,7 +161,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
                      _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32),
                      fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
                      _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
-                     int(nthreads or default_threads()))
+                     _p(bmap, ctypes.c_uint8), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle head rejected its arguments (rc={rc})")
     nf = int(nfl.value)
@@ -168,7 +170,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     rowd = {k: rd[:, i].copy() for i, k in enumerate(ROWD_FIELDS)}
     rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
     return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
-                flags=fpos[:kept][order], flag_dist=fdist[:kept][order])
+                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap)
 
 
 def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):

@@ -1,0 +1,193 @@
+// C ABI of libkia (declared in include/kia.h): argument checks, buffer layout,
+// dispatch to the gfx950 kernels.
+#include "kia.h"
+#include "kia_launch.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void set_err(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+constexpr size_t ALIGN = 256;
+size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
+  g_err[0] = '\0';
+  if (!p) { set_err("params is NULL"); return KIA_ERR_INVALID_ARG; }
+  if (p->B < 0 || p->H < 0 || p->T < 0) {
+    set_err("B, H, T must be >= 0 (got %lld, %lld, %lld)", (long long)p->B, (long long)p->H, (long long)p->T);
+    return KIA_ERR_INVALID_ARG;
+  }
+  if (p->D < 1) { set_err("D must be >= 1 (got %lld)", (long long)p->D); return KIA_ERR_INVALID_ARG; }
+  if (p->D != 64 && p->D != 128) {
+    set_err("head dim D=%lld is not built (supported: 64, 128)", (long long)p->D);
+    return KIA_ERR_UNSUPPORTED;
+  }
+  if (p->K < 1 || p->K > 64) { set_err("K must be in 1..64 (got %d)", p->K); return KIA_ERR_INVALID_ARG; }
+  if (p->causal != 0 && p->causal != 1) { set_err("causal must be 0 or 1"); return KIA_ERR_INVALID_ARG; }
+  if (p->calib != KIA_CALIB_MINMAX && p->calib != KIA_CALIB_FWM) { set_err("bad calib %d", p->calib); return KIA_ERR_INVALID_ARG; }
+  if (p->recon != KIA_RECON_LERP && p->recon != KIA_RECON_NEAREST) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
+  if (p->ste != KIA_STE_WEIGHT && p->ste != KIA_STE_PROB) { set_err("bad ste %d", p->ste); return KIA_ERR_INVALID_ARG; }
+  if (p->grad != KIA_GRAD_FULL && p->grad != KIA_GRAD_DETACHED) { set_err("bad grad %d", p->grad); return KIA_ERR_INVALID_ARG; }
+  if (p->dtype != KIA_F32 && p->dtype != KIA_BF16) { set_err("bad dtype %d", p->dtype); return KIA_ERR_INVALID_ARG; }
+  if (!std::isfinite(p->scale) || p->scale < 0.f) { set_err("scale must be finite and >= 0"); return KIA_ERR_INVALID_ARG; }
+  if (p->calib == KIA_CALIB_FWM && !(std::isfinite(p->tau) && p->tau > 0.f)) {
+    set_err("FWM needs a finite tau > 0 (got %g)", (double)p->tau);
+    return KIA_ERR_INVALID_ARG;
+  }
+  // index ranges the kernels rely on: per-head offsets in int, grid size in int
+  if (p->T > (1 << 20)) { set_err("T=%lld exceeds 2^20", (long long)p->T); return KIA_ERR_UNSUPPORTED; }
+  const long long heads = (long long)p->B * (long long)p->H;
+  if (p->B > 0 && heads / p->B != p->H) { set_err("B*H overflows"); return KIA_ERR_INVALID_ARG; }
+  if (heads * ((p->T + 31) / 32) > 0x7fffffffLL) { set_err("grid too large"); return KIA_ERR_UNSUPPORTED; }
+  pr->nheads = (int)heads;
+  pr->T = (int)p->T;
+  pr->D = (int)p->D;
+  pr->K = p->K;
+  pr->causal = p->causal;
+  pr->tau = p->tau;
+  pr->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
+  pr->calib = p->calib;
+  pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
+  pr->full = p->grad == KIA_GRAD_FULL;
+  pr->bf16 = p->dtype == KIA_BF16;
+  return KIA_OK;
+}
+
+struct Layout {
+  size_t off[9];
+  size_t rowrec_bytes;
+  size_t ws_off[3];
+  size_t ws_bytes;
+};
+
+Layout layout(const kia::Problem& pr) {
+  Layout L;
+  const size_t N = (size_t)pr.nheads * pr.T;
+  size_t o = 0;
+  for (int i = 0; i < 8; ++i) { L.off[i] = o; o += round_up(N * 4); }
+  L.off[8] = o;
+  if (pr.mode == kia::NEAREST_P) o += round_up(N * pr.D * 4);
+  L.rowrec_bytes = o;
+  o = 0;
+  for (int i = 0; i < 3; ++i) { L.ws_off[i] = o; o += round_up(N * 4); }
+  L.ws_bytes = o;
+  return L;
+}
+
+kia::RowRec carve(const kia::Problem& pr, void* base) {
+  const Layout L = layout(pr);
+  char* b = static_cast<char*>(base);
+  kia::RowRec r;
+  r.M = reinterpret_cast<float*>(b + L.off[0]);
+  r.m = reinterpret_cast<float*>(b + L.off[1]);
+  r.amax = reinterpret_cast<int32_t*>(b + L.off[2]);
+  r.amin = reinterpret_cast<int32_t*>(b + L.off[3]);
+  r.nA = reinterpret_cast<int32_t*>(b + L.off[4]);
+  r.nC = reinterpret_cast<int32_t*>(b + L.off[5]);
+  r.WN = reinterpret_cast<float*>(b + L.off[6]);
+  r.WL = reinterpret_cast<float*>(b + L.off[7]);
+  r.OL = pr.mode == kia::NEAREST_P ? reinterpret_cast<float*>(b + L.off[8]) : nullptr;
+  return r;
+}
+
+kia_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KIA_OK;
+  set_err("%s: %s", what, hipGetErrorString(e));
+  return KIA_ERR_HIP;
+}
+
+bool empty(const kia::Problem& pr) { return pr.nheads == 0 || pr.T == 0; }
+
+}  // namespace
+
+extern "C" {
+
+kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, size_t* bwd_ws_bytes) {
+  kia::Problem pr;
+  kia_status_t st = check_params(p, &pr);
+  if (st != KIA_OK) return st;
+  const Layout L = layout(pr);
+  if (rowrec_bytes) *rowrec_bytes = L.rowrec_bytes;
+  if (bwd_ws_bytes) *bwd_ws_bytes = L.ws_bytes;
+  return KIA_OK;
+}
+
+kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                         float* o, void* rowrec, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = check_params(p, &pr);
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  if (!q || !k || !v || !o || !rowrec) { set_err("kia_forward: null buffer"); return KIA_ERR_INVALID_ARG; }
+  kia::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.rec = carve(pr, rowrec);
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
+  return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
+}
+
+kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                          const float* o, const void* d_o, const void* rowrec,
+                          float* dq, float* dk, float* dv, void* workspace, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = check_params(p, &pr);
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  if (!q || !k || !v || !o || !d_o || !rowrec || !dq || !dk || !dv || !workspace) {
+    set_err("kia_backward: null buffer");
+    return KIA_ERR_INVALID_ARG;
+  }
+  const Layout L = layout(pr);
+  kia::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = d_o;
+  a.rec = carve(pr, const_cast<void*>(rowrec));
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  char* ws = static_cast<char*>(workspace);
+  a.Dvec = reinterpret_cast<float*>(ws + L.ws_off[0]);
+  a.alpha = reinterpret_cast<float*>(ws + L.ws_off[1]);
+  a.beta = reinterpret_cast<float*>(ws + L.ws_off[2]);
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
+  return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream)), "kia_backward launch");
+}
+
+kia_status_t kia_debug_bins(const kia_params_t* p, const void* q, const void* k, const void* rowrec,
+                            uint8_t* bins, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = check_params(p, &pr);
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  if (!q || !k || !rowrec || !bins) { set_err("kia_debug_bins: null buffer"); return KIA_ERR_INVALID_ARG; }
+  kia::BinsArgs a;
+  a.q = q; a.k = k;
+  a.rec = carve(pr, const_cast<void*>(rowrec));
+  a.bins = bins;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
+  return hip_status(kia::launch_bins(pr, a, static_cast<hipStream_t>(stream)), "kia_debug_bins launch");
+}
+
+const char* kia_status_string(kia_status_t s) {
+  switch (s) {
+    case KIA_OK: return "KIA_OK";
+    case KIA_ERR_INVALID_ARG: return "KIA_ERR_INVALID_ARG";
+    case KIA_ERR_UNSUPPORTED: return "KIA_ERR_UNSUPPORTED";
+    case KIA_ERR_WORKSPACE: return "KIA_ERR_WORKSPACE";
+    case KIA_ERR_HIP: return "KIA_ERR_HIP";
+  }
+  return "KIA_ERR_UNKNOWN";
+}
+
+const char* kia_last_error(void) { return g_err; }
+
+}  // extern "C"

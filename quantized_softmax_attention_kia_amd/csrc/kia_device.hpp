@@ -1,0 +1,191 @@
+// Device-side building blocks of the K-interval attention kernels for gfx950.
+//
+// Every kernel computes scores, calibration, grid tables and bin decisions
+// through the functions in this file, with the same instruction sequence, so a
+// score recomputed in the backward is bit-identical to the forward's score and
+// every kernel takes the same bin decisions.
+//
+// Operator: "Pretraining Transformers with Quantized Softmax in Attention",
+// §3 (Objects and calibration; Reconstruction) and App. A (edge cases).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kia_launch.hpp"
+
+namespace kia {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int KMAX = 64;
+constexpr float DEGENERATE_EPS = 1e-12f;
+
+// ---------------------------------------------------------------------------------------------
+// 32x32x2 fp32 MFMA.  Operands: lane l supplies A[l%32][l/32] and B[l/32][l%32].
+// Accumulator: lane l, register v holds C[crow(v, l/32)][l%32].
+__device__ __forceinline__ f16v mfma32(float a, float b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int crow(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
+
+__device__ __forceinline__ f16v zero16() {
+  f16v z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Input element types: float32, or bfloat16 stored as raw uint16 bits.
+template <typename T> struct Ld;
+template <> struct Ld<float> {
+  __device__ static f4v four(const float* p) { return *reinterpret_cast<const f4v*>(p); }
+};
+template <> struct Ld<uint16_t> {
+  __device__ static f4v four(const uint16_t* p) {
+    uint2 raw = *reinterpret_cast<const uint2*>(p);
+    f4v r;
+    r[0] = __uint_as_float(raw.x << 16);
+    r[1] = __uint_as_float(raw.x & 0xffff0000u);
+    r[2] = __uint_as_float(raw.y << 16);
+    r[3] = __uint_as_float(raw.y & 0xffff0000u);
+    return r;
+  }
+};
+
+// Dimension order of a score dot product: MFMA step 4q+e takes dims 8q+e (lanes 0-31)
+// and 8q+4+e (lanes 32-63).  A lane's register operand for its own row holds, at index
+// 4q+e, dim 8q + 4(l/32) + e.
+template <int D, typename T>
+__device__ __forceinline__ void load_row_operand(float (&reg)[D / 2], const T* row, bool valid, float mul) {
+  const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    f4v x = valid ? Ld<T>::four(row + 8 * q + 4 * g) : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) reg[4 * q + e] = x[e] * mul;
+  }
+}
+
+// Tile product over the head dimension: C[a][b] = sum_d Arows[a][d] * Brow_b[d], where the
+// A rows (32 of them, stride ld floats) sit in LDS and lane l's register operand holds its
+// own B row (l%32).  Used for S^T = K Q^T, S = Q K^T (bit-identical by operand symmetry of
+// the MFMA) and for the dO V^T products.
+template <int D>
+__device__ __forceinline__ f16v tile_dot(const float* arows, int ld, const float (&breg)[D / 2]) {
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+  const float* row = arows + c * ld + 4 * g;
+  f16v acc = zero16();
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    f4v a = *reinterpret_cast<const f4v*>(row + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma32(a[e], breg[4 * q + e], acc);
+  }
+  return acc;
+}
+
+// out[nb] += sum_v coef[v] * Brows[crow(v, g)][32 nb + l%32]: contracts the 32-long side
+// of an accumulator-layout tile (coef) with 32 LDS rows (stride ld).  Gives O += P V,
+// dQ += dS K, dV += P^T dO and dK += dS^T Q depending on which tile layout coef is in.
+template <int D>
+__device__ __forceinline__ void tile_accum(f16v (&out)[D / 32], const f16v& coef, const float* brows, int ld) {
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float* row = brows + crow(v, g) * ld + c;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) out[nb] = mfma32(coef[v], row[32 * nb], out[nb]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-row calibration (§3 "Objects and calibration"; App. A degenerate branch).
+struct RowCal {
+  float origin;  // score at u = 0: m (MinMax) or M (FWM: u is measured from M - tau)
+  float inv_h;   // 1/h
+  float kappa;   // 1 on the regular MinMax branch (h depends on M, m), 0 on the degenerate one
+};
+
+template <int CAL>
+__device__ __forceinline__ RowCal row_calibration(float M, float m, int K, float tau) {
+  RowCal rc;
+  if (CAL == MINMAX) {
+    const float span = M - m;
+    const bool deg = !(span > DEGENERATE_EPS);
+    const float h = deg ? 1.0f : span / (float)K;
+    rc.origin = m;
+    rc.inv_h = 1.0f / h;
+    rc.kappa = deg ? 0.0f : 1.0f;
+  } else {
+    rc.origin = M;
+    rc.inv_h = (float)K / tau;
+    rc.kappa = 1.0f;
+  }
+  return rc;
+}
+
+// Grid value e^{b_r}: MinMax b_r = (1 - r/K)(m - M); FWM b_r = -tau + r tau/K.
+template <int CAL>
+__device__ __forceinline__ float grid_value(float M, float m, int K, float tau, int r) {
+  float b;
+  if (CAL == MINMAX) b = (1.0f - (float)r / (float)K) * (m - M);
+  else b = -tau + (float)r * (tau / (float)K);
+  return expf(b);
+}
+
+// Bin decision for one score: interval index r in [0, K-1], local position t in [0, 1],
+// and the FWM tail flag (z = s - M < -tau).
+struct Decision {
+  int r;
+  float t;
+  bool tail;
+};
+
+template <int CAL>
+__device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, float tau) {
+  Decision d;
+  float u;
+  if (CAL == MINMAX) {
+    u = (s - rc.origin) * rc.inv_h;
+    d.tail = false;
+  } else {
+    const float z = s - rc.origin;
+    d.tail = z < -tau;
+    u = (fmaxf(z, -tau) + tau) * rc.inv_h;
+  }
+  int r = (int)floorf(u);
+  r = min(max(r, 0), K - 1);
+  d.r = r;
+  d.t = fminf(fmaxf(u - (float)r, 0.0f), 1.0f);
+  return d;
+}
+
+// Reconstructed weights of one key (§3 "Reconstruction"), from the row's grid table.
+struct Weights {
+  float E0, E1;  // e^{b_r}, e^{b_{r+1}}
+  float wL;      // LERP: (1-t) E0 + t E1
+  float wN;      // Nearest: E0 or E1 at index r + 1[t >= 1/2]
+};
+
+__device__ __forceinline__ Weights weights(const Decision& d, const float* trow) {
+  Weights w;
+  w.E0 = trow[d.r];
+  w.E1 = trow[d.r + 1];
+  w.wL = fmaf(d.t, w.E1 - w.E0, w.E0);
+  w.wN = (d.t >= 0.5f) ? w.E1 : w.E0;
+  return w;
+}
+
+// XCD-aware work order: the dispatcher hands consecutive workgroups to the 8 XCDs in turn;
+// this maps them so that each XCD walks a contiguous range of logical tiles (the tiles of
+// the same heads, whose K/V then stay in that XCD's L2).
+__device__ __forceinline__ int logical_block() {
+  const int nb = gridDim.x, b = blockIdx.x;
+  if ((nb & 7) == 0) return (b & 7) * (nb >> 3) + (b >> 3);
+  return b;
+}
+
+}  // namespace kia

@@ -1,0 +1,75 @@
+// Internal interface between the C ABI (kia_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kia {
+
+enum Calib { MINMAX = 0, FWM = 1 };
+// reconstruction and surrogate: LERP; Nearest with the Weight-STE point (P^N, W^N);
+// Nearest with the Prob-STE point (P^L, W^L)
+enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2 };
+
+// Per-row record written by the forward and read by the backward (struct of arrays).
+struct RowRec {
+  float* M;
+  float* m;
+  int32_t* amax;
+  int32_t* amin;
+  int32_t* nA;
+  int32_t* nC;
+  float* WN;
+  float* WL;
+  float* OL;  // [N, D], Nearest + Prob-STE only (else nullptr)
+};
+
+struct Problem {
+  int nheads;   // B * H
+  int T, D, K;
+  int causal;
+  float tau, scale;
+  int calib, mode, full, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  RowRec rec;
+  int T, K, causal;
+  float tau, scale;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;
+  const void* dO;
+  RowRec rec;  // read only
+  float* dq;
+  float* dk;
+  float* dv;
+  float* Dvec;   // [N] sum_j P_j g_j at the surrogate's normalization point
+  float* alpha;  // [N] extremum gradient per tied maximum key
+  float* beta;   // [N] extremum gradient per tied minimum key (MinMax)
+  int T, K, causal;
+  float tau, scale;
+};
+
+struct BinsArgs {
+  const void* q;
+  const void* k;
+  RowRec rec;
+  uint8_t* bins;
+  int T, K, causal;
+  float tau, scale;
+};
+
+hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s);
+
+}  // namespace kia

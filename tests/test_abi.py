@@ -1,0 +1,89 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/kia.h declares, and rejects bad arguments before any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kia.h")
+
+
+@pytest.fixture(scope="module")
+def kb():
+    from quantized_softmax_attention_kia_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kia_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(kb):
+    names = declared_functions()
+    assert set(names) == set(kb.EXPORTS), names
+    lib = ctypes.CDLL(kb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings(kb):
+    for code, name in kb.STATUS.items():
+        assert kb._lib.kia_status_string(code).decode() == name
+
+
+def params(kb, **kw):
+    base = dict(B=2, H=3, T=100, D=64, causal=1, K=4, tau=8.0, scale=0.0, calib=0, recon=0, ste=0, grad=0, dtype=0)
+    base.update(kw)
+    return kb.Params(**base)
+
+
+def ws(kb, p):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = kb._lib.kia_workspace_size(ctypes.byref(p), ctypes.byref(a), ctypes.byref(b))
+    return st, a.value, b.value
+
+
+def test_workspace_layout(kb):
+    N = 2 * 3 * 100
+    rnd = lambda x: (x + 255) // 256 * 256
+    st, rr, w = ws(kb, params(kb))
+    assert st == 0 and rr == 8 * rnd(N * 4) and w == 3 * rnd(N * 4)
+    st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
+    assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4)
+    st, rr, w = ws(kb, params(kb, B=0))
+    assert st == 0 and rr == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(K=0), -1), (dict(K=65), -1), (dict(D=48), -2), (dict(D=0), -1), (dict(T=-1), -1),
+    (dict(calib=1, tau=0.0), -1), (dict(calib=1, tau=float("nan")), -1), (dict(calib=2), -1),
+    (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=3), -1), (dict(dtype=7), -1),
+    (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1),
+])
+def test_rejects_bad_params(kb, bad, status):
+    p = params(kb, **bad)
+    st, _, _ = ws(kb, p)
+    assert st == status
+    assert kb._lib.kia_last_error().decode() != ""
+    # the compute entry points reject the same parameters before any launch
+    assert kb._lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) == status
+
+
+def test_rejects_null_buffers(kb):
+    p = params(kb)
+    assert kb._lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) == -1
+    assert "null" in kb._lib.kia_last_error().decode()
+    assert kb._lib.kia_backward(ctypes.byref(p), *([None] * 11)) == -1
+    assert kb._lib.kia_debug_bins(ctypes.byref(p), None, None, None, None, None) == -1
+
+
+def test_empty_problem_is_ok_without_buffers(kb):
+    for kw in (dict(B=0), dict(H=0), dict(T=0)):
+        p = params(kb, **kw)
+        assert kb._lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) == 0
+        assert kb._lib.kia_backward(ctypes.byref(p), *([None] * 11)) == 0
+    assert kb._lib.kia_forward(None, None, None, None, None, None, None) == -1
