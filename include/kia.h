@@ -78,12 +78,17 @@ typedef struct {
 
 /*
  * Sizes of the two caller-owned buffers for `p` (host-only, no GPU needed).
- *  rowrec_bytes: the per-row record written by kia_forward and read by
- *    kia_backward (row extrema, their first index and tie counts, W^N, W^L,
- *    and for Nearest with Prob-STE the LERP output O^L).  Layout (offsets are
- *    multiples of 256 bytes), N = B*H*T:
+ *  rowrec_bytes: the record written by kia_forward and read by kia_backward:
+ *    per row the extrema, their first index and tie counts, W^N, W^L, for
+ *    Nearest with Prob-STE the LERP output O^L, and the scores themselves.
+ *    Layout (offsets are multiples of 256 bytes), N = B*H*T, nt = ceil(T/32):
  *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N];
- *      float OL[N*D] (Nearest + Prob-STE only).
+ *      float OL[N*D] (Nearest + Prob-STE only);
+ *      float S[B*H][tiles][1024]: the scores s_ij = scale * Q_i . K_j, computed with
+ *        exact products and double accumulation and rounded once to float, in
+ *        32 x 32 tiles (query tile, key tile); tiles = nt(nt+1)/2 when causal
+ *        (key tile <= query tile), nt^2 otherwise.  About 2 T^2 bytes per head
+ *        when causal.
  *  bwd_ws_bytes: scratch for kia_backward (per-row D_i, alpha_i, beta_i).
  * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
  * KIA_ERR_UNSUPPORTED for parameters kia_forward would reject.
@@ -109,22 +114,39 @@ kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, co
  *  rowrec:  the record written by kia_forward with the same params.
  *  dq, dk, dv: device float32 [B,H,T,D], written (not accumulated).
  *  workspace: device, bwd_ws_bytes (kia_workspace_size); contents on entry are ignored.
+ * The backward reads the scores stored in rowrec; it does not recompute them.
  */
 kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
                           const float* o, const void* d_o, const void* rowrec,
                           float* dq, float* dk, float* dv, void* workspace, void* stream);
 
 /*
+ * The two stages of kia_backward, for callers that schedule or time them
+ * separately; kia_backward runs exactly these two in this order.
+ *  kia_backward_dq   (first): writes dq, and per-row D_i, alpha_i, beta_i into
+ *                    `workspace` (the extremum gradient per tied arg-max / arg-min key).
+ *  kia_backward_dkdv (second): reads `workspace` as kia_backward_dq left it and
+ *                    writes dk, dv.  Both on the same stream, dkdv after dq.
+ * Arguments as for kia_backward.
+ */
+kia_status_t kia_backward_dq(const kia_params_t* p, const void* q, const void* k, const void* v,
+                             const float* o, const void* d_o, const void* rowrec, float* dq,
+                             void* workspace, void* stream);
+kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void* k, const void* v,
+                               const void* d_o, const void* rowrec, float* dk, float* dv,
+                               void* workspace, void* stream);
+
+/*
  * Test hook: the reconstruction decision of every (query, key) pair as the
  * kernels take it, for bit-exact comparison of bin decisions.
+ *  rowrec: the record written by kia_forward with the same params (its stored
+ *        scores and row extrema decide the bins).
  *  bins: device uint8 [B,H,T,T]: for visible keys the Nearest index l in 0..K
  *        (recon = Nearest) or the interval index r in 0..K-1 (recon = LERP);
  *        254 for FWM tail keys; 255 for keys the query does not see.
- *  rowrec: the record written by kia_forward with the same params.
- * Requires K <= 64 (always true) and costs O(B*H*T*T) bytes; meant for small T.
+ * Costs O(B*H*T*T) bytes; meant for small T.
  */
-kia_status_t kia_debug_bins(const kia_params_t* p, const void* q, const void* k, const void* rowrec,
-                            uint8_t* bins, void* stream);
+kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream);
 
 /* Static string naming a status code. */
 const char* kia_status_string(kia_status_t status);

@@ -40,6 +40,12 @@
  * this is how a test checks that a result computed in fp32 is one of the
  * answers that are correct within the boundary guard.
  *
+ * Near-boundary positions are those within `guard` (in units of the interval
+ * width) of a boundary, or within the distance that representing the scores in
+ * fp32 (the operator's precision) can move u: a score rounded to fp32 moves by
+ * at most one unit in its last place, 2^-23 |s|, and u inherits that change in s
+ * and in the row extrema it is measured from.
+ *
  * Mutations: cfg.mutation != 0 plants one known mistake; tests use this to
  * show that the pins catch such mistakes.  Zero in every other use.
  */
@@ -86,9 +92,9 @@ typedef struct {
 } ko_cfg_t;
 
 /* per-row record: doubles */
-enum { RD_M = 0, RD_m, RD_h, RD_WL, RD_WN, RD_a, RD_b, RD_gapM, RD_gapm, RD_D, RD_N };
+enum { RD_M = 0, RD_m, RD_h, RD_WL, RD_WN, RD_a, RD_b, RD_gapM, RD_gapm, RD_D, RD_tolM, RD_tolm, RD_N };
 /* per-row record: ints */
-enum { RI_amax = 0, RI_amin, RI_nA, RI_nC, RI_degenerate, RI_N };
+enum { RI_amax = 0, RI_amin, RI_nA, RI_nC, RI_degenerate, RI_amax2, RI_amin2, RI_N };
 
 #define DEGENERATE_EPS 1e-12
 
@@ -125,7 +131,8 @@ static void flag_push(ko_flags_t *f, int row, int key, int kind, double dist) {
 static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const double *g,
                         const uint8_t *flip, double *P, double *dS, double *PL_out,
                         double *u_out, int32_t *r_out, double *t_out, int32_t *ell_out, uint8_t *tail_out,
-                        double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags) {
+                        double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags,
+                        const double *eb) {
   const int K = cfg->K;
   const int mut = cfg->mutation;
   double *E = (double *)malloc(sizeof(double) * (K + 1));
@@ -149,10 +156,13 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
   }
   int amax = -1, amin = -1, nA = 0, nC = 0;
   double belowM = -INFINITY, abovem = INFINITY;
+  int ibelowM = -1, iabovem = -1;
   for (int j = 0; j < n; ++j) {
-    if (s[j] == M) { if (amax < 0) amax = j; nA++; } else if (s[j] > belowM) belowM = s[j];
-    if (s[j] == m) { if (amin < 0) amin = j; nC++; } else if (s[j] < abovem) abovem = s[j];
+    if (s[j] == M) { if (amax < 0) amax = j; nA++; } else if (s[j] > belowM) { belowM = s[j]; ibelowM = j; }
+    if (s[j] == m) { if (amin < 0) amin = j; nC++; } else if (s[j] < abovem) { abovem = s[j]; iabovem = j; }
   }
+  /* rounding-error bounds of the extrema (0 without eb) */
+  const double ebM = eb ? eb[amax] : 0.0, ebm = eb ? eb[amin] : 0.0;
   double h;
   int degenerate = 0;
   if (cfg->calib == KO_MINMAX) {
@@ -181,15 +191,21 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
       tj = (mut == MUT_TAIL_INCLUSIVE) ? (z <= -cfg->tau) : (z < -cfg->tau);
       double zc = z < -cfg->tau ? -cfg->tau : (z > 0.0 ? 0.0 : z);   /* clip(z, -tau, 0) */
       uj = (zc + cfg->tau) / h;
-      if (flags && fabs(z + cfg->tau) / h < flags->guard)
-        flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_TAIL, fabs(z + cfg->tau) / h);
     }
     if (flags) {
+      /* guard in u units: the stated guard, or the rounding bound of u if larger */
+      double gj = flags->guard;
+      if (eb) {
+        double eu = (cfg->calib == KO_MINMAX) ? (eb[j] + 2.0 * ebm + ebM) / h : (eb[j] + ebM) / h;
+        if (eu > gj) gj = eu;
+      }
+      if (cfg->calib == KO_FWM && fabs(s[j] - M + cfg->tau) / h < gj)
+        flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_TAIL, fabs(s[j] - M + cfg->tau) / h);
       double kint = floor(uj + 0.5);
-      if (K >= 2 && kint >= 1 && kint <= K - 1 && fabs(uj - kint) < flags->guard)
+      if (K >= 2 && kint >= 1 && kint <= K - 1 && fabs(uj - kint) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_INTERVAL, fabs(uj - kint));
       double khalf = floor(uj) + 0.5;
-      if (cfg->recon == KO_NEAREST && khalf < K && fabs(uj - khalf) < flags->guard)
+      if (cfg->recon == KO_NEAREST && khalf < K && fabs(uj - khalf) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_NEAREST, fabs(uj - khalf));
     }
     int rj = (mut == MUT_INTERVAL_ROUND) ? (int)floor(uj + 0.5) : (int)floor(uj);
@@ -303,9 +319,12 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
   if (rowd) {
     rowd[RD_M] = M; rowd[RD_m] = m; rowd[RD_h] = h; rowd[RD_WL] = WL; rowd[RD_WN] = WN;
     rowd[RD_a] = a; rowd[RD_b] = b; rowd[RD_gapM] = M - belowM; rowd[RD_gapm] = abovem - m; rowd[RD_D] = Dsum;
+    rowd[RD_tolM] = eb ? ebM + (ibelowM >= 0 ? eb[ibelowM] : 0.0) : 0.0;
+    rowd[RD_tolm] = eb ? ebm + (iabovem >= 0 ? eb[iabovem] : 0.0) : 0.0;
   }
   if (rowi) {
     rowi[RI_amax] = amax; rowi[RI_amin] = amin; rowi[RI_nA] = nA; rowi[RI_nC] = nC; rowi[RI_degenerate] = degenerate;
+    rowi[RI_amax2] = ibelowM; rowi[RI_amin2] = iabovem;   /* runner-up keys (-1 if none) */
   }
   free(E); free(bgrid); free(u); free(t); free(wL); free(wN); free(Delta); free(gam); free(r); free(ell); free(tail);
 }
@@ -317,7 +336,7 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
   if (!cfg || n < 1 || cfg->K < 1 || !s || !P || (g && !dS)) return -1;
   if (cfg->calib == KO_FWM && !(cfg->tau > 0.0)) return -1;
   if (u && !(r && t && ell && tail)) return -1;
-  ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL);
+  ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL, NULL);
   return 0;
 }
 
@@ -329,13 +348,18 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
  * flips: nflip triples (row, key, bits).  flags: optional near-boundary report.
  * bins: optional [T, T] decision map: Nearest index l (Nearest) or interval index r
  * (LERP) for visible keys, 254 for FWM tail keys, 255 for keys the query does not see.
+ * row_mask: optional [T]; rows with 0 are skipped (their O, dQ rows stay 0 and they
+ * add nothing to dK, dV), so a caller can get the contributions of chosen rows alone.
+ * absout: optional [4, T, D]: the same sums with every term replaced by its absolute
+ * value (sum_j P|V|, scale sum_j |dS||K|, scale sum_i |dS||Q|, sum_i P|dO|), the
+ * scale against which cancellation in an output element is judged.
  */
 int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
             const double *Q, const double *Kt, const double *V, const double *dO,
             double *O, double *dQ, double *dK, double *dV, double *rowd, int32_t *rowi,
             int64_t nflip, const int32_t *flips,
             double guard, int64_t flag_cap, int32_t *flag_pos, double *flag_dist, int64_t *nflags,
-            uint8_t *bins, int nthreads) {
+            uint8_t *bins, const uint8_t *row_mask, double *absout, int nthreads) {
   if (!cfg || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
   if (dO && !(dQ && dK && dV)) return -1;
   if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
@@ -355,17 +379,25 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
   }
   /* thread-private dK, dV accumulators, summed in thread order at the end */
   double *accK = NULL, *accV = NULL;
+  double *absK = NULL, *absV = NULL;
   if (dO) {
     accK = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
     accV = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
     if (!accK || !accV) { free(accK); free(accV); return -2; }
+    if (absout) {
+      absK = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
+      absV = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
+      if (!absK || !absV) { free(accK); free(accV); free(absK); free(absV); return -2; }
+    }
   }
+  if (absout) memset(absout, 0, sizeof(double) * 4 * (size_t)T * D);
   const double dq_scale = (mut == MUT_DQ_NO_SCALE) ? 1.0 : scale;
 
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
 #endif
   for (int i = 0; i < T; ++i) {
+    if (row_mask && !row_mask[i]) continue;
     int tid = 0;
 #ifdef _OPENMP
     tid = omp_get_thread_num();
@@ -377,12 +409,18 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
     double *Pv = (double *)malloc(sizeof(double) * n);
     double *dS = dO ? (double *)malloc(sizeof(double) * n) : NULL;
     int32_t *kid = (int32_t *)malloc(sizeof(int32_t) * n);
+    double *eb = (double *)malloc(sizeof(double) * n);
     uint8_t *flip = NULL;
     for (int j = 0; j < n; ++j) {
       kid[j] = j;
-      double acc = 0.0;
-      for (int k = 0; k < D; ++k) acc += Q[(size_t)i * D + k] * Kt[(size_t)j * D + k];
+      double acc = 0.0, aabs = 0.0;
+      for (int k = 0; k < D; ++k) {
+        acc += Q[(size_t)i * D + k] * Kt[(size_t)j * D + k];
+        aabs += fabs(Q[(size_t)i * D + k] * Kt[(size_t)j * D + k]);
+      }
       s[j] = scale * acc;
+      /* one fp32 ulp of the score, 2^-23 |s|, plus the double accumulation's own bound */
+      eb[j] = 1.1920928955078125e-07 * fabs(s[j]) + 1e-15 * fabs(scale) * aabs;
       if (dO) {
         double ga = 0.0;
         for (int k = 0; k < D; ++k) ga += dO[(size_t)i * D + k] * V[(size_t)j * D + k];
@@ -404,7 +442,7 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
       dtail = (uint8_t *)malloc(n);
     }
     ko_row_impl(cfg, n, s, g, flip, P, dS, Pv, du, dr, dt, dl, dtail,
-                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl);
+                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl, eb);
     if (bins) {
       for (int j = 0; j < T; ++j) bins[(size_t)i * T + j] = 255;
       for (int j = 0; j < n && j < T; ++j)
@@ -421,6 +459,9 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
     /* O_i = sum_j P_ij V_j */
     for (int j = 0; j < n; ++j)
       for (int k = 0; k < D; ++k) O[(size_t)i * D + k] += P[j] * V[(size_t)j * D + k];
+    if (absout)
+      for (int j = 0; j < n; ++j)
+        for (int k = 0; k < D; ++k) absout[(size_t)i * D + k] += P[j] * fabs(V[(size_t)j * D + k]);
     if (dO) {
       double *aK = accK + (size_t)tid * T * D, *aV = accV + (size_t)tid * T * D;
       for (int j = 0; j < n; ++j) {
@@ -431,8 +472,18 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
           aV[(size_t)j * D + k] += Pv[j] * dO[(size_t)i * D + k];
         }
       }
+      if (absout) {
+        double *bK = absK + (size_t)tid * T * D, *bV = absV + (size_t)tid * T * D;
+        double *bQ = absout + (size_t)T * D;
+        for (int j = 0; j < n; ++j)
+          for (int k = 0; k < D; ++k) {
+            bQ[(size_t)i * D + k] += fabs(scale * dS[j] * Kt[(size_t)j * D + k]);
+            bK[(size_t)j * D + k] += fabs(scale * dS[j] * Q[(size_t)i * D + k]);
+            bV[(size_t)j * D + k] += fabs(Pv[j] * dO[(size_t)i * D + k]);
+          }
+      }
     }
-    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip);
+    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip); free(eb);
   }
   if (dO) {
     for (int th = 0; th < nthreads; ++th)
@@ -440,7 +491,14 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
         dK[x] += accK[(size_t)th * T * D + x];
         dV[x] += accV[(size_t)th * T * D + x];
       }
-    free(accK); free(accV);
+    if (absout) {
+      for (int th = 0; th < nthreads; ++th)
+        for (size_t x = 0; x < (size_t)T * D; ++x) {
+          absout[2 * (size_t)T * D + x] += absK[(size_t)th * T * D + x];
+          absout[3 * (size_t)T * D + x] += absV[(size_t)th * T * D + x];
+        }
+    }
+    free(accK); free(accV); free(absK); free(absV);
   }
   if (nflags) *nflags = fl ? fl->count : 0;
   return 0;

@@ -35,8 +35,8 @@ MUTATIONS = {
     "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
     "x_index": 17, "detach_keeps_m": 18,
 }
-ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D")
-ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate")
+ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
+ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")
 
 
 def build(force: bool = False) -> str:
@@ -90,7 +90,7 @@ def _load():
         lib.ko_row.restype = ctypes.c_int
         lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                 dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
-                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, ctypes.c_int]
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up, dp, ctypes.c_int]
         lib.ko_head.restype = ctypes.c_int
         assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
         _lib = lib
@@ -135,9 +135,11 @@ def row(cfg: OracleConfig, s, g=None, flip=None):
 
 
 def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=None,
-         guard=0.0, flag_cap=0, bins=False, nthreads=None):
+         guard=0.0, flag_cap=0, bins=False, rows=None, absolute=False, nthreads=None):
     """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags
-    (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible)."""
+    (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible).
+    rows: optional list of row indices; only those rows are computed (their contributions alone).
+    absolute: also return abs = {O, dQ, dK, dV}: the same sums of absolute values of the terms."""
     lib = _load()
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
@@ -154,6 +156,11 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     fpos = np.zeros((max(flag_cap, 1), 3), np.int32); fdist = np.zeros(max(flag_cap, 1))
     nfl = ctypes.c_int64(0)
     bmap = np.zeros((T, T), np.uint8) if bins else None
+    rmask = None
+    if rows is not None:
+        rmask = np.zeros(T, np.uint8)
+        rmask[np.asarray(list(rows), dtype=np.int64)] = 1
+    aout = np.zeros((4, T, D)) if absolute else None
     c = cfg._c()
     rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
                      _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
@@ -161,7 +168,8 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
                      _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32),
                      fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
                      _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
-                     _p(bmap, ctypes.c_uint8), int(nthreads or default_threads()))
+                     _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), _p(aout, ctypes.c_double),
+                     int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle head rejected its arguments (rc={rc})")
     nf = int(nfl.value)
@@ -170,7 +178,8 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     rowd = {k: rd[:, i].copy() for i, k in enumerate(ROWD_FIELDS)}
     rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
     return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
-                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap)
+                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap,
+                abs=None if aout is None else dict(O=aout[0], dQ=aout[1], dK=aout[2], dV=aout[3]))
 
 
 def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):

@@ -40,8 +40,8 @@ class Params(ctypes.Structure):
                 ("ste", ctypes.c_int32), ("grad", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
-EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_debug_bins", "kia_status_string",
-           "kia_last_error")
+EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
+           "kia_debug_bins", "kia_status_string", "kia_last_error")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -53,8 +53,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kia_workspace_size.argtypes = [P, sz, sz]
     lib.kia_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.kia_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.kia_debug_bins.argtypes = [P, vp, vp, vp, vp, vp]
-    for f in ("kia_workspace_size", "kia_forward", "kia_backward", "kia_debug_bins"):
+    lib.kia_backward_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kia_backward_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kia_debug_bins.argtypes = [P, vp, vp, vp]
+    for f in ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
+              "kia_debug_bins"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kia_status_string.argtypes = [ctypes.c_int]
     lib.kia_status_string.restype = ctypes.c_char_p
@@ -130,9 +133,20 @@ def kia_backward(p: Params, q, k, v, o, d_o, rowrec, dq, dk, dv, workspace, stre
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
 
 
-def kia_debug_bins(p: Params, q, k, rowrec, bins, stream=None) -> None:
-    _check_inputs(p, q, k)
-    _check(_lib.kia_debug_bins(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(rowrec), _ptr(bins), _stream(stream)))
+def kia_backward_dq(p: Params, q, k, v, o, d_o, rowrec, dq, workspace, stream=None) -> None:
+    _check_inputs(p, q, k, v, d_o)
+    _check(_lib.kia_backward_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowrec),
+                                _ptr(dq), _ptr(workspace), _stream(stream)))
+
+
+def kia_backward_dkdv(p: Params, q, k, v, d_o, rowrec, dk, dv, workspace, stream=None) -> None:
+    _check_inputs(p, q, k, v, d_o)
+    _check(_lib.kia_backward_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(rowrec),
+                                  _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
+
+
+def kia_debug_bins(p: Params, rowrec, bins, stream=None) -> None:
+    _check(_lib.kia_debug_bins(ctypes.byref(p), _ptr(rowrec), _ptr(bins), _stream(stream)))
 
 
 # ------------------------------------------------------------------ tensor-level convenience
@@ -158,9 +172,9 @@ def backward(p: Params, q, k, v, o, d_o, rowrec, stream=None):
     return dq, dk, dv
 
 
-def debug_bins(p: Params, q, k, rowrec, stream=None):
-    bins = torch.empty((p.B, p.H, p.T, p.T), device=q.device, dtype=torch.uint8)
-    kia_debug_bins(p, q, k, rowrec, bins, stream)
+def debug_bins(p: Params, rowrec, stream=None):
+    bins = torch.empty((p.B, p.H, p.T, p.T), device=rowrec.device, dtype=torch.uint8)
+    kia_debug_bins(p, rowrec, bins, stream)
     return bins
 
 

@@ -57,7 +57,7 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   pr->K = p->K;
   pr->causal = p->causal;
   pr->tau = p->tau;
-  pr->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->D);
+  pr->scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
   pr->calib = p->calib;
   pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
   pr->full = p->grad == KIA_GRAD_FULL;
@@ -66,8 +66,10 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
 }
 
 struct Layout {
-  size_t off[9];
+  size_t off[10];
   size_t rowrec_bytes;
+  int nt;
+  size_t tiles_per_head;
   size_t ws_off[3];
   size_t ws_bytes;
 };
@@ -79,6 +81,10 @@ Layout layout(const kia::Problem& pr) {
   for (int i = 0; i < 8; ++i) { L.off[i] = o; o += round_up(N * 4); }
   L.off[8] = o;
   if (pr.mode == kia::NEAREST_P) o += round_up(N * pr.D * 4);
+  L.nt = (pr.T + 31) / 32;
+  L.tiles_per_head = pr.causal ? (size_t)L.nt * (L.nt + 1) / 2 : (size_t)L.nt * L.nt;
+  L.off[9] = o;
+  o += (size_t)pr.nheads * L.tiles_per_head * 1024 * 4;
   L.rowrec_bytes = o;
   o = 0;
   for (int i = 0; i < 3; ++i) { L.ws_off[i] = o; o += round_up(N * 4); }
@@ -99,6 +105,9 @@ kia::RowRec carve(const kia::Problem& pr, void* base) {
   r.WN = reinterpret_cast<float*>(b + L.off[6]);
   r.WL = reinterpret_cast<float*>(b + L.off[7]);
   r.OL = pr.mode == kia::NEAREST_P ? reinterpret_cast<float*>(b + L.off[8]) : nullptr;
+  r.S = reinterpret_cast<float*>(b + L.off[9]);
+  r.nt = L.nt;
+  r.tiles_per_head = L.tiles_per_head;
   return r;
 }
 
@@ -138,15 +147,16 @@ kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, co
   return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
 }
 
-kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
-                          const float* o, const void* d_o, const void* rowrec,
-                          float* dq, float* dk, float* dv, void* workspace, void* stream) {
+static kia_status_t backward_stages(const kia_params_t* p, const void* q, const void* k, const void* v,
+                                    const float* o, const void* d_o, const void* rowrec, float* dq, float* dk,
+                                    float* dv, void* workspace, void* stream, int stages, const char* name) {
   kia::Problem pr;
   kia_status_t st = check_params(p, &pr);
   if (st != KIA_OK) return st;
   if (empty(pr)) return KIA_OK;
-  if (!q || !k || !v || !o || !d_o || !rowrec || !dq || !dk || !dv || !workspace) {
-    set_err("kia_backward: null buffer");
+  const bool need_dq = stages & 1, need_kv = stages & 2;
+  if (!q || !k || !v || !d_o || !rowrec || !workspace || (need_dq && (!o || !dq)) || (need_kv && (!dk || !dv))) {
+    set_err("%s: null buffer", name);
     return KIA_ERR_INVALID_ARG;
   }
   const Layout L = layout(pr);
@@ -158,22 +168,39 @@ kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, c
   a.Dvec = reinterpret_cast<float*>(ws + L.ws_off[0]);
   a.alpha = reinterpret_cast<float*>(ws + L.ws_off[1]);
   a.beta = reinterpret_cast<float*>(ws + L.ws_off[2]);
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
-  return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream)), "kia_backward launch");
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale;
+  return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);
 }
 
-kia_status_t kia_debug_bins(const kia_params_t* p, const void* q, const void* k, const void* rowrec,
-                            uint8_t* bins, void* stream) {
+kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                          const float* o, const void* d_o, const void* rowrec,
+                          float* dq, float* dk, float* dv, void* workspace, void* stream) {
+  return backward_stages(p, q, k, v, o, d_o, rowrec, dq, dk, dv, workspace, stream, 3, "kia_backward");
+}
+
+kia_status_t kia_backward_dq(const kia_params_t* p, const void* q, const void* k, const void* v,
+                             const float* o, const void* d_o, const void* rowrec, float* dq,
+                             void* workspace, void* stream) {
+  return backward_stages(p, q, k, v, o, d_o, rowrec, dq, nullptr, nullptr, workspace, stream, 1, "kia_backward_dq");
+}
+
+kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void* k, const void* v,
+                               const void* d_o, const void* rowrec, float* dk, float* dv,
+                               void* workspace, void* stream) {
+  return backward_stages(p, q, k, v, nullptr, d_o, rowrec, nullptr, dk, dv, workspace, stream, 2,
+                         "kia_backward_dkdv");
+}
+
+kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream) {
   kia::Problem pr;
   kia_status_t st = check_params(p, &pr);
   if (st != KIA_OK) return st;
   if (empty(pr)) return KIA_OK;
-  if (!q || !k || !rowrec || !bins) { set_err("kia_debug_bins: null buffer"); return KIA_ERR_INVALID_ARG; }
+  if (!rowrec || !bins) { set_err("kia_debug_bins: null buffer"); return KIA_ERR_INVALID_ARG; }
   kia::BinsArgs a;
-  a.q = q; a.k = k;
   a.rec = carve(pr, const_cast<void*>(rowrec));
   a.bins = bins;
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau;
   return hip_status(kia::launch_bins(pr, a, static_cast<hipStream_t>(stream)), "kia_debug_bins launch");
 }
 

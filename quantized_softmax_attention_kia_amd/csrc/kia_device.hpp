@@ -1,9 +1,11 @@
 // Device-side building blocks of the K-interval attention kernels for gfx950.
 //
-// Every kernel computes scores, calibration, grid tables and bin decisions
-// through the functions in this file, with the same instruction sequence, so a
-// score recomputed in the backward is bit-identical to the forward's score and
-// every kernel takes the same bin decisions.
+// Scores are computed once, in the forward, on the fp64 MFMA (products of fp32
+// inputs are exact in double, the sum is accumulated in double and the scale
+// applied in double) and rounded once to fp32; the forward stores them as
+// 32 x 32 tiles that every later pass reads back.  Calibration, grid tables and
+// bin decisions go through the functions below in every kernel, so all kernels
+// take the same decisions on the same stored scores.
 //
 // Operator: "Pretraining Transformers with Quantized Softmax in Attention",
 // §3 (Objects and calibration; Reconstruction) and App. A (edge cases).
@@ -18,6 +20,7 @@ namespace kia {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef double d4v __attribute__((ext_vector_type(4)));
 
 constexpr int KMAX = 64;
 constexpr float DEGENERATE_EPS = 1e-12f;
@@ -35,6 +38,22 @@ __device__ __forceinline__ f16v zero16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
+}
+
+// 16x16x4 fp64 MFMA.  Operands: lane l supplies A[l%16][l/16] and B[l/16][l%16].
+// Accumulator: lane l, register v holds C[4v + l/16][l%16].
+__device__ __forceinline__ d4v mfma64(double a, double b, d4v c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stored score tiles.  A tile holds the 32 x 32 scores of (query tile qt, key tile kt) in the
+// accumulator order of the fp32 32x32x2 MFMA computing S^T: element (query a, key b) sits at
+// float offset v * 64 + a + 32 g where b = crow(v, g).  So a lane whose query is l%32 reads
+// its 16 scores at offsets v * 64 + l, one coalesced 256-byte load per register.
+// Causal heads store the tiles kt <= qt only.
+__device__ __forceinline__ size_t tile_index(int qt, int kt, int nt, int causal) {
+  return causal ? (size_t)qt * (qt + 1) / 2 + kt : (size_t)qt * nt + kt;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -71,8 +90,7 @@ __device__ __forceinline__ void load_row_operand(float (&reg)[D / 2], const T* r
 
 // Tile product over the head dimension: C[a][b] = sum_d Arows[a][d] * Brow_b[d], where the
 // A rows (32 of them, stride ld floats) sit in LDS and lane l's register operand holds its
-// own B row (l%32).  Used for S^T = K Q^T, S = Q K^T (bit-identical by operand symmetry of
-// the MFMA) and for the dO V^T products.
+// own B row (l%32).  Used for the dO V^T products (g_ij = dO_i . V_j).
 template <int D>
 __device__ __forceinline__ f16v tile_dot(const float* arows, int ld, const float (&breg)[D / 2]) {
   const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
@@ -85,6 +103,37 @@ __device__ __forceinline__ f16v tile_dot(const float* arows, int ld, const float
     for (int e = 0; e < 4; ++e) acc = mfma32(a[e], breg[4 * q + e], acc);
   }
   return acc;
+}
+
+// Scores of one 32 (query) x 32 (key) tile in double: four 16x16 sub-tiles of S^T = K Q^T.
+// K rows (32, stride ld floats) sit in LDS; qr holds the lane's query operand:
+// qr[qb * (D/4) + 4j + e] = Q[16 qb + l%16][16 j + 4 (l/16) + e] (MFMA step 4j + e).
+// acc[kb][qb] register v = sum_d K[16 kb + 4 v + l/16][d] * Q[16 qb + l%16][d], exact products
+// accumulated in double.
+template <int D>
+__device__ __forceinline__ void score_tile_f64(const float* krows, int ld, const float (&qr)[D / 2],
+                                               d4v (&acc)[2][2]) {
+  const int l = threadIdx.x & 63, G = l >> 4, c = l & 15;
+  const float* r0 = krows + c * ld + 4 * G;
+  const float* r1 = krows + (16 + c) * ld + 4 * G;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) acc[kb][qb] = d4v{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const f4v k0 = *reinterpret_cast<const f4v*>(r0 + 16 * j);
+    const f4v k1 = *reinterpret_cast<const f4v*>(r1 + 16 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double a0 = k0[e], a1 = k1[e];
+      const double b0 = qr[4 * j + e], b1 = qr[D / 4 + 4 * j + e];
+      acc[0][0] = mfma64(a0, b0, acc[0][0]);
+      acc[0][1] = mfma64(a0, b1, acc[0][1]);
+      acc[1][0] = mfma64(a1, b0, acc[1][0]);
+      acc[1][1] = mfma64(a1, b1, acc[1][1]);
+    }
+  }
 }
 
 // out[nb] += sum_v coef[v] * Brows[crow(v, g)][32 nb + l%32]: contracts the 32-long side
@@ -102,38 +151,43 @@ __device__ __forceinline__ void tile_accum(f16v (&out)[D / 32], const f16v& coef
 }
 
 // ---------------------------------------------------------------------------------------------
-// Per-row calibration (§3 "Objects and calibration"; App. A degenerate branch).
+// Per-row calibration (§3 "Objects and calibration"; App. A degenerate branch).  The position
+// u of a key is formed in double from its stored fp32 score: with K up to 64, u reaches K and
+// an fp32 u would lose the low bits of the local position t.
 struct RowCal {
-  float origin;  // score at u = 0: m (MinMax) or M (FWM: u is measured from M - tau)
-  float inv_h;   // 1/h
-  float kappa;   // 1 on the regular MinMax branch (h depends on M, m), 0 on the degenerate one
+  double origin;  // score at u = 0: m (MinMax) or M (FWM: u is measured from M - tau)
+  double inv_h;   // 1/h
+  float inv_hf;   // 1/h rounded to float (secant slopes)
+  float kappa;    // 1 on the regular MinMax branch (h depends on M, m), 0 on the degenerate one
 };
 
 template <int CAL>
 __device__ __forceinline__ RowCal row_calibration(float M, float m, int K, float tau) {
   RowCal rc;
   if (CAL == MINMAX) {
-    const float span = M - m;
-    const bool deg = !(span > DEGENERATE_EPS);
-    const float h = deg ? 1.0f : span / (float)K;
-    rc.origin = m;
-    rc.inv_h = 1.0f / h;
+    const double span = (double)M - (double)m;
+    const bool deg = !(span > (double)DEGENERATE_EPS);
+    const double h = deg ? 1.0 : span / (double)K;
+    rc.origin = (double)m;
+    rc.inv_h = 1.0 / h;
     rc.kappa = deg ? 0.0f : 1.0f;
   } else {
-    rc.origin = M;
-    rc.inv_h = (float)K / tau;
+    rc.origin = (double)M;
+    rc.inv_h = (double)K / (double)tau;
     rc.kappa = 1.0f;
   }
+  rc.inv_hf = (float)rc.inv_h;
   return rc;
 }
 
-// Grid value e^{b_r}: MinMax b_r = (1 - r/K)(m - M); FWM b_r = -tau + r tau/K.
+// Grid value e^{b_r} (exponent and exponential in double, rounded to float):
+// MinMax b_r = (1 - r/K)(m - M); FWM b_r = -tau + r tau/K.
 template <int CAL>
 __device__ __forceinline__ float grid_value(float M, float m, int K, float tau, int r) {
-  float b;
-  if (CAL == MINMAX) b = (1.0f - (float)r / (float)K) * (m - M);
-  else b = -tau + (float)r * (tau / (float)K);
-  return expf(b);
+  double b;
+  if (CAL == MINMAX) b = (1.0 - (double)r / (double)K) * ((double)m - (double)M);
+  else b = -(double)tau + (double)r * ((double)tau / (double)K);
+  return (float)exp(b);
 }
 
 // Bin decision for one score: interval index r in [0, K-1], local position t in [0, 1],
@@ -147,19 +201,19 @@ struct Decision {
 template <int CAL>
 __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, float tau) {
   Decision d;
-  float u;
+  double u;
   if (CAL == MINMAX) {
-    u = (s - rc.origin) * rc.inv_h;
+    u = ((double)s - rc.origin) * rc.inv_h;
     d.tail = false;
   } else {
-    const float z = s - rc.origin;
-    d.tail = z < -tau;
-    u = (fmaxf(z, -tau) + tau) * rc.inv_h;
+    const double z = (double)s - rc.origin;
+    d.tail = z < -(double)tau;
+    u = (fmax(z, -(double)tau) + (double)tau) * rc.inv_h;
   }
-  int r = (int)floorf(u);
+  int r = (int)floor(u);
   r = min(max(r, 0), K - 1);
   d.r = r;
-  d.t = fminf(fmaxf(u - (float)r, 0.0f), 1.0f);
+  d.t = (float)fmin(fmax(u - (double)r, 0.0), 1.0);
   return d;
 }
 

@@ -4,14 +4,20 @@
 // of a row depends on the row's final extrema, so the online-softmax rescale
 // does not apply.  One workgroup owns 128 query rows of one head (4 waves x 32
 // rows) and sweeps the visible key tiles twice:
-//   pass 1  S^T = K Q^T on the fp32 MFMA -> row max / min, first arg, tie counts;
+//   pass 1  scores of each 32 x 32 tile on the fp64 MFMA (exact products of the
+//           fp32 inputs, double accumulation, scale applied in double), rounded
+//           once to fp32 and stored for every later pass; row max / min, first
+//           index attaining them and tie counts on the stored values;
 //   then    per-row calibration and the (K+1)-entry grid table e^{b_r} in LDS
-//           (the only exponentials of the pass);
-//   pass 2  recompute S^T (same instructions, bit-identical scores) -> bin
-//           decision -> LERP / Nearest weight from the table (no exp) -> row
-//           sums W^L, W^N -> O += w V on the MFMA (and O^L += w^L V for Nearest
-//           with Prob-STE) -> O = num / W (strict hard forward for Nearest).
-// K and V tiles are staged through LDS and shared by the four waves.
+//           (the only exponentials of the operator);
+//   pass 2  stored scores -> bin decision -> LERP / Nearest weight from the
+//           table (no exp) -> row sums W^L, W^N -> O += w V on the fp32 MFMA (and
+//           O^L += w^L V for Nearest with Prob-STE) -> O = num / W (the strict
+//           hard forward for Nearest).  Row sums are kept in double and each
+//           tile's P V is summed into a fresh accumulator before joining the
+//           running O, so the precision of O (which the backward's D_i = dO . O
+//           amplifies) does not decay with T.
+// K (pass 1) and V (pass 2) tiles are staged through LDS and shared by the waves.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
 
@@ -21,10 +27,11 @@ namespace kia {
 
 constexpr int FWD_BM = 128;  // query rows per workgroup
 constexpr int BN = 32;       // keys per tile
+constexpr int SCR = 80;      // row stride of the per-wave tile scratch (bank-conflict free writes)
 
 // Stage 32 rows of a [T, D] head tensor (rows row0..row0+31, zero past T) into LDS.
 template <int D, typename T>
-__device__ __forceinline__ void stage_rows(float* dst, int ld, const T* src, int row0, int nrows, float mul) {
+__device__ __forceinline__ void stage_rows(float* dst, int ld, const T* src, int row0, int nrows) {
   constexpr int CH = BN * D / 4;
 #pragma unroll
   for (int id = threadIdx.x; id < CH; id += 256) {
@@ -32,25 +39,47 @@ __device__ __forceinline__ void stage_rows(float* dst, int ld, const T* src, int
     const int gr = row0 + r;
     f4v x = f4v{0.f, 0.f, 0.f, 0.f};
     if (gr < nrows) x = Ld<T>::four(src + (size_t)gr * D + c4);
-    if (mul != 1.0f) x *= mul;
     *reinterpret_cast<f4v*>(dst + r * ld + c4) = x;
   }
 }
 
 template <int D>
 struct FwdSmem {
-  float Ks[BN * (D + 4)];
-  float Vs[BN * (D + 8)];
-  float tbl[FWD_BM * (KMAX + 1)];
-  float rowW[FWD_BM];
-  float rowWL[FWD_BM];
+  union {
+    float Ks[BN * (D + 4)];  // pass 1
+    float Vs[BN * (D + 8)];  // pass 2
+  };
+  float scratch[4][16 * SCR];  // per-wave tile re-layout (pass 1)
+  float rowM[FWD_BM], rowm[FWD_BM], rowW[FWD_BM], rowWL[FWD_BM];
+  int rowax[FWD_BM], rowan[FWD_BM], rowcx[FWD_BM], rowcn[FWD_BM];
+  // followed in dynamic LDS by the grid table: FWD_BM rows x (K + 1) floats
 };
+
+struct Ext {  // running max / min with first index and count
+  float mx, mn;
+  int ax, an, cx, cn;
+};
+
+__device__ __forceinline__ void ext_merge(Ext& a, int lanemask) {
+  const float mx2 = __shfl_xor(a.mx, lanemask), mn2 = __shfl_xor(a.mn, lanemask);
+  const int ax2 = __shfl_xor(a.ax, lanemask), an2 = __shfl_xor(a.an, lanemask);
+  const int cx2 = __shfl_xor(a.cx, lanemask), cn2 = __shfl_xor(a.cn, lanemask);
+  const float M = fmaxf(a.mx, mx2), m = fminf(a.mn, mn2);
+  a.ax = min(a.mx == M ? a.ax : INT_MAX, mx2 == M ? ax2 : INT_MAX);
+  a.an = min(a.mn == m ? a.an : INT_MAX, mn2 == m ? an2 : INT_MAX);
+  a.cx = (a.mx == M ? a.cx : 0) + (mx2 == M ? cx2 : 0);
+  a.cn = (a.mn == m ? a.cn : 0) + (mn2 == m ? cn2 : 0);
+  a.mx = M;
+  a.mn = m;
+}
 
 template <int D, int CAL, int MODE, typename TIn>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
-  __shared__ FwdSmem<D> sm;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FwdSmem<D>& sm = *reinterpret_cast<FwdSmem<D>*>(smem_raw);
   constexpr int LDK = D + 4, LDV = D + 8;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
+  const int G = l >> 4, c16 = l & 15;
   const int T = a.T, K = a.K, ts = K + 1;
   const int nqt = (T + FWD_BM - 1) / FWD_BM;
   const int L = logical_block();
@@ -61,69 +90,104 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
   const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
   const int qb0 = qt * FWD_BM, qw0 = qb0 + 32 * w, qi = qw0 + c;
+  const int qtw = qw0 / BN;  // the wave's query tile
   const bool qvalid = qi < T;
   const int qlast_w = min(qw0 + 31, T - 1);
   const int kend = a.causal ? min(T, qb0 + FWD_BM) : T;
   const int ntiles = (kend + BN - 1) / BN;
   const int rl = 32 * w + c;
+  float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
 
-  float qreg[D / 2];
-  load_row_operand<D>(qreg, Qp + (size_t)qi * D, qvalid, a.scale);
-
-  // ---- pass 1: row extrema, first index attaining them, tie counts
-  float mx = -INFINITY, mn = INFINITY;
-  int ax = INT_MAX, an = INT_MAX, cx = 0, cn = 0;
+  // ---- pass 1: scores (fp64 MFMA) stored once; row extrema with first index and tie counts
+  float qr[D / 2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qw0 + 16 * qb + c16;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      f4v x = f4v{0.f, 0.f, 0.f, 0.f};
+      if (row < T) x = Ld<TIn>::four(Qp + (size_t)row * D + 16 * j + 4 * G);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qr[qb * (D / 4) + 4 * j + e] = x[e];
+    }
+  }
+  Ext ex[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) ex[qb] = Ext{-INFINITY, INFINITY, INT_MAX, INT_MAX, 0, 0};
+  float* scr = sm.scratch[w];
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     __syncthreads();
-    stage_rows<D>(sm.Ks, LDK, Kp, k0, T, 1.0f);
+    stage_rows<D>(sm.Ks, LDK, Kp, k0, T);
     __syncthreads();
     if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    const f16v s = tile_dot<D>(sm.Ks, LDK, qreg);
+    d4v acc[2][2];
+    score_tile_f64<D>(sm.Ks, LDK, qr, acc);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = k0 + crow(v, g);
-      const bool ok = qvalid && key < T && (!a.causal || key <= qi);
-      const float x = s[v];
-      if (ok) {
-        if (x > mx) { mx = x; ax = key; cx = 1; } else if (x == mx) { ++cx; }
-        if (x < mn) { mn = x; an = key; cn = 1; } else if (x == mn) { ++cn; }
-      }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float x = (float)(a.scale * acc[kb][qb][v]);
+          const int klo = 16 * kb + 4 * v + G, qlo = 16 * qb + c16;
+          const int key = k0 + klo, query = qw0 + qlo;
+          const bool ok = query < T && key < T && (!a.causal || key <= query);
+          Ext& e = ex[qb];
+          if (ok) {
+            if (x > e.mx) { e.mx = x; e.ax = key; e.cx = 1; } else if (x == e.mx) { ++e.cx; }
+            if (x < e.mn) { e.mn = x; e.an = key; e.cn = 1; } else if (x == e.mn) { ++e.cn; }
+          }
+          // re-layout into the stored tile order: (query qlo, key klo) -> v' * 64 + qlo + 32 g'
+          const int gp = (klo >> 2) & 1, vp = 4 * (klo >> 3) + (klo & 3);
+          scr[vp * SCR + qlo + 32 * gp] = x;
+        }
+    float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) St[v * 64 + l] = scr[v * SCR + l];
+  }
+  // merge the four lanes that share a query row (lanes c16 + 16 G)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    ext_merge(ex[qb], 16);
+    ext_merge(ex[qb], 32);
+    if (G == 0) {
+      const int r2 = 32 * w + 16 * qb + c16;
+      sm.rowM[r2] = ex[qb].mx;
+      sm.rowm[r2] = ex[qb].mn;
+      sm.rowax[r2] = ex[qb].ax;
+      sm.rowan[r2] = ex[qb].an;
+      sm.rowcx[r2] = ex[qb].cx;
+      sm.rowcn[r2] = ex[qb].cn;
     }
   }
-  // merge the two half-waves that share a query row
-  float M, m;
-  int amax, amin, nA, nC;
-  {
-    const float mx2 = __shfl_xor(mx, 32), mn2 = __shfl_xor(mn, 32);
-    const int ax2 = __shfl_xor(ax, 32), an2 = __shfl_xor(an, 32);
-    const int cx2 = __shfl_xor(cx, 32), cn2 = __shfl_xor(cn, 32);
-    M = fmaxf(mx, mx2);
-    m = fminf(mn, mn2);
-    amax = min(mx == M ? ax : INT_MAX, mx2 == M ? ax2 : INT_MAX);
-    amin = min(mn == m ? an : INT_MAX, mn2 == m ? an2 : INT_MAX);
-    nA = (mx == M ? cx : 0) + (mx2 == M ? cx2 : 0);
-    nC = (mn == m ? cn : 0) + (mn2 == m ? cn2 : 0);
-  }
+  // pass 2 reads back the tiles stored above: complete the stores and drop stale L1 lines
+  __threadfence();
+  __syncthreads();
+  // from here on lane l works on query row l%32 of the wave
+  const float M = sm.rowM[rl], m = sm.rowm[rl];
 
   // ---- calibration and grid table (K+1 exponentials per row)
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
-  float* trow = sm.tbl + rl * ts;
+  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D>));
+  float* trow = tbl + rl * ts;
   for (int r = g; r <= K; r += 2) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
 
   // ---- pass 2: reconstruct, normalize, multiply by V
-  float sumL = 0.f, sumN = 0.f;
+  double sumL = 0.0, sumN = 0.0;  // row sums of positive weights: double, no absorption of small terms
   f16v o[D / 32], ol[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     __syncthreads();
-    stage_rows<D>(sm.Ks, LDK, Kp, k0, T, 1.0f);
-    stage_rows<D>(sm.Vs, LDV, Vp, k0, T, 1.0f);
+    stage_rows<D>(sm.Vs, LDV, Vp, k0, T);
     __syncthreads();
     if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    const f16v s = tile_dot<D>(sm.Ks, LDK, qreg);
+    const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+    f16v s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = St[v * 64 + l];
     f16v p, pl;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -134,29 +198,43 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       const bool keep = ok && !d.tail;
       const float wl = keep ? wt.wL : 0.f;
       const float wn = keep ? wt.wN : 0.f;
-      sumL += wl;
-      sumN += wn;
+      sumL += (double)wl;
+      sumN += (double)wn;
       p[v] = (MODE == LERP) ? wl : wn;
       pl[v] = wl;
     }
-    tile_accum<D>(o, p, sm.Vs, LDV);
-    if (MODE == NEAREST_P) tile_accum<D>(ol, pl, sm.Vs, LDV);
+    // each tile's P V goes into a fresh accumulator, then into the running sum: the long
+    // accumulation chain then holds one add per tile instead of one per MFMA step
+    f16v ot[D / 32];
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
+    tile_accum<D>(ot, p, sm.Vs, LDV);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[nb] += ot[nb];
+    if (MODE == NEAREST_P) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
+      tile_accum<D>(ot, pl, sm.Vs, LDV);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) ol[nb] += ot[nb];
+    }
   }
   sumL += __shfl_xor(sumL, 32);
   sumN += __shfl_xor(sumN, 32);
+  const float WLf = (float)sumL, WNf = (float)sumN;
   if (g == 0) {
-    sm.rowW[rl] = (MODE == LERP) ? sumL : sumN;
-    sm.rowWL[rl] = sumL;
+    sm.rowW[rl] = (MODE == LERP) ? WLf : WNf;
+    sm.rowWL[rl] = WLf;
     if (qvalid) {
       const size_t row = (size_t)head * T + qi;
       a.rec.M[row] = M;
       a.rec.m[row] = m;
-      a.rec.amax[row] = amax;
-      a.rec.amin[row] = amin;
-      a.rec.nA[row] = nA;
-      a.rec.nC[row] = nC;
-      a.rec.WN[row] = sumN;
-      a.rec.WL[row] = sumL;
+      a.rec.amax[row] = sm.rowax[rl];
+      a.rec.amin[row] = sm.rowan[rl];
+      a.rec.nA[row] = sm.rowcx[rl];
+      a.rec.nC[row] = sm.rowcn[rl];
+      a.rec.WN[row] = WNf;
+      a.rec.WL[row] = WLf;
     }
   }
   __syncthreads();
@@ -179,40 +257,37 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   }
 }
 
-// Test hook: the bin decision of every (query, key) pair, from the forward's row record.
-template <int D, int CAL, bool NEAREST, typename TIn>
+template <int D>
+constexpr size_t fwd_smem_bytes(int K) {
+  return sizeof(FwdSmem<D>) + sizeof(float) * (FWD_BM * (K + 1));
+}
+
+// Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
+template <int CAL, bool NEAREST>
 __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
-  __shared__ float Ks[BN * (D + 4)];
-  constexpr int LDK = D + 4;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
-  const int T = a.T, K = a.K;
-  const int nqt = (T + FWD_BM - 1) / FWD_BM;
-  const int L = logical_block();
-  const int head = L / nqt, qt = L % nqt;
-  const size_t hb = (size_t)head * T * D;
-  const TIn* Qp = reinterpret_cast<const TIn*>(a.q) + hb;
-  const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
-  const int qw0 = qt * FWD_BM + 32 * w, qi = qw0 + c;
+  const int T = a.T, K = a.K, nt = a.rec.nt;
+  const int L = blockIdx.x;
+  const int head = L / nt, qt = L % nt;
+  const int qi = qt * BN + c;
   const bool qvalid = qi < T;
-  float qreg[D / 2];
-  load_row_operand<D>(qreg, Qp + (size_t)qi * D, qvalid, a.scale);
   const size_t row = (size_t)head * T + (qvalid ? qi : 0);
   const RowCal rc = row_calibration<CAL>(a.rec.M[row], a.rec.m[row], K, a.tau);
-  const int ntiles = (T + BN - 1) / BN;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * BN;
-    __syncthreads();
-    stage_rows<D>(Ks, LDK, Kp, k0, T, 1.0f);
-    __syncthreads();
-    const f16v s = tile_dot<D>(Ks, LDK, qreg);
+  const float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
+  const int kt_end = a.causal ? qt + 1 : nt;
+  for (int kt = w; kt < nt; kt += 4) {
+    const bool stored = kt < kt_end;
+    const float* St = Sh + (stored ? tile_index(qt, kt, nt, a.causal) : 0) * 1024;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int key = k0 + crow(v, g);
+      const int key = kt * BN + crow(v, g);
       if (!qvalid || key >= T) continue;
-      const bool ok = !a.causal || key <= qi;
-      const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+      const bool ok = stored && (!a.causal || key <= qi);
       uint8_t val = 255;
-      if (ok) val = d.tail ? 254 : (uint8_t)(NEAREST ? d.r + (d.t >= 0.5f ? 1 : 0) : d.r);
+      if (ok) {
+        const Decision d = decide<CAL>(St[v * 64 + l], rc, K, a.tau);
+        val = d.tail ? 254 : (uint8_t)(NEAREST ? d.r + (d.t >= 0.5f ? 1 : 0) : d.r);
+      }
       a.bins[(size_t)head * T * T + (size_t)qi * T + key] = val;
     }
   }
@@ -222,7 +297,8 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
 template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
-  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(256), 0, s, a);
+  const size_t smem = fwd_smem_bytes<D>(p.K);
+  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE>
@@ -245,26 +321,14 @@ hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
   return p.D == 128 ? fwd_cl<128>(p, a, s) : fwd_cl<64>(p, a, s);
 }
 
-template <int D, int CAL, bool NEAREST, typename TIn>
+template <int CAL, bool NEAREST>
 static hipError_t bins_go(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
-  hipLaunchKernelGGL((bins_kernel<D, CAL, NEAREST, TIn>), dim3(p.nheads * nqt), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bins_kernel<CAL, NEAREST>), dim3(p.nheads * a.rec.nt), dim3(256), 0, s, a);
   return hipGetLastError();
 }
-template <int D, int CAL, bool NEAREST>
-static hipError_t bins_dt(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  return p.bf16 ? bins_go<D, CAL, NEAREST, uint16_t>(p, a, s) : bins_go<D, CAL, NEAREST, float>(p, a, s);
-}
-template <int D, int CAL>
-static hipError_t bins_md(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  return p.mode == LERP ? bins_dt<D, CAL, false>(p, a, s) : bins_dt<D, CAL, true>(p, a, s);
-}
-template <int D>
-static hipError_t bins_cl(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  return p.calib == FWM ? bins_md<D, FWM>(p, a, s) : bins_md<D, MINMAX>(p, a, s);
-}
 hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  return p.D == 128 ? bins_cl<128>(p, a, s) : bins_cl<64>(p, a, s);
+  if (p.calib == FWM) return p.mode == LERP ? bins_go<FWM, false>(p, a, s) : bins_go<FWM, true>(p, a, s);
+  return p.mode == LERP ? bins_go<MINMAX, false>(p, a, s) : bins_go<MINMAX, true>(p, a, s);
 }
 
 }  // namespace kia

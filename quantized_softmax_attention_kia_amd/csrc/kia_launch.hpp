@@ -22,13 +22,17 @@ struct RowRec {
   float* WN;
   float* WL;
   float* OL;  // [N, D], Nearest + Prob-STE only (else nullptr)
+  float* S;   // stored score tiles: per head, tiles_per_head tiles of 1024 floats
+  int nt;     // number of 32-row tiles along T
+  size_t tiles_per_head;
 };
 
 struct Problem {
   int nheads;   // B * H
   int T, D, K;
   int causal;
-  float tau, scale;
+  float tau;
+  double scale;
   int calib, mode, full, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
 };
 
@@ -39,7 +43,8 @@ struct FwdArgs {
   float* o;
   RowRec rec;
   int T, K, causal;
-  float tau, scale;
+  float tau;
+  double scale;  // score scale, applied in double to the fp64 dot products
 };
 
 struct BwdArgs {
@@ -60,16 +65,15 @@ struct BwdArgs {
 };
 
 struct BinsArgs {
-  const void* q;
-  const void* k;
   RowRec rec;
   uint8_t* bins;
   int T, K, causal;
-  float tau, scale;
+  float tau;
 };
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
-hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s);
+// stages: bit 0 = dq kernel (dQ, D_i, alpha, beta), bit 1 = dkdv kernel (dK, dV)
+hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s, int stages);
 hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s);
 
 }  // namespace kia

@@ -50,10 +50,14 @@ def ws(kb, p):
 def test_workspace_layout(kb):
     N = 2 * 3 * 100
     rnd = lambda x: (x + 255) // 256 * 256
+    nt = (100 + 31) // 32
+    tiles = 2 * 3 * nt * (nt + 1) // 2 * 4096        # stored causal score tiles
     st, rr, w = ws(kb, params(kb))
-    assert st == 0 and rr == 8 * rnd(N * 4) and w == 3 * rnd(N * 4)
+    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 3 * rnd(N * 4)
     st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
-    assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4)
+    assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
+    st, rr, w = ws(kb, params(kb, causal=0))
+    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096
     st, rr, w = ws(kb, params(kb, B=0))
     assert st == 0 and rr == 0
 
@@ -78,7 +82,7 @@ def test_rejects_null_buffers(kb):
     assert kb._lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) == -1
     assert "null" in kb._lib.kia_last_error().decode()
     assert kb._lib.kia_backward(ctypes.byref(p), *([None] * 11)) == -1
-    assert kb._lib.kia_debug_bins(ctypes.byref(p), None, None, None, None, None) == -1
+    assert kb._lib.kia_debug_bins(ctypes.byref(p), None, None, None) == -1
 
 
 def test_empty_problem_is_ok_without_buffers(kb):

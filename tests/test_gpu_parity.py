@@ -105,7 +105,7 @@ def test_bins_bitexact(kb, variant, K):
     cfg = kb.Config(*full[:4], K=K, tau=3.0)
     qt, kt, vt = (torch.from_numpy(x).cuda() for x in (q, k, v))
     o, rowrec, p = kb.forward(cfg, qt, kt, vt)
-    bins = kb.debug_bins(p, qt, kt, rowrec)
+    bins = kb.debug_bins(p, rowrec)
     torch.cuda.synchronize()
     bins = bins.cpu().numpy()
     for h in range(2):
