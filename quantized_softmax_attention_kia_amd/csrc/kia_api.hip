@@ -70,7 +70,7 @@ struct Layout {
   size_t rowrec_bytes;
   int nt;
   size_t tiles_per_head;
-  size_t ws_off[3];
+  size_t ws_off[2];
   size_t ws_bytes;
 };
 
@@ -87,7 +87,10 @@ Layout layout(const kia::Problem& pr) {
   o += (size_t)pr.nheads * L.tiles_per_head * 1024 * 4;
   L.rowrec_bytes = o;
   o = 0;
-  for (int i = 0; i < 3; ++i) { L.ws_off[i] = o; o += round_up(N * 4); }
+  L.ws_off[0] = o;                       // per-row record, 64 bytes per row
+  o += round_up(N * 64);
+  L.ws_off[1] = o;                       // grid tables, K + 1 floats per row
+  o += round_up(N * (size_t)(pr.K + 1) * 4);
   L.ws_bytes = o;
   return L;
 }
@@ -143,6 +146,7 @@ kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, co
   kia::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.rec = carve(pr, rowrec);
+  a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
   return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
 }
@@ -165,9 +169,9 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   a.rec = carve(pr, const_cast<void*>(rowrec));
   a.dq = dq; a.dk = dk; a.dv = dv;
   char* ws = static_cast<char*>(workspace);
-  a.Dvec = reinterpret_cast<float*>(ws + L.ws_off[0]);
-  a.alpha = reinterpret_cast<float*>(ws + L.ws_off[1]);
-  a.beta = reinterpret_cast<float*>(ws + L.ws_off[2]);
+  a.rowp = reinterpret_cast<kia::RowP*>(ws + L.ws_off[0]);
+  a.tab = reinterpret_cast<float*>(ws + L.ws_off[1]);
+  a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale;
   return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);
 }

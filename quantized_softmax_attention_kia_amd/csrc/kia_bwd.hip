@@ -15,43 +15,42 @@
 // key(s), split evenly among ties.
 //
 // Both kernels read the scores the forward stored (no score recomputation):
-//   dq kernel   (query-major, 128 rows per workgroup): D_i, dQ_self = sum dS_self K
+//   dq kernel   (query-major, 64 rows per workgroup): D_i, dQ_self = sum dS_self K
 //               on the MFMA, the row sums a_i, b_i; then the extremum terms of dQ
 //               (gathered rows of K at the arg-max / arg-min; a second sweep adds
-//               extra tied keys when a row has any); writes dQ, alpha = a/nA,
-//               beta = b/nC and D_i.
-//   dkdv kernel (key-major, 128 keys per workgroup): dV += P^T dO, dK += dS^T Q,
+//               extra tied keys when a row has any); writes dQ and, per row, the
+//               record the key-major pass needs (calibration, 1/W, D_i,
+//               alpha = a/nA, beta = b/nC) and the grid table.
+//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q,
 //               where dS carries alpha / beta on the arg-max / arg-min keys, so the
 //               scatter of the calibration gradient into dK needs no atomics.  Each
 //               wave transposes its stored score tile through LDS.
+// Both sweep their tiles while the next tile's operands are already being loaded.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
 
 namespace kia {
 
+constexpr int NW = 2;         // waves per workgroup
+constexpr int NT = 64 * NW;   // threads per workgroup
 constexpr int BN = 32;        // keys per tile (dq kernel) / queries per tile (dkdv kernel)
-constexpr int DQ_BM = 128;    // query rows per dq workgroup
-constexpr int KV_BN = 128;    // key rows per dkdv workgroup
+constexpr int DQ_BM = 32 * NW;  // query rows per dq workgroup
+constexpr int KV_BN = 32 * NW;  // key rows per dkdv workgroup
 constexpr int TLD = 33;       // row stride of the LDS tile transpose
+constexpr int TBL_CH = (BN * (KMAX + 1) + NT - 1) / NT;  // grid-table floats per thread per tile
+
+// Per query row, written by the dq kernel for the key-major pass (64 bytes).
+struct RowP {
+  double origin, inv_h;
+  float inv_hf, invWf, invWg, Di;
+  float alpha, beta, M, m;
+  int amax, amin, pad0, pad1;
+};
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p);
 template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
   return __uint_as_float(((uint32_t)*p) << 16);
-}
-
-template <int D, typename T>
-__device__ __forceinline__ void stage_rows(float* dst, int ld, const T* src, int row0, int nrows, float mul) {
-  constexpr int CH = BN * D / 4;
-#pragma unroll
-  for (int id = threadIdx.x; id < CH; id += 256) {
-    const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
-    const int gr = row0 + r;
-    f4v x = f4v{0.f, 0.f, 0.f, 0.f};
-    if (gr < nrows) x = Ld<T>::four(src + (size_t)gr * D + c4);
-    if (mul != 1.0f) x *= mul;
-    *reinterpret_cast<f4v*>(dst + r * ld + c4) = x;
-  }
 }
 
 // ============================================================================ dq kernel
@@ -65,7 +64,7 @@ struct DqSmem {
 };
 
 template <int D, int CAL, int MODE, bool FULL, typename TIn>
-__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<D>& sm = *reinterpret_cast<DqSmem<D>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D>));
@@ -73,9 +72,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, ts = K + 1;
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
-  const int L = logical_block();
-  const int head = L / nqt;
-  const int qt = nqt - 1 - (L % nqt);
+  int head, rank;
+  block_work(a.nheads, head, rank);
+  const int qt = a.causal ? nqt - 1 - rank : rank;
   const size_t hb = (size_t)head * T * D;
   const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
   const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
@@ -89,6 +88,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const int rl = 32 * w + c;
   const size_t row = (size_t)head * T + (qvalid ? qi : 0);
   const float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
+  auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
   float doreg[D / 2];
   load_row_operand<D>(doreg, dOp + (size_t)qi * D, qvalid, 1.0f);
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const float M = a.rec.M[row], m = a.rec.m[row];
   const int amax = a.rec.amax[row], amin = a.rec.amin[row];
   const int nA = a.rec.nA[row], nC = a.rec.nC[row];
+  const float Wf = (MODE == LERP) ? a.rec.WL[row] : a.rec.WN[row];
   const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
   const float invWg = 1.0f / Wg;
 
@@ -115,12 +116,16 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     }
     Di = (float)(part + __shfl_xor(part, 32));
   }
-  if (g == 0 && qvalid) a.Dvec[row] = Di;
 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
   float* trow = tbl + rl * ts;
+  float* gtab = a.tab + row * ts;
   if (qvalid)
-    for (int r = g; r <= K; r += 2) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+    for (int r = g; r <= K; r += 2) {
+      const float e = grid_value<CAL>(M, m, K, a.tau, r);
+      trow[r] = e;
+      gtab[r] = e;   // the key-major pass reads the table instead of recomputing it
+    }
   // extra tied extrema (beyond the first index) need a second sweep to find them
   const bool rowties = FULL && qvalid && (M != m) && (nA > 1 || (CAL == MINMAX && nC > 1));
   const bool blockties = __syncthreads_or(rowties);
@@ -130,18 +135,33 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) dq[nb] = zero16();
 
+  TileRegs<D, NT, TIn> kr, vr;
+  kr.load(Kp, 0, T);
+  vr.load(Vp, 0, T);
+  f16v snext;
+  if (active(0)) {
+    const float* St = Sh + tile_index(qtw, 0, a.rec.nt, a.causal) * 1024;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+  }
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     __syncthreads();
-    stage_rows<D>(sm.Ks, LD, Kp, k0, T, 1.0f);
-    stage_rows<D>(sm.Vs, LD, Vp, k0, T, 1.0f);
+    kr.store(sm.Ks, LD, 1.0f);
+    vr.store(sm.Vs, LD, 1.0f);
     __syncthreads();
-    if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
-    f16v s;
+    const f16v s = snext;  // S^T: row = key, column = query
+    if (kt + 1 < ntiles) {
+      kr.load(Kp, k0 + BN, T);
+      vr.load(Vp, k0 + BN, T);
+      if (active(kt + 1)) {
+        const float* St = Sh + tile_index(qtw, kt + 1, a.rec.nt, a.causal) * 1024;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = St[v * 64 + l];  // S^T: row = key, column = query
-    const f16v gt = tile_dot<D>(sm.Vs, LD, doreg);          // (dO V^T)^T: g_ij = dO_i . V_j
+        for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+      }
+    }
+    if (!active(kt)) continue;
+    const f16v gt = tile_dot<D>(sm.Vs, LD, doreg);  // (dO V^T)^T: g_ij = dO_i . V_j
     f16v ds;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -188,19 +208,20 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     for (int kt = 0; kt < ntiles; ++kt) {
       const int k0 = kt * BN;
       __syncthreads();
-      stage_rows<D>(sm.Ks, LD, Kp, k0, T, 1.0f);
+      kr.load(Kp, k0, T);
+      kr.store(sm.Ks, LD, 1.0f);
       __syncthreads();
-      if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
+      if (!active(kt)) continue;
       const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
       f16v inj;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float s = St[v * 64 + l];
+        const float sv = St[v * 64 + l];
         const int key = k0 + crow(v, g);
         const bool ok = rowties && key < T && (!a.causal || key <= qi);
         float x = 0.f;
-        if (ok && s == M && key != amax) x += alpha;
-        if (CAL == MINMAX && ok && s == m && key != amin) x += beta;
+        if (ok && sv == M && key != amax) x += alpha;
+        if (CAL == MINMAX && ok && sv == m && key != amin) x += beta;
         inj[v] = x;
       }
       tile_accum<D>(dq, inj, sm.Ks, LD);
@@ -212,8 +233,21 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     sm.amax[rl] = qvalid ? amax : 0;
     sm.amin[rl] = qvalid ? amin : 0;
     if (qvalid) {
-      a.alpha[row] = alpha;
-      a.beta[row] = beta;
+      RowP rp;
+      rp.origin = rc.origin;
+      rp.inv_h = rc.inv_h;
+      rp.inv_hf = rc.inv_hf;
+      rp.invWf = 1.0f / Wf;
+      rp.invWg = invWg;
+      rp.Di = Di;
+      rp.alpha = FULL ? alpha : 0.f;
+      rp.beta = FULL ? beta : 0.f;
+      rp.M = M;
+      rp.m = m;
+      rp.amax = amax;
+      rp.amin = amin;
+      rp.pad0 = rp.pad1 = 0;
+      a.rowp[row] = rp;
     }
   }
   __syncthreads();
@@ -240,34 +274,60 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 }
 
 // ============================================================================ dkdv kernel
-struct RowP {         // per query row, 64 bytes
-  double origin, inv_h;
-  float inv_hf, invWf, invWg, Di;
-  float alpha, beta, M, m;
-  int amax, amin;
-};
-
 template <int D>
 struct KvSmem {
   float Qs[BN * (D + 4)];
   float dOs[BN * (D + 4)];
-  float St[4][BN * TLD];  // per-wave transpose of the stored score tile
+  float St[NW][BN * TLD];  // per-wave transpose of the stored score tile
   RowP rp[BN];
-  // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
+  float tbl[BN * (KMAX + 1)];
 };
 
+// Operands of one query tile for the key-major pass, held in registers while the previous
+// tile computes: Q and dO rows, the wave's stored score tile, the row records and grid tables.
+template <int D, typename TIn>
+struct KvPrefetch {
+  TileRegs<D, NT, TIn> q, dO;
+  float s[16];
+  f4v rp;
+  float tb[TBL_CH];
+};
+
+template <int D, typename TIn>
+__device__ __forceinline__ void kv_load(KvPrefetch<D, TIn>& pf, const BwdArgs& a, const TIn* Qp, const TIn* dOp,
+                                        const float* Sh, int head, int qt, int ktw, bool act) {
+  const int T = a.T, ts = a.K + 1, q0 = qt * BN, tid = threadIdx.x, l = tid & 63;
+  pf.q.load(Qp, q0, T);
+  pf.dO.load(dOp, q0, T);
+  if (act) {
+    const float* Sg = Sh + tile_index(qt, ktw, a.rec.nt, a.causal) * 1024;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pf.s[v] = Sg[v * 64 + l];
+  }
+  {  // 32 rows x 64 bytes: one float4 per thread
+    const int rr = tid >> 2, part = tid & 3;
+    pf.rp = f4v{0.f, 0.f, 0.f, 0.f};
+    if (q0 + rr < T)
+      pf.rp = reinterpret_cast<const f4v*>(a.rowp + (size_t)head * T + q0 + rr)[part];
+  }
+  const int nvalid = max(0, min(BN, T - q0)) * ts;
+  const float* gt = a.tab + ((size_t)head * T + q0) * ts;
+#pragma unroll
+  for (int i = 0; i < TBL_CH; ++i) {
+    const int idx = tid + i * NT;
+    pf.tb[i] = idx < nvalid ? gt[idx] : 0.f;
+  }
+}
+
 template <int D, int CAL, int MODE, bool FULL, typename TIn>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  KvSmem<D>& sm = *reinterpret_cast<KvSmem<D>*>(smem_raw);
-  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(KvSmem<D>));
+__global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
+  __shared__ KvSmem<D> sm;
   constexpr int LD = D + 4;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, ts = K + 1, nt = a.rec.nt;
   const int nkt = (T + KV_BN - 1) / KV_BN;
-  const int L = logical_block();
-  const int head = L / nkt;
-  const int kt = L % nkt;  // low key tiles see the most queries: heaviest first
+  int head, kt;
+  block_work(a.nheads, head, kt);  // low key tiles see the most queries: heaviest first
   const size_t hb = (size_t)head * T * D;
   const TIn* Qp = reinterpret_cast<const TIn*>(a.q) + hb;
   const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
@@ -277,6 +337,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const bool kvalid = kj < T;
   const float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
   float* tr = sm.St[w];
+  auto active = [&](int qt) { return kw0 < T && (!a.causal || ktw <= qt); };  // wave-uniform
+  (void)nkt;
 
   float vreg[D / 2];
   load_row_operand<D>(vreg, Vp + (size_t)kj * D, kvalid, 1.0f);
@@ -285,51 +347,28 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = zero16(); dv[nb] = zero16(); }
 
   const int qt_first = a.causal ? kb0 / BN : 0;
+  KvPrefetch<D, TIn> pf;
+  if (qt_first < nt) kv_load<D, TIn>(pf, a, Qp, dOp, Sh, head, qt_first, ktw, active(qt_first));
   for (int qt = qt_first; qt < nt; ++qt) {
     const int q0 = qt * BN;
-    const bool active = kw0 < T && (!a.causal || ktw <= qt);  // wave-uniform
+    const bool act = active(qt);
     __syncthreads();
-    stage_rows<D>(sm.Qs, LD, Qp, q0, T, a.scale);
-    stage_rows<D>(sm.dOs, LD, dOp, q0, T, 1.0f);
-    if (active) {
+    pf.q.store(sm.Qs, LD, a.scale);
+    pf.dO.store(sm.dOs, LD, 1.0f);
+    if (act) {
       // stored tile (qt, ktw): element (query l%32, key crow(v, g)) at v * 64 + l
-      const float* Sg = Sh + tile_index(qt, ktw, nt, a.causal) * 1024;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tr[c * TLD + crow(v, g)] = Sg[v * 64 + l];
+      for (int v = 0; v < 16; ++v) tr[c * TLD + crow(v, g)] = pf.s[v];
     }
-    if (tid < BN) {
-      const int qr = q0 + tid;
-      RowP rp;
-      if (qr < T) {
-        const size_t row = (size_t)head * T + qr;
-        const float M = a.rec.M[row], m = a.rec.m[row];
-        const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
-        rp.origin = rc.origin;
-        rp.inv_h = rc.inv_h;
-        rp.inv_hf = rc.inv_hf;
-        rp.invWf = 1.0f / ((MODE == LERP) ? a.rec.WL[row] : a.rec.WN[row]);
-        rp.invWg = 1.0f / ((MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row]);
-        rp.Di = a.Dvec[row];
-        rp.alpha = FULL ? a.alpha[row] : 0.f;
-        rp.beta = FULL ? a.beta[row] : 0.f;
-        rp.M = M;
-        rp.m = m;
-        rp.amax = a.rec.amax[row];
-        rp.amin = a.rec.amin[row];
-      } else {
-        rp.origin = 0.0; rp.inv_h = 1.0; rp.inv_hf = 1.f; rp.invWf = 0.f; rp.invWg = 0.f;
-        rp.Di = 0.f; rp.alpha = 0.f; rp.beta = 0.f; rp.M = 0.f; rp.m = 0.f;
-        rp.amax = -1; rp.amin = -1;
-      }
-      sm.rp[tid] = rp;
+    reinterpret_cast<f4v*>(sm.rp)[tid] = pf.rp;
+#pragma unroll
+    for (int i = 0; i < TBL_CH; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < BN * ts) sm.tbl[idx] = pf.tb[i];
     }
     __syncthreads();
-    for (int idx = tid; idx < BN * ts; idx += 256) {
-      const int rr = idx / ts, r = idx - rr * ts;
-      tbl[idx] = (q0 + rr < T) ? grid_value<CAL>(sm.rp[rr].M, sm.rp[rr].m, K, a.tau, r) : 0.f;
-    }
-    __syncthreads();
-    if (!active) continue;
+    if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, Sh, head, qt + 1, ktw, active(qt + 1));
+    if (!act) continue;
     f16v s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = tr[crow(v, g) * TLD + c];  // S: row = query, column = key
@@ -346,7 +385,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       rc.inv_hf = rp.inv_hf;
       rc.kappa = 1.f;
       const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-      const Weights wt = weights(d, tbl + rr * ts);
+      const Weights wt = weights(d, sm.tbl + rr * ts);
       const bool keep = ok && !d.tail;
       const float wf = (MODE == LERP) ? wt.wL : wt.wN;
       const float Delta = (wt.E1 - wt.E0) * rp.inv_hf;
@@ -382,14 +421,13 @@ static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int 
   if (stage & 1) {
     const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
     const size_t smem = sizeof(DqSmem<D>) + sizeof(float) * DQ_BM * (p.K + 1);
-    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nqt), dim3(256), smem, s, a);
+    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage & 2) {
     const int nkt = (p.T + KV_BN - 1) / KV_BN;
-    const size_t smem = sizeof(KvSmem<D>) + sizeof(float) * BN * (p.K + 1);
-    hipLaunchKernelGGL((dkdv_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nkt), dim3(256), smem, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -233,13 +233,49 @@ __device__ __forceinline__ Weights weights(const Decision& d, const float* trow)
   return w;
 }
 
-// XCD-aware work order: the dispatcher hands consecutive workgroups to the 8 XCDs in turn;
-// this maps them so that each XCD walks a contiguous range of logical tiles (the tiles of
-// the same heads, whose K/V then stay in that XCD's L2).
-__device__ __forceinline__ int logical_block() {
-  const int nb = gridDim.x, b = blockIdx.x;
-  if ((nb & 7) == 0) return (b & 7) * (nb >> 3) + (b >> 3);
-  return b;
+// Work order.  The dispatcher hands workgroup b to XCD b % 8.  Each XCD gets a contiguous range
+// of heads (their K, V and score tiles then stay in that XCD's L2) and walks its tiles heaviest
+// first over all of its heads (rank 0 = most work), so the hardware's greedy dispatch balances
+// the causal triangle across CUs.  Falls back to rank-major order when the head count is not a
+// multiple of 8.
+__device__ __forceinline__ void block_work(int nheads, int& head, int& rank) {
+  const int b = blockIdx.x;
+  if ((nheads & 7) == 0) {
+    const int x = b & 7, i = b >> 3, hpx = nheads >> 3;
+    rank = i / hpx;
+    head = x * hpx + i % hpx;
+  } else {
+    rank = b / nheads;
+    head = b % nheads;
+  }
 }
+
+// Stage rows of a [T, D] head tensor through registers: each of NT threads holds
+// CH = 32*D/4/NT float4 chunks of a 32-row tile (rows row0.., zero past nrows).
+template <int D, int NT, typename T>
+struct TileRegs {
+  static constexpr int CH = 32 * D / 4 / NT;
+  f4v x[CH];
+  __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int id = threadIdx.x + i * NT;
+      const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
+      const int gr = row0 + r;
+      x[i] = f4v{0.f, 0.f, 0.f, 0.f};
+      if (gr < nrows) x[i] = Ld<T>::four(src + (size_t)gr * D + c4);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int ld, float mul) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int id = threadIdx.x + i * NT;
+      const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
+      f4v y = x[i];
+      if (mul != 1.0f) y *= mul;
+      *reinterpret_cast<f4v*>(dst + r * ld + c4) = y;
+    }
+  }
+};
 
 }  // namespace kia

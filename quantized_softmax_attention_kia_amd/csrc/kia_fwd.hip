@@ -2,8 +2,10 @@
 //
 // "Pretraining Transformers with Quantized Softmax in Attention", §3: the grid
 // of a row depends on the row's final extrema, so the online-softmax rescale
-// does not apply.  One workgroup owns 128 query rows of one head (4 waves x 32
-// rows) and sweeps the visible key tiles twice:
+// does not apply.  One workgroup owns 64 query rows of one head (2 waves x 32
+// rows; small workgroups, heaviest first, so the causal triangle balances over
+// the CUs) and sweeps the visible key tiles twice, loading the next tile while
+// it computes the current one:
 //   pass 1  scores of each 32 x 32 tile on the fp64 MFMA (exact products of the
 //           fp32 inputs, double accumulation, scale applied in double), rounded
 //           once to fp32 and stored for every later pass; row max / min, first
@@ -25,23 +27,11 @@
 
 namespace kia {
 
-constexpr int FWD_BM = 128;  // query rows per workgroup
-constexpr int BN = 32;       // keys per tile
-constexpr int SCR = 80;      // row stride of the per-wave tile scratch (bank-conflict free writes)
-
-// Stage 32 rows of a [T, D] head tensor (rows row0..row0+31, zero past T) into LDS.
-template <int D, typename T>
-__device__ __forceinline__ void stage_rows(float* dst, int ld, const T* src, int row0, int nrows) {
-  constexpr int CH = BN * D / 4;
-#pragma unroll
-  for (int id = threadIdx.x; id < CH; id += 256) {
-    const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
-    const int gr = row0 + r;
-    f4v x = f4v{0.f, 0.f, 0.f, 0.f};
-    if (gr < nrows) x = Ld<T>::four(src + (size_t)gr * D + c4);
-    *reinterpret_cast<f4v*>(dst + r * ld + c4) = x;
-  }
-}
+constexpr int NW = 2;              // waves per workgroup
+constexpr int NT = 64 * NW;        // threads per workgroup
+constexpr int FWD_BM = 32 * NW;    // query rows per workgroup
+constexpr int BN = 32;             // keys per tile
+constexpr int SCR = 80;            // row stride of the per-wave tile scratch (bank-conflict free writes)
 
 template <int D>
 struct FwdSmem {
@@ -49,7 +39,7 @@ struct FwdSmem {
     float Ks[BN * (D + 4)];  // pass 1
     float Vs[BN * (D + 8)];  // pass 2
   };
-  float scratch[4][16 * SCR];  // per-wave tile re-layout (pass 1)
+  float scratch[NW][16 * SCR];  // per-wave tile re-layout (pass 1)
   float rowM[FWD_BM], rowm[FWD_BM], rowW[FWD_BM], rowWL[FWD_BM];
   int rowax[FWD_BM], rowan[FWD_BM], rowcx[FWD_BM], rowcn[FWD_BM];
   // followed in dynamic LDS by the grid table: FWD_BM rows x (K + 1) floats
@@ -74,7 +64,7 @@ __device__ __forceinline__ void ext_merge(Ext& a, int lanemask) {
 }
 
 template <int D, int CAL, int MODE, typename TIn>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FwdSmem<D>& sm = *reinterpret_cast<FwdSmem<D>*>(smem_raw);
   constexpr int LDK = D + 4, LDV = D + 8;
@@ -82,9 +72,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int G = l >> 4, c16 = l & 15;
   const int T = a.T, K = a.K, ts = K + 1;
   const int nqt = (T + FWD_BM - 1) / FWD_BM;
-  const int L = logical_block();
-  const int head = L / nqt;
-  const int qt = nqt - 1 - (L % nqt);  // heaviest (latest) query tiles of a head first
+  int head, rank;
+  block_work(a.nheads, head, rank);
+  const int qt = a.causal ? nqt - 1 - rank : rank;  // rank 0: the latest query tile, the most keys
   const size_t hb = (size_t)head * T * D;
   const TIn* Qp = reinterpret_cast<const TIn*>(a.q) + hb;
   const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
@@ -115,11 +105,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) ex[qb] = Ext{-INFINITY, INFINITY, INT_MAX, INT_MAX, 0, 0};
   float* scr = sm.scratch[w];
+  TileRegs<D, NT, TIn> kr;
+  kr.load(Kp, 0, T);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     __syncthreads();
-    stage_rows<D>(sm.Ks, LDK, Kp, k0, T);
+    kr.store(sm.Ks, LDK, 1.0f);
     __syncthreads();
+    if (kt + 1 < ntiles) kr.load(Kp, k0 + BN, T);  // next tile in flight during this one
     if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
     d4v acc[2][2];
     score_tile_f64<D>(sm.Ks, LDK, qr, acc);
@@ -178,16 +171,30 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   f16v o[D / 32], ol[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
+  TileRegs<D, NT, TIn> vr;
+  vr.load(Vp, 0, T);
+  f16v snext;
+  const bool act0 = qw0 < T;
+  if (act0) {
+    const float* St = Sh + tile_index(qtw, 0, a.rec.nt, a.causal) * 1024;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+  }
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     __syncthreads();
-    stage_rows<D>(sm.Vs, LDV, Vp, k0, T);
+    vr.store(sm.Vs, LDV, 1.0f);
     __syncthreads();
-    if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
-    f16v s;
+    const f16v s = snext;
+    if (kt + 1 < ntiles) {  // next V tile and next score tile in flight during this one
+      vr.load(Vp, k0 + BN, T);
+      if (qw0 < T && (!a.causal || k0 + BN <= qlast_w)) {
+        const float* St = Sh + tile_index(qtw, kt + 1, a.rec.nt, a.causal) * 1024;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = St[v * 64 + l];
+        for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+      }
+    }
+    if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
     f16v p, pl;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 }
 
 template <int D>
-constexpr size_t fwd_smem_bytes(int K) {
+size_t fwd_smem_bytes(int K) {
   return sizeof(FwdSmem<D>) + sizeof(float) * (FWD_BM * (K + 1));
 }
 
@@ -298,7 +305,7 @@ template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
   const size_t smem = fwd_smem_bytes<D>(p.K);
-  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(256), smem, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE>

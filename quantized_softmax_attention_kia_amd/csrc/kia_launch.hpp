@@ -36,7 +36,10 @@ struct Problem {
   int calib, mode, full, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
 };
 
+struct RowP;  // per-row record of the backward (kia_bwd.hip)
+
 struct FwdArgs {
+  int nheads;
   const void* q;
   const void* k;
   const void* v;
@@ -48,6 +51,7 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
+  int nheads;
   const void* q;
   const void* k;
   const void* v;
@@ -57,9 +61,8 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* Dvec;   // [N] sum_j P_j g_j at the surrogate's normalization point
-  float* alpha;  // [N] extremum gradient per tied maximum key
-  float* beta;   // [N] extremum gradient per tied minimum key (MinMax)
+  RowP* rowp;    // [N] per-row record written by the dq kernel for the key-major pass
+  float* tab;    // [N, K+1] grid tables written by the dq kernel
   int T, K, causal;
   float tau, scale;
 };
