@@ -89,9 +89,12 @@ typedef struct {
  *        32 x 32 tiles (query tile, key tile); tiles = nt(nt+1)/2 when causal
  *        (key tile <= query tile), nt^2 otherwise.  About 2 T^2 bytes per head
  *        when causal.
- *  bwd_ws_bytes: scratch for kia_backward: per row a 64-byte record (calibration,
- *    1/W, D_i, and the extremum gradients alpha_i = a_i/nA_i, beta_i = b_i/nC_i)
- *    and the K+1 grid values.
+ *  bwd_ws_bytes: scratch for kia_backward: two arrays of float tiles numbered
+ *    like S, P[B*H][tiles][1024] (the forward's normalized weights: P^L for LERP,
+ *    the hard P^N for Nearest) and dS[B*H][tiles][1024] (the unscaled score
+ *    gradients, extremum terms included), both key-major: element (query tile
+ *    row a, key tile column b) of a tile at float offset v*64 + b + 32*g, where
+ *    a = 8*(v/4) + 4*g + v%4.
  * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
  * KIA_ERR_UNSUPPORTED for parameters kia_forward would reject.
  */
@@ -125,8 +128,8 @@ kia_status_t kia_backward(const kia_params_t* p, const void* q, const void* k, c
 /*
  * The two stages of kia_backward, for callers that schedule or time them
  * separately; kia_backward runs exactly these two in this order.
- *  kia_backward_dq   (first): writes dq, and per row the record and grid table
- *                    described under kia_workspace_size into `workspace`.
+ *  kia_backward_dq   (first): writes dq, and the P and dS tiles described under
+ *                    kia_workspace_size into `workspace`.
  *  kia_backward_dkdv (second): reads `workspace` as kia_backward_dq left it and
  *                    writes dk, dv.  Both on the same stream, dkdv after dq.
  * Arguments as for kia_backward.

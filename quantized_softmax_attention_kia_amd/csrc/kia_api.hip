@@ -87,10 +87,11 @@ Layout layout(const kia::Problem& pr) {
   o += (size_t)pr.nheads * L.tiles_per_head * 1024 * 4;
   L.rowrec_bytes = o;
   o = 0;
-  L.ws_off[0] = o;                       // per-row record, 64 bytes per row
-  o += round_up(N * 64);
-  L.ws_off[1] = o;                       // grid tables, K + 1 floats per row
-  o += round_up(N * (size_t)(pr.K + 1) * 4);
+  const size_t tile_bytes = (size_t)pr.nheads * L.tiles_per_head * 1024 * 4;
+  L.ws_off[0] = o;                       // key-major P tiles
+  o += tile_bytes;
+  L.ws_off[1] = o;                       // key-major dS tiles
+  o += tile_bytes;
   L.ws_bytes = o;
   return L;
 }
@@ -169,8 +170,8 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   a.rec = carve(pr, const_cast<void*>(rowrec));
   a.dq = dq; a.dk = dk; a.dv = dv;
   char* ws = static_cast<char*>(workspace);
-  a.rowp = reinterpret_cast<kia::RowP*>(ws + L.ws_off[0]);
-  a.tab = reinterpret_cast<float*>(ws + L.ws_off[1]);
+  a.pt = reinterpret_cast<float*>(ws + L.ws_off[0]);
+  a.dst = reinterpret_cast<float*>(ws + L.ws_off[1]);
   a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale;
   return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);

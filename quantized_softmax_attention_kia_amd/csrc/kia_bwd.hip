@@ -14,17 +14,17 @@
 // a is added to the score gradient of the arg-max key(s) and b to the arg-min
 // key(s), split evenly among ties.
 //
-// Both kernels read the scores the forward stored (no score recomputation):
-//   dq kernel   (query-major, 64 rows per workgroup): D_i, dQ_self = sum dS_self K
-//               on the MFMA, the row sums a_i, b_i; then the extremum terms of dQ
-//               (gathered rows of K at the arg-max / arg-min; a second sweep adds
-//               extra tied keys when a row has any); writes dQ and, per row, the
-//               record the key-major pass needs (calibration, 1/W, D_i,
-//               alpha = a/nA, beta = b/nC) and the grid table.
-//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q,
-//               where dS carries alpha / beta on the arg-max / arg-min keys, so the
-//               scatter of the calibration gradient into dK needs no atomics.  Each
-//               wave transposes its stored score tile through LDS.
+// The dq kernel reads the scores the forward stored (no score recomputation) and takes
+// every bin decision of the backward; the dkdv kernel only contracts what it wrote:
+//   dq kernel   (query-major, 64 rows per workgroup): D_i, g = dO V^T and dS on the MFMA
+//               and the VALU, dQ_self = sum dS_self K, the row sums a_i, b_i, then the
+//               extremum terms of dQ (gathered rows of K at the arg-max / arg-min; a second
+//               sweep adds extra tied keys when a row has any).  Per tile it also writes the
+//               normalized forward weights P and the score gradients dS, transposed through
+//               LDS into key-major tiles, and after the sweep adds alpha_i = a_i/nA_i and
+//               beta_i = b_i/nC_i into dS at the row's extremum keys.
+//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q, straight
+//               from those tiles: no decisions, no row records, no atomics.
 // Both sweep their tiles while the next tile's operands are already being loaded.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
@@ -37,15 +37,6 @@ constexpr int BN = 32;        // keys per tile (dq kernel) / queries per tile (d
 constexpr int DQ_BM = 32 * NW;  // query rows per dq workgroup
 constexpr int KV_BN = 32 * NW;  // key rows per dkdv workgroup
 constexpr int TLD = 33;       // row stride of the LDS tile transpose
-constexpr int TBL_CH = (BN * (KMAX + 1) + NT - 1) / NT;  // grid-table floats per thread per tile
-
-// Per query row, written by the dq kernel for the key-major pass (64 bytes).
-struct RowP {
-  double origin, inv_h;
-  float inv_hf, invWf, invWg, Di;
-  float alpha, beta, M, m;
-  int amax, amin, pad0, pad1;
-};
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p);
 template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
@@ -53,11 +44,22 @@ template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
   return __uint_as_float(((uint32_t)*p) << 16);
 }
 
+// Key-major tiles of P and dS written by the dq kernel: tile (qt, kt) holds element
+// (query a, key b) at float offset v * 64 + b + 32 g where a = crow(v, g), the operand
+// order of tile_accum when the lane's output row is the key.  Same tile numbering as the
+// stored scores.
+__device__ __forceinline__ size_t kmajor_offset(int a, int b) {
+  const int g = (a >> 2) & 1, v = 4 * (a >> 3) + (a & 3);
+  return (size_t)v * 64 + b + 32 * g;
+}
+
 // ============================================================================ dq kernel
 template <int D>
 struct DqSmem {
   float Ks[BN * (D + 4)];
   float Vs[BN * (D + 4)];
+  float Pt[NW][BN * TLD];   // per-wave transposes of the P and dS tiles
+  float dSt[NW][BN * TLD];
   float alpha[DQ_BM], beta[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
   // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 1) floats
@@ -87,7 +89,12 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
   const int rl = 32 * w + c;
   const size_t row = (size_t)head * T + (qvalid ? qi : 0);
-  const float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
+  const size_t tbase = (size_t)head * a.rec.tiles_per_head;
+  const float* Sh = a.rec.S + tbase * 1024;
+  float* Ph = a.pt + tbase * 1024;
+  float* dSh = a.dst + tbase * 1024;
+  float* trp = sm.Pt[w];
+  float* trd = sm.dSt[w];
   auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
   float doreg[D / 2];
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
   const int nA = a.rec.nA[row], nC = a.rec.nC[row];
   const float Wf = (MODE == LERP) ? a.rec.WL[row] : a.rec.WN[row];
   const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
-  const float invWg = 1.0f / Wg;
+  const float invWf = 1.0f / Wf, invWg = 1.0f / Wg;
 
   // D_i = dO_i . O_i (O^L_i for Nearest with Prob-STE): sum_j P_j g_j at the normalization point
   float Di;
@@ -119,13 +126,8 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
   float* trow = tbl + rl * ts;
-  float* gtab = a.tab + row * ts;
   if (qvalid)
-    for (int r = g; r <= K; r += 2) {
-      const float e = grid_value<CAL>(M, m, K, a.tau, r);
-      trow[r] = e;
-      gtab[r] = e;   // the key-major pass reads the table instead of recomputing it
-    }
+    for (int r = g; r <= K; r += 2) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
   // extra tied extrema (beyond the first index) need a second sweep to find them
   const bool rowties = FULL && qvalid && (M != m) && (nA > 1 || (CAL == MINMAX && nC > 1));
   const bool blockties = __syncthreads_or(rowties);
@@ -174,6 +176,9 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       const float gam = keep ? (gt[v] - Di) * invWg : 0.f;
       const float dS = gam * Delta;
       ds[v] = dS;
+      // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
+      trp[c * TLD + crow(v, g)] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
+      trd[c * TLD + crow(v, g)] = dS;
       if (FULL) {
         sds += (double)dS;
         if (CAL == MINMAX) {
@@ -185,14 +190,26 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       }
     }
     tile_accum<D>(dq, ds, sm.Ks, LD);
+    // the wave's P and dS tiles, read back key-major and written as one 256-byte row per register
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int qr = crow(v, g);
+      Ph[to + v * 64 + l] = trp[qr * TLD + c];
+      dSh[to + v * 64 + l] = trd[qr * TLD + c];
+    }
   }
 
   // extremum terms of the row: alpha per tied max key, beta per tied min key
   float alpha = 0.f, beta = 0.f;
+  const bool inject = FULL && qvalid && M != m;  // M == m: every grid value is 1, both terms vanish
   if (FULL) {
     acc_a += __shfl_xor(acc_a, 32);
     sds += __shfl_xor(sds, 32);
-    if (qvalid && M != m) {  // M == m: every grid value is 1 and both terms vanish exactly
+    if (inject) {
       if (CAL == MINMAX) {
         const double A = acc_a / (double)K;
         const double Bm = -sds - A;
@@ -200,6 +217,17 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
         beta = (float)(Bm / (double)nC);
       } else {
         alpha = (float)(-sds / (double)nA);
+      }
+    }
+    // dS of the first arg-max / arg-min key of the row gains alpha / beta; the tiles were
+    // written by lanes of this wave, visible to the whole workgroup after the barrier
+    __syncthreads();
+    if (inject && g == 0) {
+      float* e = dSh + tile_index(qtw, amax / BN, a.rec.nt, a.causal) * 1024 + kmajor_offset(c, amax % BN);
+      *e = *e + alpha;
+      if (CAL == MINMAX) {
+        float* f = dSh + tile_index(qtw, amin / BN, a.rec.nt, a.causal) * 1024 + kmajor_offset(c, amin % BN);
+        *f = *f + beta;
       }
     }
   }
@@ -212,7 +240,8 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       kr.store(sm.Ks, LD, 1.0f);
       __syncthreads();
       if (!active(kt)) continue;
-      const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+      const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+      const float* St = Sh + to;
       f16v inj;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -223,6 +252,10 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
         if (ok && sv == M && key != amax) x += alpha;
         if (CAL == MINMAX && ok && sv == m && key != amin) x += beta;
         inj[v] = x;
+        if (x != 0.f) {
+          float* e = dSh + to + kmajor_offset(c, crow(v, g));
+          *e = *e + x;
+        }
       }
       tile_accum<D>(dq, inj, sm.Ks, LD);
     }
@@ -232,23 +265,6 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
     sm.beta[rl] = beta;
     sm.amax[rl] = qvalid ? amax : 0;
     sm.amin[rl] = qvalid ? amin : 0;
-    if (qvalid) {
-      RowP rp;
-      rp.origin = rc.origin;
-      rp.inv_h = rc.inv_h;
-      rp.inv_hf = rc.inv_hf;
-      rp.invWf = 1.0f / Wf;
-      rp.invWg = invWg;
-      rp.Di = Di;
-      rp.alpha = FULL ? alpha : 0.f;
-      rp.beta = FULL ? beta : 0.f;
-      rp.M = M;
-      rp.m = m;
-      rp.amax = amax;
-      rp.amin = amin;
-      rp.pad0 = rp.pad1 = 0;
-      a.rowp[row] = rp;
-    }
   }
   __syncthreads();
 #pragma unroll
@@ -278,125 +294,64 @@ template <int D>
 struct KvSmem {
   float Qs[BN * (D + 4)];
   float dOs[BN * (D + 4)];
-  float St[NW][BN * TLD];  // per-wave transpose of the stored score tile
-  RowP rp[BN];
-  float tbl[BN * (KMAX + 1)];
 };
 
-// Operands of one query tile for the key-major pass, held in registers while the previous
-// tile computes: Q and dO rows, the wave's stored score tile, the row records and grid tables.
+// Operands of one query tile, held in registers while the previous tile computes: the Q and
+// dO rows (shared by the workgroup through LDS) and the wave's P and dS tiles.
 template <int D, typename TIn>
 struct KvPrefetch {
   TileRegs<D, NT, TIn> q, dO;
-  float s[16];
-  f4v rp;
-  float tb[TBL_CH];
+  f16v p, ds;
 };
 
 template <int D, typename TIn>
 __device__ __forceinline__ void kv_load(KvPrefetch<D, TIn>& pf, const BwdArgs& a, const TIn* Qp, const TIn* dOp,
-                                        const float* Sh, int head, int qt, int ktw, bool act) {
-  const int T = a.T, ts = a.K + 1, q0 = qt * BN, tid = threadIdx.x, l = tid & 63;
-  pf.q.load(Qp, q0, T);
-  pf.dO.load(dOp, q0, T);
+                                        size_t tbase, int qt, int ktw, bool act) {
+  const int l = threadIdx.x & 63;
+  pf.q.load(Qp, qt * BN, a.T);
+  pf.dO.load(dOp, qt * BN, a.T);
   if (act) {
-    const float* Sg = Sh + tile_index(qt, ktw, a.rec.nt, a.causal) * 1024;
+    const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) pf.s[v] = Sg[v * 64 + l];
-  }
-  {  // 32 rows x 64 bytes: one float4 per thread
-    const int rr = tid >> 2, part = tid & 3;
-    pf.rp = f4v{0.f, 0.f, 0.f, 0.f};
-    if (q0 + rr < T)
-      pf.rp = reinterpret_cast<const f4v*>(a.rowp + (size_t)head * T + q0 + rr)[part];
-  }
-  const int nvalid = max(0, min(BN, T - q0)) * ts;
-  const float* gt = a.tab + ((size_t)head * T + q0) * ts;
-#pragma unroll
-  for (int i = 0; i < TBL_CH; ++i) {
-    const int idx = tid + i * NT;
-    pf.tb[i] = idx < nvalid ? gt[idx] : 0.f;
+    for (int v = 0; v < 16; ++v) {
+      pf.p[v] = a.pt[to + v * 64 + l];
+      pf.ds[v] = a.dst[to + v * 64 + l];
+    }
   }
 }
 
-template <int D, int CAL, int MODE, bool FULL, typename TIn>
+template <int D, typename TIn>
 __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
   __shared__ KvSmem<D> sm;
   constexpr int LD = D + 4;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
-  const int T = a.T, K = a.K, ts = K + 1, nt = a.rec.nt;
-  const int nkt = (T + KV_BN - 1) / KV_BN;
+  const int T = a.T, nt = a.rec.nt;
   int head, kt;
   block_work(a.nheads, head, kt);  // low key tiles see the most queries: heaviest first
   const size_t hb = (size_t)head * T * D;
   const TIn* Qp = reinterpret_cast<const TIn*>(a.q) + hb;
-  const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
   const TIn* dOp = reinterpret_cast<const TIn*>(a.dO) + hb;
-  const int kb0 = kt * KV_BN, kw0 = kb0 + 32 * w, kj = kw0 + c;
+  const int kb0 = kt * KV_BN, kw0 = kb0 + 32 * w;
   const int ktw = kw0 / BN;  // the wave's key tile
-  const bool kvalid = kj < T;
-  const float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
-  float* tr = sm.St[w];
+  const size_t tbase = (size_t)head * a.rec.tiles_per_head;
   auto active = [&](int qt) { return kw0 < T && (!a.causal || ktw <= qt); };  // wave-uniform
-  (void)nkt;
 
-  float vreg[D / 2];
-  load_row_operand<D>(vreg, Vp + (size_t)kj * D, kvalid, 1.0f);
   f16v dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = zero16(); dv[nb] = zero16(); }
 
   const int qt_first = a.causal ? kb0 / BN : 0;
   KvPrefetch<D, TIn> pf;
-  if (qt_first < nt) kv_load<D, TIn>(pf, a, Qp, dOp, Sh, head, qt_first, ktw, active(qt_first));
+  if (qt_first < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt_first, ktw, active(qt_first));
   for (int qt = qt_first; qt < nt; ++qt) {
-    const int q0 = qt * BN;
     const bool act = active(qt);
     __syncthreads();
     pf.q.store(sm.Qs, LD, a.scale);
     pf.dO.store(sm.dOs, LD, 1.0f);
-    if (act) {
-      // stored tile (qt, ktw): element (query l%32, key crow(v, g)) at v * 64 + l
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tr[c * TLD + crow(v, g)] = pf.s[v];
-    }
-    reinterpret_cast<f4v*>(sm.rp)[tid] = pf.rp;
-#pragma unroll
-    for (int i = 0; i < TBL_CH; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < BN * ts) sm.tbl[idx] = pf.tb[i];
-    }
     __syncthreads();
-    if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, Sh, head, qt + 1, ktw, active(qt + 1));
+    const f16v p = pf.p, ds = pf.ds;  // element (query crow(v, g), key c); zero where masked
+    if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt + 1, ktw, active(qt + 1));
     if (!act) continue;
-    f16v s;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = tr[crow(v, g) * TLD + c];  // S: row = query, column = key
-    const f16v gg = tile_dot<D>(sm.dOs, LD, vreg);                 // g_ij = dO_i . V_j
-    f16v p, ds;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = crow(v, g), qr = q0 + rr;
-      const RowP& rp = sm.rp[rr];
-      const bool ok = qr < T && kvalid && (!a.causal || kj <= qr);
-      RowCal rc;
-      rc.origin = rp.origin;
-      rc.inv_h = rp.inv_h;
-      rc.inv_hf = rp.inv_hf;
-      rc.kappa = 1.f;
-      const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-      const Weights wt = weights(d, sm.tbl + rr * ts);
-      const bool keep = ok && !d.tail;
-      const float wf = (MODE == LERP) ? wt.wL : wt.wN;
-      const float Delta = (wt.E1 - wt.E0) * rp.inv_hf;
-      float dS = (gg[v] - rp.Di) * rp.invWg * Delta;
-      if (FULL) {
-        if (s[v] == rp.M || kj == rp.amax) dS += rp.alpha;
-        if (CAL == MINMAX && (s[v] == rp.m || kj == rp.amin)) dS += rp.beta;
-      }
-      p[v] = keep ? wf * rp.invWf : 0.f;
-      ds[v] = ok ? (d.tail ? 0.f : dS) : 0.f;
-    }
     tile_accum<D>(dv, p, sm.dOs, LD);
     tile_accum<D>(dk, ds, sm.Qs, LD);
   }
@@ -416,6 +371,12 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------- launchers
+template <int D, typename TIn>
+static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  const int nkt = (p.T + KV_BN - 1) / KV_BN;
+  hipLaunchKernelGGL((dkdv_kernel<D, TIn>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
 template <int D, int CAL, int MODE, bool FULL, typename TIn>
 static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int stage) {
   if (stage & 1) {
@@ -425,11 +386,7 @@ static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage & 2) {
-    const int nkt = (p.T + KV_BN - 1) / KV_BN;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
-    return hipGetLastError();
-  }
+  if (stage & 2) return dkdv_go<D, TIn>(p, a, s);
   return hipSuccess;
 }
 template <int D, int CAL, int MODE, bool FULL>

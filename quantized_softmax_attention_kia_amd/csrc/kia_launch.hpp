@@ -36,8 +36,6 @@ struct Problem {
   int calib, mode, full, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
 };
 
-struct RowP;  // per-row record of the backward (kia_bwd.hip)
-
 struct FwdArgs {
   int nheads;
   const void* q;
@@ -61,8 +59,8 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  RowP* rowp;    // [N] per-row record written by the dq kernel for the key-major pass
-  float* tab;    // [N, K+1] grid tables written by the dq kernel
+  float* pt;     // key-major tiles of the forward's P, written by the dq kernel
+  float* dst;    // key-major tiles of dS (extremum terms included), written by the dq kernel
   int T, K, causal;
   float tau, scale;
 };
@@ -75,7 +73,7 @@ struct BinsArgs {
 };
 
 hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
-// stages: bit 0 = dq kernel (dQ, D_i, alpha, beta), bit 1 = dkdv kernel (dK, dV)
+// stages: bit 0 = dq kernel (dQ and the P, dS tiles), bit 1 = dkdv kernel (dK, dV)
 hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s, int stages);
 hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s);
 

@@ -53,11 +53,11 @@ def test_workspace_layout(kb):
     nt = (100 + 31) // 32
     tiles = 2 * 3 * nt * (nt + 1) // 2 * 4096        # stored causal score tiles
     st, rr, w = ws(kb, params(kb))
-    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == rnd(N * 64) + rnd(N * 5 * 4)
+    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles   # key-major P and dS tiles
     st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
     assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
     st, rr, w = ws(kb, params(kb, causal=0))
-    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096
+    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096 and w == 2 * 2 * 3 * nt * nt * 4096
     st, rr, w = ws(kb, params(kb, B=0))
     assert st == 0 and rr == 0
 
