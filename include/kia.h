@@ -92,9 +92,9 @@ typedef struct {
  *  bwd_ws_bytes: scratch for kia_backward: two arrays of float tiles numbered
  *    like S, P[B*H][tiles][1024] (the forward's normalized weights: P^L for LERP,
  *    the hard P^N for Nearest) and dS[B*H][tiles][1024] (the unscaled score
- *    gradients, extremum terms included), both key-major: element (query tile
- *    row a, key tile column b) of a tile at float offset v*64 + b + 32*g, where
- *    a = 8*(v/4) + 4*g + v%4.
+ *    gradients, extremum terms included).  Within a tile of S, P or dS, element
+ *    (query row a, key column b of the tile) sits at float offset v*64 + a + 32*g,
+ *    where b = 8*(v/4) + 4*g + v%4.
  * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
  * KIA_ERR_UNSUPPORTED for parameters kia_forward would reject.
  */

@@ -20,11 +20,13 @@
 //               and the VALU, dQ_self = sum dS_self K, the row sums a_i, b_i, then the
 //               extremum terms of dQ (gathered rows of K at the arg-max / arg-min; a second
 //               sweep adds extra tied keys when a row has any).  Per tile it also writes the
-//               normalized forward weights P and the score gradients dS, transposed through
-//               LDS into key-major tiles, and after the sweep adds alpha_i = a_i/nA_i and
-//               beta_i = b_i/nC_i into dS at the row's extremum keys.
-//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q, straight
-//               from those tiles: no decisions, no row records, no atomics.
+//               normalized forward weights P and the score gradients dS, in the tile order of
+//               the stored scores, and after the sweep adds alpha_i = a_i/nA_i and
+//               beta_i = b_i/nC_i into dS at the row's extremum keys (each element is patched
+//               by the lane that wrote it).
+//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q from those
+//               tiles, each transposed by its wave through LDS: no decisions, no row
+//               records, no atomics.
 // Both sweep their tiles while the next tile's operands are already being loaded.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
@@ -44,29 +46,28 @@ template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) {
   return __uint_as_float(((uint32_t)*p) << 16);
 }
 
-// Key-major tiles of P and dS written by the dq kernel: tile (qt, kt) holds element
-// (query a, key b) at float offset v * 64 + b + 32 g where a = crow(v, g), the operand
-// order of tile_accum when the lane's output row is the key.  Same tile numbering as the
-// stored scores.
-__device__ __forceinline__ size_t kmajor_offset(int a, int b) {
-  const int g = (a >> 2) & 1, v = 4 * (a >> 3) + (a & 3);
-  return (size_t)v * 64 + b + 32 * g;
+// Offset of element (query a, key b) inside a stored tile (scores, P, dS): v * 64 + a + 32 g
+// where b = crow(v, g).  Lane l = a + 32 g of the wave owning the query tile holds it.
+__device__ __forceinline__ int stored_offset(int a, int b) {
+  const int g = (b >> 2) & 1, v = 4 * (b >> 3) + (b & 3);
+  return v * 64 + a + 32 * g;
 }
+__device__ __forceinline__ int stored_lane_group(int b) { return (b >> 2) & 1; }
 
 // ============================================================================ dq kernel
 template <int D>
 struct DqSmem {
   float Ks[BN * (D + 4)];
   float Vs[BN * (D + 4)];
-  float Pt[NW][BN * TLD];   // per-wave transposes of the P and dS tiles
-  float dSt[NW][BN * TLD];
+  float dOs[DQ_BM * (D + 4)];  // the workgroup's dO rows
   float alpha[DQ_BM], beta[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
   // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 1) floats
 };
 
+// At D = 64 the register budget is held to two waves per SIMD.
 template <int D, int CAL, int MODE, bool FULL, typename TIn>
-__global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dq_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<D>& sm = *reinterpret_cast<DqSmem<D>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D>));
@@ -93,12 +94,18 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
   const float* Sh = a.rec.S + tbase * 1024;
   float* Ph = a.pt + tbase * 1024;
   float* dSh = a.dst + tbase * 1024;
-  float* trp = sm.Pt[w];
-  float* trd = sm.dSt[w];
   auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
-  float doreg[D / 2];
-  load_row_operand<D>(doreg, dOp + (size_t)qi * D, qvalid, 1.0f);
+  {  // the workgroup's dO rows, read from LDS by every dO V^T product
+    TileRegs<D, NT, TIn> dr;
+#pragma unroll
+    for (int h = 0; h < DQ_BM / BN; ++h) {
+      dr.load(dOp, qb0 + h * BN, T);
+      dr.store(sm.dOs + h * BN * LD, LD, 1.0f);
+    }
+  }
+  const float* dOw = sm.dOs + 32 * w * LD;
+  __syncthreads();
 
   // row record of the forward
   const float M = a.rec.M[row], m = a.rec.m[row];
@@ -112,13 +119,15 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
   float Di;
   {
     const float* X = ((MODE == NEAREST_P) ? a.rec.OL : a.o) + hb + (size_t)qi * D + 4 * g;
+    const float* Y = dOw + c * LD + 4 * g;
     double part = 0.0;
     if (qvalid) {
 #pragma unroll
       for (int q = 0; q < D / 8; ++q) {
         const f4v x = *reinterpret_cast<const f4v*>(X + 8 * q);
+        const f4v y = *reinterpret_cast<const f4v*>(Y + 8 * q);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fma((double)doreg[4 * q + e], (double)x[e], part);
+        for (int e = 0; e < 4; ++e) part = fma((double)y[e], (double)x[e], part);
       }
     }
     Di = (float)(part + __shfl_xor(part, 32));
@@ -163,7 +172,10 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       }
     }
     if (!active(kt)) continue;
-    const f16v gt = tile_dot<D>(sm.Vs, LD, doreg);  // (dO V^T)^T: g_ij = dO_i . V_j
+    const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+    float* Pw = Ph + to;
+    float* dSw = dSh + to;
+    const f16v gt = tile_dot_lds<D>(sm.Vs, dOw, LD);  // (dO V^T)^T: g_ij = dO_i . V_j
     f16v ds;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -177,8 +189,8 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       const float dS = gam * Delta;
       ds[v] = dS;
       // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
-      trp[c * TLD + crow(v, g)] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
-      trd[c * TLD + crow(v, g)] = dS;
+      Pw[v * 64 + l] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
+      dSw[v * 64 + l] = dS;
       if (FULL) {
         sds += (double)dS;
         if (CAL == MINMAX) {
@@ -190,17 +202,6 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
       }
     }
     tile_accum<D>(dq, ds, sm.Ks, LD);
-    // the wave's P and dS tiles, read back key-major and written as one 256-byte row per register
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int qr = crow(v, g);
-      Ph[to + v * 64 + l] = trp[qr * TLD + c];
-      dSh[to + v * 64 + l] = trd[qr * TLD + c];
-    }
   }
 
   // extremum terms of the row: alpha per tied max key, beta per tied min key
@@ -219,16 +220,15 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
         alpha = (float)(-sds / (double)nA);
       }
     }
-    // dS of the first arg-max / arg-min key of the row gains alpha / beta; the tiles were
-    // written by lanes of this wave, visible to the whole workgroup after the barrier
-    __syncthreads();
-    if (inject && g == 0) {
-      float* e = dSh + tile_index(qtw, amax / BN, a.rec.nt, a.causal) * 1024 + kmajor_offset(c, amax % BN);
+    // dS of the first arg-max / arg-min key of the row gains alpha / beta, added by the lane
+    // that stored the element (program order makes its own store visible to it)
+    if (inject && g == stored_lane_group(amax % BN)) {
+      float* e = dSh + tile_index(qtw, amax / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amax % BN);
       *e = *e + alpha;
-      if (CAL == MINMAX) {
-        float* f = dSh + tile_index(qtw, amin / BN, a.rec.nt, a.causal) * 1024 + kmajor_offset(c, amin % BN);
-        *f = *f + beta;
-      }
+    }
+    if (CAL == MINMAX && inject && g == stored_lane_group(amin % BN)) {
+      float* e = dSh + tile_index(qtw, amin / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amin % BN);
+      *e = *e + beta;
     }
   }
   if (FULL && blockties) {
@@ -252,10 +252,7 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a) {
         if (ok && sv == M && key != amax) x += alpha;
         if (CAL == MINMAX && ok && sv == m && key != amin) x += beta;
         inj[v] = x;
-        if (x != 0.f) {
-          float* e = dSh + to + kmajor_offset(c, crow(v, g));
-          *e = *e + x;
-        }
+        if (x != 0.f) dSh[to + v * 64 + l] += x;  // stored by this lane in the first sweep
       }
       tile_accum<D>(dq, inj, sm.Ks, LD);
     }
@@ -294,6 +291,8 @@ template <int D>
 struct KvSmem {
   float Qs[BN * (D + 4)];
   float dOs[BN * (D + 4)];
+  float Pt[NW][BN * TLD];   // per-wave transposes of the P and dS tiles
+  float dSt[NW][BN * TLD];
 };
 
 // Operands of one query tile, held in registers while the previous tile computes: the Q and
@@ -321,7 +320,7 @@ __device__ __forceinline__ void kv_load(KvPrefetch<D, TIn>& pf, const BwdArgs& a
 }
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   __shared__ KvSmem<D> sm;
   constexpr int LD = D + 4;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
@@ -335,6 +334,8 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
   const int ktw = kw0 / BN;  // the wave's key tile
   const size_t tbase = (size_t)head * a.rec.tiles_per_head;
   auto active = [&](int qt) { return kw0 < T && (!a.causal || ktw <= qt); };  // wave-uniform
+  float* trp = sm.Pt[w];
+  float* trd = sm.dSt[w];
 
   f16v dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -348,10 +349,23 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a) {
     __syncthreads();
     pf.q.store(sm.Qs, LD, a.scale);
     pf.dO.store(sm.dOs, LD, 1.0f);
+    if (act) {
+      // tile (qt, ktw) as stored: element (query l%32, key crow(v, g)) at v * 64 + l
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        trp[c * TLD + crow(v, g)] = pf.p[v];
+        trd[c * TLD + crow(v, g)] = pf.ds[v];
+      }
+    }
     __syncthreads();
-    const f16v p = pf.p, ds = pf.ds;  // element (query crow(v, g), key c); zero where masked
     if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt + 1, ktw, active(qt + 1));
     if (!act) continue;
+    f16v p, ds;  // element (query crow(v, g), key c); zero where masked
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = trp[crow(v, g) * TLD + c];
+      ds[v] = trd[crow(v, g) * TLD + c];
+    }
     tile_accum<D>(dv, p, sm.dOs, LD);
     tile_accum<D>(dk, ds, sm.Qs, LD);
   }

@@ -105,6 +105,23 @@ __device__ __forceinline__ f16v tile_dot(const float* arows, int ld, const float
   return acc;
 }
 
+// The same product with both operands in LDS: C[a][b] = sum_d Arows[a][d] * Brows[b][d].
+template <int D>
+__device__ __forceinline__ f16v tile_dot_lds(const float* arows, const float* brows, int ld) {
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+  const float* ra = arows + c * ld + 4 * g;
+  const float* rb = brows + c * ld + 4 * g;
+  f16v acc = zero16();
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    const f4v x = *reinterpret_cast<const f4v*>(ra + 8 * q);
+    const f4v y = *reinterpret_cast<const f4v*>(rb + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma32(x[e], y[e], acc);
+  }
+  return acc;
+}
+
 // Scores of one 32 (query) x 32 (key) tile in double: four 16x16 sub-tiles of S^T = K Q^T.
 // K rows (32, stride ld floats) sit in LDS; qr holds the lane's query operand:
 // qr[qb * (D/4) + 4j + e] = Q[16 qb + l%16][16 j + 4 (l/16) + e] (MFMA step 4j + e).

@@ -63,8 +63,9 @@ __device__ __forceinline__ void ext_merge(Ext& a, int lanemask) {
   a.mn = m;
 }
 
+// At D = 64 the register budget is held to two waves per SIMD.
 template <int D, int CAL, int MODE, typename TIn>
-__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FwdSmem<D>& sm = *reinterpret_cast<FwdSmem<D>*>(smem_raw);
   constexpr int LDK = D + 4, LDV = D + 8;
