@@ -287,42 +287,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 }
 
 // ============================================================================ dkdv kernel
-template <int D>
+// Number of bf16 slices that represent an input element exactly enough: bf16 inputs are exact.
+template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
+
+template <int D, int NS>
 struct KvSmem {
-  float Qs[BN * (D + 4)];
-  float dOs[BN * (D + 4)];
-  float Pt[NW][BN * TLD];   // per-wave transposes of the P and dS tiles
-  float dSt[NW][BN * TLD];
+  __bf16 QT[NS * D * TP];   // Q^T of the query tile, bf16 slices
+  __bf16 dOT[NS * D * TP];  // dO^T of the query tile
 };
 
 // Operands of one query tile, held in registers while the previous tile computes: the Q and
-// dO rows (shared by the workgroup through LDS) and the wave's P and dS tiles.
+// dO rows (staged through LDS for the workgroup) and the wave's P and dS values.
 template <int D, typename TIn>
 struct KvPrefetch {
-  TileRegs<D, NT, TIn> q, dO;
-  f16v p, ds;
+  PairRegs<D, TIn> q, dO;
+  f4v p[4], ds[4];
 };
 
+// Lane (c, g) loads, for its key c of the wave's key tile, the stored P and dS of the queries
+// crow(v, g) (v = 0..15): in a stored tile they sit at v_c * 64 + 32 g_c + (query) with
+// c = crow(v_c, g_c), so they form four aligned runs of four floats.
 template <int D, typename TIn>
 __device__ __forceinline__ void kv_load(KvPrefetch<D, TIn>& pf, const BwdArgs& a, const TIn* Qp, const TIn* dOp,
                                         size_t tbase, int qt, int ktw, bool act) {
-  const int l = threadIdx.x & 63;
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
   pf.q.load(Qp, qt * BN, a.T);
   pf.dO.load(dOp, qt * BN, a.T);
   if (act) {
-    const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024;
+    const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024 +
+                      (4 * (c >> 3) + (c & 3)) * 64 + 32 * ((c >> 2) & 1) + 4 * g;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      pf.p[v] = a.pt[to + v * 64 + l];
-      pf.ds[v] = a.dst[to + v * 64 + l];
+    for (int q = 0; q < 4; ++q) {
+      pf.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
+      pf.ds[q] = *reinterpret_cast<const f4v*>(a.dst + to + 8 * q);
     }
   }
 }
 
 template <int D, typename TIn>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
-  __shared__ KvSmem<D> sm;
-  constexpr int LD = D + 4;
+  constexpr int NS = nslices<TIn>();
+  __shared__ KvSmem<D, NS> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, nt = a.rec.nt;
   int head, kt;
@@ -334,8 +339,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const int ktw = kw0 / BN;  // the wave's key tile
   const size_t tbase = (size_t)head * a.rec.tiles_per_head;
   auto active = [&](int qt) { return kw0 < T && (!a.causal || ktw <= qt); };  // wave-uniform
-  float* trp = sm.Pt[w];
-  float* trd = sm.dSt[w];
 
   f16v dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -347,27 +350,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   for (int qt = qt_first; qt < nt; ++qt) {
     const bool act = active(qt);
     __syncthreads();
-    pf.q.store(sm.Qs, LD, a.scale);
-    pf.dO.store(sm.dOs, LD, 1.0f);
-    if (act) {
-      // tile (qt, ktw) as stored: element (query l%32, key crow(v, g)) at v * 64 + l
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        trp[c * TLD + crow(v, g)] = pf.p[v];
-        trd[c * TLD + crow(v, g)] = pf.ds[v];
-      }
-    }
+    pf.q.template store_t<NS>(sm.QT);
+    pf.dO.template store_t<NS>(sm.dOT);
     __syncthreads();
+    // element (query crow(v, g), key c) of P and dS; zero where masked
+    float p[16], ds[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { p[4 * q + e] = pf.p[q][e]; ds[4 * q + e] = pf.ds[q][e]; }
     if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt + 1, ktw, active(qt + 1));
     if (!act) continue;
-    f16v p, ds;  // element (query crow(v, g), key c); zero where masked
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = trp[crow(v, g) * TLD + c];
-      ds[v] = trd[crow(v, g) * TLD + c];
+    for (int b = 0; b < 2; ++b) {
+      const Split8 ps = split8(p + 8 * b), dss = split8(ds + 8 * b);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        dv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), dv[nb]);
+        dk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), dk[nb]);
+      }
     }
-    tile_accum<D>(dv, p, sm.dOs, LD);
-    tile_accum<D>(dk, ds, sm.Qs, LD);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
       float* pv = a.dv + hb + (size_t)key * D + c;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
-        pk[32 * nb] = dk[nb][v];
+        pk[32 * nb] = dk[nb][v] * a.scale;
         pv[32 * nb] = dv[nb][v];
       }
     }

@@ -74,6 +74,119 @@ template <> struct Ld<uint16_t> {
   }
 };
 
+// ---------------------------------------------------------------------------------------------
+// bf16 MFMA (32x32x16): lane l supplies A[l%32][8(l/32) + e] and B[8(l/32) + e][l%32] for e < 8;
+// the accumulator has the layout of the fp32 32x32 MFMA.  These run on the matrix pipe, beside
+// the VALU, while the fp32 / fp64 MFMAs share the VALU's issue.  An fp32 product is carried out
+// on three bf16 slices per operand, x = h + m + l (each the round-to-nearest-even bf16 of what
+// the previous slices leave; |x - (h + m + l)| <= 2^-24 |x|), keeping the six slice products
+// whose weight is at least 2^-16 of h h'.
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16v mfma_bf16(bf8v a, bf8v b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split8 {
+  bf8v h, m, l;
+};
+
+__device__ __forceinline__ Split8 split8(const float* x) {
+  Split8 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    const float r = x[e] - (float)h;   // exact: h is within a factor 2 of x
+    const __bf16 m = (__bf16)r;
+    s.h[e] = h;
+    s.m[e] = m;
+    s.l[e] = (__bf16)(r - (float)m);
+  }
+  return s;
+}
+
+// c += A B for one 16-deep block.  NSB = 1 when B is exact in bf16 (its m, l slices are zero).
+template <int NSB>
+__device__ __forceinline__ f16v mfma_split(const Split8& a, const Split8& b, f16v c) {
+  c = mfma_bf16(a.l, b.h, c);
+  if (NSB == 3) {
+    c = mfma_bf16(a.m, b.m, c);
+    c = mfma_bf16(a.h, b.l, c);
+  }
+  c = mfma_bf16(a.m, b.h, c);
+  if (NSB == 3) c = mfma_bf16(a.h, b.m, c);
+  return mfma_bf16(a.h, b.h, c);
+}
+
+// A 32-row tile of a [T, D] head tensor staged transposed into LDS as NS bf16 slices,
+// XT[s][d * TP + r] (r = row within the tile), the B operand of a bf16 product that contracts
+// over the rows.  Thread t of the 128 holds rows 2 (t % 16) and 2 (t % 16) + 1 at the columns
+// (t / 16) * CW ... + CW - 1 and writes each pair of rows as one 32-bit word.  TP = 36 keeps
+// both the pair writes and the 8-byte operand reads free of bank conflicts.
+constexpr int TP = 36;
+
+template <int D, typename T>
+struct PairRegs {
+  static constexpr int CW = D / 8;
+  float x0[CW], x1[CW];
+  __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
+    const int t = threadIdx.x, rp = t & 15, cg = t >> 4;
+    const int r0 = row0 + 2 * rp;
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      const f4v a = r0 < nrows ? Ld<T>::four(src + (size_t)r0 * D + cg * CW + 4 * j) : f4v{0.f, 0.f, 0.f, 0.f};
+      const f4v b = r0 + 1 < nrows ? Ld<T>::four(src + (size_t)(r0 + 1) * D + cg * CW + 4 * j)
+                                   : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x0[4 * j + e] = a[e]; x1[4 * j + e] = b[e]; }
+    }
+  }
+  template <int NS>
+  __device__ __forceinline__ void store_t(__bf16* xt) const {
+    const int t = threadIdx.x, rp = t & 15, cg = t >> 4;
+    uint32_t* w = reinterpret_cast<uint32_t*>(xt);
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int at = ((cg * CW + j) * TP + 2 * rp) >> 1;
+      const __bf16 h0 = (__bf16)x0[j], h1 = (__bf16)x1[j];
+      w[at] = pack(h0, h1);
+      if (NS == 3) {
+        const float r0 = x0[j] - (float)h0, r1 = x1[j] - (float)h1;
+        const __bf16 m0 = (__bf16)r0, m1 = (__bf16)r1;
+        w[at + (D * TP >> 1)] = pack(m0, m1);
+        w[at + (D * TP)] = pack((__bf16)(r0 - (float)m0), (__bf16)(r1 - (float)m1));
+      }
+    }
+  }
+  __device__ static __forceinline__ uint32_t pack(__bf16 lo, __bf16 hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+};
+
+// B operand slices for k-block b (rows 16b .. 16b+15) and output column n of the transposed tile.
+// Lane (n, g) supplies rows 16b + 4g + (0..3) and 16b + 8 + 4g + (0..3): the rows that the
+// accumulator-layout coefficients v = 8b .. 8b+7 of lane (., g) stand for (crow(v, g)).
+template <int D, int NS>
+__device__ __forceinline__ Split8 load_bt(const __bf16* xt, int b, int n) {
+  const int g = (threadIdx.x & 63) >> 5;
+  Split8 r;
+  const __bf16* p = xt + n * TP + 16 * b + 4 * g;
+  auto rd = [&](const __bf16* q) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(q);
+    const uint2 hi = *reinterpret_cast<const uint2*>(q + 8);
+    bf8v v;
+    const uint4 u = uint4{lo.x, lo.y, hi.x, hi.y};
+    __builtin_memcpy(&v, &u, 16);
+    return v;
+  };
+  r.h = rd(p);
+  if (NS == 3) {
+    r.m = rd(p + D * TP);
+    r.l = rd(p + 2 * D * TP);
+  }
+  return r;
+}
+
 // Dimension order of a score dot product: MFMA step 4q+e takes dims 8q+e (lanes 0-31)
 // and 8q+4+e (lanes 32-63).  A lane's register operand for its own row holds, at index
 // 4q+e, dim 8q + 4(l/32) + e.
