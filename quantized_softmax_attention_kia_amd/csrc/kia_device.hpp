@@ -105,32 +105,31 @@ __device__ __forceinline__ Split8 split8(const float* x) {
   return s;
 }
 
-// c += A B for one 16-deep block.  NSB = 1 when B is exact in bf16 (its m, l slices are zero).
-template <int NSB>
+// c += A B for one 16-deep block, smallest products first.  NSA / NSB = 1 when that operand is
+// exact in bf16 (its m, l slices are zero and are not read).
+template <int NSB, int NSA = 3>
 __device__ __forceinline__ f16v mfma_split(const Split8& a, const Split8& b, f16v c) {
-  c = mfma_bf16(a.l, b.h, c);
-  if (NSB == 3) {
-    c = mfma_bf16(a.m, b.m, c);
-    c = mfma_bf16(a.h, b.l, c);
-  }
-  c = mfma_bf16(a.m, b.h, c);
+  if (NSA == 3) c = mfma_bf16(a.l, b.h, c);
+  if (NSA == 3 && NSB == 3) c = mfma_bf16(a.m, b.m, c);
+  if (NSB == 3) c = mfma_bf16(a.h, b.l, c);
+  if (NSA == 3) c = mfma_bf16(a.m, b.h, c);
   if (NSB == 3) c = mfma_bf16(a.h, b.m, c);
   return mfma_bf16(a.h, b.h, c);
 }
 
 // A 32-row tile of a [T, D] head tensor staged transposed into LDS as NS bf16 slices,
 // XT[s][d * TP + r] (r = row within the tile), the B operand of a bf16 product that contracts
-// over the rows.  Thread t of the 128 holds rows 2 (t % 16) and 2 (t % 16) + 1 at the columns
-// (t / 16) * CW ... + CW - 1 and writes each pair of rows as one 32-bit word.  TP = 36 keeps
-// both the pair writes and the 8-byte operand reads free of bank conflicts.
+// over the rows.  Thread t of the NTH staging threads holds rows 2 (t % 16) and 2 (t % 16) + 1
+// at the columns (t / 16) * CW ... + CW - 1 and writes each pair of rows as one 32-bit word.
+// TP = 36 keeps the 8-byte operand reads free of bank conflicts.
 constexpr int TP = 36;
 
-template <int D, typename T>
+template <int D, typename T, int NTH = 128>
 struct PairRegs {
-  static constexpr int CW = D / 8;
+  static constexpr int CW = D * 16 / NTH;
   float x0[CW], x1[CW];
   __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
-    const int t = threadIdx.x, rp = t & 15, cg = t >> 4;
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
     const int r0 = row0 + 2 * rp;
 #pragma unroll
     for (int j = 0; j < CW / 4; ++j) {
@@ -143,7 +142,7 @@ struct PairRegs {
   }
   template <int NS>
   __device__ __forceinline__ void store_t(__bf16* xt) const {
-    const int t = threadIdx.x, rp = t & 15, cg = t >> 4;
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
     uint32_t* w = reinterpret_cast<uint32_t*>(xt);
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
@@ -162,6 +161,57 @@ struct PairRegs {
     return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
 };
+
+// A 32-row tile staged in its natural layout as NS bf16 slices, XN[s][r * NP + d], for A / B
+// operands that contract over the columns (8 consecutive columns per lane).  Thread t of the
+// NTH holds PER consecutive values of one row.  NP = D + 8 keeps the 16-byte reads and writes
+// free of bank conflicts.
+template <int D>
+constexpr int np() { return D + 8; }
+
+template <int D, typename T, int NTH = 128>
+struct RowRegs {
+  static constexpr int PER = 32 * D / NTH;
+  float x[PER];
+  __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+    const int gr = row0 + r;
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const f4v a = gr < nrows ? Ld<T>::four(src + (size_t)gr * D + c0 + 4 * j) : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = a[e];
+    }
+  }
+  template <int NS>
+  __device__ __forceinline__ void store(__bf16* xn) const {
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+#pragma unroll
+    for (int j = 0; j < PER / 8; ++j) {
+      const Split8 sp = split8(x + 8 * j);
+      __bf16* o = xn + r * np<D>() + c0 + 8 * j;
+      *reinterpret_cast<bf8v*>(o) = sp.h;
+      if (NS == 3) {
+        *reinterpret_cast<bf8v*>(o + 32 * np<D>()) = sp.m;
+        *reinterpret_cast<bf8v*>(o + 64 * np<D>()) = sp.l;
+      }
+    }
+  }
+};
+
+// Slices of 8 consecutive columns 16 kb + 8 (l/32) .. of row `row` of a natural-layout tile.
+template <int D, int NS>
+__device__ __forceinline__ Split8 load_an(const __bf16* xn, int row, int kb) {
+  const int g = (threadIdx.x & 63) >> 5;
+  const __bf16* p = xn + row * np<D>() + 16 * kb + 8 * g;
+  Split8 r;
+  r.h = *reinterpret_cast<const bf8v*>(p);
+  if (NS == 3) {
+    r.m = *reinterpret_cast<const bf8v*>(p + 32 * np<D>());
+    r.l = *reinterpret_cast<const bf8v*>(p + 64 * np<D>());
+  }
+  return r;
+}
 
 // B operand slices for k-block b (rows 16b .. 16b+15) and output column n of the transposed tile.
 // Lane (n, g) supplies rows 16b + 4g + (0..3) and 16b + 8 + 4g + (0..3): the rows that the

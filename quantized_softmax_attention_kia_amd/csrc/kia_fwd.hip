@@ -2,261 +2,525 @@
 //
 // "Pretraining Transformers with Quantized Softmax in Attention", §3: the grid
 // of a row depends on the row's final extrema, so the online-softmax rescale
-// does not apply.  One workgroup owns 64 query rows of one head (2 waves x 32
-// rows; small workgroups, heaviest first, so the causal triangle balances over
-// the CUs) and sweeps the visible key tiles twice, loading the next tile while
-// it computes the current one:
-//   pass 1  scores of each 32 x 32 tile on the fp64 MFMA (exact products of the
-//           fp32 inputs, double accumulation, scale applied in double), rounded
-//           once to fp32 and stored for every later pass; row max / min, first
-//           index attaining them and tie counts on the stored values;
+// does not apply.  A workgroup owns 32 query rows of one head (heaviest first); its
+// FWD_NW waves split the visible key tiles between them (wave w takes every
+// FWD_NW-th), so the longest rows do not hold the whole kernel back, and sweep them
+// twice, loading the next tile while they compute the current one; partial results
+// meet in LDS, in a fixed order:
+//   pass 1  scores of each 32 x 32 tile as bf16 slice products on the matrix pipe
+//           (K operands loaded straight from memory into registers) with a
+//           rigorous error bound per row, stored for every later pass; the row
+//           max / min, first index attaining them and tie counts are then settled
+//           on exact scores (double products and sums, rounded once to fp32): the
+//           winner alone when the runner-up is farther than twice the bound, else
+//           every candidate within it, each patched into the stored tile;
 //   then    per-row calibration and the (K+1)-entry grid table e^{b_r} in LDS
 //           (the only exponentials of the operator);
-//   pass 2  stored scores -> bin decision -> LERP / Nearest weight from the
-//           table (no exp) -> row sums W^L, W^N -> O += w V on the fp32 MFMA (and
-//           O^L += w^L V for Nearest with Prob-STE) -> O = num / W (the strict
-//           hard forward for Nearest).  Row sums are kept in double and each
-//           tile's P V is summed into a fresh accumulator before joining the
-//           running O, so the precision of O (which the backward's D_i = dO . O
-//           amplifies) does not decay with T.
-// K (pass 1) and V (pass 2) tiles are staged through LDS and shared by the waves.
+//   pass 2  stored scores -> bin decision (one closer to a boundary than the
+//           bound is taken again on the exact score, patched in likewise, so every
+//           pass decides as on exact scores) -> LERP / Nearest weight from the table
+//           (no exp) -> row sums W^L, W^N -> O += w V as bf16 slice products on the
+//           matrix pipe, V^T staged in LDS by the wave (and O^L += w^L V for Nearest
+//           with Prob-STE) -> O = num / W (the strict hard forward for Nearest).  Row sums are kept in double and each tile's P V is summed
+//           into a fresh accumulator before joining the running O, so the
+//           precision of O (which the backward's D_i = dO . O amplifies) does not
+//           decay with T.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace kia {
 
-constexpr int NW = 2;              // waves per workgroup
-constexpr int NT = 64 * NW;        // threads per workgroup
-constexpr int FWD_BM = 32 * NW;    // query rows per workgroup
-constexpr int BN = 32;             // keys per tile
-constexpr int SCR = 80;            // row stride of the per-wave tile scratch (bank-conflict free writes)
+constexpr int FWD_NW = 2;            // waves per workgroup, splitting the key tiles of a query tile
+constexpr int FWD_NT = 64 * FWD_NW;
+constexpr int BN = 32;               // keys per tile, query rows per workgroup
 
-template <int D>
+template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
+
+// Approximate extrema of a row: largest value, its first key and the runner-up; smallest
+// value, its first key and the runner-up.  Keys reach a lane in increasing order.
+struct Top2 {
+  float mx, mx2, mn, mn2;
+  int ax, an;
+};
+// Exact extrema of a row over the stored scores: value, first key, count of ties.
+struct XExt {
+  float v;
+  int k, n;
+};
+
+template <int D, int NS>
+constexpr int fwd_wave_bytes() {  // per wave: V^T slices of its key tile, later its partial O
+  return NS * D * TP * 2 > D / 32 * 4096 ? NS * D * TP * 2 : D / 32 * 4096;
+}
+
+template <int D, int NS>
 struct FwdSmem {
-  union {
-    float Ks[BN * (D + 4)];  // pass 1
-    float Vs[BN * (D + 8)];  // pass 2
-  };
-  float scratch[NW][16 * SCR];  // per-wave tile re-layout (pass 1)
-  float rowM[FWD_BM], rowm[FWD_BM], rowW[FWD_BM], rowWL[FWD_BM];
-  int rowax[FWD_BM], rowan[FWD_BM], rowcx[FWD_BM], rowcn[FWD_BM];
-  // followed in dynamic LDS by the grid table: FWD_BM rows x (K + 1) floats
+  __align__(16) unsigned char wave[FWD_NW][fwd_wave_bytes<D, NS>()];
+  Top2 ext[FWD_NW][BN];
+  float amx[FWD_NW][BN];
+  XExt xM[FWD_NW][BN], xm[FWD_NW][BN];
+  double sL[FWD_NW][BN], sN[FWD_NW][BN];
+  float rowW[BN], rowWL[BN];
+  // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
 };
 
-struct Ext {  // running max / min with first index and count
-  float mx, mn;
-  int ax, an, cx, cn;
+// LDS written by some lanes of the wave and read by others: the wave's LDS operations run in
+// program order, so only the compiler has to be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Error bound of a score taken from bf16 slice products (u = 2^-24).  With fp32 inputs each
+// operand is split into three slices (x = h + m + l + e, |m| <= 2^-8 |x|, |l| <= 2^-16 |x|,
+// |e| <= 2^-24 |x|); h h' is accumulated apart from the five smaller products kept (their
+// magnitudes add up to at most 0.008 |q_d k_d|), every product exact in fp32.  Any order of
+// n fp32 additions errs by at most (n - 1) u sum|terms|, so the two sums err by at most
+// 1.008 (D - 1) u S and 5D u 0.008 S (S = sum_d |q_d k_d|), the dropped products by 4.1 u S,
+// and the final add, the fp32 scale product and the rounding of the exact score to fp32 by
+// 4 u |s|.  S <= 1.01 A, where A is the fp32 sum of |q_h| |k_h| (|x| <= |h| / (1 - 2^-8)),
+// one more bf16 product.  With bf16 inputs only h h' exists, exact in bf16.  So
+// |s~ - s| <= scale * ACC_C * A + 2^-22 |s~|, and a decision this bound cannot settle is taken
+// again on the score recomputed exactly (double products and sums, rounded once).
+template <int D, int NS>
+constexpr double acc_c() {
+  return NS == 3 ? 1.01 * (1.008 * (D - 1) + 0.04 * D + 4.1) * 0x1p-24 : 1.01 * D * 0x1p-24;
+}
+
+// The exact score of one (query, key) pair: products and sum in double, scale in double,
+// rounded once to fp32 -- the value the bound is measured against.
+template <int D, typename TIn>
+__device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, double scale) {
+  double acc = 0.0;
+#pragma unroll 4
+  for (int d = 0; d < D; d += 4) {
+    const f4v x = Ld<TIn>::four(qrow + d), y = Ld<TIn>::four(krow + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fma((double)x[e], (double)y[e], acc);
+  }
+  return (float)(scale * acc);
+}
+
+// One lane's operand of a row for the score product: columns 16 kb + 8 (l/32) .. + 7.
+template <int D, typename TIn> struct RowOp;
+template <int D> struct RowOp<D, float> {
+  float x[D / 2];
+  __device__ __forceinline__ void load(const float* base, int row, int nrows) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f4v a = row < nrows ? *reinterpret_cast<const f4v*>(base + (size_t)row * D + 16 * kb + 8 * g + 4 * h)
+                                  : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[8 * kb + 4 * h + e] = a[e];
+      }
+  }
+  __device__ __forceinline__ Split8 split(int kb) const { return split8(x + 8 * kb); }
+};
+template <int D> struct RowOp<D, uint16_t> {
+  uint4 x[D / 16];
+  __device__ __forceinline__ void load(const uint16_t* base, int row, int nrows) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      x[kb] = row < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)row * D + 16 * kb + 8 * g)
+                          : uint4{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ Split8 split(int kb) const {
+    Split8 s;
+    __builtin_memcpy(&s.h, &x[kb], 16);
+    return s;
+  }
 };
 
-__device__ __forceinline__ void ext_merge(Ext& a, int lanemask) {
-  const float mx2 = __shfl_xor(a.mx, lanemask), mn2 = __shfl_xor(a.mn, lanemask);
-  const int ax2 = __shfl_xor(a.ax, lanemask), an2 = __shfl_xor(a.an, lanemask);
-  const int cx2 = __shfl_xor(a.cx, lanemask), cn2 = __shfl_xor(a.cn, lanemask);
-  const float M = fmaxf(a.mx, mx2), m = fminf(a.mn, mn2);
-  a.ax = min(a.mx == M ? a.ax : INT_MAX, mx2 == M ? ax2 : INT_MAX);
-  a.an = min(a.mn == m ? a.an : INT_MAX, mn2 == m ? an2 : INT_MAX);
-  a.cx = (a.mx == M ? a.cx : 0) + (mx2 == M ? cx2 : 0);
-  a.cn = (a.mn == m ? a.cn : 0) + (mn2 == m ? cn2 : 0);
-  a.mx = M;
-  a.mn = m;
+__device__ __forceinline__ bf8v bf_abs(bf8v v) {
+  uint4 u;
+  __builtin_memcpy(&u, &v, 16);
+  u.x &= 0x7fff7fffu; u.y &= 0x7fff7fffu; u.z &= 0x7fff7fffu; u.w &= 0x7fff7fffu;
+  bf8v r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+__device__ __forceinline__ void top2(Top2& e, float x, int key) {
+  const bool gx = x > e.mx;
+  e.mx2 = gx ? e.mx : (x > e.mx2 ? x : e.mx2);
+  e.ax = gx ? key : e.ax;
+  e.mx = gx ? x : e.mx;
+  const bool ln = x < e.mn;
+  e.mn2 = ln ? e.mn : (x < e.mn2 ? x : e.mn2);
+  e.an = ln ? key : e.an;
+  e.mn = ln ? x : e.mn;
+}
+// Merge the extrema of another set of keys; on equal maxima / minima the lower key wins.
+__device__ __forceinline__ void top2_combine(Top2& e, const Top2& o) {
+  const bool tx = o.mx > e.mx || (o.mx == e.mx && o.ax < e.ax);
+  const float lowx = tx ? e.mx : o.mx, hi2x = e.mx2 > o.mx2 ? e.mx2 : o.mx2;
+  e.mx2 = lowx > hi2x ? lowx : hi2x;
+  e.ax = tx ? o.ax : e.ax;
+  e.mx = tx ? o.mx : e.mx;
+  const bool tn = o.mn < e.mn || (o.mn == e.mn && o.an < e.an);
+  const float highn = tn ? e.mn : o.mn, lo2n = e.mn2 < o.mn2 ? e.mn2 : o.mn2;
+  e.mn2 = highn < lo2n ? highn : lo2n;
+  e.an = tn ? o.an : e.an;
+  e.mn = tn ? o.mn : e.mn;
+}
+__device__ __forceinline__ void top2_merge(Top2& e, int lanemask) {
+  Top2 o;
+  o.mx = __shfl_xor(e.mx, lanemask); o.mx2 = __shfl_xor(e.mx2, lanemask); o.ax = __shfl_xor(e.ax, lanemask);
+  o.mn = __shfl_xor(e.mn, lanemask); o.mn2 = __shfl_xor(e.mn2, lanemask); o.an = __shfl_xor(e.an, lanemask);
+  top2_combine(e, o);
+}
+
+__device__ __forceinline__ void xext_combine(XExt& a, const XExt& b, bool is_max) {
+  const float v = is_max ? (a.v > b.v ? a.v : b.v) : (a.v < b.v ? a.v : b.v);
+  a.k = min(a.v == v ? a.k : INT_MAX, b.v == v ? b.k : INT_MAX);
+  a.n = (a.v == v ? a.n : 0) + (b.v == v ? b.n : 0);
+  a.v = v;
+}
+__device__ __forceinline__ void xext_merge(XExt& a, int lanemask, bool is_max) {
+  XExt b;
+  b.v = __shfl_xor(a.v, lanemask);
+  b.k = __shfl_xor(a.k, lanemask);
+  b.n = __shfl_xor(a.n, lanemask);
+  xext_combine(a, b, is_max);
 }
 
 // At D = 64 the register budget is held to two waves per SIMD.
 template <int D, int CAL, int MODE, typename TIn>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
+  constexpr int NS = nslices<TIn>();
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  FwdSmem<D>& sm = *reinterpret_cast<FwdSmem<D>*>(smem_raw);
-  constexpr int LDK = D + 4, LDV = D + 8;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
-  const int G = l >> 4, c16 = l & 15;
-  const int T = a.T, K = a.K, ts = K + 1;
-  const int nqt = (T + FWD_BM - 1) / FWD_BM;
+  FwdSmem<D, NS>& sm = *reinterpret_cast<FwdSmem<D, NS>*>(smem_raw);
+  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D, NS>));
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+  const int T = a.T, K = a.K, ts = K + 1, nt = a.rec.nt;
   int head, rank;
   block_work(a.nheads, head, rank);
-  const int qt = a.causal ? nqt - 1 - rank : rank;  // rank 0: the latest query tile, the most keys
+  const int qt = a.causal ? nt - 1 - rank : rank;  // rank 0: the latest query tile, the most keys
   const size_t hb = (size_t)head * T * D;
-  const TIn* Qp = reinterpret_cast<const TIn*>(a.q) + hb;
   const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
   const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
-  const int qb0 = qt * FWD_BM, qw0 = qb0 + 32 * w, qi = qw0 + c;
-  const int qtw = qw0 / BN;  // the wave's query tile
+  const int q0 = qt * BN, qi = q0 + c;
   const bool qvalid = qi < T;
-  const int qlast_w = min(qw0 + 31, T - 1);
-  const int kend = a.causal ? min(T, qb0 + FWD_BM) : T;
-  const int ntiles = (kend + BN - 1) / BN;
-  const int rl = 32 * w + c;
+  const int ntiles = a.causal ? qt + 1 : nt;  // wave w takes key tiles w, w + FWD_NW, ...
   float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
+  __bf16* VT = reinterpret_cast<__bf16*>(sm.wave[w]);
+  // a tile whose every (query, key) pair is visible needs no masks
+  auto full_tile = [&](int kt) { return kt * BN + BN <= T && q0 + BN <= T && (!a.causal || kt < qt); };
+  auto stored_at = [&](int key) {  // where the lane that stored (qi, key) keeps it
+    return tile_index(qt, key / BN, nt, a.causal) * 1024 + (4 * ((key & 31) >> 3) + (key & 3)) * 64 + l;
+  };
 
-  // ---- pass 1: scores (fp64 MFMA) stored once; row extrema with first index and tie counts
-  float qr[D / 2];
+  // ---- pass 1: scores (bf16 slice products) stored once; approximate row extrema
+  // lane (c, g) holds query q0 + c and, in register v of a tile, key k0 + crow(v, g): the order of
+  // the stored tiles, so pass 2 reads back exactly what this lane wrote.
+  const float scale_f = (float)a.scale;
+  const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + hb + (size_t)(qvalid ? qi : 0) * D;
+  Split8 qs[D / 16];
+  bf8v qa[D / 16];
+  {
+    RowOp<D, TIn> qr;
+    qr.load(reinterpret_cast<const TIn*>(a.q) + hb, qi, T);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qw0 + 16 * qb + c16;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      f4v x = f4v{0.f, 0.f, 0.f, 0.f};
-      if (row < T) x = Ld<TIn>::four(Qp + (size_t)row * D + 16 * j + 4 * G);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qr[qb * (D / 4) + 4 * j + e] = x[e];
+    for (int kb = 0; kb < D / 16; ++kb) {
+      qs[kb] = qr.split(kb);
+      qa[kb] = bf_abs(qs[kb].h);
     }
   }
-  Ext ex[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) ex[qb] = Ext{-INFINITY, INFINITY, INT_MAX, INT_MAX, 0, 0};
-  float* scr = sm.scratch[w];
-  TileRegs<D, NT, TIn> kr;
-  kr.load(Kp, 0, T);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  Top2 ex{-INFINITY, -INFINITY, INFINITY, INFINITY, INT_MAX, INT_MAX};
+  float amx = 0.f;  // largest sum of |q_h| |k_h| over the row's visible keys
+  RowOp<D, TIn> kr;
+  if (w < ntiles) kr.load(Kp, w * BN + c, T);
+  for (int kt = w; kt < ntiles; kt += FWD_NW) {
     const int k0 = kt * BN;
-    __syncthreads();
-    kr.store(sm.Ks, LDK, 1.0f);
-    __syncthreads();
-    if (kt + 1 < ntiles) kr.load(Kp, k0 + BN, T);  // next tile in flight during this one
-    if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    d4v acc[2][2];
-    score_tile_f64<D>(sm.Ks, LDK, qr, acc);
+    const RowOp<D, TIn> cur = kr;
+    if (kt + FWD_NW < ntiles) kr.load(Kp, k0 + FWD_NW * BN + c, T);  // next tile in flight
+    f16v acc = zero16(), asm_ = zero16(), aacc = zero16();  // h h', the smaller products, |h| |h'|
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float x = (float)(a.scale * acc[kb][qb][v]);
-          const int klo = 16 * kb + 4 * v + G, qlo = 16 * qb + c16;
-          const int key = k0 + klo, query = qw0 + qlo;
-          const bool ok = query < T && key < T && (!a.causal || key <= query);
-          Ext& e = ex[qb];
-          if (ok) {
-            if (x > e.mx) { e.mx = x; e.ax = key; e.cx = 1; } else if (x == e.mx) { ++e.cx; }
-            if (x < e.mn) { e.mn = x; e.an = key; e.cn = 1; } else if (x == e.mn) { ++e.cn; }
-          }
-          // re-layout into the stored tile order: (query qlo, key klo) -> v' * 64 + qlo + 32 g'
-          const int gp = (klo >> 2) & 1, vp = 4 * (klo >> 3) + (klo & 3);
-          scr[vp * SCR + qlo + 32 * gp] = x;
-        }
-    float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) St[v * 64 + l] = scr[v * SCR + l];
-  }
-  // merge the four lanes that share a query row (lanes c16 + 16 G)
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    ext_merge(ex[qb], 16);
-    ext_merge(ex[qb], 32);
-    if (G == 0) {
-      const int r2 = 32 * w + 16 * qb + c16;
-      sm.rowM[r2] = ex[qb].mx;
-      sm.rowm[r2] = ex[qb].mn;
-      sm.rowax[r2] = ex[qb].ax;
-      sm.rowan[r2] = ex[qb].an;
-      sm.rowcx[r2] = ex[qb].cx;
-      sm.rowcn[r2] = ex[qb].cn;
+    for (int kb = 0; kb < D / 16; ++kb) {
+      const Split8 ks = cur.split(kb);
+      if (NS == 3) {
+        asm_ = mfma_bf16(ks.l, qs[kb].h, asm_);
+        asm_ = mfma_bf16(ks.m, qs[kb].m, asm_);
+        asm_ = mfma_bf16(ks.h, qs[kb].l, asm_);
+        asm_ = mfma_bf16(ks.m, qs[kb].h, asm_);
+        asm_ = mfma_bf16(ks.h, qs[kb].m, asm_);
+      }
+      acc = mfma_bf16(ks.h, qs[kb].h, acc);
+      aacc = mfma_bf16(bf_abs(ks.h), qa[kb], aacc);
     }
+    if (NS == 3) acc += asm_;
+    float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+    auto epilogue = [&](auto masked) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float x = acc[v] * scale_f;
+        const int key = k0 + crow(v, g);
+        St[v * 64] = x;
+        const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
+        if (ok) {
+          top2(ex, x, key);
+          amx = aacc[v] > amx ? aacc[v] : amx;
+        }
+      }
+    };
+    if (full_tile(kt)) epilogue(std::false_type{});
+    else epilogue(std::true_type{});
   }
-  // pass 2 reads back the tiles stored above: complete the stores and drop stale L1 lines
-  __threadfence();
+  top2_merge(ex, 32);
+  amx = fmaxf(amx, __shfl_xor(amx, 32));
+  if (g == 0) {
+    sm.ext[w][c] = ex;
+    sm.amx[w][c] = amx;
+  }
   __syncthreads();
-  // from here on lane l works on query row l%32 of the wave
-  const float M = sm.rowM[rl], m = sm.rowm[rl];
+  ex = sm.ext[0][c];
+  amx = sm.amx[0][c];
+#pragma unroll
+  for (int v = 1; v < FWD_NW; ++v) {
+    top2_combine(ex, sm.ext[v][c]);
+    amx = fmaxf(amx, sm.amx[v][c]);
+  }
+  // error bound of the row's scores, and of u in interval widths (below)
+  const float srow = fmaxf(fabsf(ex.mx), fabsf(ex.mn));
+  const float Erow = (float)(a.scale * acc_c<D, NS>()) * amx + 0x1p-22f * srow + 1e-30f;
 
-  // ---- calibration and grid table (K+1 exponentials per row)
+  // ---- exact extrema: a clear winner is recomputed exactly (by every wave; the lane that stored
+  // it patches it); a near-tie rescans the row, each wave its own key tiles
+  const bool clearM = ex.mx - ex.mx2 > 2.f * Erow, clearm = ex.mn2 - ex.mn > 2.f * Erow;
+  XExt xM{ex.mx, ex.ax, 1}, xm{ex.mn, ex.an, 1};
+  if (qvalid && clearM) {
+    xM.v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.ax * D, a.scale);
+    if (w == (ex.ax / BN) % FWD_NW && g == ((ex.ax >> 2) & 1)) Sh[stored_at(ex.ax)] = xM.v;
+  }
+  if (qvalid && clearm) {
+    xm.v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.an * D, a.scale);
+    if (w == (ex.an / BN) % FWD_NW && g == ((ex.an >> 2) & 1)) Sh[stored_at(ex.an)] = xm.v;
+  }
+  const bool scanM = qvalid && !clearM, scanm = qvalid && !clearm;
+  if (__syncthreads_or(scanM || scanm)) {
+    // every stored score within 2 Erow of the approximate extremum is recomputed and patched
+    const float thrM = ex.mx - 2.f * Erow, thrm = ex.mn + 2.f * Erow;
+    XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
+    for (int kt = w; kt < ntiles; kt += FWD_NW) {
+      float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt * BN + crow(v, g);
+        const bool ok = qvalid && key < T && (!a.causal || key <= qi);
+        const float x = St[v * 64];
+        const bool cM = scanM && ok && x >= thrM, cm = scanm && ok && x <= thrm;
+        if (cM || cm) {
+          const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)key * D, a.scale);
+          St[v * 64] = xe;
+          if (cM) {
+            if (xe > yM.v) { yM.v = xe; yM.k = key; yM.n = 1; } else if (xe == yM.v) { ++yM.n; }
+          }
+          if (cm) {
+            if (xe < ym.v) { ym.v = xe; ym.k = key; ym.n = 1; } else if (xe == ym.v) { ++ym.n; }
+          }
+        }
+      }
+    }
+    xext_merge(yM, 32, true);
+    xext_merge(ym, 32, false);
+    if (g == 0) {
+      sm.xM[w][c] = yM;
+      sm.xm[w][c] = ym;
+    }
+    __syncthreads();
+    yM = sm.xM[0][c];
+    ym = sm.xm[0][c];
+#pragma unroll
+    for (int v = 1; v < FWD_NW; ++v) {
+      xext_combine(yM, sm.xM[v][c], true);
+      xext_combine(ym, sm.xm[v][c], false);
+    }
+    if (scanM) xM = yM;
+    if (scanm) xm = ym;
+  }
+  const float M = xM.v, m = xm.v;
+  if (w == 0 && g == 0 && qvalid) {
+    const size_t row = (size_t)head * T + qi;
+    a.rec.M[row] = M;
+    a.rec.m[row] = m;
+    a.rec.amax[row] = xM.k;
+    a.rec.amin[row] = CAL == MINMAX ? xm.k : 0;
+    a.rec.nA[row] = xM.n;
+    a.rec.nC[row] = CAL == MINMAX ? xm.n : 0;
+  }
+
+  // ---- calibration and grid table (K+1 exponentials per row), shared by the waves
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
-  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D>));
-  float* trow = tbl + rl * ts;
-  for (int r = g; r <= K; r += 2) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+  // the error bound in interval widths, with room for the rounding of t itself
+  const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f;
+  float* trow = tbl + c * ts;
+  for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+  __syncthreads();
 
   // ---- pass 2: reconstruct, normalize, multiply by V
   double sumL = 0.0, sumN = 0.0;  // row sums of positive weights: double, no absorption of small terms
   f16v o[D / 32], ol[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
-  TileRegs<D, NT, TIn> vr;
-  vr.load(Vp, 0, T);
+  PairRegs<D, TIn, 64> vr;
   f16v snext;
-  const bool act0 = qw0 < T;
-  if (act0) {
-    const float* St = Sh + tile_index(qtw, 0, a.rec.nt, a.causal) * 1024;
+  if (w < ntiles) {
+    vr.load(Vp, w * BN, T);
+    const float* St = Sh + tile_index(qt, w, nt, a.causal) * 1024;
 #pragma unroll
     for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
   }
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = w; kt < ntiles; kt += FWD_NW) {
     const int k0 = kt * BN;
-    __syncthreads();
-    vr.store(sm.Vs, LDV, 1.0f);
-    __syncthreads();
-    const f16v s = snext;
-    if (kt + 1 < ntiles) {  // next V tile and next score tile in flight during this one
-      vr.load(Vp, k0 + BN, T);
-      if (qw0 < T && (!a.causal || k0 + BN <= qlast_w)) {
-        const float* St = Sh + tile_index(qtw, kt + 1, a.rec.nt, a.causal) * 1024;
+    vr.template store_t<NS>(VT);
+    wave_lds_sync();
+    f16v s = snext;
+    float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+    if (kt + FWD_NW < ntiles) {  // next V tile and next score tile in flight during this one
+      vr.load(Vp, k0 + FWD_NW * BN, T);
+      const float* St = Sh + tile_index(qt, kt + FWD_NW, nt, a.causal) * 1024;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+      for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
+    }
+    float p[16], pl[16];
+    double tL, tN;  // the tile's weight sums, joined to the row sums once the tile is settled
+    uint32_t risky = 0;
+    auto weigh = [&](auto masked, auto check) {
+      tL = 0.0;
+      tN = 0.0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + crow(v, g);
+        const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
+        const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+        if (decltype(check)::value) {
+          // a decision within the score's error bound of a boundary must be taken on the exact score
+          bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1);
+          if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < du;
+          if (CAL == FWM) r = r || fabs((double)s[v] - ((double)M - (double)a.tau)) <= (double)Erow;
+          risky |= (ok && r) ? (1u << v) : 0u;
+        }
+        const Weights wt = weights(d, trow);
+        const bool keep = ok && !d.tail;
+        const float wl = keep ? wt.wL : 0.f;
+        const float wn = keep ? wt.wN : 0.f;
+        tL += (double)wl;
+        if (MODE != LERP) tN += (double)wn;
+        p[v] = (MODE == LERP) ? wl : wn;
+        pl[v] = wl;
       }
-    }
-    if (qw0 >= T || (a.causal && k0 > qlast_w)) continue;
-    f16v p, pl;
+    };
+    const bool full = full_tile(kt);
+    if (full) weigh(std::false_type{}, std::true_type{});
+    else weigh(std::true_type{}, std::true_type{});
+    if (__any(risky != 0u)) {
+      // rare: the exact scores replace the stored ones (this lane stored them) for every later
+      // pass, and the tile is weighed again on them
+      for (int v = 0; v < 16; ++v) {
+        if ((risky >> v) & 1u) Sw[v * 64] = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(v, g)) * D, a.scale);
+      }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = k0 + crow(v, g);
-      const bool ok = qvalid && key < T && (!a.causal || key <= qi);
-      const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-      const Weights wt = weights(d, trow);
-      const bool keep = ok && !d.tail;
-      const float wl = keep ? wt.wL : 0.f;
-      const float wn = keep ? wt.wN : 0.f;
-      sumL += (double)wl;
-      sumN += (double)wn;
-      p[v] = (MODE == LERP) ? wl : wn;
-      pl[v] = wl;
+      for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
+      if (full) weigh(std::false_type{}, std::false_type{});
+      else weigh(std::true_type{}, std::false_type{});
     }
-    // each tile's P V goes into a fresh accumulator, then into the running sum: the long
-    // accumulation chain then holds one add per tile instead of one per MFMA step
+    sumL += tL;
+    sumN += tN;
+    // each tile's P V (bf16 slice products on the matrix pipe) goes into a fresh accumulator,
+    // then into the running sum: the long accumulation chain then holds one add per tile
     f16v ot[D / 32];
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
-    tile_accum<D>(ot, p, sm.Vs, LDV);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const Split8 ps = split8(p + 8 * b);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+    }
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) o[nb] += ot[nb];
     if (MODE == NEAREST_P) {
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
-      tile_accum<D>(ot, pl, sm.Vs, LDV);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const Split8 ps = split8(pl + 8 * b);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+      }
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ol[nb] += ot[nb];
     }
+    wave_lds_sync();  // this tile's V^T reads come before the next tile's staging
   }
+
+  // ---- the waves' partial row sums and outputs meet in LDS; wave 0 adds them in wave order
   sumL += __shfl_xor(sumL, 32);
   sumN += __shfl_xor(sumN, 32);
-  const float WLf = (float)sumL, WNf = (float)sumN;
   if (g == 0) {
-    sm.rowW[rl] = (MODE == LERP) ? WLf : WNf;
-    sm.rowWL[rl] = WLf;
+    sm.sL[w][c] = sumL;
+    sm.sN[w][c] = sumN;
+  }
+  float* part = reinterpret_cast<float*>(sm.wave[w]);  // this wave's V^T is no longer read
+  auto gather = [&](f16v (&acc)[D / 32]) {
+    __syncthreads();
+    if (w > 0) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[(nb * 16 + v) * 64 + l] = acc[nb][v];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int u = 1; u < FWD_NW; ++u) {
+        const float* op = reinterpret_cast<const float*>(sm.wave[u]);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[nb][v] += op[(nb * 16 + v) * 64 + l];
+      }
+    }
+  };
+  gather(o);
+  if (MODE == NEAREST_P) gather(ol);
+  if (w != 0) return;
+  sumL = sm.sL[0][c];
+  sumN = sm.sN[0][c];
+#pragma unroll
+  for (int u = 1; u < FWD_NW; ++u) {
+    sumL += sm.sL[u][c];
+    sumN += sm.sN[u][c];
+  }
+  const float WLf = (float)sumL, WNf = (MODE == LERP) ? WLf : (float)sumN;
+  if (g == 0) {
+    sm.rowW[c] = (MODE == LERP) ? WLf : WNf;
+    sm.rowWL[c] = WLf;
     if (qvalid) {
       const size_t row = (size_t)head * T + qi;
-      a.rec.M[row] = M;
-      a.rec.m[row] = m;
-      a.rec.amax[row] = sm.rowax[rl];
-      a.rec.amin[row] = sm.rowan[rl];
-      a.rec.nA[row] = sm.rowcx[rl];
-      a.rec.nC[row] = sm.rowcn[rl];
       a.rec.WN[row] = WNf;
       a.rec.WL[row] = WLf;
     }
   }
-  __syncthreads();
-  // O = num / W; lane l holds rows crow(v, g) of the wave's 32 and columns 32 nb + c
+  wave_lds_sync();
+  // O = num / W; lane l holds rows crow(v, g) of the tile and columns 32 nb + c
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int qrow = qw0 + crow(v, g);
+    const int qrow = q0 + crow(v, g);
     if (qrow < T) {
-      const float inv = 1.0f / sm.rowW[32 * w + crow(v, g)];
+      const float inv = 1.0f / sm.rowW[crow(v, g)];
       float* orow = a.o + hb + (size_t)qrow * D + c;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) orow[32 * nb] = o[nb][v] * inv;
       if (MODE == NEAREST_P) {
-        const float invl = 1.0f / sm.rowWL[32 * w + crow(v, g)];
+        const float invl = 1.0f / sm.rowWL[crow(v, g)];
         float* olrow = a.rec.OL + hb + (size_t)qrow * D + c;
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) olrow[32 * nb] = ol[nb][v] * invl;
@@ -265,9 +529,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   }
 }
 
-template <int D>
+template <int D, typename TIn>
 size_t fwd_smem_bytes(int K) {
-  return sizeof(FwdSmem<D>) + sizeof(float) * (FWD_BM * (K + 1));
+  return sizeof(FwdSmem<D, nslices<TIn>()>) + sizeof(float) * (BN * (K + 1));
 }
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
@@ -304,9 +568,9 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
 // ------------------------------------------------------------------------------- launchers
 template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
-  const size_t smem = fwd_smem_bytes<D>(p.K);
-  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+  const int nqt = (p.T + BN - 1) / BN;
+  const size_t smem = fwd_smem_bytes<D, TIn>(p.K);
+  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE>
