@@ -296,13 +296,21 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // it patches it); a near-tie rescans the row, each wave its own key tiles
   const bool clearM = ex.mx - ex.mx2 > 2.f * Erow, clearm = ex.mn2 - ex.mn > 2.f * Erow;
   XExt xM{ex.mx, ex.ax, 1}, xm{ex.mn, ex.an, 1};
-  if (qvalid && clearM) {
-    xM.v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.ax * D, a.scale);
-    if (w == (ex.ax / BN) % FWD_NW && g == ((ex.ax >> 2) & 1)) Sh[stored_at(ex.ax)] = xM.v;
-  }
-  if (qvalid && clearm) {
-    xm.v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.an * D, a.scale);
-    if (w == (ex.an / BN) % FWD_NW && g == ((ex.an >> 2) & 1)) Sh[stored_at(ex.an)] = xm.v;
+  {
+    // wave 0 takes the maximum, wave 1 % FWD_NW the minimum; the values meet in LDS and the
+    // lane that stored each element patches it
+    if (qvalid && clearM && w == 0) sm.xM[0][c].v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.ax * D, a.scale);
+    if (qvalid && clearm && w == 1 % FWD_NW) sm.xm[0][c].v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.an * D, a.scale);
+    __syncthreads();
+    if (qvalid && clearM) {
+      xM.v = sm.xM[0][c].v;
+      if (w == (ex.ax / BN) % FWD_NW && g == ((ex.ax >> 2) & 1)) Sh[stored_at(ex.ax)] = xM.v;
+    }
+    if (qvalid && clearm) {
+      xm.v = sm.xm[0][c].v;
+      if (w == (ex.an / BN) % FWD_NW && g == ((ex.an >> 2) & 1)) Sh[stored_at(ex.an)] = xm.v;
+    }
+    __syncthreads();  // the LDS slots are reused by a rescan below
   }
   const bool scanM = qvalid && !clearM, scanm = qvalid && !clearm;
   if (__syncthreads_or(scanM || scanm)) {
@@ -369,94 +377,86 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   f16v o[D / 32], ol[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
+  // the next V tile is loaded while this one computes, except under Nearest with Prob-STE,
+  // whose second output accumulator takes those registers
+  constexpr bool VPRE = MODE != NEAREST_P;
   PairRegs<D, TIn, 64> vr;
-  f16v snext;
-  if (w < ntiles) {
-    vr.load(Vp, w * BN, T);
-    const float* St = Sh + tile_index(qt, w, nt, a.causal) * 1024;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
-  }
+  if (VPRE && w < ntiles) vr.load(Vp, w * BN, T);
   for (int kt = w; kt < ntiles; kt += FWD_NW) {
     const int k0 = kt * BN;
+    if (!VPRE) vr.load(Vp, k0, T);
+    float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+    float s[16];  // this lane's scores of the tile, as it stored them in pass 1
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
     vr.template store_t<NS>(VT);
     wave_lds_sync();
-    f16v s = snext;
-    float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
-    if (kt + FWD_NW < ntiles) {  // next V tile and next score tile in flight during this one
-      vr.load(Vp, k0 + FWD_NW * BN, T);
-      const float* St = Sh + tile_index(qt, kt + FWD_NW, nt, a.causal) * 1024;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
-    }
-    float p[16], pl[16];
-    double tL, tN;  // the tile's weight sums, joined to the row sums once the tile is settled
-    uint32_t risky = 0;
-    auto weigh = [&](auto masked, auto check) {
-      tL = 0.0;
-      tN = 0.0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + crow(v, g);
-        const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
-        const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-        if (decltype(check)::value) {
-          // a decision within the score's error bound of a boundary must be taken on the exact score
-          bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1);
-          if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < du;
-          if (CAL == FWM) r = r || fabs((double)s[v] - ((double)M - (double)a.tau)) <= (double)Erow;
-          risky |= (ok && r) ? (1u << v) : 0u;
-        }
-        const Weights wt = weights(d, trow);
-        const bool keep = ok && !d.tail;
-        const float wl = keep ? wt.wL : 0.f;
-        const float wn = keep ? wt.wN : 0.f;
-        tL += (double)wl;
-        if (MODE != LERP) tN += (double)wn;
-        p[v] = (MODE == LERP) ? wl : wn;
-        pl[v] = wl;
-      }
-    };
+    if (VPRE && kt + FWD_NW < ntiles) vr.load(Vp, k0 + FWD_NW * BN, T);  // next V tile in flight
     const bool full = full_tile(kt);
-    if (full) weigh(std::false_type{}, std::true_type{});
-    else weigh(std::true_type{}, std::true_type{});
-    if (__any(risky != 0u)) {
-      // rare: the exact scores replace the stored ones (this lane stored them) for every later
-      // pass, and the tile is weighed again on them
-      for (int v = 0; v < 16; ++v) {
-        if ((risky >> v) & 1u) Sw[v * 64] = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(v, g)) * D, a.scale);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
-      if (full) weigh(std::false_type{}, std::false_type{});
-      else weigh(std::true_type{}, std::false_type{});
-    }
-    sumL += tL;
-    sumN += tN;
     // each tile's P V (bf16 slice products on the matrix pipe) goes into a fresh accumulator,
     // then into the running sum: the long accumulation chain then holds one add per tile
-    f16v ot[D / 32];
+    f16v ot[D / 32], otl[D / 32];
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
+    for (int nb = 0; nb < D / 32; ++nb) { ot[nb] = zero16(); otl[nb] = zero16(); }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const Split8 ps = split8(p + 8 * b);
+    for (int b = 0; b < 2; ++b) {  // half tiles: keys crow(v, g) for v = 8b .. 8b+7
+      float p[8], pl[8];
+      double tL, tN;  // the half tile's weight sums, joined to the row sums once it is settled
+      uint32_t risky = 0;
+      auto weigh = [&](auto masked, auto check) {
+        tL = 0.0;
+        tN = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = 8 * b + j, key = k0 + crow(v, g);
+          const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
+          const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+          if (decltype(check)::value) {
+            // a decision within the score's error bound of a boundary must be taken on the exact score
+            bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1);
+            if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < du;
+            if (CAL == FWM) r = r || fabs((double)s[v] - ((double)M - (double)a.tau)) <= (double)Erow;
+            risky |= (ok && r) ? (1u << j) : 0u;
+          }
+          const Weights wt = weights(d, trow);
+          const bool keep = ok && !d.tail;
+          const float wl = keep ? wt.wL : 0.f;
+          const float wn = keep ? wt.wN : 0.f;
+          tL += (double)wl;
+          if (MODE != LERP) tN += (double)wn;
+          p[j] = (MODE == LERP) ? wl : wn;
+          pl[j] = wl;
+        }
+      };
+      if (full) weigh(std::false_type{}, std::true_type{});
+      else weigh(std::true_type{}, std::true_type{});
+      if (__any(risky != 0u)) {
+        // rare: the exact scores replace the stored ones (this lane stored them) for every later
+        // pass, and the half tile is weighed again on them
+        for (int j = 0; j < 8; ++j) {
+          if ((risky >> j) & 1u)
+            Sw[(8 * b + j) * 64] = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[8 * b + j] = Sw[(8 * b + j) * 64];
+        if (full) weigh(std::false_type{}, std::false_type{});
+        else weigh(std::true_type{}, std::false_type{});
+      }
+      sumL += tL;
+      sumN += tN;
+      const Split8 ps = split8(p);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+      if (MODE == NEAREST_P) {
+        const Split8 psl = split8(pl);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) otl[nb] = mfma_split<NS>(psl, load_bt<D, NS>(VT, b, 32 * nb + c), otl[nb]);
+      }
     }
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) o[nb] += ot[nb];
-    if (MODE == NEAREST_P) {
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const Split8 ps = split8(pl + 8 * b);
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) ol[nb] += ot[nb];
+    for (int nb = 0; nb < D / 32; ++nb) {
+      o[nb] += ot[nb];
+      if (MODE == NEAREST_P) ol[nb] += otl[nb];
     }
     wave_lds_sync();  // this tile's V^T reads come before the next tile's staging
   }
