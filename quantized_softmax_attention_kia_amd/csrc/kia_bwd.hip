@@ -287,8 +287,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 }
 
 // ============================================================================ dkdv kernel
-// Number of bf16 slices that represent an input element exactly enough: bf16 inputs are exact.
-template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
 
 template <int D, int NS>
 struct KvSmem {

@@ -87,6 +87,9 @@ __device__ __forceinline__ f16v mfma_bf16(bf8v a, bf8v b, f16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Number of bf16 slices that represent an input element exactly enough: bf16 inputs are exact.
+template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
+
 struct Split8 {
   bf8v h, m, l;
 };
@@ -213,6 +216,42 @@ __device__ __forceinline__ Split8 load_an(const __bf16* xn, int row, int kb) {
   return r;
 }
 
+// One lane's operand of a row of a [T, D] tensor for a product that contracts over the columns:
+// columns 16 kb + 8 (l/32) .. + 7, split into bf16 slices on demand (bf16 inputs are their own
+// single slice).
+template <int D, typename TIn> struct RowOp;
+template <int D> struct RowOp<D, float> {
+  float x[D / 2];
+  __device__ __forceinline__ void load(const float* base, int row, int nrows) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f4v a = row < nrows ? *reinterpret_cast<const f4v*>(base + (size_t)row * D + 16 * kb + 8 * g + 4 * h)
+                                  : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[8 * kb + 4 * h + e] = a[e];
+      }
+  }
+  __device__ __forceinline__ Split8 split(int kb) const { return split8(x + 8 * kb); }
+};
+template <int D> struct RowOp<D, uint16_t> {
+  uint4 x[D / 16];
+  __device__ __forceinline__ void load(const uint16_t* base, int row, int nrows) {
+    const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+      x[kb] = row < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)row * D + 16 * kb + 8 * g)
+                          : uint4{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ Split8 split(int kb) const {
+    Split8 s;
+    __builtin_memcpy(&s.h, &x[kb], 16);
+    return s;
+  }
+};
+
 // B operand slices for k-block b (rows 16b .. 16b+15) and output column n of the transposed tile.
 // Lane (n, g) supplies rows 16b + 4g + (0..3) and 16b + 8 + 4g + (0..3): the rows that the
 // accumulator-layout coefficients v = 8b .. 8b+7 of lane (., g) stand for (crow(v, g)).
@@ -328,6 +367,14 @@ __device__ __forceinline__ void tile_accum(f16v (&out)[D / 32], const f16v& coef
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) out[nb] = mfma32(coef[v], row[32 * nb], out[nb]);
   }
+}
+
+// LDS written by some lanes of the wave and read by others: the wave's LDS operations run in
+// program order, so only the compiler has to be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------------------------------------

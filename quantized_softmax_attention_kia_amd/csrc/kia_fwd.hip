@@ -37,7 +37,6 @@ constexpr int FWD_NW = 2;            // waves per workgroup, splitting the key t
 constexpr int FWD_NT = 64 * FWD_NW;
 constexpr int BN = 32;               // keys per tile, query rows per workgroup
 
-template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
 
 // Approximate extrema of a row: largest value, its first key and the runner-up; smallest
 // value, its first key and the runner-up.  Keys reach a lane in increasing order.
@@ -66,14 +65,6 @@ struct FwdSmem {
   float rowW[BN], rowWL[BN];
   // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
 };
-
-// LDS written by some lanes of the wave and read by others: the wave's LDS operations run in
-// program order, so only the compiler has to be kept from moving them across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Error bound of a score taken from bf16 slice products (u = 2^-24).  With fp32 inputs each
 // operand is split into three slices (x = h + m + l + e, |m| <= 2^-8 |x|, |l| <= 2^-16 |x|,
@@ -104,40 +95,6 @@ __device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, d
   }
   return (float)(scale * acc);
 }
-
-// One lane's operand of a row for the score product: columns 16 kb + 8 (l/32) .. + 7.
-template <int D, typename TIn> struct RowOp;
-template <int D> struct RowOp<D, float> {
-  float x[D / 2];
-  __device__ __forceinline__ void load(const float* base, int row, int nrows) {
-    const int g = (threadIdx.x & 63) >> 5;
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f4v a = row < nrows ? *reinterpret_cast<const f4v*>(base + (size_t)row * D + 16 * kb + 8 * g + 4 * h)
-                                  : f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[8 * kb + 4 * h + e] = a[e];
-      }
-  }
-  __device__ __forceinline__ Split8 split(int kb) const { return split8(x + 8 * kb); }
-};
-template <int D> struct RowOp<D, uint16_t> {
-  uint4 x[D / 16];
-  __device__ __forceinline__ void load(const uint16_t* base, int row, int nrows) {
-    const int g = (threadIdx.x & 63) >> 5;
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb)
-      x[kb] = row < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)row * D + 16 * kb + 8 * g)
-                          : uint4{0u, 0u, 0u, 0u};
-  }
-  __device__ __forceinline__ Split8 split(int kb) const {
-    Split8 s;
-    __builtin_memcpy(&s.h, &x[kb], 16);
-    return s;
-  }
-};
 
 __device__ __forceinline__ bf8v bf_abs(bf8v v) {
   uint4 u;

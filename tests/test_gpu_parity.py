@@ -162,6 +162,55 @@ def test_tied_extrema(kb):
         compare_all_heads(full, q, k, v, do, got)
 
 
+def grid_inputs(seed, B, H, T, D, rel):
+    """Q, K on the integers -2..2 times (1 + rel N(0,1)): the scores sit on a coarse grid (and the
+    row extrema and interval boundaries with them) up to a perturbation of relative size rel."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-2, 3, (B, H, T, D)).astype(np.float32)
+    k = rng.integers(-2, 3, (B, H, T, D)).astype(np.float32)
+    q *= (1.0 + rel * rng.standard_normal(q.shape)).astype(np.float32)
+    k *= (1.0 + rel * rng.standard_normal(k.shape)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    do = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("variant", [("minmax", "lerp", "prob", "full", 4, 8.0),
+                                     ("minmax", "nearest", "weight", "full", 8, 8.0),
+                                     ("fwm", "nearest", "prob", "full", 4, 2.0),
+                                     ("fwm", "lerp", "prob", "full", 16, 3.0)],
+                         ids=lambda v: "-".join(str(x) for x in v))
+def test_near_boundary_scores(kb, variant):
+    # Many decisions fall within the error bound of the forward's bf16 slice-product scores but
+    # farther from the boundary than the parity guard: they agree with the oracle only if the
+    # forward retakes them on exactly recomputed scores (and patches those into the stored
+    # tiles that the backward and the bins hook read).
+    import torch
+    q, k, v, do = grid_inputs(50, 1, 2, 96, 64, 3e-6)
+    say(f"[near-boundary] 1x2x96x64 grid seed=50 {variant}")
+    got, (qt, kt, rowrec, p) = gpu_run(kb, variant, q, k, v, do)
+    compare_all_heads(variant, q, k, v, do, got)
+    bins = kb.debug_bins(p, rowrec)
+    torch.cuda.synchronize()
+    bins = bins.cpu().numpy()
+    for h in range(2):
+        say("   ", parity.check_bins(ocfg(variant), q[0, h], k[0, h], bins[0, h]))
+
+
+def test_near_tied_extrema(kb):
+    # keys that are copies of one another up to a relative 1e-7: row maxima / minima closer than
+    # the score bound, settled by recomputing every candidate exactly
+    q, k, v, do = make_inputs(1, 2, 100, 64, 51, q_scale=2.0)
+    k[0, :, 3] *= 3.0
+    rng = np.random.default_rng(52)
+    for j in (10, 50, 77):
+        k[0, :, j] = k[0, :, 3] * (1.0 + 1e-7 * rng.standard_normal(64)).astype(np.float32)
+    for variant in [v_ + (4, 8.0) for v_ in VARIANTS16[::2]]:
+        say(f"[near-ties] {variant}")
+        got, _ = gpu_run(kb, variant, q, k, v, do)
+        compare_all_heads(variant, q, k, v, do, got)
+
+
 def test_window_and_scale_extremes(kb):
     # tiny FWM window (most keys in the tail), large K, large scores
     q, k, v, do = make_inputs(1, 1, 128, 64, 42, q_scale=6.0)
