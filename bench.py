@@ -97,6 +97,9 @@ def main() -> int:
     ap.add_argument("--workload", default="gpt2")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
+                         "byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -144,6 +147,16 @@ def main() -> int:
             kb.kia_backward_dkdv(r["p"], qt, kt, vt, dot, r["rowrec"], r["dk"], r["dv"], r["ws"], stream)
             if events is not None:
                 events[i][3].record(stream)
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy} MiB read, {args.calibrate_copy} MiB written")
+        del src, dst
 
     for _ in range(args.warmup):
         one_step()

@@ -324,6 +324,22 @@ __device__ __forceinline__ f16v tile_dot_lds(const float* arows, const float* br
   return acc;
 }
 
+// The same product with A's rows in registers: lane l holds row l%32 of A at the dims
+// 8q + 4(l/32) .. + 3 (q < D/8) and B's rows sit in LDS.
+template <int D>
+__device__ __forceinline__ f16v tile_dot_ra(const f4v (&arow)[D / 8], const float* brows, int ld) {
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+  const float* rb = brows + c * ld + 4 * g;
+  f16v acc = zero16();
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    const f4v y = *reinterpret_cast<const f4v*>(rb + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma32(arow[q][e], y[e], acc);
+  }
+  return acc;
+}
+
 // Scores of one 32 (query) x 32 (key) tile in double: four 16x16 sub-tiles of S^T = K Q^T.
 // K rows (32, stride ld floats) sit in LDS; qr holds the lane's query operand:
 // qr[qb * (D/4) + 4j + e] = Q[16 qb + l%16][16 j + 4 (l/16) + e] (MFMA step 4j + e).
@@ -477,8 +493,9 @@ __device__ __forceinline__ void block_work(int nheads, int& head, int& rank) {
   }
 }
 
-// Stage rows of a [T, D] head tensor through registers: each of NT threads holds
-// CH = 32*D/4/NT float4 chunks of a 32-row tile (rows row0.., zero past nrows).
+// Stage rows of a [T, D] head tensor through registers: each of NT staging threads (thread
+// threadIdx.x % NT) holds CH = 32*D/4/NT float4 chunks of a 32-row tile (rows row0.., zero past
+// nrows).
 template <int D, int NT, typename T>
 struct TileRegs {
   static constexpr int CH = 32 * D / 4 / NT;
@@ -486,7 +503,7 @@ struct TileRegs {
   __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = threadIdx.x % NT + i * NT;
       const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
       const int gr = row0 + r;
       x[i] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -496,7 +513,7 @@ struct TileRegs {
   __device__ __forceinline__ void store(float* dst, int ld, float mul) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = threadIdx.x + i * NT;
+      const int id = threadIdx.x % NT + i * NT;
       const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
       f4v y = x[i];
       if (mul != 1.0f) y *= mul;
