@@ -38,7 +38,6 @@ constexpr int NT = 64 * NW;   // threads per workgroup
 constexpr int BN = 32;        // keys per tile (dq kernel) / queries per tile (dkdv kernel)
 constexpr int DQ_BM = 32 * NW;  // query rows per dq workgroup
 constexpr int KV_BN = 32 * NW;  // key rows per dkdv workgroup
-constexpr int TLD = 33;       // row stride of the LDS tile transpose
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p);
 template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
@@ -55,23 +54,30 @@ __device__ __forceinline__ int stored_offset(int a, int b) {
 __device__ __forceinline__ int stored_lane_group(int b) { return (b >> 2) & 1; }
 
 // ============================================================================ dq kernel
-template <int D>
+template <int D, int NS>
 struct DqSmem {
-  float Ks[BN * (D + 4)];
-  float Vs[BN * (D + 4)];
-  float dOs[DQ_BM * (D + 4)];  // the workgroup's dO rows
+  __align__(16) __bf16 KT[NS * D * TP];         // K^T of the key tile, bf16 slices (dQ += dS K)
+  __align__(16) __bf16 VN[NS * BN * np<D>()];   // V rows of the key tile, bf16 slices (g = V dO^T)
+  // the smallest slice of each lane's dO row, read back only by that lane (registers hold the
+  // other two)
+  __align__(16) __bf16 dOl[NS == 3 ? DQ_BM * np<D>() : 8];
   float alpha[DQ_BM], beta[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
   // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 1) floats
 };
 
+template <int D, typename TIn>
+size_t dq_smem_bytes(int K) {
+  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * DQ_BM * (K + 1);
+}
+
 // At D = 64 the register budget is held to two waves per SIMD.
 template <int D, int CAL, int MODE, bool FULL, typename TIn>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dq_kernel(BwdArgs a) {
+  constexpr int NS = nslices<TIn>();
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  DqSmem<D>& sm = *reinterpret_cast<DqSmem<D>*>(smem_raw);
-  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D>));
-  constexpr int LD = D + 4;
+  DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
+  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS>));
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, ts = K + 1;
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
@@ -96,16 +102,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   float* dSh = a.dst + tbase * 1024;
   auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
-  {  // the workgroup's dO rows, read from LDS by every dO V^T product
-    TileRegs<D, NT, TIn> dr;
+  // the lane's dO row as bf16 slices, columns 16 kb + 8 g ..: the B operand of every g = V dO^T
+  Split8 dos[D / 16];
+  __bf16* dol = sm.dOl + (NS == 3 ? rl * np<D>() + 8 * g : 0);
+  {
+    RowOp<D, TIn> dr;
+    dr.load(dOp, qi, T);
 #pragma unroll
-    for (int h = 0; h < DQ_BM / BN; ++h) {
-      dr.load(dOp, qb0 + h * BN, T);
-      dr.store(sm.dOs + h * BN * LD, LD, 1.0f);
+    for (int kb = 0; kb < D / 16; ++kb) {
+      dos[kb] = dr.split(kb);
+      if (NS == 3) *reinterpret_cast<bf8v*>(dol + 16 * kb) = dos[kb].l;
     }
   }
-  const float* dOw = sm.dOs + 32 * w * LD;
-  __syncthreads();
 
   // row record of the forward
   const float M = a.rec.M[row], m = a.rec.m[row];
@@ -119,13 +127,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   float Di;
   {
     const float* X = ((MODE == NEAREST_P) ? a.rec.OL : a.o) + hb + (size_t)qi * D + 4 * g;
-    const float* Y = dOw + c * LD + 4 * g;
+    const TIn* Y = dOp + (size_t)qi * D + 4 * g;
     double part = 0.0;
     if (qvalid) {
 #pragma unroll
       for (int q = 0; q < D / 8; ++q) {
         const f4v x = *reinterpret_cast<const f4v*>(X + 8 * q);
-        const f4v y = *reinterpret_cast<const f4v*>(Y + 8 * q);
+        const f4v y = Ld<TIn>::four(Y + 8 * q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) part = fma((double)y[e], (double)x[e], part);
       }
@@ -146,62 +154,75 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) dq[nb] = zero16();
 
-  TileRegs<D, NT, TIn> kr, vr;
+  PairRegs<D, TIn, NT> kr;  // K rows of the next key tile, staged as the workgroup's K^T slices
+  RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
   kr.load(Kp, 0, T);
   vr.load(Vp, 0, T);
-  f16v snext;
-  if (active(0)) {
-    const float* St = Sh + tile_index(qtw, 0, a.rec.nt, a.causal) * 1024;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
-  }
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
+    const bool act = active(kt);
+    const size_t to = tile_index(qtw, act ? kt : 0, a.rec.nt, a.causal) * 1024;
+    float s[16];  // stored scores: query c, key k0 + crow(v, g); in flight during the staging and g
+    if (act) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = Sh[to + v * 64 + l];
+    }
     __syncthreads();
-    kr.store(sm.Ks, LD, 1.0f);
-    vr.store(sm.Vs, LD, 1.0f);
+    kr.template store_t<NS>(sm.KT);
+    vr.template store<NS>(sm.VN);
     __syncthreads();
-    const f16v s = snext;  // S^T: row = key, column = query
     if (kt + 1 < ntiles) {
       kr.load(Kp, k0 + BN, T);
       vr.load(Vp, k0 + BN, T);
-      if (active(kt + 1)) {
-        const float* St = Sh + tile_index(qtw, kt + 1, a.rec.nt, a.causal) * 1024;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) snext[v] = St[v * 64 + l];
-      }
     }
-    if (!active(kt)) continue;
-    const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
+    if (!act) continue;
     float* Pw = Ph + to;
     float* dSw = dSh + to;
-    const f16v gt = tile_dot_lds<D>(sm.Vs, dOw, LD);  // (dO V^T)^T: g_ij = dO_i . V_j
-    f16v ds;
+    // (dO V^T)^T as bf16 slice products: register v holds g = dO_i . V_j for query c, key k0 + crow(v, g)
+    f16v gt = zero16();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = k0 + crow(v, g);
-      const bool ok = qvalid && key < T && (!a.causal || key <= qi);
-      const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-      const Weights wt = weights(d, trow);
-      const bool keep = ok && !d.tail;
-      const float Delta = keep ? (wt.E1 - wt.E0) * rc.inv_hf : 0.f;
-      const float gam = keep ? (gt[v] - Di) * invWg : 0.f;
-      const float dS = gam * Delta;
-      ds[v] = dS;
-      // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
-      Pw[v * 64 + l] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
-      dSw[v * 64 + l] = dS;
-      if (FULL) {
-        sds += (double)dS;
-        if (CAL == MINMAX) {
-          const float rf = (float)d.r;
-          // K * dw/dM = (r - K) w + t e^{b_{r+1}} - kappa (r + t) Delta
-          const float dMk = fmaf(rf - (float)K, wt.wL, d.t * wt.E1) - rc.kappa * (rf + d.t) * Delta;
-          acc_a = fma((double)gam, (double)dMk, acc_a);
+    for (int kb = 0; kb < D / 16; ++kb) {
+      Split8 db;
+      db.h = dos[kb].h;
+      if (NS == 3) {
+        db.m = dos[kb].m;
+        db.l = *reinterpret_cast<const bf8v*>(dol + 16 * kb);
+      }
+      gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), db, gt);
+    }
+    // half tiles (keys crow(v, g), v = 8 b .. 8 b + 7): decisions, weights and dS, then their share of
+    // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g))
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int v = 8 * b + j, key = k0 + crow(v, g);
+        const bool ok = qvalid && key < T && (!a.causal || key <= qi);
+        const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+        const Weights wt = weights(d, trow);
+        const bool keep = ok && !d.tail;
+        const float Delta = keep ? (wt.E1 - wt.E0) * rc.inv_hf : 0.f;
+        const float gam = keep ? (gt[v] - Di) * invWg : 0.f;
+        const float dS = gam * Delta;
+        ds[j] = dS;
+        // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
+        Pw[v * 64 + l] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
+        dSw[v * 64 + l] = dS;
+        if (FULL) {
+          sds += (double)dS;
+          if (CAL == MINMAX) {
+            const float rf = (float)d.r;
+            // K * dw/dM = (r - K) w + t e^{b_{r+1}} - kappa (r + t) Delta
+            const float dMk = fmaf(rf - (float)K, wt.wL, d.t * wt.E1) - rc.kappa * (rf + d.t) * Delta;
+            acc_a = fma((double)gam, (double)dMk, acc_a);
+          }
         }
       }
+      const Split8 dss = split8(ds);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.KT, b, 32 * nb + c), dq[nb]);
     }
-    tile_accum<D>(dq, ds, sm.Ks, LD);
   }
 
   // extremum terms of the row: alpha per tied max key, beta per tied min key
@@ -237,12 +258,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
       const int k0 = kt * BN;
       __syncthreads();
       kr.load(Kp, k0, T);
-      kr.store(sm.Ks, LD, 1.0f);
+      kr.template store_t<NS>(sm.KT);
       __syncthreads();
       if (!active(kt)) continue;
       const size_t to = tile_index(qtw, kt, a.rec.nt, a.causal) * 1024;
       const float* St = Sh + to;
-      f16v inj;
+      float inj[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float sv = St[v * 64 + l];
@@ -254,7 +275,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         inj[v] = x;
         if (x != 0.f) dSh[to + v * 64 + l] += x;  // stored by this lane in the first sweep
       }
-      tile_accum<D>(dq, inj, sm.Ks, LD);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const Split8 is = split8(inj + 8 * b);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma_split<NS>(is, load_bt<D, NS>(sm.KT, b, 32 * nb + c), dq[nb]);
+      }
     }
   }
   if (g == 0) {
@@ -395,7 +421,7 @@ template <int D, int CAL, int MODE, bool FULL, typename TIn>
 static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int stage) {
   if (stage & 1) {
     const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
-    const size_t smem = sizeof(DqSmem<D>) + sizeof(float) * DQ_BM * (p.K + 1);
+    const size_t smem = dq_smem_bytes<D, TIn>(p.K);
     hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
