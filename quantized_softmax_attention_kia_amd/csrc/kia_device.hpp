@@ -94,17 +94,46 @@ struct Split8 {
   bf8v h, m, l;
 };
 
-__device__ __forceinline__ Split8 split8(const float* x) {
-  Split8 s;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = (__bf16)x[e];
-    const float r = x[e] - (float)h;   // exact: h is within a factor 2 of x
-    const __bf16 m = (__bf16)r;
-    s.h[e] = h;
-    s.m[e] = m;
-    s.l[e] = (__bf16)(r - (float)m);
+// Two floats rounded to bf16 (round to nearest even) in one packed conversion: a in the low
+// half, b in the high half.
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{a, b}, bf2v));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Three-slice split of two floats, each slice packed as a bf16 pair (a low, b high).  Each
+// residual is exact: a slice is within a factor 2 of what it rounds.
+struct SplitPair {
+  uint32_t h, m, l;
+};
+template <int NS = 3>
+__device__ __forceinline__ SplitPair split_pair(float a, float b) {
+  SplitPair s;
+  s.h = cvt_pk_bf16(a, b);
+  if (NS == 3) {
+    const float ra = a - bf16_lo(s.h), rb = b - bf16_hi(s.h);
+    s.m = cvt_pk_bf16(ra, rb);
+    s.l = cvt_pk_bf16(ra - bf16_lo(s.m), rb - bf16_hi(s.m));
   }
+  return s;
+}
+
+__device__ __forceinline__ Split8 split8(const float* x) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const SplitPair sp = split_pair(x[2 * e], x[2 * e + 1]);
+    h[e] = sp.h;
+    m[e] = sp.m;
+    l[e] = sp.l;
+  }
+  Split8 s;
+  __builtin_memcpy(&s.h, h, 16);
+  __builtin_memcpy(&s.m, m, 16);
+  __builtin_memcpy(&s.l, l, 16);
   return s;
 }
 
@@ -150,18 +179,13 @@ struct PairRegs {
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       const int at = ((cg * CW + j) * TP + 2 * rp) >> 1;
-      const __bf16 h0 = (__bf16)x0[j], h1 = (__bf16)x1[j];
-      w[at] = pack(h0, h1);
+      const SplitPair sp = split_pair<NS>(x0[j], x1[j]);
+      w[at] = sp.h;
       if (NS == 3) {
-        const float r0 = x0[j] - (float)h0, r1 = x1[j] - (float)h1;
-        const __bf16 m0 = (__bf16)r0, m1 = (__bf16)r1;
-        w[at + (D * TP >> 1)] = pack(m0, m1);
-        w[at + (D * TP)] = pack((__bf16)(r0 - (float)m0), (__bf16)(r1 - (float)m1));
+        w[at + (D * TP >> 1)] = sp.m;
+        w[at + (D * TP)] = sp.l;
       }
     }
-  }
-  __device__ static __forceinline__ uint32_t pack(__bf16 lo, __bf16 hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
 };
 
