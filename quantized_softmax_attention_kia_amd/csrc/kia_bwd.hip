@@ -78,7 +78,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS>));
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, ts = K + 1;
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
   int head, rank;
@@ -352,7 +352,7 @@ template <int D, typename TIn>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int NS = nslices<TIn>();
   __shared__ KvSmem<D, NS> sm;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, nt = a.rec.nt;
   int head, kt;
   block_work(a.nheads, head, kt);  // low key tiles see the most queries: heaviest first

@@ -409,6 +409,9 @@ __device__ __forceinline__ void tile_accum(f16v (&out)[D / 32], const f16v& coef
   }
 }
 
+// The wave's index in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // LDS written by some lanes of the wave and read by others: the wave's LDS operations run in
 // program order, so only the compiler has to be kept from moving them across this point.
 __device__ __forceinline__ void wave_lds_sync() {

@@ -105,15 +105,15 @@ __device__ __forceinline__ bf8v bf_abs(bf8v v) {
   return r;
 }
 
+// With mx >= mx2 the new runner-up is the median of (x, mx, mx2); likewise for the minimum.
+// A value equal to the extremum keeps the earlier key and becomes the runner-up (a tie).
 __device__ __forceinline__ void top2(Top2& e, float x, int key) {
-  const bool gx = x > e.mx;
-  e.mx2 = gx ? e.mx : (x > e.mx2 ? x : e.mx2);
-  e.ax = gx ? key : e.ax;
-  e.mx = gx ? x : e.mx;
-  const bool ln = x < e.mn;
-  e.mn2 = ln ? e.mn : (x < e.mn2 ? x : e.mn2);
-  e.an = ln ? key : e.an;
-  e.mn = ln ? x : e.mn;
+  e.ax = x > e.mx ? key : e.ax;
+  e.mx2 = __builtin_amdgcn_fmed3f(x, e.mx, e.mx2);
+  e.mx = fmaxf(x, e.mx);
+  e.an = x < e.mn ? key : e.an;
+  e.mn2 = __builtin_amdgcn_fmed3f(x, e.mn, e.mn2);
+  e.mn = fminf(x, e.mn);
 }
 // Merge the extrema of another set of keys; on equal maxima / minima the lower key wins.
 __device__ __forceinline__ void top2_combine(Top2& e, const Top2& o) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FwdSmem<D, NS>& sm = *reinterpret_cast<FwdSmem<D, NS>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D, NS>));
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 5, c = l & 31;
+  const int w = wave_id(), l = threadIdx.x & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, ts = K + 1, nt = a.rec.nt;
   int head, rank;
   block_work(a.nheads, head, rank);
@@ -191,7 +191,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       qa[kb] = bf_abs(qs[kb].h);
     }
   }
-  Top2 ex{-INFINITY, -INFINITY, INFINITY, INFINITY, INT_MAX, INT_MAX};
+  // keys are tracked without the lane's 4 g (crow(v, g) = crow(v, 0) + 4 g), a wave-uniform value
+  Top2 ex{-INFINITY, -INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4};
   float amx = 0.f;  // largest sum of |q_h| |k_h| over the row's visible keys
   RowOp<D, TIn> kr;
   if (w < ntiles) kr.load(Kp, w * BN + c, T);
@@ -223,14 +224,16 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         St[v * 64] = x;
         const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
         if (ok) {
-          top2(ex, x, key);
-          amx = aacc[v] > amx ? aacc[v] : amx;
+          top2(ex, x, k0 + crow(v, 0));
+          amx = fmaxf(amx, aacc[v]);
         }
       }
     };
     if (full_tile(kt)) epilogue(std::false_type{});
     else epilogue(std::true_type{});
   }
+  ex.ax += 4 * g;
+  ex.an += 4 * g;
   top2_merge(ex, 32);
   amx = fmaxf(amx, __shfl_xor(amx, 32));
   if (g == 0) {
@@ -494,7 +497,7 @@ size_t fwd_smem_bytes(int K) {
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
 template <int CAL, bool NEAREST>
 __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, c = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, nt = a.rec.nt;
   const int L = blockIdx.x;
   const int head = L / nt, qt = L % nt;
