@@ -429,6 +429,7 @@ struct RowCal {
   double inv_h;   // 1/h
   float inv_hf;   // 1/h rounded to float (secant slopes)
   float kappa;    // 1 on the regular MinMax branch (h depends on M, m), 0 on the degenerate one
+  float origin_f; // the origin as a float (m or M: exact)
 };
 
 template <int CAL>
@@ -447,6 +448,7 @@ __device__ __forceinline__ RowCal row_calibration(float M, float m, int K, float
     rc.kappa = 1.0f;
   }
   rc.inv_hf = (float)rc.inv_h;
+  rc.origin_f = CAL == MINMAX ? m : M;
   return rc;
 }
 
@@ -487,6 +489,28 @@ __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, flo
   return d;
 }
 
+// The same decision with u formed in float, for a caller that checks it against a margin.  Each
+// of the (at most four) roundings on the way to u errs by at most 2^-24 of a quantity below
+// (K + 1) interval widths, so this u is within (K + 1) 2^-22 of decide()'s: a decision whose t
+// is farther than that from 0, 1 (interior boundaries) and 1/2 (Nearest) is decide()'s, and so
+// is the FWM tail flag when |(s - M) + tau| (in float) exceeds tau 2^-21.
+template <int CAL>
+__device__ __forceinline__ Decision decide_fast(float s, const RowCal& rc, int K, float tau) {
+  Decision d;
+  float u;
+  if (CAL == MINMAX) {
+    u = (s - rc.origin_f) * rc.inv_hf;
+    d.tail = false;
+  } else {
+    const float z = s - rc.origin_f;
+    d.tail = z < -tau;
+    u = (fmaxf(z, -tau) + tau) * rc.inv_hf;
+  }
+  const int r = min(max((int)floorf(u), 0), K - 1);
+  d.r = r;
+  d.t = __builtin_amdgcn_fmed3f(u - (float)r, 0.f, 1.f);
+  return d;
+}
 // Reconstructed weights of one key (§3 "Reconstruction"), from the row's grid table.
 struct Weights {
   float E0, E1;  // e^{b_r}, e^{b_{r+1}}

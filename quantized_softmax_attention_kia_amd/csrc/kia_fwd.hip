@@ -326,8 +326,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 
   // ---- calibration and grid table (K+1 exponentials per row), shared by the waves
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
-  // the error bound in interval widths, with room for the rounding of t itself
-  const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f;
+  // the error bound in interval widths, with room for the float arithmetic of decide_fast and the
+  // rounding of t itself
+  const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f + (float)(K + 1) * 0x1p-22f;
+  const float edge = Erow + a.tau * 0x1p-21f;  // FWM window edge: margin of |(s - M) + tau|
   float* trow = tbl + c * ts;
   for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
   __syncthreads();
@@ -370,12 +372,14 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         for (int j = 0; j < 8; ++j) {
           const int v = 8 * b + j, key = k0 + crow(v, g);
           const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
-          const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+          // first pass: float arithmetic, checked against the margin; again: the exact decision
+          const Decision d = decltype(check)::value ? decide_fast<CAL>(s[v], rc, K, a.tau)
+                                                    : decide<CAL>(s[v], rc, K, a.tau);
           if (decltype(check)::value) {
             // a decision within the score's error bound of a boundary must be taken on the exact score
             bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1);
             if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < du;
-            if (CAL == FWM) r = r || fabs((double)s[v] - ((double)M - (double)a.tau)) <= (double)Erow;
+            if (CAL == FWM) r = r || fabsf((s[v] - M) + a.tau) <= edge;
             risky |= (ok && r) ? (1u << j) : 0u;
           }
           const Weights wt = weights(d, trow);
