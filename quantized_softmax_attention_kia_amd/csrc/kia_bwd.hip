@@ -58,17 +58,14 @@ template <int D, int NS>
 struct DqSmem {
   __align__(16) __bf16 KT[NS * D * TP];         // K^T of the key tile, bf16 slices (dQ += dS K)
   __align__(16) __bf16 VN[NS * BN * np<D>()];   // V rows of the key tile, bf16 slices (g = V dO^T)
-  // the smallest slice of each lane's dO row, read back only by that lane (registers hold the
-  // other two)
-  __align__(16) __bf16 dOl[NS == 3 ? DQ_BM * np<D>() : 8];
   float alpha[DQ_BM], beta[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
-  // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 1) floats
+  // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 3) floats
 };
 
 template <int D, typename TIn>
 size_t dq_smem_bytes(int K) {
-  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * DQ_BM * (K + 1);
+  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * DQ_BM * (K + 3);
 }
 
 // At D = 64 the register budget is held to two waves per SIMD.
@@ -79,7 +76,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS>));
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
-  const int T = a.T, K = a.K, ts = K + 1;
+  const int T = a.T, K = a.K, ts = K + 3;  // grid table row: e^{b_0} .. e^{b_K}, then two zeros
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
   int head, rank;
   block_work(a.nheads, head, rank);
@@ -104,15 +101,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 
   // the lane's dO row as bf16 slices, columns 16 kb + 8 g ..: the B operand of every g = V dO^T
   Split8 dos[D / 16];
-  __bf16* dol = sm.dOl + (NS == 3 ? rl * np<D>() + 8 * g : 0);
   {
     RowOp<D, TIn> dr;
     dr.load(dOp, qi, T);
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      dos[kb] = dr.split(kb);
-      if (NS == 3) *reinterpret_cast<bf8v*>(dol + 16 * kb) = dos[kb].l;
-    }
+    for (int kb = 0; kb < D / 16; ++kb) dos[kb] = dr.split(kb);
   }
 
   // row record of the forward
@@ -143,13 +136,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
   float* trow = tbl + rl * ts;
-  if (qvalid)
-    for (int r = g; r <= K; r += 2) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+  for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
   // extra tied extrema (beyond the first index) need a second sweep to find them
   const bool rowties = FULL && qvalid && (M != m) && (nA > 1 || (CAL == MINMAX && nC > 1));
   const bool blockties = __syncthreads_or(rowties);
 
-  double acc_a = 0.0, sds = 0.0;  // calibration sums: terms of both signs, summed in double
+  double acc_a = 0.0, sds = 0.0;  // calibration sums of the row (terms of both signs)
   f16v dq[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) dq[nb] = zero16();
@@ -158,15 +150,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
   kr.load(Kp, 0, T);
   vr.load(Vp, 0, T);
+  // stored scores of a tile: query c, key k0 + crow(v, g); loaded one tile ahead
+  auto load_s = [&](int kt, float (&dst)[16]) {
+    const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024 + l;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dst[v] = St[v * 64];
+  };
+  float snext[16];
+  if (active(0)) load_s(0, snext);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * BN;
     const bool act = active(kt);
     const size_t to = tile_index(qtw, act ? kt : 0, a.rec.nt, a.causal) * 1024;
-    float s[16];  // stored scores: query c, key k0 + crow(v, g); in flight during the staging and g
-    if (act) {
+    float s[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = Sh[to + v * 64 + l];
-    }
+    for (int v = 0; v < 16; ++v) s[v] = snext[v];
+    if (kt + 1 < ntiles && active(kt + 1)) load_s(kt + 1, snext);
     __syncthreads();
     kr.template store_t<NS>(sm.KT);
     vr.template store<NS>(sm.VN);
@@ -181,43 +180,43 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     // (dO V^T)^T as bf16 slice products: register v holds g = dO_i . V_j for query c, key k0 + crow(v, g)
     f16v gt = zero16();
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      Split8 db;
-      db.h = dos[kb].h;
-      if (NS == 3) {
-        db.m = dos[kb].m;
-        db.l = *reinterpret_cast<const bf8v*>(dol + 16 * kb);
-      }
-      gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), db, gt);
-    }
+    for (int kb = 0; kb < D / 16; ++kb) gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), dos[kb], gt);
     // half tiles (keys crow(v, g), v = 8 b .. 8 b + 7): decisions, weights and dS, then their share of
-    // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g))
+    // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g)).  A key
+    // that is not visible, or in the FWM tail, takes the table's two zero entries (r = K + 1): its
+    // weight, slope, dS and calibration terms are then exactly zero.
+    const int lim = (qvalid ? (a.causal ? min(qi, T - 1) : T - 1) : -1) - k0 - 4 * g;  // crow(v, 0) <= lim
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float ds[8];
+      // the half tile's calibration terms, summed in float (8 terms) and then joined in double
+      float hs = 0.f, ha = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int v = 8 * b + j, key = k0 + crow(v, g);
-        const bool ok = qvalid && key < T && (!a.causal || key <= qi);
-        const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+        const int v = 8 * b + j;
+        Decision d = decide<CAL>(s[v], rc, K, a.tau);
+        if (!(crow(v, 0) <= lim) || d.tail) d.r = K + 1;
         const Weights wt = weights(d, trow);
-        const bool keep = ok && !d.tail;
-        const float Delta = keep ? (wt.E1 - wt.E0) * rc.inv_hf : 0.f;
-        const float gam = keep ? (gt[v] - Di) * invWg : 0.f;
+        const float Delta = (wt.E1 - wt.E0) * rc.inv_hf;
+        const float gam = (gt[v] - Di) * invWg;
         const float dS = gam * Delta;
         ds[j] = dS;
         // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
-        Pw[v * 64 + l] = keep ? ((MODE == LERP) ? wt.wL : wt.wN) * invWf : 0.f;
+        Pw[v * 64 + l] = ((MODE == LERP) ? wt.wL : wt.wN) * invWf;
         dSw[v * 64 + l] = dS;
         if (FULL) {
-          sds += (double)dS;
+          hs += dS;
           if (CAL == MINMAX) {
             const float rf = (float)d.r;
             // K * dw/dM = (r - K) w + t e^{b_{r+1}} - kappa (r + t) Delta
             const float dMk = fmaf(rf - (float)K, wt.wL, d.t * wt.E1) - rc.kappa * (rf + d.t) * Delta;
-            acc_a = fma((double)gam, (double)dMk, acc_a);
+            ha = fmaf(gam, dMk, ha);
           }
         }
+      }
+      if (FULL) {
+        sds += (double)hs;
+        if (CAL == MINMAX) acc_a += (double)ha;
       }
       const Split8 dss = split8(ds);
 #pragma unroll
