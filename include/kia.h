@@ -83,12 +83,15 @@ typedef struct {
  *    Nearest with Prob-STE the LERP output O^L, and the scores themselves.
  *    Layout (offsets are multiples of 256 bytes), N = B*H*T, nt = ceil(T/32):
  *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N];
+ *      (m, amin and nC belong to MinMax; under FWM m = M and amin = nC = 0)
  *      float OL[N*D] (Nearest + Prob-STE only);
- *      float S[B*H][tiles][1024]: the scores s_ij = scale * Q_i . K_j, computed with
- *        exact products and double accumulation and rounded once to float, in
+ *      float S[B*H][tiles][1024]: the scores s_ij = scale * Q_i . K_j as floats, in
  *        32 x 32 tiles (query tile, key tile); tiles = nt(nt+1)/2 when causal
  *        (key tile <= query tile), nt^2 otherwise.  About 2 T^2 bytes per head
- *        when causal.
+ *        when causal.  Each is within a rigorous per-row bound of the exactly
+ *        rounded score (exact products, double sum, one rounding), and equal to it
+ *        wherever that bound could change an extremum or a bin decision, so every
+ *        decision taken on S is the one the exactly rounded scores give.
  *  bwd_ws_bytes: scratch for kia_backward: two arrays of float tiles numbered
  *    like S, P[B*H][tiles][1024] (the forward's normalized weights: P^L for LERP,
  *    the hard P^N for Nearest) and dS[B*H][tiles][1024] (the unscaled score

@@ -138,7 +138,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   float* trow = tbl + rl * ts;
   for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
   // extra tied extrema (beyond the first index) need a second sweep to find them
-  const bool rowties = FULL && qvalid && (M != m) && (nA > 1 || (CAL == MINMAX && nC > 1));
+  // (a MinMax row with M == m has every grid value 1: both extremum terms vanish; FWM records m = M)
+  const bool flat = CAL == MINMAX && M == m;
+  const bool rowties = FULL && qvalid && !flat && (nA > 1 || (CAL == MINMAX && nC > 1));
   const bool blockties = __syncthreads_or(rowties);
 
   double acc_a = 0.0, sds = 0.0;  // calibration sums of the row (terms of both signs)
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 
   // extremum terms of the row: alpha per tied max key, beta per tied min key
   float alpha = 0.f, beta = 0.f;
-  const bool inject = FULL && qvalid && M != m;  // M == m: every grid value is 1, both terms vanish
+  const bool inject = FULL && qvalid && !flat;
   if (FULL) {
     acc_a += __shfl_xor(acc_a, 32);
     sds += __shfl_xor(sds, 32);
@@ -386,11 +388,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     if (!act) continue;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+      // the half tile's LDS operands are read first, so that their latency overlaps the splits
+      Split8 bo[D / 32], bq[D / 32];
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        bo[nb] = load_bt<D, NS>(sm.dOT, b, 32 * nb + c);
+        bq[nb] = load_bt<D, NS>(sm.QT, b, 32 * nb + c);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the splits
       const Split8 ps = split8(p + 8 * b), dss = split8(ds + 8 * b);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
-        dv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), dv[nb]);
-        dk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), dk[nb]);
+        dv[nb] = mfma_split<NS>(ps, bo[nb], dv[nb]);
+        dk[nb] = mfma_split<NS>(dss, bq[nb], dk[nb]);
       }
     }
   }

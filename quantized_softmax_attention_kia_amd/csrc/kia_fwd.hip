@@ -10,10 +10,10 @@
 //   pass 1  scores of each 32 x 32 tile as bf16 slice products on the matrix pipe
 //           (K operands loaded straight from memory into registers) with a
 //           rigorous error bound per row, stored for every later pass; the row
-//           max / min, first index attaining them and tie counts are then settled
-//           on exact scores (double products and sums, rounded once to fp32): the
-//           winner alone when the runner-up is farther than twice the bound, else
-//           every candidate within it, each patched into the stored tile;
+//           max (and for MinMax min), first index attaining it and tie count are then
+//           settled on exact scores (double products and sums, rounded once to fp32)
+//           of every candidate within twice the bound, each patched into the stored
+//           tile by the lane that stored it;
 //   then    per-row calibration and the (K+1)-entry grid table e^{b_r} in LDS
 //           (the only exponentials of the operator);
 //   pass 2  stored scores -> bin decision (one closer to a boundary than the
@@ -73,13 +73,13 @@ struct FwdSmem {
 // n fp32 additions errs by at most (n - 1) u sum|terms|, so the two sums err by at most
 // 1.008 (D - 1) u S and 5D u 0.008 S (S = sum_d |q_d k_d|), the dropped products by 4.1 u S,
 // and the final add, the fp32 scale product and the rounding of the exact score to fp32 by
-// 4 u |s|.  S <= 1.01 A, where A is the fp32 sum of |q_h| |k_h| (|x| <= |h| / (1 - 2^-8)),
-// one more bf16 product.  With bf16 inputs only h h' exists, exact in bf16.  So
-// |s~ - s| <= scale * ACC_C * A + 2^-22 |s~|, and a decision this bound cannot settle is taken
+// 4 u |s| <= 4 u S (scale folded in).  S <= 1.01 A, where A is the fp32 sum of |q_h| |k_h|
+// (|x| <= |h| / (1 - 2^-8)), one more bf16 product.  With bf16 inputs only h h' exists, exact
+// in bf16.  So |s~ - s| <= scale * ACC_C * A, and a decision this bound cannot settle is taken
 // again on the score recomputed exactly (double products and sums, rounded once).
 template <int D, int NS>
 constexpr double acc_c() {
-  return NS == 3 ? 1.01 * (1.008 * (D - 1) + 0.04 * D + 4.1) * 0x1p-24 : 1.01 * D * 0x1p-24;
+  return NS == 3 ? 1.01 * (1.008 * (D - 1) + 0.04 * D + 8.1) * 0x1p-24 : 1.01 * (D + 4) * 0x1p-24;
 }
 
 // The exact score of one (query, key) pair: products and sum in double, scale in double,
@@ -87,13 +87,31 @@ constexpr double acc_c() {
 template <int D, typename TIn>
 __device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, double scale) {
   double acc = 0.0;
-#pragma unroll 4
+#pragma unroll 8
   for (int d = 0; d < D; d += 4) {
     const f4v x = Ld<TIn>::four(qrow + d), y = Ld<TIn>::four(krow + d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = fma((double)x[e], (double)y[e], acc);
   }
   return (float)(scale * acc);
+}
+
+// Exact scores of one query against two keys in one sweep (the loads of both in flight together).
+template <int D, typename TIn>
+__device__ __forceinline__ void exact_score2(const TIn* qrow, const TIn* k1, const TIn* k2, double scale,
+                                             float& s1, float& s2) {
+  double a1 = 0.0, a2 = 0.0;
+#pragma unroll 8
+  for (int d = 0; d < D; d += 4) {
+    const f4v x = Ld<TIn>::four(qrow + d), y1 = Ld<TIn>::four(k1 + d), y2 = Ld<TIn>::four(k2 + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a1 = fma((double)x[e], (double)y1[e], a1);
+      a2 = fma((double)x[e], (double)y2[e], a2);
+    }
+  }
+  s1 = (float)(scale * a1);
+  s2 = (float)(scale * a2);
 }
 
 __device__ __forceinline__ bf8v bf_abs(bf8v v) {
@@ -107,13 +125,17 @@ __device__ __forceinline__ bf8v bf_abs(bf8v v) {
 
 // With mx >= mx2 the new runner-up is the median of (x, mx, mx2); likewise for the minimum.
 // A value equal to the extremum keeps the earlier key and becomes the runner-up (a tie).
+// The minimum is tracked for MinMax only (FWM calibrates on the maximum alone).
+template <int CAL>
 __device__ __forceinline__ void top2(Top2& e, float x, int key) {
   e.ax = x > e.mx ? key : e.ax;
   e.mx2 = __builtin_amdgcn_fmed3f(x, e.mx, e.mx2);
   e.mx = fmaxf(x, e.mx);
-  e.an = x < e.mn ? key : e.an;
-  e.mn2 = __builtin_amdgcn_fmed3f(x, e.mn, e.mn2);
-  e.mn = fminf(x, e.mn);
+  if (CAL == MINMAX) {
+    e.an = x < e.mn ? key : e.an;
+    e.mn2 = __builtin_amdgcn_fmed3f(x, e.mn, e.mn2);
+    e.mn = fminf(x, e.mn);
+  }
 }
 // Merge the extrema of another set of keys; on equal maxima / minima the lower key wins.
 __device__ __forceinline__ void top2_combine(Top2& e, const Top2& o) {
@@ -224,7 +246,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         St[v * 64] = x;
         const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
         if (ok) {
-          top2(ex, x, k0 + crow(v, 0));
+          top2<CAL>(ex, x, k0 + crow(v, 0));
           amx = fmaxf(amx, aacc[v]);
         }
       }
@@ -234,6 +256,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   }
   ex.ax += 4 * g;
   ex.an += 4 * g;
+  const Top2 loc = ex;  // this lane's own extrema: keys whose scores it stored
   top2_merge(ex, 32);
   amx = fmaxf(amx, __shfl_xor(amx, 32));
   if (g == 0) {
@@ -249,41 +272,44 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     amx = fmaxf(amx, sm.amx[v][c]);
   }
   // error bound of the row's scores, and of u in interval widths (below)
-  const float srow = fmaxf(fabsf(ex.mx), fabsf(ex.mn));
-  const float Erow = (float)(a.scale * acc_c<D, NS>()) * amx + 0x1p-22f * srow + 1e-30f;
+  const float Erow = (float)(a.scale * acc_c<D, NS>()) * amx + 1e-30f;
 
-  // ---- exact extrema: a clear winner is recomputed exactly (by every wave; the lane that stored
-  // it patches it); a near-tie rescans the row, each wave its own key tiles
-  const bool clearM = ex.mx - ex.mx2 > 2.f * Erow, clearm = ex.mn2 - ex.mn > 2.f * Erow;
-  XExt xM{ex.mx, ex.ax, 1}, xm{ex.mn, ex.an, 1};
-  {
-    // wave 0 takes the maximum, wave 1 % FWD_NW the minimum; the values meet in LDS and the
-    // lane that stored each element patches it
-    if (qvalid && clearM && w == 0) sm.xM[0][c].v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.ax * D, a.scale);
-    if (qvalid && clearm && w == 1 % FWD_NW) sm.xm[0][c].v = exact_score<D, TIn>(qrow, Kp + (size_t)ex.an * D, a.scale);
-    __syncthreads();
-    if (qvalid && clearM) {
-      xM.v = sm.xM[0][c].v;
-      if (w == (ex.ax / BN) % FWD_NW && g == ((ex.ax >> 2) & 1)) Sh[stored_at(ex.ax)] = xM.v;
+  // ---- exact extrema.  Every key whose exact score can attain the row maximum (minimum) has a
+  // stored score within 2 Erow of the approximate one: a candidate.  A lane holding one candidate
+  // per side recomputes it exactly and patches the element it stored; a lane holding two
+  // (rare) makes the workgroup rescan its tiles for every candidate.  First index and tie
+  // count are then taken over exact values.
+  const float thrM = ex.mx - 2.f * Erow, thrm = ex.mn + 2.f * Erow;
+  XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
+  const bool multi = qvalid && (loc.mx2 >= thrM || (CAL == MINMAX && loc.mn2 <= thrm));
+  if (!__syncthreads_or(multi)) {
+    const bool cM = qvalid && loc.mx >= thrM, cm = CAL == MINMAX && qvalid && loc.mn <= thrm;
+    if (cM || cm) {
+      const int kM = cM ? loc.ax : loc.an, km = cm ? loc.an : loc.ax;
+      float xM_, xm_;
+      if (CAL == MINMAX) exact_score2<D, TIn>(qrow, Kp + (size_t)kM * D, Kp + (size_t)km * D, a.scale, xM_, xm_);
+      else xM_ = exact_score<D, TIn>(qrow, Kp + (size_t)kM * D, a.scale);
+      if (cM) {
+        Sh[stored_at(kM)] = xM_;
+        yM = XExt{xM_, kM, 1};
+      }
+      if (cm) {
+        Sh[stored_at(km)] = xm_;
+        ym = XExt{xm_, km, 1};
+      }
     }
-    if (qvalid && clearm) {
-      xm.v = sm.xm[0][c].v;
-      if (w == (ex.an / BN) % FWD_NW && g == ((ex.an >> 2) & 1)) Sh[stored_at(ex.an)] = xm.v;
-    }
-    __syncthreads();  // the LDS slots are reused by a rescan below
-  }
-  const bool scanM = qvalid && !clearM, scanm = qvalid && !clearm;
-  if (__syncthreads_or(scanM || scanm)) {
+  } else {
     // every stored score within 2 Erow of the approximate extremum is recomputed and patched
-    const float thrM = ex.mx - 2.f * Erow, thrm = ex.mn + 2.f * Erow;
-    XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
+    const bool scanM = qvalid, scanm = CAL == MINMAX && qvalid;
     for (int kt = w; kt < ntiles; kt += FWD_NW) {
       float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+      float x[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[v] = St[v * 64];
       for (int v = 0; v < 16; ++v) {
         const int key = kt * BN + crow(v, g);
-        const bool ok = qvalid && key < T && (!a.causal || key <= qi);
-        const float x = St[v * 64];
-        const bool cM = scanM && ok && x >= thrM, cm = scanm && ok && x <= thrm;
+        const bool ok = key < T && (!a.causal || key <= qi);
+        const bool cM = scanM && ok && x[v] >= thrM, cm = scanm && ok && x[v] <= thrm;
         if (cM || cm) {
           const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)key * D, a.scale);
           St[v * 64] = xe;
@@ -296,23 +322,21 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         }
       }
     }
-    xext_merge(yM, 32, true);
-    xext_merge(ym, 32, false);
-    if (g == 0) {
-      sm.xM[w][c] = yM;
-      sm.xm[w][c] = ym;
-    }
-    __syncthreads();
-    yM = sm.xM[0][c];
-    ym = sm.xm[0][c];
-#pragma unroll
-    for (int v = 1; v < FWD_NW; ++v) {
-      xext_combine(yM, sm.xM[v][c], true);
-      xext_combine(ym, sm.xm[v][c], false);
-    }
-    if (scanM) xM = yM;
-    if (scanm) xm = ym;
   }
+  xext_merge(yM, 32, true);
+  if (CAL == MINMAX) xext_merge(ym, 32, false);
+  if (g == 0) {
+    sm.xM[w][c] = yM;
+    sm.xm[w][c] = ym;
+  }
+  __syncthreads();
+  XExt xM = sm.xM[0][c], xm = sm.xm[0][c];
+#pragma unroll
+  for (int v = 1; v < FWD_NW; ++v) {
+    xext_combine(xM, sm.xM[v][c], true);
+    if (CAL == MINMAX) xext_combine(xm, sm.xm[v][c], false);
+  }
+  if (CAL == FWM) xm = xM;  // FWM: no minimum (recorded as M)
   const float M = xM.v, m = xm.v;
   if (w == 0 && g == 0 && qvalid) {
     const size_t row = (size_t)head * T + qi;
@@ -362,6 +386,14 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     for (int nb = 0; nb < D / 32; ++nb) { ot[nb] = zero16(); otl[nb] = zero16(); }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {  // half tiles: keys crow(v, g) for v = 8b .. 8b+7
+      // the half tile's V^T operands are read from LDS first, so that their latency overlaps the
+      // weighing (not under Nearest with Prob-STE, whose second accumulator takes the registers)
+      Split8 vb[D / 32];
+      if (MODE != NEAREST_P) {
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       float p[8], pl[8];
       double tL, tN;  // the half tile's weight sums, joined to the row sums once it is settled
       uint32_t risky = 0;
@@ -408,13 +440,17 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
       sumL += tL;
       sumN += tN;
+      if (MODE == NEAREST_P) {
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
+      }
       const Split8 ps = split8(p);
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+      for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
       if (MODE == NEAREST_P) {
         const Split8 psl = split8(pl);
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) otl[nb] = mfma_split<NS>(psl, load_bt<D, NS>(VT, b, 32 * nb + c), otl[nb]);
+        for (int nb = 0; nb < D / 32; ++nb) otl[nb] = mfma_split<NS>(psl, vb[nb], otl[nb]);
       }
     }
 #pragma unroll
