@@ -38,11 +38,11 @@ constexpr int FWD_NT = 64 * FWD_NW;
 constexpr int BN = 32;               // keys per tile, query rows per workgroup
 
 
-// Approximate extrema of a row: largest value, its first key and the runner-up; smallest
-// value, its first key and the runner-up.  Keys reach a lane in increasing order.
-struct Top2 {
-  float mx, mx2, mn, mn2;
-  int ax, an;
+// Approximate extrema of the keys one lane stored: the three largest values and the keys of the
+// first two, likewise for the smallest.  Keys reach a lane in increasing order.
+struct Lane3 {
+  float mx, mx2, mx3, mn, mn2, mn3;
+  int ax, ax2, an, an2;
 };
 // Exact extrema of a row over the stored scores: value, first key, count of ties.
 struct XExt {
@@ -58,8 +58,7 @@ constexpr int fwd_wave_bytes() {  // per wave: V^T slices of its key tile, later
 template <int D, int NS>
 struct FwdSmem {
   __align__(16) unsigned char wave[FWD_NW][fwd_wave_bytes<D, NS>()];
-  Top2 ext[FWD_NW][BN];
-  float amx[FWD_NW][BN];
+  float rmx[FWD_NW][BN], rmn[FWD_NW][BN], amx[FWD_NW][BN];
   XExt xM[FWD_NW][BN], xm[FWD_NW][BN];
   double sL[FWD_NW][BN], sN[FWD_NW][BN];
   float rowW[BN], rowWL[BN];
@@ -123,38 +122,36 @@ __device__ __forceinline__ bf8v bf_abs(bf8v v) {
   return r;
 }
 
-// With mx >= mx2 the new runner-up is the median of (x, mx, mx2); likewise for the minimum.
-// A value equal to the extremum keeps the earlier key and becomes the runner-up (a tie).
-// The minimum is tracked for MinMax only (FWM calibrates on the maximum alone).
+// With mx >= mx2 >= mx3 the new second and third values are medians of (x, mx, mx2) and
+// (x, mx2, mx3); likewise for the minimum.  A value equal to the extremum keeps the earlier key
+// and becomes the second (a tie).  The minimum is tracked for MinMax only (FWM calibrates on the
+// maximum alone); under FWM only the first key and the second value are kept.
 template <int CAL>
-__device__ __forceinline__ void top2(Top2& e, float x, int key) {
-  e.ax = x > e.mx ? key : e.ax;
+__device__ __forceinline__ void track(Lane3& e, float x, int key) {
+  const bool g1 = x > e.mx;
+  if (CAL == MINMAX) {
+    e.ax2 = g1 ? e.ax : (x > e.mx2 ? key : e.ax2);
+    e.mx3 = __builtin_amdgcn_fmed3f(x, e.mx2, e.mx3);
+  }
+  e.ax = g1 ? key : e.ax;
   e.mx2 = __builtin_amdgcn_fmed3f(x, e.mx, e.mx2);
   e.mx = fmaxf(x, e.mx);
   if (CAL == MINMAX) {
-    e.an = x < e.mn ? key : e.an;
+    const bool l1 = x < e.mn;
+    e.an2 = l1 ? e.an : (x < e.mn2 ? key : e.an2);
+    e.mn3 = __builtin_amdgcn_fmed3f(x, e.mn2, e.mn3);
+    e.an = l1 ? key : e.an;
     e.mn2 = __builtin_amdgcn_fmed3f(x, e.mn, e.mn2);
     e.mn = fminf(x, e.mn);
   }
 }
-// Merge the extrema of another set of keys; on equal maxima / minima the lower key wins.
-__device__ __forceinline__ void top2_combine(Top2& e, const Top2& o) {
-  const bool tx = o.mx > e.mx || (o.mx == e.mx && o.ax < e.ax);
-  const float lowx = tx ? e.mx : o.mx, hi2x = e.mx2 > o.mx2 ? e.mx2 : o.mx2;
-  e.mx2 = lowx > hi2x ? lowx : hi2x;
-  e.ax = tx ? o.ax : e.ax;
-  e.mx = tx ? o.mx : e.mx;
-  const bool tn = o.mn < e.mn || (o.mn == e.mn && o.an < e.an);
-  const float highn = tn ? e.mn : o.mn, lo2n = e.mn2 < o.mn2 ? e.mn2 : o.mn2;
-  e.mn2 = highn < lo2n ? highn : lo2n;
-  e.an = tn ? o.an : e.an;
-  e.mn = tn ? o.mn : e.mn;
-}
-__device__ __forceinline__ void top2_merge(Top2& e, int lanemask) {
-  Top2 o;
-  o.mx = __shfl_xor(e.mx, lanemask); o.mx2 = __shfl_xor(e.mx2, lanemask); o.ax = __shfl_xor(e.ax, lanemask);
-  o.mn = __shfl_xor(e.mn, lanemask); o.mn2 = __shfl_xor(e.mn2, lanemask); o.an = __shfl_xor(e.an, lanemask);
-  top2_combine(e, o);
+
+// One more exact value of a side: a larger (smaller) one replaces the extremum, an equal one
+// is a tie (the lower key is the first index).
+__device__ __forceinline__ void xext_add(XExt& a, float v, int key, bool is_max) {
+  const bool better = is_max ? v > a.v : v < a.v;
+  if (better) { a.v = v; a.k = key; a.n = 1; }
+  else if (v == a.v) { a.k = min(a.k, key); ++a.n; }
 }
 
 __device__ __forceinline__ void xext_combine(XExt& a, const XExt& b, bool is_max) {
@@ -214,7 +211,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     }
   }
   // keys are tracked without the lane's 4 g (crow(v, g) = crow(v, 0) + 4 g), a wave-uniform value
-  Top2 ex{-INFINITY, -INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4};
+  Lane3 ex{-INFINITY, -INFINITY, -INFINITY, INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4,
+           INT_MAX - 4, INT_MAX - 4};
   float amx = 0.f;  // largest sum of |q_h| |k_h| over the row's visible keys
   RowOp<D, TIn> kr;
   if (w < ntiles) kr.load(Kp, w * BN + c, T);
@@ -246,7 +244,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         St[v * 64] = x;
         const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
         if (ok) {
-          top2<CAL>(ex, x, k0 + crow(v, 0));
+          track<CAL>(ex, x, k0 + crow(v, 0));
           amx = fmaxf(amx, aacc[v]);
         }
       }
@@ -255,70 +253,97 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     else epilogue(std::true_type{});
   }
   ex.ax += 4 * g;
+  ex.ax2 += 4 * g;
   ex.an += 4 * g;
-  const Top2 loc = ex;  // this lane's own extrema: keys whose scores it stored
-  top2_merge(ex, 32);
-  amx = fmaxf(amx, __shfl_xor(amx, 32));
-  if (g == 0) {
-    sm.ext[w][c] = ex;
-    sm.amx[w][c] = amx;
+  ex.an2 += 4 * g;
+  const Lane3& loc = ex;  // this lane's own extrema: keys whose scores it stored
+  // the row's approximate extrema and error bound: lanes of a row, then the waves, in LDS
+  {
+    const float rmx = fmaxf(loc.mx, __shfl_xor(loc.mx, 32)), rmn = fminf(loc.mn, __shfl_xor(loc.mn, 32));
+    amx = fmaxf(amx, __shfl_xor(amx, 32));
+    if (g == 0) {
+      sm.rmx[w][c] = rmx;
+      sm.rmn[w][c] = rmn;
+      sm.amx[w][c] = amx;
+    }
   }
   __syncthreads();
-  ex = sm.ext[0][c];
+  float rowmx = sm.rmx[0][c], rowmn = sm.rmn[0][c];
   amx = sm.amx[0][c];
 #pragma unroll
   for (int v = 1; v < FWD_NW; ++v) {
-    top2_combine(ex, sm.ext[v][c]);
+    rowmx = fmaxf(rowmx, sm.rmx[v][c]);
+    rowmn = fminf(rowmn, sm.rmn[v][c]);
     amx = fmaxf(amx, sm.amx[v][c]);
   }
   // error bound of the row's scores, and of u in interval widths (below)
   const float Erow = (float)(a.scale * acc_c<D, NS>()) * amx + 1e-30f;
 
   // ---- exact extrema.  Every key whose exact score can attain the row maximum (minimum) has a
-  // stored score within 2 Erow of the approximate one: a candidate.  A lane holding one candidate
-  // per side recomputes it exactly and patches the element it stored; a lane holding two
-  // (rare) makes the workgroup rescan its tiles for every candidate.  First index and tie
-  // count are then taken over exact values.
-  const float thrM = ex.mx - 2.f * Erow, thrm = ex.mn + 2.f * Erow;
+  // stored score within 2 Erow of the approximate one: a candidate.  Each lane recomputes its own
+  // candidates exactly (MinMax: up to two per side, whose keys it kept; FWM: one) and patches the
+  // elements it stored; a lane holding more (rare) rescans its tiles for them.  First index and
+  // tie count are then taken over exact values.
+  const float thrM = rowmx - 2.f * Erow, thrm = rowmn + 2.f * Erow;
   XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
-  const bool multi = qvalid && (loc.mx2 >= thrM || (CAL == MINMAX && loc.mn2 <= thrm));
-  if (!__syncthreads_or(multi)) {
-    const bool cM = qvalid && loc.mx >= thrM, cm = CAL == MINMAX && qvalid && loc.mn <= thrm;
-    if (cM || cm) {
-      const int kM = cM ? loc.ax : loc.an, km = cm ? loc.an : loc.ax;
-      float xM_, xm_;
-      if (CAL == MINMAX) exact_score2<D, TIn>(qrow, Kp + (size_t)kM * D, Kp + (size_t)km * D, a.scale, xM_, xm_);
-      else xM_ = exact_score<D, TIn>(qrow, Kp + (size_t)kM * D, a.scale);
-      if (cM) {
-        Sh[stored_at(kM)] = xM_;
-        yM = XExt{xM_, kM, 1};
-      }
-      if (cm) {
-        Sh[stored_at(km)] = xm_;
-        ym = XExt{xm_, km, 1};
-      }
+  // number of candidates of each side that this lane's kept keys cover (FWM keeps one key)
+  const bool scanM = qvalid && (CAL == MINMAX ? loc.mx3 >= thrM : loc.mx2 >= thrM);
+  const bool scanm = CAL == MINMAX && qvalid && loc.mn3 <= thrm;
+  const bool oneM = qvalid && loc.mx >= thrM && !scanM, onem = CAL == MINMAX && qvalid && loc.mn <= thrm && !scanm;
+  const bool twoM = CAL == MINMAX && oneM && loc.mx2 >= thrM, twom = CAL == MINMAX && onem && loc.mn2 <= thrm;
+  auto exact_pair = [&](bool dM, int kM, bool dm, int km) {
+    // exact scores of a max and a min candidate (either may be absent), patched in
+    float xM_, xm_;
+    const int kM_ = dM ? kM : km, km_ = dm ? km : kM;
+    if (CAL == MINMAX) exact_score2<D, TIn>(qrow, Kp + (size_t)kM_ * D, Kp + (size_t)km_ * D, a.scale, xM_, xm_);
+    else xM_ = exact_score<D, TIn>(qrow, Kp + (size_t)kM_ * D, a.scale);
+    if (dM) {
+      Sh[stored_at(kM_)] = xM_;
+      xext_add(yM, xM_, kM_, true);
     }
-  } else {
-    // every stored score within 2 Erow of the approximate extremum is recomputed and patched
-    const bool scanM = qvalid, scanm = CAL == MINMAX && qvalid;
-    for (int kt = w; kt < ntiles; kt += FWD_NW) {
-      float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
-      float x[16];
+    if (dm) {
+      Sh[stored_at(km_)] = xm_;
+      xext_add(ym, xm_, km_, false);
+    }
+  };
+  if (oneM || onem) exact_pair(oneM, loc.ax, onem, loc.an);
+  if (CAL == MINMAX && __any(twoM || twom)) {
+    if (twoM || twom) exact_pair(twoM, loc.ax2, twom, loc.an2);
+  }
+  if (__any(scanM || scanm)) {
+    constexpr int TB = 4;  // tiles per batch of loads
+    for (int kt0 = w; kt0 < ntiles; kt0 += TB * FWD_NW) {
+      uint32_t cand[TB];  // per tile: bit v for a max candidate, bit 16 + v for a min candidate
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x[v] = St[v * 64];
-      for (int v = 0; v < 16; ++v) {
-        const int key = kt * BN + crow(v, g);
-        const bool ok = key < T && (!a.causal || key <= qi);
-        const bool cM = scanM && ok && x[v] >= thrM, cm = scanm && ok && x[v] <= thrm;
-        if (cM || cm) {
+      for (int i = 0; i < TB; ++i) {
+        const int kt = kt0 + i * FWD_NW;
+        cand[i] = 0u;
+        if ((scanM || scanm) && kt < ntiles) {
+          const float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+          float x[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x[v] = St[v * 64];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kt * BN + crow(v, g);
+            const bool ok = key < T && (!a.causal || key <= qi);
+            cand[i] |= (scanM && ok && x[v] >= thrM) ? 1u << v : 0u;
+            cand[i] |= (scanm && ok && x[v] <= thrm) ? 1u << (16 + v) : 0u;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        const int kt = kt0 + i * FWD_NW;
+        uint32_t bits = cand[i] | (cand[i] >> 16);
+        while (bits) {
+          const int v = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const int key = kt * BN + crow(v, g);
           const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)key * D, a.scale);
-          St[v * 64] = xe;
-          if (cM) {
-            if (xe > yM.v) { yM.v = xe; yM.k = key; yM.n = 1; } else if (xe == yM.v) { ++yM.n; }
-          }
-          if (cm) {
-            if (xe < ym.v) { ym.v = xe; ym.k = key; ym.n = 1; } else if (xe == ym.v) { ++ym.n; }
-          }
+          Sh[tile_index(qt, kt, nt, a.causal) * 1024 + v * 64 + l] = xe;
+          if ((cand[i] >> v) & 1u) xext_add(yM, xe, key, true);
+          if ((cand[i] >> (16 + v)) & 1u) xext_add(ym, xe, key, false);
         }
       }
     }
