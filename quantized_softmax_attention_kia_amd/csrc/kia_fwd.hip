@@ -454,12 +454,17 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       if (__any(risky != 0u)) {
         // rare: the exact scores replace the stored ones (this lane stored them) for every later
         // pass, and the half tile is weighed again on them
-        for (int j = 0; j < 8; ++j) {
-          if ((risky >> j) & 1u)
-            Sw[(8 * b + j) * 64] = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
-        }
+        uint32_t bits = risky;
+        while (__any(bits != 0u)) {
+          const int j = bits ? __builtin_ctz(bits) : 0;
+          if (bits) {
+            const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
+            Sw[(8 * b + j) * 64] = xe;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s[8 * b + j] = Sw[(8 * b + j) * 64];
+            for (int jj = 0; jj < 8; ++jj) s[8 * b + jj] = jj == j ? xe : s[8 * b + jj];
+            bits &= bits - 1u;
+          }
+        }
         if (full) weigh(std::false_type{}, std::false_type{});
         else weigh(std::true_type{}, std::false_type{});
       }
