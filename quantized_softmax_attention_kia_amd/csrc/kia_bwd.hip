@@ -321,31 +321,20 @@ struct KvSmem {
   __bf16 dOT[NS * D * TP];  // dO^T of the query tile
 };
 
-// Operands of one query tile, held in registers while the previous tile computes: the Q and
-// dO rows (staged through LDS for the workgroup) and the wave's P and dS values.
-template <int D, typename TIn>
-struct KvPrefetch {
-  PairRegs<D, TIn> q, dO;
-  f4v p[4], ds[4];
-};
-
 // Lane (c, g) loads, for its key c of the wave's key tile, the stored P and dS of the queries
 // crow(v, g) (v = 0..15): in a stored tile they sit at v_c * 64 + 32 g_c + (query) with
 // c = crow(v_c, g_c), so they form four aligned runs of four floats.
-template <int D, typename TIn>
-__device__ __forceinline__ void kv_load(KvPrefetch<D, TIn>& pf, const BwdArgs& a, const TIn* Qp, const TIn* dOp,
-                                        size_t tbase, int qt, int ktw, bool act) {
+struct KvTile {
+  f4v p[4], ds[4];
+};
+__device__ __forceinline__ void kv_load(KvTile& t, const BwdArgs& a, size_t tbase, int qt, int ktw) {
   const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-  pf.q.load(Qp, qt * BN, a.T);
-  pf.dO.load(dOp, qt * BN, a.T);
-  if (act) {
-    const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024 +
-                      (4 * (c >> 3) + (c & 3)) * 64 + 32 * ((c >> 2) & 1) + 4 * g;
+  const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024 +
+                    (4 * (c >> 3) + (c & 3)) * 64 + 32 * ((c >> 2) & 1) + 4 * g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pf.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
-      pf.ds[q] = *reinterpret_cast<const f4v*>(a.dst + to + 8 * q);
-    }
+  for (int q = 0; q < 4; ++q) {
+    t.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
+    t.ds[q] = *reinterpret_cast<const f4v*>(a.dst + to + 8 * q);
   }
 }
 
@@ -370,39 +359,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = zero16(); dv[nb] = zero16(); }
 
   const int qt_first = a.causal ? kb0 / BN : 0;
-  KvPrefetch<D, TIn> pf;
-  if (qt_first < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt_first, ktw, active(qt_first));
-  for (int qt = qt_first; qt < nt; ++qt) {
-    const bool act = active(qt);
+  // the workgroup's Q and dO rows of the next query tile, staged through LDS as bf16 slices;
+  // the wave's P and dS of a tile, in two buffers taken in turn
+  PairRegs<D, TIn> qr, dr;
+  KvTile t0, t1;
+  auto stage = [&](int qt) {
     __syncthreads();
-    pf.q.template store_t<NS>(sm.QT);
-    pf.dO.template store_t<NS>(sm.dOT);
+    qr.template store_t<NS>(sm.QT);
+    dr.template store_t<NS>(sm.dOT);
     __syncthreads();
+    if (qt + 1 < nt) {
+      qr.load(Qp, (qt + 1) * BN, T);
+      dr.load(dOp, (qt + 1) * BN, T);
+    }
+  };
+  auto contract = [&](const KvTile& t) {
     // element (query crow(v, g), key c) of P and dS; zero where masked
     float p[16], ds[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { p[4 * q + e] = pf.p[q][e]; ds[4 * q + e] = pf.ds[q][e]; }
-    if (qt + 1 < nt) kv_load<D, TIn>(pf, a, Qp, dOp, tbase, qt + 1, ktw, active(qt + 1));
-    if (!act) continue;
+      for (int e = 0; e < 4; ++e) { p[4 * q + e] = t.p[q][e]; ds[4 * q + e] = t.ds[q][e]; }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      // the half tile's LDS operands are read first, so that their latency overlaps the splits
-      Split8 bo[D / 32], bq[D / 32];
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) {
-        bo[nb] = load_bt<D, NS>(sm.dOT, b, 32 * nb + c);
-        bq[nb] = load_bt<D, NS>(sm.QT, b, 32 * nb + c);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the splits
       const Split8 ps = split8(p + 8 * b), dss = split8(ds + 8 * b);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
-        dv[nb] = mfma_split<NS>(ps, bo[nb], dv[nb]);
-        dk[nb] = mfma_split<NS>(dss, bq[nb], dk[nb]);
+        dv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), dv[nb]);
+        dk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), dk[nb]);
       }
     }
+  };
+  if (qt_first < nt) {
+    qr.load(Qp, qt_first * BN, T);
+    dr.load(dOp, qt_first * BN, T);
+    if (active(qt_first)) kv_load(t0, a, tbase, qt_first, ktw);
+  }
+  for (int qt = qt_first; qt < nt; qt += 2) {
+    stage(qt);
+    if (qt + 1 < nt && active(qt + 1)) kv_load(t1, a, tbase, qt + 1, ktw);
+    if (active(qt)) contract(t0);
+    if (qt + 1 >= nt) break;
+    stage(qt + 1);
+    if (qt + 2 < nt && active(qt + 2)) kv_load(t0, a, tbase, qt + 2, ktw);
+    if (active(qt + 1)) contract(t1);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {

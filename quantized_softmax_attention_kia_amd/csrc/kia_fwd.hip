@@ -214,16 +214,13 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   Lane3 ex{-INFINITY, -INFINITY, -INFINITY, INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4,
            INT_MAX - 4, INT_MAX - 4};
   float amx = 0.f;  // largest sum of |q_h| |k_h| over the row's visible keys
-  RowOp<D, TIn> kr;
-  if (w < ntiles) kr.load(Kp, w * BN + c, T);
-  for (int kt = w; kt < ntiles; kt += FWD_NW) {
+  // one key tile: its scores from the K operand kr (slice products), stored, and tracked
+  auto score_tile = [&](int kt, const RowOp<D, TIn>& kr) {
     const int k0 = kt * BN;
-    const RowOp<D, TIn> cur = kr;
-    if (kt + FWD_NW < ntiles) kr.load(Kp, k0 + FWD_NW * BN + c, T);  // next tile in flight
     f16v acc = zero16(), asm_ = zero16(), aacc = zero16();  // h h', the smaller products, |h| |h'|
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
-      const Split8 ks = cur.split(kb);
+      const Split8 ks = kr.split(kb);
       if (NS == 3) {
         asm_ = mfma_bf16(ks.l, qs[kb].h, asm_);
         asm_ = mfma_bf16(ks.m, qs[kb].m, asm_);
@@ -251,6 +248,16 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     };
     if (full_tile(kt)) epilogue(std::false_type{});
     else epilogue(std::true_type{});
+  };
+  // two operand buffers in turn: the next tile's K is in flight while this one computes
+  RowOp<D, TIn> kr0, kr1;
+  if (w < ntiles) kr0.load(Kp, w * BN + c, T);
+  for (int kt = w; kt < ntiles; kt += 2 * FWD_NW) {
+    if (kt + FWD_NW < ntiles) kr1.load(Kp, (kt + FWD_NW) * BN + c, T);
+    score_tile(kt, kr0);
+    if (kt + FWD_NW >= ntiles) break;
+    if (kt + 2 * FWD_NW < ntiles) kr0.load(Kp, (kt + 2 * FWD_NW) * BN + c, T);
+    score_tile(kt + FWD_NW, kr1);
   }
   ex.ax += 4 * g;
   ex.ax2 += 4 * g;
