@@ -11,8 +11,9 @@
  * Attention" (Zhu, Hu, Kozlowski), §3 "Objects and calibration" and
  * "Reconstruction", App. A "Edge cases and conventions", App. B (normalization
  * Jacobian, LERP own-score slope, full calibration gradient (MinMax) = eq. (1),
- * detach (legacy), Weight-STE, Prob-STE, FWM), App. C.2 (iii) (strict hard
- * forward).  Steps follow the pages' order and notation: calibration ->
+ * detach (legacy) and its P1 projection, Weight-STE, Prob-STE, FWM), App. C.2
+ * (iii) (strict hard forward), §5.1 and the single-channel ablation paragraph of
+ * App. I (max_only / min_only keep one extremum's calibration term).  Steps follow the pages' order and notation: calibration ->
  * interval index r_j and local position t_j -> LERP / Nearest weights ->
  * normalization -> P V; backward: gamma (normalization Jacobian) -> Delta
  * (secant slope) -> calibration terms through the row extrema -> dS -> dQ, dK, dV.
@@ -32,6 +33,11 @@
  *  - interval index r = clamp(floor(u), 0, K-1); Nearest rounds t = 1/2 up.
  *  - FWM: z = -tau is inside the window; only z < -tau is tail (weight 0).
  *  - tied extrema: the extremum's gradient is split evenly among tied keys.
+ *  - max_only / min_only: the full score gradient with the other extremum's term
+ *    dropped (g_self + g_M, g_self + g_m); FWM has no minimum term, so its
+ *    max_only is the full gradient and its min_only the detached one.
+ *  - P1: the detached score gradient minus its mean over the row's visible
+ *    (causal) keys, tail keys included, so every row sums to zero.
  *
  * Flip list: a test may ask the oracle to take, at named (row, key) positions,
  * the other valid decision at a bin boundary (the other interval at an integer
@@ -60,7 +66,7 @@
 enum { KO_MINMAX = 0, KO_FWM = 1 };
 enum { KO_LERP = 0, KO_NEAREST = 1 };
 enum { KO_WEIGHT_STE = 0, KO_PROB_STE = 1 };
-enum { KO_FULL = 0, KO_DETACHED = 1 };
+enum { KO_FULL = 0, KO_DETACHED = 1, KO_MAX_ONLY = 2, KO_MIN_ONLY = 3, KO_P1 = 4 };
 
 enum { FLIP_INTERVAL = 1, FLIP_NEAREST = 2, FLIP_TAIL = 4 };
 
@@ -83,7 +89,9 @@ enum {
   MUT_DV_WITH_PL = 15,      /* Nearest dV uses P^L instead of the forward P^N */
   MUT_FWM_GRID_SHIFT = 16,  /* FWM grid b_r = -tau + (r+1)h */
   MUT_X_INDEX = 17,         /* X uses r instead of r+1 in its second term */
-  MUT_DETACH_KEEPS_M = 18   /* detached mode keeps the M channel */
+  MUT_DETACH_KEEPS_M = 18,  /* detached mode keeps the M channel */
+  MUT_ONLY_SWAPPED = 19,    /* max_only keeps the m channel, min_only the M channel */
+  MUT_P1_SKIP_TAIL = 20     /* P1 shifts only the keys inside the FWM window */
 };
 
 typedef struct {
@@ -273,9 +281,14 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
     }
     for (int j = 0; j < n; ++j) if (tail[j]) dS[j] = 0.0;
 
-    /* --- calibration gradient through the row extrema (App. B) --- */
-    int full = (cfg->grad == KO_FULL);
-    if (full || mut == MUT_DETACH_KEEPS_M) {
+    /* --- calibration gradient through the row extrema (App. B); max_only / min_only keep
+       one of its two channels --- */
+    int keepM = cfg->grad == KO_FULL || cfg->grad == KO_MAX_ONLY || (cfg->grad == KO_DETACHED && mut == MUT_DETACH_KEEPS_M);
+    int keepm = cfg->grad == KO_FULL || cfg->grad == KO_MIN_ONLY;
+    if (mut == MUT_ONLY_SWAPPED && (cfg->grad == KO_MAX_ONLY || cfg->grad == KO_MIN_ONLY)) {
+      int tmp = keepM; keepM = keepm; keepm = tmp;
+    }
+    if (keepM || keepm) {
       if (cfg->calib == KO_MINMAX) {
         for (int j = 0; j < n; ++j) {
           double rho = (r[j] + t[j]) / K;
@@ -294,11 +307,12 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
           a += gam[j] * dM;
           b += gam[j] * dm;
         }
-        if (!full) b = 0.0;   /* only reachable under MUT_DETACH_KEEPS_M */
       } else {
         /* FWM: in-window keys have dw/dM = -Delta, tail keys contribute nothing */
         for (int j = 0; j < n; ++j) if (!tail[j]) a += -gam[j] * Delta[j];
       }
+      if (!keepM) a = 0.0;
+      if (!keepm) b = 0.0;
       /* the extremum gradient is split evenly among tied keys */
       for (int j = 0; j < n; ++j) {
         if (s[j] == M) {
@@ -310,6 +324,15 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
           else dS[j] += b / nC;
         }
       }
+    }
+    /* --- P1 (App. B "Detach"): the detached row projected onto the zero-sum subspace by
+       subtracting its mean over the row's visible keys --- */
+    if (cfg->grad == KO_P1) {
+      double sum = 0.0;
+      for (int j = 0; j < n; ++j) sum += dS[j];
+      const double mean = sum / n;
+      for (int j = 0; j < n; ++j)
+        if (!(mut == MUT_P1_SKIP_TAIL && tail[j])) dS[j] -= mean;
     }
   }
 

@@ -25,7 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "libkia_oracle.so")
 CALIB = {"minmax": 0, "fwm": 1}
 RECON = {"lerp": 0, "nearest": 1}
 STE = {"weight": 0, "prob": 1}
-GRAD = {"full": 0, "detached": 1}
+GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 
 FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL = 1, 2, 4
 MUTATIONS = {
@@ -33,7 +33,7 @@ MUTATIONS = {
     "wste_uses_lerp": 5, "dk_with_do": 6, "tail_inclusive": 7, "no_tie_split": 8,
     "nearest_fwd_lerp": 9, "extrema_all_keys": 10, "dq_no_scale": 11, "no_hsafe": 12,
     "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
-    "x_index": 17, "detach_keeps_m": 18,
+    "x_index": 17, "detach_keeps_m": 18, "only_swapped": 19, "p1_skip_tail": 20,
 }
 ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
 ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")

@@ -11,6 +11,11 @@ among tied entries, which is the tie convention the pages state.
 Readings shared with the oracle (each a reading of a silent point, not a
 formula copied from it): the clamp on t passes the gradient at its bounds;
 degenerate MinMax rows use the constant width 1; Nearest rounds t = 1/2 up.
+
+Gradient modes: "detached" detaches both row extrema; "max_only" / "min_only"
+detach only the other extremum (the single-channel ablation of App. I); "p1"
+is the detached gradient with a hook on the scores that projects each row's
+gradient onto the zero-sum subspace over its visible keys (App. B "Detach").
 """
 import torch
 
@@ -28,8 +33,12 @@ def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0):
     pos_inf = torch.tensor(float("inf"), dtype=dt)
     M = torch.where(mask, s, -pos_inf).amax(dim=1, keepdim=True)
     m = torch.where(mask, s, pos_inf).amin(dim=1, keepdim=True)
-    if grad == "detached":
+    if grad in ("detached", "p1"):
         M, m = M.detach(), m.detach()
+    elif grad == "max_only":
+        m = m.detach()
+    elif grad == "min_only":
+        M = M.detach()
     rr = torch.arange(K + 1, dtype=dt)
     R = s.shape[0]
     if calib == "minmax":
@@ -75,7 +84,10 @@ def row_grad(s, g, calib, recon, ste, grad, K, tau=8.0):
     mask = torch.ones_like(s, dtype=torch.bool)
     P = row_probs(s, mask, calib, recon, ste, grad, K, tau)
     (P * g).sum().backward()
-    return P.detach()[0], s.grad[0]
+    dS = s.grad[0]
+    if grad == "p1":
+        dS = dS - dS.mean()
+    return P.detach()[0], dS
 
 
 def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, scale=None):
@@ -90,6 +102,9 @@ def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, sc
     mask = torch.ones(T, T, dtype=torch.bool)
     if causal:
         mask = torch.tril(mask)
+    if grad == "p1":
+        cnt = mask.sum(dim=1, keepdim=True).to(S.dtype)
+        S.register_hook(lambda gS: torch.where(mask, gS - torch.where(mask, gS, 0.0).sum(1, keepdim=True) / cnt, gS))
     P = row_probs(S, mask, calib, recon, ste, grad, K, tau)
     O = P @ V
     (O * dO).sum().backward()

@@ -6,8 +6,10 @@ and raises AssertionError when the oracle disagrees with:
     derivation route for every backward term, including ties);
   * central finite differences of the oracle's own double forward (LERP, and
     dV for Nearest);
-  * the zero-sum identity of the full calibration gradient and its violation
-    under detached extrema (App. B, §5.1);
+  * the zero-sum identity of the full calibration gradient and of the P1
+    projection, and its violation under detached extrema (App. B, §5.1);
+  * the channel decomposition g_full = g_self + g_M + g_m of the single-channel
+    ablations (App. I);
   * the two-key softmax identity (App. B, Verification);
   * the interpolation bounds of a chord of exp and the K -> infinity limit;
   * brute-force nearest grid centre in score coordinates;
@@ -31,6 +33,15 @@ from oracle import oracle as ORC
 
 VARIANTS = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest")
             for s in ("weight", "prob") for g in ("full", "detached")]
+# the range_grad ablations (App. I single-channel modes, App. B P1 projection)
+VARIANTS += [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
+             ("nearest", "prob")) for g in ("max_only", "min_only", "p1")]
+
+
+def zero_sum_mode(cfg):
+    """Modes whose row score gradients sum to zero: full, P1, and FWM's max_only (FWM has no
+    minimum channel, so max_only is its full gradient)."""
+    return cfg.grad in ("full", "p1") or (cfg.calib == "fwm" and cfg.grad == "max_only")
 
 
 def cfg_of(calib, recon, ste, grad, K=4, tau=8.0, mutation=None):
@@ -125,18 +136,36 @@ def pin_autograd_head(cfg):
 
 
 def pin_zero_sum(cfg):
-    """Full gradient: every row's score gradient sums to zero; detached: it does not."""
+    """Full gradient and P1: every row's score gradient sums to zero; detached and the
+    single-channel modes (other than FWM's max_only): it does not."""
     nonzero = 0
     rows = _random_rows(23, cfg)
     for s, g in rows:
         res = ORC.row(cfg, s, g)
         tot, mag = abs(res["dS"].sum()), np.abs(res["dS"]).sum()
-        if cfg.grad == "full":
+        if zero_sum_mode(cfg):
             assert tot <= 1e-12 * mag + 1e-300, f"zero-sum violated: {tot} vs {mag}"
         elif tot > 1e-6 * mag:
             nonzero += 1
-    if cfg.grad == "detached":
-        assert nonzero >= len(rows) // 2, "detached gradient unexpectedly zero-sum"
+    if not zero_sum_mode(cfg):
+        assert nonzero >= len(rows) // 2, f"{cfg.grad} gradient unexpectedly zero-sum"
+
+
+def pin_channel_additivity(cfg):
+    """App. I: g_full = g_self + g_M + g_m, g_max_only = g_self + g_M, g_min_only = g_self + g_m,
+    so max_only + min_only - detached = full; FWM has no g_m: max_only = full, min_only = detached."""
+    if cfg.grad not in ("max_only", "min_only"):
+        return
+    other = {"max_only": "min_only", "min_only": "max_only"}[cfg.grad]
+    for s, g in _random_rows(29, cfg, count=12):
+        got = ORC.row(cfg, s, g)["dS"]
+        oth = ORC.row(dataclasses.replace(cfg, grad=other), s, g)["dS"]
+        det = ORC.row(dataclasses.replace(cfg, grad="detached", mutation=None), s, g)["dS"]
+        full = ORC.row(dataclasses.replace(cfg, grad="full", mutation=None), s, g)["dS"]
+        if cfg.calib == "minmax":
+            _close(got + oth - det, full, 1e-12, 1e-14, "max_only + min_only - detached vs full")
+        else:
+            _close(got, full if cfg.grad == "max_only" else det, 1e-14, 0.0, f"FWM {cfg.grad}")
 
 
 def pin_two_key(cfg):
@@ -244,10 +273,10 @@ def pin_shift_invariance(cfg):
     _close(b["O"], a["O"], 1e-10, 1e-12, "O under key shift")
     _close(b["dV"], a["dV"], 1e-10, 1e-12, "dV under key shift")
     _close(b["dK"], a["dK"], 1e-8, 1e-11, "dK under key shift")
-    if cfg.grad == "full":
-        _close(b["dQ"], a["dQ"], 1e-8, 1e-11, "dQ under key shift (full)")
+    if zero_sum_mode(cfg):
+        _close(b["dQ"], a["dQ"], 1e-8, 1e-11, "dQ under key shift (zero-sum rows)")
     else:
-        assert np.max(np.abs(b["dQ"] - a["dQ"])) > 1e-8, "detached dQ unexpectedly shift-invariant"
+        assert np.max(np.abs(b["dQ"] - a["dQ"])) > 1e-8, f"{cfg.grad} dQ unexpectedly shift-invariant"
 
 
 def pin_degenerate_and_causal_edges(cfg):
@@ -260,7 +289,7 @@ def pin_degenerate_and_causal_edges(cfg):
         _close(res["P"], np.full(n, 1.0 / n), 1e-15, 0.0, "degenerate P")
         if cfg.calib == "minmax":
             assert np.all(np.abs(res["dS"]) <= 1e-15), "degenerate MinMax row has a gradient"
-        assert abs(res["dS"].sum()) <= 1e-15 or cfg.grad == "detached", "degenerate row not zero-sum"
+        assert abs(res["dS"].sum()) <= 1e-15 or not zero_sum_mode(cfg), "degenerate row not zero-sum"
     Q, K, V, dO = _head_inputs(19, 9, 5, 2.0)
     r = ORC.head(cfg, Q, K, V, dO, nthreads=1)
     assert np.array_equal(r["O"][0], V[0]), "causal row 0 must return V_0"
@@ -335,6 +364,7 @@ def pin_golden(cfg):
             assert res[key] == int(case[key]), f"{name}: {key}"
 
 
-PINS = [pin_golden, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_two_key,
+PINS = [pin_golden, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
+        pin_two_key,
         pin_reconstruction_bounds, pin_nearest_brute_force, pin_finite_differences, pin_shift_invariance,
         pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit]
