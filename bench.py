@@ -64,8 +64,9 @@ def read_traffic(kernel: str):
     return None
 
 
-def cpu_baseline(workload, q, k, v, do, budget_s: float):
+def cpu_baseline(workload, q, k, v, do, budget_s: float, grad: str = "full"):
     """The oracle, as it stands, on a bounded sample: heads in order, every variant, until the budget."""
+    import dataclasses
     from oracle import oracle as ORC
     threads = ORC.default_threads()
     B, H, T, D = q.shape
@@ -75,7 +76,8 @@ def cpu_baseline(workload, q, k, v, do, budget_s: float):
     for b in range(B):
         for h in range(H):
             for var in workload.variants:
-                ORC.head(ORC.OracleConfig.of(var), q[b, h], k[b, h], v[b, h], do[b, h], nthreads=threads)
+                cfg = dataclasses.replace(ORC.OracleConfig.of(var), grad=grad)
+                ORC.head(cfg, q[b, h], k[b, h], v[b, h], do[b, h], nthreads=threads)
                 flops += 12.0 * D * pairs
             done_heads += 1
             if time.perf_counter() - t0 >= budget_s:
@@ -97,6 +99,8 @@ def main() -> int:
     ap.add_argument("--workload", default="gpt2")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grad", default="full", choices=["full", "detached", "max_only", "min_only", "p1"],
+                    help="gradient mode of every variant (the headline is full)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
                          "byte counters)")
@@ -123,10 +127,13 @@ def main() -> int:
     runs = []
     for var in wl.variants:
         cfg = kb.Config.of(var)
+        if args.grad != cfg.grad:
+            import dataclasses
+            cfg = dataclasses.replace(cfg, grad=args.grad)
         p = kb.make_params(cfg, qt.shape, tdt)
         rr, ws = kb.kia_workspace_size(p)
         runs.append(dict(
-            name=var.name, p=p,
+            name=var.name if args.grad == "full" else f"{var.name}:{args.grad}", p=p,
             o=torch.empty(qt.shape, device=dev, dtype=torch.float32),
             rowrec=torch.empty(max(rr, 1), device=dev, dtype=torch.uint8),
             dq=torch.empty(qt.shape, device=dev, dtype=torch.float32),
@@ -198,7 +205,7 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    traffic = read_traffic(kernel_key)
+    traffic = read_traffic(kernel_key) if args.grad == "full" else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "
@@ -207,7 +214,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample ...")
-        cpu = cpu_baseline(wl, q, k, v, do, args.cpu_seconds)
+        cpu = cpu_baseline(wl, q, k, v, do, args.cpu_seconds, args.grad)
         log(f"cpu baseline {cpu}")
 
     line = {
@@ -217,7 +224,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: B={wl.B} H={wl.H} T={wl.T} D={wl.D} causal {wl.dtype} N(0,1) seed {wl.seed}; "
-                        f"one step = fwd+bwd (full calibration gradients) of "
+                        f"one step = fwd+bwd ({args.grad} calibration gradients) of "
                         + ", ".join(r["name"] for r in runs),
             "B": wl.B, "H": wl.H, "T": wl.T, "D": wl.D, "causal": True,
             "alg_flops_per_step": step_flops,

@@ -21,7 +21,11 @@
  * Delta_j = (e^{b_{r+1}} - e^{b_r})/h, and, in full mode, the calibration
  * gradient through the row extrema (split evenly among tied keys) that makes
  * every row's score gradient sum to zero.  Detached mode drops the extremum
- * terms (the legacy ablation of §5.1).
+ * terms (the legacy ablation of §5.1).  The range_grad ablations of §5.1 and
+ * App. I: max_only / min_only keep only the maximum's / the minimum's term
+ * (FWM has no minimum term: its max_only is full, its min_only detached); P1
+ * (App. B "Detach") subtracts from each row of the detached score gradient its
+ * mean over the row's visible keys.
  *
  * Conventions shared by every entry point:
  *  - Tensors Q, K, V, dO are [B, H, T, D], C-contiguous, in device memory, of
@@ -59,8 +63,14 @@ typedef enum { KIA_CALIB_MINMAX = 0, KIA_CALIB_FWM = 1 } kia_calib_t;
 typedef enum { KIA_RECON_LERP = 0, KIA_RECON_NEAREST = 1 } kia_recon_t;
 /* surrogate placement; ignored under LERP (both give the LERP Jacobian) */
 typedef enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 } kia_ste_t;
-/* full calibration gradient, or the detached-extrema ablation */
-typedef enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACHED = 1 } kia_grad_t;
+/* full calibration gradient, or one of the range_grad ablations */
+typedef enum {
+  KIA_GRAD_FULL = 0,
+  KIA_GRAD_DETACHED = 1,
+  KIA_GRAD_MAX_ONLY = 2, /* only the row maximum's calibration term */
+  KIA_GRAD_MIN_ONLY = 3, /* only the row minimum's calibration term */
+  KIA_GRAD_P1 = 4        /* detached, each row projected onto zero sum over its visible keys */
+} kia_grad_t;
 typedef enum { KIA_F32 = 0, KIA_BF16 = 1 } kia_dtype_t;
 
 typedef struct {
@@ -95,7 +105,9 @@ typedef struct {
  *  bwd_ws_bytes: scratch for kia_backward: two arrays of float tiles numbered
  *    like S, P[B*H][tiles][1024] (the forward's normalized weights: P^L for LERP,
  *    the hard P^N for Nearest) and dS[B*H][tiles][1024] (the unscaled score
- *    gradients, extremum terms included).  Within a tile of S, P or dS, element
+ *    gradients, extremum terms included; under P1 the detached ones, before the
+ *    projection), then float rowmean[N] (P1: each row's mean of dS over its
+ *    visible keys).  Within a tile of S, P or dS, element
  *    (query row a, key column b of the tile) sits at float offset v*64 + a + 32*g,
  *    where b = 8*(v/4) + 4*g + v%4.
  * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
@@ -109,7 +121,7 @@ kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, siz
  *  o:       device float32 [B,H,T,D], written.
  *  rowrec:  device, rowrec_bytes (kia_workspace_size), written; it must be
  *           passed unchanged to kia_backward with identical params.
- * Forwards under KIA_GRAD_FULL and KIA_GRAD_DETACHED are bit-identical.
+ * Forwards under every kia_grad_t are bit-identical.
  */
 kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
                          float* o, void* rowrec, void* stream);

@@ -39,7 +39,7 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   if (p->calib != KIA_CALIB_MINMAX && p->calib != KIA_CALIB_FWM) { set_err("bad calib %d", p->calib); return KIA_ERR_INVALID_ARG; }
   if (p->recon != KIA_RECON_LERP && p->recon != KIA_RECON_NEAREST) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
   if (p->ste != KIA_STE_WEIGHT && p->ste != KIA_STE_PROB) { set_err("bad ste %d", p->ste); return KIA_ERR_INVALID_ARG; }
-  if (p->grad != KIA_GRAD_FULL && p->grad != KIA_GRAD_DETACHED) { set_err("bad grad %d", p->grad); return KIA_ERR_INVALID_ARG; }
+  if (p->grad < KIA_GRAD_FULL || p->grad > KIA_GRAD_P1) { set_err("bad grad %d", p->grad); return KIA_ERR_INVALID_ARG; }
   if (p->dtype != KIA_F32 && p->dtype != KIA_BF16) { set_err("bad dtype %d", p->dtype); return KIA_ERR_INVALID_ARG; }
   if (!std::isfinite(p->scale) || p->scale < 0.f) { set_err("scale must be finite and >= 0"); return KIA_ERR_INVALID_ARG; }
   if (p->calib == KIA_CALIB_FWM && !(std::isfinite(p->tau) && p->tau > 0.f)) {
@@ -60,7 +60,9 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   pr->scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
   pr->calib = p->calib;
   pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
-  pr->full = p->grad == KIA_GRAD_FULL;
+  pr->gk = p->grad == KIA_GRAD_DETACHED ? kia::GK_DETACHED : (p->grad == KIA_GRAD_P1 ? kia::GK_P1 : kia::GK_SUMS);
+  pr->keepM = p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MAX_ONLY;
+  pr->keepm = (p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MIN_ONLY) && p->calib == KIA_CALIB_MINMAX;
   pr->bf16 = p->dtype == KIA_BF16;
   return KIA_OK;
 }
@@ -70,7 +72,7 @@ struct Layout {
   size_t rowrec_bytes;
   int nt;
   size_t tiles_per_head;
-  size_t ws_off[2];
+  size_t ws_off[3];
   size_t ws_bytes;
 };
 
@@ -92,6 +94,8 @@ Layout layout(const kia::Problem& pr) {
   o += tile_bytes;
   L.ws_off[1] = o;                       // key-major dS tiles
   o += tile_bytes;
+  L.ws_off[2] = o;                       // per-row mean of the detached dS (P1)
+  o += round_up(N * 4);
   L.ws_bytes = o;
   return L;
 }
@@ -172,8 +176,10 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   char* ws = static_cast<char*>(workspace);
   a.pt = reinterpret_cast<float*>(ws + L.ws_off[0]);
   a.dst = reinterpret_cast<float*>(ws + L.ws_off[1]);
+  a.rowmean = reinterpret_cast<float*>(ws + L.ws_off[2]);
   a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale;
+  a.keepM = pr.keepM; a.keepm = pr.keepm; a.p1 = pr.gk == kia::GK_P1;
   return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);
 }
 

@@ -58,7 +58,7 @@ template <int D, int NS>
 struct DqSmem {
   __align__(16) __bf16 KT[NS * D * TP];         // K^T of the key tile, bf16 slices (dQ += dS K)
   __align__(16) __bf16 VN[NS * BN * np<D>()];   // V rows of the key tile, bf16 slices (g = V dO^T)
-  float alpha[DQ_BM], beta[DQ_BM];
+  float alpha[DQ_BM], beta[DQ_BM], mean[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
   // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 3) floats
 };
@@ -68,9 +68,13 @@ size_t dq_smem_bytes(int K) {
   return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * DQ_BM * (K + 3);
 }
 
+// GK: GK_SUMS (full, max_only, min_only: the calibration sums, with the extremum terms that
+// a.keepM / a.keepm select), GK_DETACHED, or GK_P1 (detached; each row's dS mean over its visible
+// keys is recorded for the dkdv kernel and taken out of dQ through the sum of the visible K rows).
 // At D = 64 the register budget is held to two waves per SIMD.
-template <int D, int CAL, int MODE, bool FULL, typename TIn>
+template <int D, int CAL, int MODE, int GK, typename TIn>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dq_kernel(BwdArgs a) {
+  constexpr bool SUMS = GK == GK_SUMS, P1 = GK == GK_P1;
   constexpr int NS = nslices<TIn>();
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
@@ -140,13 +144,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   // extra tied extrema (beyond the first index) need a second sweep to find them
   // (a MinMax row with M == m has every grid value 1: both extremum terms vanish; FWM records m = M)
   const bool flat = CAL == MINMAX && M == m;
-  const bool rowties = FULL && qvalid && !flat && (nA > 1 || (CAL == MINMAX && nC > 1));
+  const bool rowties = SUMS && qvalid && !flat && ((a.keepM && nA > 1) || (CAL == MINMAX && a.keepm && nC > 1));
   const bool blockties = __syncthreads_or(rowties);
 
   double acc_a = 0.0, sds = 0.0;  // calibration sums of the row (terms of both signs)
-  f16v dq[D / 32];
+  f16v dq[D / 32], pk[P1 ? D / 32 : 1];  // pk: P1 only, the sum of the visible K rows
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) dq[nb] = zero16();
+  if (P1) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) pk[nb] = zero16();
+  }
 
   PairRegs<D, TIn, NT> kr;  // K rows of the next key tile, staged as the workgroup's K^T slices
   RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
@@ -206,8 +214,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
         Pw[v * 64 + l] = ((MODE == LERP) ? wt.wL : wt.wN) * invWf;
         dSw[v * 64 + l] = dS;
-        if (FULL) {
-          hs += dS;
+        if (SUMS || P1) hs += dS;
+        if (SUMS) {
           if (CAL == MINMAX) {
             const float rf = (float)d.r;
             // K * dw/dM = (r - K) w + t e^{b_{r+1}} - kappa (r + t) Delta
@@ -216,44 +224,60 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           }
         }
       }
-      if (FULL) {
-        sds += (double)hs;
-        if (CAL == MINMAX) acc_a += (double)ha;
-      }
+      if (SUMS || P1) sds += (double)hs;
+      if (SUMS && CAL == MINMAX) acc_a += (double)ha;
       const Split8 dss = split8(ds);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.KT, b, 32 * nb + c), dq[nb]);
+      if (P1) {
+        // the sum of the row's visible K rows, for the mean's share of dQ: a 0 / 1 mask (exact in
+        // bf16) times the K^T slices
+        uint32_t mk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mk[e] = (crow(8 * b + 2 * e, 0) <= lim ? 0x3f80u : 0u) | (crow(8 * b + 2 * e + 1, 0) <= lim ? 0x3f800000u : 0u);
+        Split8 ms;
+        __builtin_memcpy(&ms.h, mk, 16);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) pk[nb] = mfma_split<NS, 1>(ms, load_bt<D, NS>(sm.KT, b, 32 * nb + c), pk[nb]);
+      }
     }
   }
 
   // extremum terms of the row: alpha per tied max key, beta per tied min key
   float alpha = 0.f, beta = 0.f;
-  const bool inject = FULL && qvalid && !flat;
-  if (FULL) {
+  const bool inject = SUMS && qvalid && !flat;
+  float mean = 0.f;  // P1: the row's mean of dS over its visible keys
+  if (P1) {
+    sds += __shfl_xor(sds, 32);
+    mean = qvalid ? (float)(sds / (double)(a.causal ? qi + 1 : T)) : 0.f;
+    if (g == 0 && qvalid) a.rowmean[row] = mean;
+  }
+  if (SUMS) {
     acc_a += __shfl_xor(acc_a, 32);
     sds += __shfl_xor(sds, 32);
     if (inject) {
       if (CAL == MINMAX) {
         const double A = acc_a / (double)K;
         const double Bm = -sds - A;
-        alpha = (float)(A / (double)nA);
-        beta = (float)(Bm / (double)nC);
+        alpha = a.keepM ? (float)(A / (double)nA) : 0.f;
+        beta = a.keepm ? (float)(Bm / (double)nC) : 0.f;
       } else {
-        alpha = (float)(-sds / (double)nA);
+        alpha = a.keepM ? (float)(-sds / (double)nA) : 0.f;
       }
     }
     // dS of the first arg-max / arg-min key of the row gains alpha / beta, added by the lane
     // that stored the element (program order makes its own store visible to it)
-    if (inject && g == stored_lane_group(amax % BN)) {
+    if (inject && a.keepM && g == stored_lane_group(amax % BN)) {
       float* e = dSh + tile_index(qtw, amax / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amax % BN);
       *e = *e + alpha;
     }
-    if (CAL == MINMAX && inject && g == stored_lane_group(amin % BN)) {
+    if (CAL == MINMAX && inject && a.keepm && g == stored_lane_group(amin % BN)) {
       float* e = dSh + tile_index(qtw, amin / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amin % BN);
       *e = *e + beta;
     }
   }
-  if (FULL && blockties) {
+  if (SUMS && blockties) {
     // second sweep: tied keys other than the first arg-max / arg-min
     for (int kt = 0; kt < ntiles; ++kt) {
       const int k0 = kt * BN;
@@ -287,6 +311,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   if (g == 0) {
     sm.alpha[rl] = alpha;
     sm.beta[rl] = beta;
+    sm.mean[rl] = mean;
     sm.amax[rl] = qvalid ? amax : 0;
     sm.amin[rl] = qvalid ? amin : 0;
   }
@@ -303,10 +328,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
         float val = dq[nb][v];
-        if (FULL) {
+        if (SUMS) {
           val = fmaf(al, ld1<TIn>(ka + 32 * nb), val);
           if (CAL == MINMAX) val = fmaf(be, ld1<TIn>(kb + 32 * nb), val);
         }
+        if (P1) val = fmaf(-sm.mean[r2], pk[nb][v], val);
         out[32 * nb] = val * a.scale;
       }
     }
@@ -324,10 +350,14 @@ struct KvSmem {
 // Lane (c, g) loads, for its key c of the wave's key tile, the stored P and dS of the queries
 // crow(v, g) (v = 0..15): in a stored tile they sit at v_c * 64 + 32 g_c + (query) with
 // c = crow(v_c, g_c), so they form four aligned runs of four floats.
+// Under P1 the tile also carries the rows' means of the detached dS (queries crow(v, g)).
+template <bool P1>
 struct KvTile {
   f4v p[4], ds[4];
+  float mean[P1 ? 16 : 1];
 };
-__device__ __forceinline__ void kv_load(KvTile& t, const BwdArgs& a, size_t tbase, int qt, int ktw) {
+template <bool P1>
+__device__ __forceinline__ void kv_load(KvTile<P1>& t, const BwdArgs& a, size_t tbase, int head, int qt, int ktw) {
   const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
   const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024 +
                     (4 * (c >> 3) + (c & 3)) * 64 + 32 * ((c >> 2) & 1) + 4 * g;
@@ -336,9 +366,17 @@ __device__ __forceinline__ void kv_load(KvTile& t, const BwdArgs& a, size_t tbas
     t.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
     t.ds[q] = *reinterpret_cast<const f4v*>(a.dst + to + 8 * q);
   }
+  if (P1) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int query = qt * BN + crow(v, g);
+      t.mean[v] = query < a.T ? a.rowmean[(size_t)head * a.T + query] : 0.f;
+    }
+  }
 }
 
-template <int D, typename TIn>
+// P1: subtract each query row's mean of the detached dS from its visible elements.
+template <int D, typename TIn, bool P1>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int NS = nslices<TIn>();
   __shared__ KvSmem<D, NS> sm;
@@ -362,7 +400,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   // the workgroup's Q and dO rows of the next query tile, staged through LDS as bf16 slices;
   // the wave's P and dS of a tile, in two buffers taken in turn
   PairRegs<D, TIn> qr, dr;
-  KvTile t0, t1;
+  KvTile<P1> t0, t1;
   auto stage = [&](int qt) {
     __syncthreads();
     qr.template store_t<NS>(sm.QT);
@@ -373,13 +411,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
       dr.load(dOp, (qt + 1) * BN, T);
     }
   };
-  auto contract = [&](const KvTile& t) {
+  auto contract = [&](const KvTile<P1>& t, int qt) {
     // element (query crow(v, g), key c) of P and dS; zero where masked
     float p[16], ds[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) { p[4 * q + e] = t.p[q][e]; ds[4 * q + e] = t.ds[q][e]; }
+    if (P1) {
+      // the query row's mean of the detached dS comes off every visible element
+      const int key = kw0 + c;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int query = qt * BN + crow(v, g);
+        if (query < T && key < T && (!a.causal || key <= query)) ds[v] -= t.mean[v];
+      }
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const Split8 ps = split8(p + 8 * b), dss = split8(ds + 8 * b);
@@ -393,16 +440,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   if (qt_first < nt) {
     qr.load(Qp, qt_first * BN, T);
     dr.load(dOp, qt_first * BN, T);
-    if (active(qt_first)) kv_load(t0, a, tbase, qt_first, ktw);
+    if (active(qt_first)) kv_load<P1>(t0, a, tbase, head, qt_first, ktw);
   }
   for (int qt = qt_first; qt < nt; qt += 2) {
     stage(qt);
-    if (qt + 1 < nt && active(qt + 1)) kv_load(t1, a, tbase, qt + 1, ktw);
-    if (active(qt)) contract(t0);
+    if (qt + 1 < nt && active(qt + 1)) kv_load<P1>(t1, a, tbase, head, qt + 1, ktw);
+    if (active(qt)) contract(t0, qt);
     if (qt + 1 >= nt) break;
     stage(qt + 1);
-    if (qt + 2 < nt && active(qt + 2)) kv_load(t0, a, tbase, qt + 2, ktw);
-    if (active(qt + 1)) contract(t1);
+    if (qt + 2 < nt && active(qt + 2)) kv_load<P1>(t0, a, tbase, head, qt + 2, ktw);
+    if (active(qt + 1)) contract(t1, qt + 1);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -423,28 +470,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 template <int D, typename TIn>
 static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nkt = (p.T + KV_BN - 1) / KV_BN;
-  hipLaunchKernelGGL((dkdv_kernel<D, TIn>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
+  if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
-template <int D, int CAL, int MODE, bool FULL, typename TIn>
+template <int D, int CAL, int MODE, int GK, typename TIn>
 static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int stage) {
   if (stage & 1) {
     const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
     const size_t smem = dq_smem_bytes<D, TIn>(p.K);
-    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, FULL, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage & 2) return dkdv_go<D, TIn>(p, a, s);
   return hipSuccess;
 }
-template <int D, int CAL, int MODE, bool FULL>
+template <int D, int CAL, int MODE, int GK>
 static hipError_t bwd_dt(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
-  return p.bf16 ? bwd_go<D, CAL, MODE, FULL, uint16_t>(p, a, s, st) : bwd_go<D, CAL, MODE, FULL, float>(p, a, s, st);
+  return p.bf16 ? bwd_go<D, CAL, MODE, GK, uint16_t>(p, a, s, st) : bwd_go<D, CAL, MODE, GK, float>(p, a, s, st);
 }
 template <int D, int CAL, int MODE>
 static hipError_t bwd_fl(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
-  return p.full ? bwd_dt<D, CAL, MODE, true>(p, a, s, st) : bwd_dt<D, CAL, MODE, false>(p, a, s, st);
+  switch (p.gk) {
+    case GK_SUMS: return bwd_dt<D, CAL, MODE, GK_SUMS>(p, a, s, st);
+    case GK_DETACHED: return bwd_dt<D, CAL, MODE, GK_DETACHED>(p, a, s, st);
+    default: return bwd_dt<D, CAL, MODE, GK_P1>(p, a, s, st);
+  }
 }
 template <int D, int CAL>
 static hipError_t bwd_md(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {

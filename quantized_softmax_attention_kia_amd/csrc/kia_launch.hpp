@@ -10,6 +10,9 @@ enum Calib { MINMAX = 0, FWM = 1 };
 // reconstruction and surrogate: LERP; Nearest with the Weight-STE point (P^N, W^N);
 // Nearest with the Prob-STE point (P^L, W^L)
 enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2 };
+// backward kernels by gradient mode: the calibration sums (full, max_only, min_only), the
+// detached extrema, or the detached gradient projected onto zero-sum rows (P1)
+enum GradKind { GK_SUMS = 0, GK_DETACHED = 1, GK_P1 = 2 };
 
 // Per-row record written by the forward and read by the backward (struct of arrays).
 struct RowRec {
@@ -33,7 +36,9 @@ struct Problem {
   int causal;
   float tau;
   double scale;
-  int calib, mode, full, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
+  int calib, mode, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
+  int gk;                 // GradKind
+  int keepM, keepm;       // GK_SUMS: which extremum terms are injected (max_only / min_only drop one)
 };
 
 struct FwdArgs {
@@ -61,8 +66,11 @@ struct BwdArgs {
   float* dv;
   float* pt;     // key-major tiles of the forward's P, written by the dq kernel
   float* dst;    // key-major tiles of dS (extremum terms included), written by the dq kernel
+  float* rowmean;  // P1: per row, the mean of the detached dS over the visible keys (dq writes it)
   int T, K, causal;
   float tau, scale;
+  int keepM, keepm;  // GK_SUMS: inject the maximum's / minimum's term
+  int p1;            // dkdv: subtract rowmean from the visible dS elements
 };
 
 struct BinsArgs {

@@ -53,11 +53,15 @@ def test_workspace_layout(kb):
     nt = (100 + 31) // 32
     tiles = 2 * 3 * nt * (nt + 1) // 2 * 4096        # stored causal score tiles
     st, rr, w = ws(kb, params(kb))
-    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles   # key-major P and dS tiles
+    # key-major P and dS tiles, then the per-row P1 means
+    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles + rnd(N * 4)
     st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
     assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
     st, rr, w = ws(kb, params(kb, causal=0))
-    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096 and w == 2 * 2 * 3 * nt * nt * 4096
+    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096 and w == 2 * 2 * 3 * nt * nt * 4096 + rnd(N * 4)
+    for grad in range(5):   # every gradient mode has the same layout
+        st, rr2, w2 = ws(kb, params(kb, grad=grad))
+        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4)
     st, rr, w = ws(kb, params(kb, B=0))
     assert st == 0 and rr == 0
 
@@ -65,7 +69,7 @@ def test_workspace_layout(kb):
 @pytest.mark.parametrize("bad,status", [
     (dict(K=0), -1), (dict(K=65), -1), (dict(D=48), -2), (dict(D=0), -1), (dict(T=-1), -1),
     (dict(calib=1, tau=0.0), -1), (dict(calib=1, tau=float("nan")), -1), (dict(calib=2), -1),
-    (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=3), -1), (dict(dtype=7), -1),
+    (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=5), -1), (dict(grad=-1), -1), (dict(dtype=7), -1),
     (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1),
 ])
 def test_rejects_bad_params(kb, bad, status):

@@ -19,6 +19,9 @@ pytestmark = pytest.mark.gpu
 
 VARIANTS16 = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest")
               for s in ("weight", "prob") for g in ("full", "detached")]
+# the range_grad ablations: single-channel (max_only, min_only) and the P1 projection
+ABLATIONS = [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
+             ("nearest", "prob")) for g in ("max_only", "min_only", "p1")]
 
 
 @pytest.fixture(scope="module")
@@ -89,6 +92,18 @@ def test_small_all_variants(kb, variant, shape):
     q, k, v, do = make_inputs(B, H, T, D, seed, dtype=dtype, q_scale=2.0)
     full = variant + (8, 5.0)
     say(f"[small] {shape} {full}")
+    got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
+    rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
+    say("   ", rep)
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n") + s[6])
+@pytest.mark.parametrize("variant", ABLATIONS, ids=lambda v: "-".join(v))
+def test_small_ablations(kb, variant, shape):
+    B, H, T, D, causal, seed, dtype = shape
+    q, k, v, do = make_inputs(B, H, T, D, seed, dtype=dtype, q_scale=2.0)
+    full = variant + (8, 5.0)
+    say(f"[ablation] {shape} {full}")
     got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
     rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
     say("   ", rep)

@@ -80,6 +80,28 @@ def test_workload_sampled_heads(kb, case):
         assert ratio < 1e-4, ratio
 
 
+@pytest.mark.parametrize("grad", ["max_only", "min_only", "p1"])
+def test_gpt2_ablations_sampled_heads(kb, grad):
+    """The range_grad ablations at the benchmark shape: sampled heads against the oracle; under
+    P1 every head's dK sums to zero over its keys (each score-gradient row sums to zero)."""
+    import dataclasses
+    wl = WORKLOADS["gpt2"]
+    var = dataclasses.replace(wl.variants[0], grad=grad)   # MinMax LERP K=4
+    q, k, v, do = inputs("gpt2")
+    say(f"[gpt2 ablation] B={wl.B} H={wl.H} T={wl.T} D={wl.D} seed={wl.seed} {var.calib}-{var.recon} {grad}")
+    got = run(kb, wl, var, q, k, v, do)
+    cfg = ORC.OracleConfig.of(var)
+    for b, h in parity.pick_heads(cfg, q, k, want=2):
+        gh = {key: got[key][b, h].cpu().numpy().astype(np.float64) for key in ("O", "dQ", "dK", "dV")}
+        rep = parity.check_head(cfg, q[b, h], k[b, h], v[b, h], do[b, h], gh)
+        say(f"    head ({b},{h}): {rep}")
+    if grad == "p1":
+        dk = got["dK"].double()
+        ratio = (dk.sum(dim=2).abs() / dk.abs().sum(dim=2).clamp_min(1e-30)).max().item()
+        say(f"    max_h |sum_j dK_j| / sum_j |dK_j| = {ratio:.2e}")
+        assert ratio < 1e-4, ratio
+
+
 def test_full_and_detached_forward_bitwise_identical(kb):
     wl = WORKLOADS["wide"]
     q, k, v, do = inputs("wide")
