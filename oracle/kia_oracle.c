@@ -38,6 +38,11 @@
  *    max_only is the full gradient and its min_only the detached one.
  *  - P1: the detached score gradient minus its mean over the row's visible
  *    (causal) keys, tail keys included, so every row sums to zero.
+ *  - FWM tail policies (App. D "Definition and experiment", App. C.3 stages):
+ *    zero (the paper's FWM: w = 0 below the window); floor (z <- -tau: a key
+ *    below the window weighs e^{b_0} and, its score clamped, has no gradient);
+ *    resolved (the grid b_r = -tau + r h continued below -tau, r unbounded
+ *    below, so no key is truncated and every key has the LERP slope).
  *
  * Flip list: a test may ask the oracle to take, at named (row, key) positions,
  * the other valid decision at a bin boundary (the other interval at an integer
@@ -67,6 +72,7 @@ enum { KO_MINMAX = 0, KO_FWM = 1 };
 enum { KO_LERP = 0, KO_NEAREST = 1 };
 enum { KO_WEIGHT_STE = 0, KO_PROB_STE = 1 };
 enum { KO_FULL = 0, KO_DETACHED = 1, KO_MAX_ONLY = 2, KO_MIN_ONLY = 3, KO_P1 = 4 };
+enum { KO_TAIL_ZERO = 0, KO_TAIL_FLOOR = 1, KO_TAIL_RESOLVED = 2 };
 
 enum { FLIP_INTERVAL = 1, FLIP_NEAREST = 2, FLIP_TAIL = 4 };
 
@@ -91,13 +97,24 @@ enum {
   MUT_X_INDEX = 17,         /* X uses r instead of r+1 in its second term */
   MUT_DETACH_KEEPS_M = 18,  /* detached mode keeps the M channel */
   MUT_ONLY_SWAPPED = 19,    /* max_only keeps the m channel, min_only the M channel */
-  MUT_P1_SKIP_TAIL = 20     /* P1 shifts only the keys inside the FWM window */
+  MUT_P1_SKIP_TAIL = 20,    /* P1 shifts only the keys inside the FWM window */
+  MUT_FLOOR_TAIL_SLOPE = 21, /* floored tail keys keep the slope of the first interval */
+  MUT_RESOLVED_GRID_CLAMP = 22 /* the resolved grid reads the table's end values below the window */
 };
 
 typedef struct {
   int32_t calib, recon, ste, grad, K, mutation;
   double tau;
+  int32_t tail;   /* FWM tail policy (KO_TAIL_*); zero for MinMax */
 } ko_cfg_t;
+
+/* Grid value e^{b_q} at any integer q: the table for 0 <= q <= K, else (the resolved FWM grid
+   below the window) b_q = -tau + q h computed directly. */
+static double grid_at(const double *E, int K, double tau, double h, int q, int mut) {
+  if (q >= 0 && q <= K) return E[q];
+  if (mut == MUT_RESOLVED_GRID_CLAMP) return E[q < 0 ? 0 : K];
+  return exp(-tau + q * h);
+}
 
 /* per-row record: doubles */
 enum { RD_M = 0, RD_m, RD_h, RD_WL, RD_WN, RD_a, RD_b, RD_gapM, RD_gapm, RD_D, RD_tolM, RD_tolm, RD_N };
@@ -143,6 +160,7 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
                         const double *eb) {
   const int K = cfg->K;
   const int mut = cfg->mutation;
+  const int tailp = cfg->calib == KO_FWM ? cfg->tail : KO_TAIL_ZERO;
   double *E = (double *)malloc(sizeof(double) * (K + 1));
   double *bgrid = (double *)malloc(sizeof(double) * (K + 1));
   double *u = (double *)malloc(sizeof(double) * n);
@@ -194,6 +212,9 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
     int tj = 0;
     if (cfg->calib == KO_MINMAX) {
       uj = (s[j] - m) / h;
+    } else if (tailp == KO_TAIL_RESOLVED) {
+      double z = s[j] - M;                                 /* the grid continues below -tau */
+      uj = ((z > 0.0 ? 0.0 : z) + cfg->tau) / h;
     } else {
       double z = s[j] - M;
       tj = (mut == MUT_TAIL_INCLUSIVE) ? (z <= -cfg->tau) : (z < -cfg->tau);
@@ -207,17 +228,18 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
         double eu = (cfg->calib == KO_MINMAX) ? (eb[j] + 2.0 * ebm + ebM) / h : (eb[j] + ebM) / h;
         if (eu > gj) gj = eu;
       }
-      if (cfg->calib == KO_FWM && fabs(s[j] - M + cfg->tau) / h < gj)
+      if (cfg->calib == KO_FWM && tailp != KO_TAIL_RESOLVED && fabs(s[j] - M + cfg->tau) / h < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_TAIL, fabs(s[j] - M + cfg->tau) / h);
       double kint = floor(uj + 0.5);
-      if (K >= 2 && kint >= 1 && kint <= K - 1 && fabs(uj - kint) < gj)
+      /* interval boundaries: the integers 1..K-1, and every integer below K on the resolved grid */
+      if ((tailp == KO_TAIL_RESOLVED || (K >= 2 && kint >= 1)) && kint <= K - 1 && fabs(uj - kint) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_INTERVAL, fabs(uj - kint));
       double khalf = floor(uj) + 0.5;
       if (cfg->recon == KO_NEAREST && khalf < K && fabs(uj - khalf) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_NEAREST, fabs(uj - khalf));
     }
     int rj = (mut == MUT_INTERVAL_ROUND) ? (int)floor(uj + 0.5) : (int)floor(uj);
-    if (rj < 0) rj = 0;
+    if (rj < 0 && tailp != KO_TAIL_RESOLVED) rj = 0;
     if (rj > K - 1) rj = K - 1;
     double tt = uj - rj;
     if (tt < 0.0) tt = 0.0;
@@ -229,10 +251,11 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
         uj = 0.0; rj = 0; tt = 0.0;
       }
       if (!tj && uj == 0.0) { rj = 0; tt = 0.0; }
+      if (tj && tailp == KO_TAIL_FLOOR) { uj = 0.0; rj = 0; tt = 0.0; }   /* into the tail: floored */
     }
     if (fl & FLIP_INTERVAL) {
       int kint = (int)floor(uj + 0.5);
-      if (kint >= 1 && kint <= K - 1) {
+      if ((kint >= 1 || tailp == KO_TAIL_RESOLVED) && kint <= K - 1) {
         rj = (rj == kint) ? kint - 1 : kint;
         tt = uj - rj;
         if (tt < 0.0) tt = 0.0;
@@ -248,11 +271,12 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
     u[j] = uj; r[j] = rj; t[j] = tt; ell[j] = lj; tail[j] = (uint8_t)tj;
   }
 
-  /* --- reconstruction (§3 Reconstruction) --- */
+  /* --- reconstruction (§3 Reconstruction); a floored tail key sits on the window edge (u = 0) --- */
   for (int j = 0; j < n; ++j) {
-    if (tail[j]) { wL[j] = 0.0; wN[j] = 0.0; continue; }
-    wL[j] = (1.0 - t[j]) * E[r[j]] + t[j] * E[r[j] + 1];   /* LERP between adjacent grid values */
-    wN[j] = E[ell[j]];                                       /* Nearest grid centre */
+    if (tail[j] && tailp == KO_TAIL_ZERO) { wL[j] = 0.0; wN[j] = 0.0; continue; }
+    const double Er = grid_at(E, K, cfg->tau, h, r[j], mut), Er1 = grid_at(E, K, cfg->tau, h, r[j] + 1, mut);
+    wL[j] = (1.0 - t[j]) * Er + t[j] * Er1;                 /* LERP between adjacent grid values */
+    wN[j] = grid_at(E, K, cfg->tau, h, ell[j], mut);              /* Nearest grid centre */
   }
 
   /* --- normalization (§3) and strict hard forward (App. C.2 (iii)) --- */
@@ -275,11 +299,16 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
 
     /* --- LERP own-score slope (App. B): Delta_j = (e^{b_{r+1}} - e^{b_r})/h --- */
     for (int j = 0; j < n; ++j) {
-      if (tail[j]) { Delta[j] = 0.0; continue; }
-      Delta[j] = (mut == MUT_DELTA_TIMES_H) ? (E[r[j] + 1] - E[r[j]]) * h : (E[r[j] + 1] - E[r[j]]) / h;
+      if (tail[j] && !(mut == MUT_FLOOR_TAIL_SLOPE && tailp == KO_TAIL_FLOOR)) {
+        Delta[j] = 0.0;   /* zero tail: no weight; floor: a constant weight */
+        continue;
+      }
+      const double dE = grid_at(E, K, cfg->tau, h, r[j] + 1, mut) - grid_at(E, K, cfg->tau, h, r[j], mut);
+      Delta[j] = (mut == MUT_DELTA_TIMES_H) ? dE * h : dE / h;
       dS[j] = gam[j] * Delta[j];
     }
-    for (int j = 0; j < n; ++j) if (tail[j]) dS[j] = 0.0;
+    for (int j = 0; j < n; ++j)
+      if (tail[j] && !(mut == MUT_FLOOR_TAIL_SLOPE && tailp == KO_TAIL_FLOOR)) dS[j] = 0.0;
 
     /* --- calibration gradient through the row extrema (App. B); max_only / min_only keep
        one of its two channels --- */
@@ -358,6 +387,7 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
            double *rowd, int32_t *rowi) {
   if (!cfg || n < 1 || cfg->K < 1 || !s || !P || (g && !dS)) return -1;
   if (cfg->calib == KO_FWM && !(cfg->tau > 0.0)) return -1;
+  if (cfg->tail < KO_TAIL_ZERO || cfg->tail > KO_TAIL_RESOLVED || (cfg->calib == KO_MINMAX && cfg->tail != 0)) return -1;
   if (u && !(r && t && ell && tail)) return -1;
   ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL, NULL);
   return 0;
@@ -386,6 +416,7 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
   if (!cfg || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
   if (dO && !(dQ && dK && dV)) return -1;
   if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
+  if (cfg->tail < KO_TAIL_ZERO || cfg->tail > KO_TAIL_RESOLVED || (cfg->calib == KO_MINMAX && cfg->tail != 0)) return -1;
   const int mut = cfg->mutation;
   ko_flags_t fl_store, *fl = NULL;
   if (flag_cap > 0 && flag_pos && flag_dist) {
@@ -468,8 +499,13 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
                 rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl, eb);
     if (bins) {
       for (int j = 0; j < T; ++j) bins[(size_t)i * T + j] = 255;
-      for (int j = 0; j < n && j < T; ++j)
-        bins[(size_t)i * T + j] = dtail[j] ? 254 : (uint8_t)(cfg->recon == KO_NEAREST ? dl[j] : dr[j]);
+      /* bin value: the index (interval r, or Nearest l); on the resolved FWM grid the index + 64,
+         clamped below at 0 (indices below -64 share the value 0); 254 tail, 255 not visible */
+      for (int j = 0; j < n && j < T; ++j) {
+        int idx = cfg->recon == KO_NEAREST ? dl[j] : dr[j];
+        if (cfg->calib == KO_FWM && cfg->tail == KO_TAIL_RESOLVED) idx = idx < -64 ? 0 : idx + 64;
+        bins[(size_t)i * T + j] = dtail[j] ? 254 : (uint8_t)idx;
+      }
       free(du); free(dt); free(dr); free(dl); free(dtail);
     }
     if (mut == MUT_EXTREMA_ALL_KEYS && causal) {

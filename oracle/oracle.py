@@ -26,6 +26,7 @@ CALIB = {"minmax": 0, "fwm": 1}
 RECON = {"lerp": 0, "nearest": 1}
 STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
+TAIL = {"zero": 0, "floor": 1, "resolved": 2}
 
 FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL = 1, 2, 4
 MUTATIONS = {
@@ -34,6 +35,7 @@ MUTATIONS = {
     "nearest_fwd_lerp": 9, "extrema_all_keys": 10, "dq_no_scale": 11, "no_hsafe": 12,
     "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
     "x_index": 17, "detach_keeps_m": 18, "only_swapped": 19, "p1_skip_tail": 20,
+    "floor_tail_slope": 21, "resolved_grid_clamp": 22,
 }
 ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
 ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")
@@ -52,7 +54,7 @@ def build(force: bool = False) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("calib", ctypes.c_int32), ("recon", ctypes.c_int32), ("ste", ctypes.c_int32),
                 ("grad", ctypes.c_int32), ("K", ctypes.c_int32), ("mutation", ctypes.c_int32),
-                ("tau", ctypes.c_double)]
+                ("tau", ctypes.c_double), ("tail", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -64,15 +66,17 @@ class OracleConfig:
     K: int = 4
     tau: float = 8.0
     mutation: str | None = None
+    tail: str = "zero"   # FWM tail policy: zero, floor or resolved
 
     @classmethod
     def of(cls, v, mutation=None):
-        """Build from any object with calib/recon/ste/grad/K/tau attributes."""
-        return cls(v.calib, v.recon, v.ste, v.grad, int(v.K), float(v.tau), mutation)
+        """Build from any object with calib/recon/ste/grad/K/tau (and optionally tail) attributes."""
+        return cls(v.calib, v.recon, v.ste, v.grad, int(v.K), float(v.tau), mutation, getattr(v, "tail", "zero"))
 
     def _c(self) -> _Cfg:
         return _Cfg(CALIB[self.calib], RECON[self.recon], STE[self.ste], GRAD[self.grad],
-                    int(self.K), MUTATIONS[self.mutation] if self.mutation else 0, float(self.tau))
+                    int(self.K), MUTATIONS[self.mutation] if self.mutation else 0, float(self.tau),
+                    TAIL[self.tail])
 
 
 _lib = None

@@ -16,6 +16,11 @@ Gradient modes: "detached" detaches both row extrema; "max_only" / "min_only"
 detach only the other extremum (the single-channel ablation of App. I); "p1"
 is the detached gradient with a hook on the scores that projects each row's
 gradient onto the zero-sum subspace over its visible keys (App. B "Detach").
+
+FWM tail policies (App. D, App. C.3): "zero" drops keys below the window;
+"floor" clamps z at -tau, so such a key weighs e^{-tau} and torch's clamp gives
+it no gradient; "resolved" continues the grid b_q = -tau + q h to every integer
+q below the window, with the grid value computed as exp(b_q) for any q.
 """
 import torch
 
@@ -27,7 +32,7 @@ def _st_clamp01(x):
     return x + (x.clamp(0.0, 1.0) - x).detach()
 
 
-def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0):
+def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0, tail_policy="zero"):
     """s: [R, n] float64, mask: [R, n] bool (visible keys).  Returns P [R, n]."""
     dt = s.dtype
     pos_inf = torch.tensor(float("inf"), dtype=dt)
@@ -52,17 +57,24 @@ def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0):
         h = tau / K
         b = (-tau + rr * h).expand(R, K + 1)
         z = s - M
-        tail = (z < -tau).detach()
-        u = (torch.clamp(z, -tau, 0.0) + tau) / h
+        if tail_policy == "resolved":
+            tail = torch.zeros_like(mask)
+            u = (torch.clamp(z, max=0.0) + tau) / h
+        else:
+            tail = (z < -tau).detach() if tail_policy == "zero" else torch.zeros_like(mask)
+            u = (torch.clamp(z, -tau, 0.0) + tau) / h
     u_safe = torch.where(mask, u, torch.zeros_like(u))
-    r = torch.clamp(torch.floor(u_safe.detach()), 0, K - 1).long()
+    lo = None if (calib == "fwm" and tail_policy == "resolved") else 0
+    r = torch.clamp(torch.floor(u_safe.detach()), lo, K - 1).long()
     t = _st_clamp01(u_safe - r.to(dt))
-    E = torch.exp(b)
-    Er = torch.gather(E, 1, r)
-    Er1 = torch.gather(E, 1, r + 1)
-    wL = (1.0 - t) * Er + t * Er1
     ell = r + (t.detach() >= 0.5).long()
-    wN = torch.gather(E, 1, ell)
+    if calib == "fwm":
+        Er, Er1, EN = (torch.exp(-tau + q.to(dt) * h) for q in (r, r + 1, ell))
+    else:
+        E = torch.exp(b)
+        Er, Er1, EN = (torch.gather(E, 1, q) for q in (r, r + 1, ell))
+    wL = (1.0 - t) * Er + t * Er1
+    wN = EN
     keep = mask & ~tail
     zero = torch.zeros_like(wL)
     wL = torch.where(keep, wL, zero)
@@ -77,12 +89,12 @@ def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0):
     return PL + (PN - PL).detach()
 
 
-def row_grad(s, g, calib, recon, ste, grad, K, tau=8.0):
+def row_grad(s, g, calib, recon, ste, grad, K, tau=8.0, tail_policy="zero"):
     """Single row: returns (P, dS) as float64 tensors."""
     s = torch.as_tensor(s, dtype=torch.float64).reshape(1, -1).clone().requires_grad_(True)
     g = torch.as_tensor(g, dtype=torch.float64).reshape(1, -1)
     mask = torch.ones_like(s, dtype=torch.bool)
-    P = row_probs(s, mask, calib, recon, ste, grad, K, tau)
+    P = row_probs(s, mask, calib, recon, ste, grad, K, tau, tail_policy)
     (P * g).sum().backward()
     dS = s.grad[0]
     if grad == "p1":
@@ -90,7 +102,7 @@ def row_grad(s, g, calib, recon, ste, grad, K, tau=8.0):
     return P.detach()[0], dS
 
 
-def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, scale=None):
+def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, scale=None, tail_policy="zero"):
     """One head, materialized T x T in float64: returns O, dQ, dK, dV."""
     Q = torch.as_tensor(Q, dtype=torch.float64).clone().requires_grad_(True)
     Kt = torch.as_tensor(K_, dtype=torch.float64).clone().requires_grad_(True)
@@ -105,7 +117,7 @@ def head_grad(Q, K_, V, dO, calib, recon, ste, grad, K, tau=8.0, causal=True, sc
     if grad == "p1":
         cnt = mask.sum(dim=1, keepdim=True).to(S.dtype)
         S.register_hook(lambda gS: torch.where(mask, gS - torch.where(mask, gS, 0.0).sum(1, keepdim=True) / cnt, gS))
-    P = row_probs(S, mask, calib, recon, ste, grad, K, tau)
+    P = row_probs(S, mask, calib, recon, ste, grad, K, tau, tail_policy)
     O = P @ V
     (O * dO).sum().backward()
     return O.detach(), Q.grad, Kt.grad, V.grad

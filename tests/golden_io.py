@@ -40,7 +40,7 @@ def load_cases(name="hand_rows.txt"):
             if key == "case":
                 cur = {"case": val}
                 cases.append(cur)
-            elif key == "calib":
+            elif key in ("calib", "tail_policy"):
                 cur[key] = val
             else:
                 vals = [_eval(v) for v in val.split(",")]

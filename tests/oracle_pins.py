@@ -15,9 +15,13 @@ and raises AssertionError when the oracle disagrees with:
   * brute-force nearest grid centre in score coordinates;
   * shift invariance of the output (and of dQ for the full gradient);
   * degenerate rows, causal row 0, V = 1, tied extrema, K = 1 affine LERP;
-  * the hand-derived fixtures in tests/golden/.
+  * the hand-derived fixtures in tests/golden/;
+  * for the FWM tail policies (App. D, App. C.3): floored tail keys weigh e^{-tau}
+    and carry no gradient, moving them deeper changes nothing; the resolved grid
+    keeps every key within the chord and nearest-centre bounds of e^z and
+    converges to softmax as h -> 0 even with a narrow window.
 Source: "Pretraining Transformers with Quantized Softmax in Attention", §3,
-§5.1, App. A, App. B, App. C.2.
+§5.1, App. A, App. B, App. C.2, App. C.3, App. D.
 """
 from __future__ import annotations
 
@@ -36,6 +40,9 @@ VARIANTS = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest")
 # the range_grad ablations (App. I single-channel modes, App. B P1 projection)
 VARIANTS += [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
              ("nearest", "prob")) for g in ("max_only", "min_only", "p1")]
+# the FWM tail policies (App. D tau-floor variant, App. C.3 resolved grid)
+VARIANTS += [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("lerp", "prob"),
+             ("nearest", "weight"), ("nearest", "prob")) for g in ("full", "detached")]
 
 
 def zero_sum_mode(cfg):
@@ -44,15 +51,30 @@ def zero_sum_mode(cfg):
     return cfg.grad in ("full", "p1") or (cfg.calib == "fwm" and cfg.grad == "max_only")
 
 
-def cfg_of(calib, recon, ste, grad, K=4, tau=8.0, mutation=None):
-    return ORC.OracleConfig(calib, recon, ste, grad, K, tau, mutation)
+def cfg_of(calib, recon, ste, grad, tail="zero", K=4, tau=8.0, mutation=None):
+    return ORC.OracleConfig(calib, recon, ste, grad, K, tau, mutation, tail)
+
+
+def _resolved(cfg):
+    return cfg.calib == "fwm" and cfg.tail == "resolved"
+
+
+def _tail_mask(cfg, z):
+    """Keys the policy truncates or floors: z < -tau under the zero and floor FWM policies."""
+    if cfg.calib != "fwm" or cfg.tail == "resolved":
+        return np.zeros_like(z, dtype=bool)
+    return z < -cfg.tau
+
+
+def _ar(cfg):
+    return (cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau)
 
 
 def _near_boundary(res, cfg, guard=1e-6):
     u = res["u"]
     near_int = np.abs(u - np.round(u)) < guard
     near_half = np.abs(u - (np.floor(u) + 0.5)) < guard
-    interior = (np.round(u) >= 1) & (np.round(u) <= cfg.K - 1)
+    interior = (np.round(u) <= cfg.K - 1) & ((np.round(u) >= 1) | _resolved(cfg))
     bad = (near_int & interior) | near_half
     return bool(bad.any())
 
@@ -91,7 +113,7 @@ def _close(a, b, rtol, atol, what):
 def pin_autograd_rows(cfg):
     for s, g in _random_rows(11, cfg):
         res = ORC.row(cfg, s, g)
-        P, dS = AR.row_grad(s, g, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau)
+        P, dS = AR.row_grad(s, g, *_ar(cfg), tail_policy=cfg.tail)
         _close(res["P"], P.numpy(), 1e-12, 1e-14, "row P vs autograd")
         _close(res["dS"], dS.numpy(), 1e-9, 1e-12, "row dS vs autograd")
 
@@ -109,7 +131,7 @@ def pin_autograd_ties(cfg):
         if _near_boundary(res, cfg):
             continue
         res = ORC.row(cfg, s, g)
-        P, dS = AR.row_grad(s, g, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau)
+        P, dS = AR.row_grad(s, g, *_ar(cfg), tail_policy=cfg.tail)
         _close(res["P"], P.numpy(), 1e-12, 1e-14, "tied row P vs autograd")
         _close(res["dS"], dS.numpy(), 1e-9, 1e-12, "tied row dS vs autograd")
 
@@ -127,8 +149,7 @@ def pin_autograd_head(cfg):
     for seed, T, D, causal, qs in ((1, 24, 8, True, 1.5), (2, 10, 6, False, 3.0), (3, 33, 4, True, 4.0)):
         Q, K, V, dO = _head_inputs(seed, T, D, qs)
         res = ORC.head(cfg, Q, K, V, dO, causal=causal, nthreads=2)
-        O, dQ, dK, dV = AR.head_grad(Q, K, V, dO, cfg.calib, cfg.recon, cfg.ste, cfg.grad, cfg.K, cfg.tau,
-                                     causal=causal)
+        O, dQ, dK, dV = AR.head_grad(Q, K, V, dO, *_ar(cfg), causal=causal, tail_policy=cfg.tail)
         _close(res["O"], O.numpy(), 1e-11, 1e-13, "head O vs autograd")
         _close(res["dV"], dV.numpy(), 1e-10, 1e-12, "head dV vs autograd")
         _close(res["dQ"], dQ.numpy(), 1e-8, 1e-11, "head dQ vs autograd")
@@ -198,8 +219,12 @@ def pin_reconstruction_bounds(cfg):
         z = s - res["M"]
         w = _weights(res, cfg.recon)
         h = res["h"]
-        tail = z < -cfg.tau if cfg.calib == "fwm" else np.zeros_like(z, dtype=bool)
-        assert np.all(w[tail] == 0.0), "tail weight not zero"
+        tail = _tail_mask(cfg, z)
+        if cfg.tail == "floor":
+            _close(w[tail], np.full(int(tail.sum()), math.exp(-cfg.tau)), 1e-14, 0.0, "floored tail weight")
+        else:
+            assert np.all(w[tail] == 0.0), "tail weight not zero"
+        assert np.array_equal(res["tail"].astype(bool), tail), "tail flags"
         win = ~tail
         if cfg.recon == "lerp":
             ez = np.exp(z[win])
@@ -222,13 +247,17 @@ def pin_nearest_brute_force(cfg):
         if cfg.calib == "minmax":
             grid = m + np.arange(K + 1) * (M - m) / K
         else:
-            grid = M - cfg.tau + np.arange(K + 1) * (cfg.tau / K)
+            lowest = -int(np.ceil((M - m) / (cfg.tau / K))) - 2 if _resolved(cfg) else 0
+            q = np.arange(lowest, K + 1)
+            grid = M - cfg.tau + q * (cfg.tau / K)
         for j in range(len(s)):
-            if cfg.calib == "fwm" and s[j] - M < -cfg.tau:
+            if _tail_mask(cfg, np.array([s[j] - M]))[0]:
+                assert cfg.tail != "floor" or res["ell"][j] == 0, "floored tail key not at grid point 0"
                 continue
             d = np.abs(s[j] - grid)
             best = np.flatnonzero(d <= d.min() * (1 + 1e-12) + 1e-15)
-            assert res["ell"][j] == best.max(), f"nearest index {res['ell'][j]} vs brute force {best}"
+            want = best.max() + (lowest if cfg.calib == "fwm" else 0)
+            assert res["ell"][j] == want, f"nearest index {res['ell'][j]} vs brute force {want}"
 
 
 def pin_finite_differences(cfg):
@@ -329,7 +358,8 @@ def pin_k_limit(cfg):
     g = rng.standard_normal(48)
     e = np.exp(s - s.max()); Pe = e / e.sum()
     dSe = Pe * (g - (Pe * g).sum())
-    tau = float(s.max() - s.min() + 1.0)
+    # the resolved grid is never truncated, so a narrow window converges too
+    tau = 1.0 if _resolved(cfg) else float(s.max() - s.min() + 1.0)
     errs, gerrs = [], []
     for K in (16, 64, 256):
         res = ORC.row(dataclasses.replace(cfg, K=K, tau=tau), s, g)
@@ -343,7 +373,7 @@ def pin_k_limit(cfg):
 def pin_golden(cfg):
     """Hand-derived fixtures (tests/golden/hand_rows.txt)."""
     for case in golden_io.load_cases():
-        if case["calib"] != cfg.calib:
+        if case["calib"] != cfg.calib or case.get("tail_policy", "zero") != cfg.tail:
             continue
         c = dataclasses.replace(cfg, K=int(case["K"]), tau=float(case.get("tau", cfg.tau)))
         s = np.array(case["s"], dtype=np.float64)
@@ -364,7 +394,42 @@ def pin_golden(cfg):
             assert res[key] == int(case[key]), f"{name}: {key}"
 
 
+def pin_tail_policy(cfg):
+    """Floor: a tail key weighs e^{-tau}, has no score gradient, and lowering it further changes
+    nothing.  Resolved: nothing is truncated, and a key's weight keeps following e^z below the
+    window (LERP within the chord bound, so deeper keys weigh less).  Zero: tail keys weigh 0."""
+    if cfg.calib != "fwm":
+        return
+    rng = np.random.default_rng(71)
+    for n in (6, 13, 29):
+        s = rng.standard_normal(n) * 2.0
+        h = cfg.tau / cfg.K
+        s[1] = s.max() - cfg.tau - 1.3 * h    # one key below the window
+        s[2] = s.max() - cfg.tau - 3.4 * h    # one further below
+        g = rng.standard_normal(n)
+        if _near_boundary(ORC.row(dataclasses.replace(cfg, mutation=None), s, g), cfg):
+            continue
+        res = ORC.row(cfg, s, g)
+        w = _weights(res, cfg.recon)
+        if cfg.tail == "floor":
+            assert res["tail"][1] and res["tail"][2], "keys below the window not flagged"
+            assert w[1] == w[2], "floored tail keys weigh differently"
+            assert res["dS"][1] == 0.0 or cfg.grad == "p1", "floored tail key has a gradient"
+            s2 = s.copy(); s2[1] -= 5.0
+            res2 = ORC.row(cfg, s2, g)
+            _close(res2["P"], res["P"], 1e-15, 0.0, "floor: P moved with a tail key")
+            _close(res2["dS"], res["dS"], 1e-14, 1e-16, "floor: dS moved with a tail key")
+        elif cfg.tail == "resolved":
+            assert not res["tail"].any(), "the resolved grid flagged a tail key"
+            assert w[2] < w[1] < math.exp(-cfg.tau), "resolved weights do not decrease below the window"
+            assert res["r"][1] < 0 and res["r"][2] < res["r"][1], "resolved intervals below the window"
+            if cfg.recon == "lerp":
+                assert res["dS"][1] != 0.0 and res["dS"][2] != 0.0, "resolved key below the window lacks a slope"
+        else:
+            assert w[1] == 0.0 and w[2] == 0.0, "zero-policy tail keys weigh something"
+
+
 PINS = [pin_golden, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
         pin_two_key,
         pin_reconstruction_bounds, pin_nearest_brute_force, pin_finite_differences, pin_shift_invariance,
-        pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit]
+        pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit, pin_tail_policy]
