@@ -64,7 +64,7 @@ def read_traffic(kernel: str):
     return None
 
 
-def cpu_baseline(workload, q, k, v, do, budget_s: float, grad: str = "full"):
+def cpu_baseline(variants, q, k, v, do, budget_s: float, grad: str = "full"):
     """The oracle, as it stands, on a bounded sample: heads in order, every variant, until the budget."""
     import dataclasses
     from oracle import oracle as ORC
@@ -75,7 +75,7 @@ def cpu_baseline(workload, q, k, v, do, budget_s: float, grad: str = "full"):
     t0 = time.perf_counter()
     for b in range(B):
         for h in range(H):
-            for var in workload.variants:
+            for var in variants:
                 cfg = dataclasses.replace(ORC.OracleConfig.of(var), grad=grad)
                 ORC.head(cfg, q[b, h], k[b, h], v[b, h], do[b, h], nthreads=threads)
                 flops += 12.0 * D * pairs
@@ -87,7 +87,7 @@ def cpu_baseline(workload, q, k, v, do, budget_s: float, grad: str = "full"):
         break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_heads} of {B * H} heads of the same workload, all {len(workload.variants)} variants, "
+            "sample": f"{done_heads} of {B * H} heads of the same workload, all {len(variants)} variants, "
                       f"forward+backward in double, {dt:.1f} s wall"}
 
 
@@ -101,6 +101,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad", default="full", choices=["full", "detached", "max_only", "min_only", "p1"],
                     help="gradient mode of every variant (the headline is full)")
+    ap.add_argument("--tail", default="zero", choices=["zero", "floor", "resolved"],
+                    help="tail policy of the FWM variants (the headline is zero, the FWM of the pages)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
                          "byte counters)")
@@ -115,9 +117,11 @@ def main() -> int:
     from quantized_softmax_attention_kia_amd import binding as kb
     from quantized_softmax_attention_kia_amd.inputs import WORKLOADS
 
+    import dataclasses
     wl = WORKLOADS[args.workload]
+    variants = [dataclasses.replace(v, tail=args.tail) if v.calib == "fwm" else v for v in wl.variants]
     log(f"workload {wl.name}: B={wl.B} H={wl.H} T={wl.T} D={wl.D} {wl.dtype} seed={wl.seed}; "
-        f"{len(wl.variants)} variants")
+        f"{len(variants)} variants")
     q, k, v, do = wl.inputs()
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -125,10 +129,9 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     runs = []
-    for var in wl.variants:
+    for var in variants:
         cfg = kb.Config.of(var)
         if args.grad != cfg.grad:
-            import dataclasses
             cfg = dataclasses.replace(cfg, grad=args.grad)
         p = kb.make_params(cfg, qt.shape, tdt)
         rr, ws = kb.kia_workspace_size(p)
@@ -205,7 +208,7 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    traffic = read_traffic(kernel_key) if args.grad == "full" else None
+    traffic = read_traffic(kernel_key) if args.grad == "full" and args.tail == "zero" else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "
@@ -214,7 +217,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample ...")
-        cpu = cpu_baseline(wl, q, k, v, do, args.cpu_seconds, args.grad)
+        cpu = cpu_baseline(variants, q, k, v, do, args.cpu_seconds, args.grad)
         log(f"cpu baseline {cpu}")
 
     line = {

@@ -10,7 +10,11 @@
  *     with the row maximum M and minimum m; rows with M - m <= 1e-12 use the
  *     safe width h = 1 (App. A "Edge cases and conventions");
  *   FWM: h = tau/K, b_r = -tau + r h, the score shifted by M is clipped to
- *     [-tau, 0] and keys below the window get weight 0.
+ *     [-tau, 0] and keys below the window get weight 0.  Two other tail
+ *     policies (kia_tail_t): floor (App. C.3 selection stages, App. D.4: z is
+ *     clipped up to -tau, so such a key weighs e^{-tau} and has no score
+ *     gradient) and resolved (App. D.4: the grid b_q = -tau + q h continues
+ *     below -tau with negative indices q, so no key is truncated).
  * Each key's weight is rebuilt from the grid (§3 "Reconstruction"): LERP
  * interpolates between e^{b_r} and e^{b_{r+1}} at the key's local position t;
  * Nearest takes the grid value of index r + 1[t >= 1/2].  Weights are
@@ -53,7 +57,8 @@ extern "C" {
 
 typedef enum {
   KIA_OK = 0,
-  KIA_ERR_INVALID_ARG = -1, /* null pointer, bad size or enum value, tau <= 0 under FWM */
+  KIA_ERR_INVALID_ARG = -1, /* null pointer, bad size or enum value, tau <= 0 under FWM,
+                               a tail policy other than zero under MinMax */
   KIA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
   KIA_ERR_WORKSPACE = -3,   /* reserved: a buffer smaller than kia_workspace_size asks */
   KIA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
@@ -72,6 +77,12 @@ typedef enum {
   KIA_GRAD_P1 = 4        /* detached, each row projected onto zero sum over its visible keys */
 } kia_grad_t;
 typedef enum { KIA_F32 = 0, KIA_BF16 = 1 } kia_dtype_t;
+/* FWM treatment of keys below the window (z = s - M < -tau); MinMax takes ZERO */
+typedef enum {
+  KIA_TAIL_ZERO = 0,     /* weight 0 (the FWM operator of §3) */
+  KIA_TAIL_FLOOR = 1,    /* z clipped to -tau: weight e^{-tau}, no score gradient */
+  KIA_TAIL_RESOLVED = 2  /* grid continued below -tau: every key weighed on it */
+} kia_tail_t;
 
 typedef struct {
   int64_t B, H, T, D;   /* batch, heads, sequence length, head dim; T >= 1, D in {64, 128} */
@@ -84,6 +95,7 @@ typedef struct {
   int32_t ste;          /* kia_ste_t */
   int32_t grad;         /* kia_grad_t */
   int32_t dtype;        /* kia_dtype_t of Q, K, V and dO */
+  int32_t tail;         /* kia_tail_t; must be KIA_TAIL_ZERO under MinMax */
 } kia_params_t;
 
 /*
@@ -163,7 +175,9 @@ kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void*
  *        scores and row extrema decide the bins).
  *  bins: device uint8 [B,H,T,T]: for visible keys the Nearest index l in 0..K
  *        (recon = Nearest) or the interval index r in 0..K-1 (recon = LERP);
- *        254 for FWM tail keys; 255 for keys the query does not see.
+ *        on the resolved FWM grid (indices may be negative) the index + 64,
+ *        with indices below -64 all given 0; 254 for FWM tail keys (zero and
+ *        floor policies); 255 for keys the query does not see.
  * Costs O(B*H*T*T) bytes; meant for small T.
  */
 kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream);

@@ -24,6 +24,7 @@ RECON = {"lerp": 0, "nearest": 1}
 STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+TAIL = {"zero": 0, "floor": 1, "resolved": 2}
 
 
 class KiaError(RuntimeError):
@@ -37,7 +38,8 @@ class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("causal", ctypes.c_int32), ("K", ctypes.c_int32), ("tau", ctypes.c_float),
                 ("scale", ctypes.c_float), ("calib", ctypes.c_int32), ("recon", ctypes.c_int32),
-                ("ste", ctypes.c_int32), ("grad", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("ste", ctypes.c_int32), ("grad", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("tail", ctypes.c_int32)]
 
 
 EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
@@ -85,16 +87,17 @@ class Config:
     tau: float = 8.0
     causal: bool = True
     scale: float = 0.0     # 0 selects 1/sqrt(D)
+    tail: str = "zero"     # FWM tail policy: zero, floor or resolved
 
     @classmethod
     def of(cls, v, causal=True, scale=0.0):
-        return cls(v.calib, v.recon, v.ste, v.grad, int(v.K), float(v.tau), causal, scale)
+        return cls(v.calib, v.recon, v.ste, v.grad, int(v.K), float(v.tau), causal, scale, getattr(v, "tail", "zero"))
 
 
 def make_params(cfg: Config, shape, dtype) -> Params:
     B, H, T, D = (int(x) for x in shape)
     return Params(B, H, T, D, int(bool(cfg.causal)), int(cfg.K), float(cfg.tau), float(cfg.scale),
-                  CALIB[cfg.calib], RECON[cfg.recon], STE[cfg.ste], GRAD[cfg.grad], DTYPE[dtype])
+                  CALIB[cfg.calib], RECON[cfg.recon], STE[cfg.ste], GRAD[cfg.grad], DTYPE[dtype], TAIL[cfg.tail])
 
 
 def _ptr(t):

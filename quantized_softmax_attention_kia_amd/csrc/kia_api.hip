@@ -46,6 +46,11 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
     set_err("FWM needs a finite tau > 0 (got %g)", (double)p->tau);
     return KIA_ERR_INVALID_ARG;
   }
+  if (p->tail < KIA_TAIL_ZERO || p->tail > KIA_TAIL_RESOLVED) { set_err("bad tail %d", p->tail); return KIA_ERR_INVALID_ARG; }
+  if (p->calib == KIA_CALIB_MINMAX && p->tail != KIA_TAIL_ZERO) {
+    set_err("a tail policy other than zero needs FWM (MinMax has no window)");
+    return KIA_ERR_INVALID_ARG;
+  }
   // index ranges the kernels rely on: per-head offsets in int, grid size in int
   if (p->T > (1 << 20)) { set_err("T=%lld exceeds 2^20", (long long)p->T); return KIA_ERR_UNSUPPORTED; }
   const long long heads = (long long)p->B * (long long)p->H;
@@ -58,7 +63,15 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   pr->causal = p->causal;
   pr->tau = p->tau;
   pr->scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
-  pr->calib = p->calib;
+  pr->calib = p->calib == KIA_CALIB_MINMAX ? kia::MINMAX
+              : (p->tail == KIA_TAIL_FLOOR ? kia::FWM_FLOOR : (p->tail == KIA_TAIL_RESOLVED ? kia::FWM_RES : kia::FWM));
+  // resolved grid: table levels below the window down to b <= -104, where e^b rounds to 0 in
+  // float, capped at LRES_MAX (keys below the table get their grid values computed)
+  pr->lres = 0;
+  if (pr->calib == kia::FWM_RES) {
+    const double need = std::ceil((104.0 - (double)p->tau) * (double)p->K / (double)p->tau);
+    pr->lres = need <= 0.0 ? 0 : (need >= (double)kia::LRES_MAX ? kia::LRES_MAX : (int)need);
+  }
   pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
   pr->gk = p->grad == KIA_GRAD_DETACHED ? kia::GK_DETACHED : (p->grad == KIA_GRAD_P1 ? kia::GK_P1 : kia::GK_SUMS);
   pr->keepM = p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MAX_ONLY;
@@ -152,7 +165,7 @@ kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, co
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.rec = carve(pr, rowrec);
   a.nheads = pr.nheads;
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale; a.lres = pr.lres;
   return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
 }
 
@@ -178,7 +191,7 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   a.dst = reinterpret_cast<float*>(ws + L.ws_off[1]);
   a.rowmean = reinterpret_cast<float*>(ws + L.ws_off[2]);
   a.nheads = pr.nheads;
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale; a.lres = pr.lres;
   a.keepM = pr.keepM; a.keepm = pr.keepm; a.p1 = pr.gk == kia::GK_P1;
   return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);
 }

@@ -10,7 +10,8 @@
 //           dw/dM = X - w - rho Delta and dw/dm = w - X - (1 - rho) Delta
 //           (rho = (r+t)/K, X = (r w + t e^{b_{r+1}})/K; the degenerate branch has
 //           a constant h, which drops the rho Delta part), so a + b = -sum dS_self;
-//   FWM     a = -sum_{window} gamma_j Delta_j;
+//   FWM     a = -sum_{window} gamma_j Delta_j (every key of the resolved grid of App. D.4 is in
+//           the window; a key floored onto the window edge has no slope and adds nothing);
 // a is added to the score gradient of the arg-max key(s) and b to the arg-min
 // key(s), split evenly among ties.
 //
@@ -28,8 +29,14 @@
 //               tiles, each transposed by its wave through LDS: no decisions, no row
 //               records, no atomics.
 // Both sweep their tiles while the next tile's operands are already being loaded.
+// Built once per calibration: KIA_CAL (a kia::Calib value) selects the dq kernels this build
+// supplies; the build with KIA_CAL = 0 also supplies the dkdv kernel.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
+
+#ifndef KIA_CAL
+#error "build with -DKIA_CAL=<calibration>"
+#endif
 
 namespace kia {
 
@@ -60,12 +67,13 @@ struct DqSmem {
   __align__(16) __bf16 VN[NS * BN * np<D>()];   // V rows of the key tile, bf16 slices (g = V dO^T)
   float alpha[DQ_BM], beta[DQ_BM], mean[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
-  // followed in dynamic LDS by the grid table: DQ_BM rows x (K + 3) floats
+  // followed in dynamic LDS by the grid table: MinMax DQ_BM rows x (K + 3) floats, FWM one
+  // row of lres + K + 3 floats
 };
 
-template <int D, typename TIn>
-size_t dq_smem_bytes(int K) {
-  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * DQ_BM * (K + 3);
+template <int D, int CAL, typename TIn>
+size_t dq_smem_bytes(int K, int lres) {
+  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * (CAL == MINMAX ? DQ_BM * (K + 3) : lres + K + 3);
 }
 
 // GK: GK_SUMS (full, max_only, min_only: the calibration sums, with the extremum terms that
@@ -139,8 +147,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   }
 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
-  float* trow = tbl + rl * ts;
-  for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
+  // MinMax: one table row per query row (zero for rows past T); FWM: one table for all rows, from
+  // lres levels below the window (resolved grid) to K (rows past T see no visible key)
+  float* trow;
+  if (CAL == MINMAX) {
+    trow = tbl + rl * ts;
+    for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
+  } else {
+    trow = tbl + a.lres;
+    for (int i = tid; i <= a.lres + K + 2; i += NT) tbl[i] = i <= a.lres + K ? grid_value<CAL>(M, m, K, a.tau, i - a.lres) : 0.f;
+  }
   // extra tied extrema (beyond the first index) need a second sweep to find them
   // (a MinMax row with M == m has every grid value 1: both extremum terms vanish; FWM records m = M)
   const bool flat = CAL == MINMAX && M == m;
@@ -194,7 +210,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     // half tiles (keys crow(v, g), v = 8 b .. 8 b + 7): decisions, weights and dS, then their share of
     // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g)).  A key
     // that is not visible, or in the FWM tail, takes the table's two zero entries (r = K + 1): its
-    // weight, slope, dS and calibration terms are then exactly zero.
+    // weight, slope, dS and calibration terms are then exactly zero.  A floored tail key keeps the
+    // window edge's weight and has no slope, hence no dS and no calibration term.
     const int lim = (qvalid ? (a.causal ? min(qi, T - 1) : T - 1) : -1) - k0 - 4 * g;  // crow(v, 0) <= lim
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -205,9 +222,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
       for (int j = 0; j < 8; ++j) {
         const int v = 8 * b + j;
         Decision d = decide<CAL>(s[v], rc, K, a.tau);
-        if (!(crow(v, 0) <= lim) || d.tail) d.r = K + 1;
-        const Weights wt = weights(d, trow);
-        const float Delta = (wt.E1 - wt.E0) * rc.inv_hf;
+        if (!(crow(v, 0) <= lim) || (CAL == FWM && d.tail)) d.r = K + 1;
+        const Weights wt = weights_cal<CAL>(d, trow, a.lres, K, a.tau);
+        const float Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
         const float gam = (gt[v] - Di) * invWg;
         const float dS = gam * Delta;
         ds[j] = dS;
@@ -467,6 +484,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 }
 
 // ------------------------------------------------------------------------------- launchers
+#if KIA_CAL == 0
 template <int D, typename TIn>
 static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nkt = (p.T + KV_BN - 1) / KV_BN;
@@ -474,44 +492,41 @@ static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
+hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  if (p.D == 128) return p.bf16 ? dkdv_go<128, uint16_t>(p, a, s) : dkdv_go<128, float>(p, a, s);
+  return p.bf16 ? dkdv_go<64, uint16_t>(p, a, s) : dkdv_go<64, float>(p, a, s);
+}
+#endif
 template <int D, int CAL, int MODE, int GK, typename TIn>
-static hipError_t bwd_go(const Problem& p, const BwdArgs& a, hipStream_t s, int stage) {
-  if (stage & 1) {
-    const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
-    const size_t smem = dq_smem_bytes<D, TIn>(p.K);
-    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stage & 2) return dkdv_go<D, TIn>(p, a, s);
-  return hipSuccess;
+static hipError_t dq_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
+  const size_t smem = dq_smem_bytes<D, CAL, TIn>(p.K, p.lres);
+  hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+  return hipGetLastError();
 }
 template <int D, int CAL, int MODE, int GK>
-static hipError_t bwd_dt(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
-  return p.bf16 ? bwd_go<D, CAL, MODE, GK, uint16_t>(p, a, s, st) : bwd_go<D, CAL, MODE, GK, float>(p, a, s, st);
+static hipError_t dq_dt(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  return p.bf16 ? dq_go<D, CAL, MODE, GK, uint16_t>(p, a, s) : dq_go<D, CAL, MODE, GK, float>(p, a, s);
 }
 template <int D, int CAL, int MODE>
-static hipError_t bwd_fl(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
+static hipError_t dq_gk(const Problem& p, const BwdArgs& a, hipStream_t s) {
   switch (p.gk) {
-    case GK_SUMS: return bwd_dt<D, CAL, MODE, GK_SUMS>(p, a, s, st);
-    case GK_DETACHED: return bwd_dt<D, CAL, MODE, GK_DETACHED>(p, a, s, st);
-    default: return bwd_dt<D, CAL, MODE, GK_P1>(p, a, s, st);
+    case GK_SUMS: return dq_dt<D, CAL, MODE, GK_SUMS>(p, a, s);
+    case GK_DETACHED: return dq_dt<D, CAL, MODE, GK_DETACHED>(p, a, s);
+    default: return dq_dt<D, CAL, MODE, GK_P1>(p, a, s);
   }
 }
 template <int D, int CAL>
-static hipError_t bwd_md(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
+static hipError_t dq_md(const Problem& p, const BwdArgs& a, hipStream_t s) {
   switch (p.mode) {
-    case LERP: return bwd_fl<D, CAL, LERP>(p, a, s, st);
-    case NEAREST_W: return bwd_fl<D, CAL, NEAREST_W>(p, a, s, st);
-    default: return bwd_fl<D, CAL, NEAREST_P>(p, a, s, st);
+    case LERP: return dq_gk<D, CAL, LERP>(p, a, s);
+    case NEAREST_W: return dq_gk<D, CAL, NEAREST_W>(p, a, s);
+    default: return dq_gk<D, CAL, NEAREST_P>(p, a, s);
   }
 }
-template <int D>
-static hipError_t bwd_cl(const Problem& p, const BwdArgs& a, hipStream_t s, int st) {
-  return p.calib == FWM ? bwd_md<D, FWM>(p, a, s, st) : bwd_md<D, MINMAX>(p, a, s, st);
-}
-hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s, int stages) {
-  return p.D == 128 ? bwd_cl<128>(p, a, s, stages) : bwd_cl<64>(p, a, s, stages);
+template <>
+hipError_t dq_cal<KIA_CAL>(const Problem& p, const BwdArgs& a, hipStream_t s) {
+  return p.D == 128 ? dq_md<128, KIA_CAL>(p, a, s) : dq_md<64, KIA_CAL>(p, a, s);
 }
 
 }  // namespace kia

@@ -453,7 +453,7 @@ __device__ __forceinline__ RowCal row_calibration(float M, float m, int K, float
 }
 
 // Grid value e^{b_r} (exponent and exponential in double, rounded to float):
-// MinMax b_r = (1 - r/K)(m - M); FWM b_r = -tau + r tau/K.
+// MinMax b_r = (1 - r/K)(m - M); FWM b_r = -tau + r tau/K (any integer r on the resolved grid).
 template <int CAL>
 __device__ __forceinline__ float grid_value(float M, float m, int K, float tau, int r) {
   double b;
@@ -462,18 +462,32 @@ __device__ __forceinline__ float grid_value(float M, float m, int K, float tau, 
   return (float)exp(b);
 }
 
-// Bin decision for one score: interval index r in [0, K-1], local position t in [0, 1],
-// and the FWM tail flag (z = s - M < -tau).
+// Bin decision for one score: interval index r in [0, K-1] (any r <= K-1 on the resolved FWM
+// grid), local position t in [0, 1], and the FWM tail flag (z = s - M < -tau; never set on the
+// resolved grid).
 struct Decision {
   int r;
   float t;
   bool tail;
 };
 
+// lowest interval index formed on the resolved grid: keeps the conversion to int defined (the
+// grid values there are far below the smallest float)
+constexpr int RES_RMIN = -(1 << 24);
+
 template <int CAL>
 __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, float tau) {
   Decision d;
   double u;
+  if (CAL == FWM_RES) {  // App. D.4: the grid continues below -tau, nothing is clipped below
+    const double z = (double)s - rc.origin;
+    d.tail = false;
+    u = (fmin(z, 0.0) + (double)tau) * rc.inv_h;
+    const int r = min((int)fmax(floor(u), (double)RES_RMIN), K - 1);
+    d.r = r;
+    d.t = (float)fmin(fmax(u - (double)r, 0.0), 1.0);
+    return d;
+  }
   if (CAL == MINMAX) {
     u = ((double)s - rc.origin) * rc.inv_h;
     d.tail = false;
@@ -494,10 +508,20 @@ __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, flo
 // (K + 1) interval widths, so this u is within (K + 1) 2^-22 of decide()'s: a decision whose t
 // is farther than that from 0, 1 (interior boundaries) and 1/2 (Nearest) is decide()'s, and so
 // is the FWM tail flag when |(s - M) + tau| (in float) exceeds tau 2^-21.
+// On the resolved grid |u| is not bounded by K + 1: the caller widens the margin by |r| 2^-22.
 template <int CAL>
 __device__ __forceinline__ Decision decide_fast(float s, const RowCal& rc, int K, float tau) {
   Decision d;
   float u;
+  if (CAL == FWM_RES) {
+    const float z = s - rc.origin_f;
+    d.tail = false;
+    u = (fminf(z, 0.f) + tau) * rc.inv_hf;
+    const int r = min((int)floorf(fmaxf(u, (float)RES_RMIN)), K - 1);
+    d.r = r;
+    d.t = __builtin_amdgcn_fmed3f(u - (float)r, 0.f, 1.f);
+    return d;
+  }
   if (CAL == MINMAX) {
     u = (s - rc.origin_f) * rc.inv_hf;
     d.tail = false;
@@ -522,6 +546,25 @@ __device__ __forceinline__ Weights weights(const Decision& d, const float* trow)
   Weights w;
   w.E0 = trow[d.r];
   w.E1 = trow[d.r + 1];
+  w.wL = fmaf(d.t, w.E1 - w.E0, w.E0);
+  w.wN = (d.t >= 0.5f) ? w.E1 : w.E0;
+  return w;
+}
+
+// The same for any calibration.  The FWM tables are shared by the rows (the FWM grid does not
+// depend on the row) and, on the resolved grid, start lres levels below the window: trow[r] for
+// r >= -lres.  A resolved key further below (rare: lres reaches e^{b} < 2^-149 unless K/tau is
+// large) has its grid values computed here.
+template <int CAL>
+__device__ __forceinline__ Weights weights_cal(const Decision& d, const float* trow, int lres, int K, float tau) {
+  if (CAL != FWM_RES) return weights(d, trow);
+  Weights w;
+  w.E0 = trow[max(d.r, -lres)];
+  w.E1 = trow[max(d.r + 1, -lres)];
+  if (d.r < -lres) {
+    w.E0 = grid_value<FWM_RES>(0.f, 0.f, K, tau, d.r);
+    w.E1 = grid_value<FWM_RES>(0.f, 0.f, K, tau, d.r + 1);
+  }
   w.wL = fmaf(d.t, w.E1 - w.E0, w.E0);
   w.wN = (d.t >= 0.5f) ? w.E1 : w.E0;
   return w;

@@ -14,8 +14,10 @@
 //           settled on exact scores (double products and sums, rounded once to fp32)
 //           of every candidate within twice the bound, each patched into the stored
 //           tile by the lane that stored it;
-//   then    per-row calibration and the (K+1)-entry grid table e^{b_r} in LDS
-//           (the only exponentials of the operator);
+//   then    per-row calibration and the grid table e^{b_r} in LDS (the only
+//           exponentials of the operator): K+1 entries per row under MinMax, one
+//           table for every row under FWM (from lres levels below the window on the
+//           resolved grid of App. D.4);
 //   pass 2  stored scores -> bin decision (one closer to a boundary than the
 //           bound is taken again on the exact score, patched in likewise, so every
 //           pass decides as on exact scores) -> LERP / Nearest weight from the table
@@ -25,8 +27,13 @@
 //           into a fresh accumulator before joining the running O, so the
 //           precision of O (which the backward's D_i = dO . O amplifies) does not
 //           decay with T.
+// Built once per calibration: KIA_CAL (a kia::Calib value) selects the one this build supplies.
 #include "kia_device.hpp"
 #include "kia_launch.hpp"
+
+#ifndef KIA_CAL
+#error "build with -DKIA_CAL=<calibration>"
+#endif
 
 #include <climits>
 #include <type_traits>
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     xext_combine(xM, sm.xM[v][c], true);
     if (CAL == MINMAX) xext_combine(xm, sm.xm[v][c], false);
   }
-  if (CAL == FWM) xm = xM;  // FWM: no minimum (recorded as M)
+  if (CAL != MINMAX) xm = xM;  // FWM: no minimum (recorded as M)
   const float M = xM.v, m = xm.v;
   if (w == 0 && g == 0 && qvalid) {
     const size_t row = (size_t)head * T + qi;
@@ -386,8 +393,16 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // rounding of t itself
   const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f + (float)(K + 1) * 0x1p-22f;
   const float edge = Erow + a.tau * 0x1p-21f;  // FWM window edge: margin of |(s - M) + tau|
-  float* trow = tbl + c * ts;
-  for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+  // MinMax: one table row per query row; FWM: one table for all rows, from lres levels below
+  // the window (resolved grid) to K
+  float* trow;
+  if (CAL == MINMAX) {
+    trow = tbl + c * ts;
+    for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+  } else {
+    trow = tbl + a.lres;
+    for (int i = threadIdx.x; i <= a.lres + K; i += FWD_NT) tbl[i] = grid_value<CAL>(M, m, K, a.tau, i - a.lres);
+  }
   __syncthreads();
 
   // ---- pass 2: reconstruct, normalize, multiply by V
@@ -440,14 +455,17 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
           const Decision d = decltype(check)::value ? decide_fast<CAL>(s[v], rc, K, a.tau)
                                                     : decide<CAL>(s[v], rc, K, a.tau);
           if (decltype(check)::value) {
-            // a decision within the score's error bound of a boundary must be taken on the exact score
-            bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1);
-            if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < du;
-            if (CAL == FWM) r = r || fabsf((s[v] - M) + a.tau) <= edge;
+            // a decision within the score's error bound of a boundary must be taken on the exact
+            // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid)
+            const float dur = CAL == FWM_RES ? fmaf((float)max(-d.r, 0), 0x1p-22f, du) : du;
+            bool r = (d.t < dur && (CAL == FWM_RES || d.r > 0)) || (d.t > 1.f - dur && d.r < K - 1);
+            if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < dur;
+            if (CAL == FWM || CAL == FWM_FLOOR) r = r || fabsf((s[v] - M) + a.tau) <= edge;
             risky |= (ok && r) ? (1u << j) : 0u;
           }
-          const Weights wt = weights(d, trow);
-          const bool keep = ok && !d.tail;
+          const Weights wt = weights_cal<CAL>(d, trow, a.lres, K, a.tau);
+          // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
+          const bool keep = ok && (CAL == FWM_FLOOR || !d.tail);
           const float wl = keep ? wt.wL : 0.f;
           const float wn = keep ? wt.wN : 0.f;
           tL += (double)wl;
@@ -566,9 +584,9 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   }
 }
 
-template <int D, typename TIn>
-size_t fwd_smem_bytes(int K) {
-  return sizeof(FwdSmem<D, nslices<TIn>()>) + sizeof(float) * (BN * (K + 1));
+template <int D, int CAL, typename TIn>
+size_t fwd_smem_bytes(int K, int lres) {
+  return sizeof(FwdSmem<D, nslices<TIn>()>) + sizeof(float) * (CAL == MINMAX ? BN * (K + 1) : lres + K + 1);
 }
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
@@ -595,7 +613,9 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
       uint8_t val = 255;
       if (ok) {
         const Decision d = decide<CAL>(St[v * 64 + l], rc, K, a.tau);
-        val = d.tail ? 254 : (uint8_t)(NEAREST ? d.r + (d.t >= 0.5f ? 1 : 0) : d.r);
+        const int idx = NEAREST ? d.r + (d.t >= 0.5f ? 1 : 0) : d.r;
+        // resolved grid: the index + 64, indices below -64 sharing the value 0
+        val = d.tail ? 254 : (uint8_t)(CAL == FWM_RES ? max(idx + 64, 0) : idx);
       }
       a.bins[(size_t)head * T * T + (size_t)qi * T + key] = val;
     }
@@ -606,7 +626,7 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
 template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + BN - 1) / BN;
-  const size_t smem = fwd_smem_bytes<D, TIn>(p.K);
+  const size_t smem = fwd_smem_bytes<D, CAL, TIn>(p.K, p.lres);
   hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
 }
@@ -622,12 +642,9 @@ static hipError_t fwd_md(const Problem& p, const FwdArgs& a, hipStream_t s) {
     default: return fwd_dt<D, CAL, NEAREST_P>(p, a, s);
   }
 }
-template <int D>
-static hipError_t fwd_cl(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  return p.calib == FWM ? fwd_md<D, FWM>(p, a, s) : fwd_md<D, MINMAX>(p, a, s);
-}
-hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  return p.D == 128 ? fwd_cl<128>(p, a, s) : fwd_cl<64>(p, a, s);
+template <>
+hipError_t forward_cal<KIA_CAL>(const Problem& p, const FwdArgs& a, hipStream_t s) {
+  return p.D == 128 ? fwd_md<128, KIA_CAL>(p, a, s) : fwd_md<64, KIA_CAL>(p, a, s);
 }
 
 template <int CAL, bool NEAREST>
@@ -635,9 +652,9 @@ static hipError_t bins_go(const Problem& p, const BinsArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bins_kernel<CAL, NEAREST>), dim3(p.nheads * a.rec.nt), dim3(256), 0, s, a);
   return hipGetLastError();
 }
-hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  if (p.calib == FWM) return p.mode == LERP ? bins_go<FWM, false>(p, a, s) : bins_go<FWM, true>(p, a, s);
-  return p.mode == LERP ? bins_go<MINMAX, false>(p, a, s) : bins_go<MINMAX, true>(p, a, s);
+template <>
+hipError_t bins_cal<KIA_CAL>(const Problem& p, const BinsArgs& a, hipStream_t s) {
+  return p.mode == LERP ? bins_go<KIA_CAL, false>(p, a, s) : bins_go<KIA_CAL, true>(p, a, s);
 }
 
 }  // namespace kia

@@ -1,4 +1,6 @@
-// Internal interface between the C ABI (kia_api.hip) and the kernel launchers.
+// Internal interface between the C ABI (kia_api.hip) and the kernel launchers.  The forward and
+// dq kernels are compiled once per calibration (kia_fwd.hip, kia_bwd.hip built with KIA_CAL = 0..3),
+// each build supplying that calibration's specializations declared below.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,7 +8,13 @@
 
 namespace kia {
 
-enum Calib { MINMAX = 0, FWM = 1 };
+// MinMax, and FWM under its three tail policies: keys below the window weigh 0 (FWM), sit on
+// the window edge with weight e^{-tau} and no slope (FWM_FLOOR), or stay on the grid continued
+// below -tau (FWM_RES)
+enum Calib { MINMAX = 0, FWM = 1, FWM_FLOOR = 2, FWM_RES = 3 };
+constexpr int NCALIB = 4;
+// grid levels below the window held in the FWM_RES table (lower ones are computed on the fly)
+constexpr int LRES_MAX = 1024;
 // reconstruction and surrogate: LERP; Nearest with the Weight-STE point (P^N, W^N);
 // Nearest with the Prob-STE point (P^L, W^L)
 enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2 };
@@ -39,6 +47,7 @@ struct Problem {
   int calib, mode, bf16;  // mode: LERP / NEAREST_W / NEAREST_P
   int gk;                 // GradKind
   int keepM, keepm;       // GK_SUMS: which extremum terms are injected (max_only / min_only drop one)
+  int lres;               // FWM_RES: grid levels below the window in the table (0 otherwise)
 };
 
 struct FwdArgs {
@@ -50,7 +59,8 @@ struct FwdArgs {
   RowRec rec;
   int T, K, causal;
   float tau;
-  double scale;  // score scale, applied in double to the fp64 dot products
+  double scale;  // score scale, applied in double to the exact scores
+  int lres;      // FWM_RES: grid levels below the window in the table
 };
 
 struct BwdArgs {
@@ -71,6 +81,7 @@ struct BwdArgs {
   float tau, scale;
   int keepM, keepm;  // GK_SUMS: inject the maximum's / minimum's term
   int p1;            // dkdv: subtract rowmean from the visible dS elements
+  int lres;          // FWM_RES: grid levels below the window in the table
 };
 
 struct BinsArgs {
@@ -80,9 +91,51 @@ struct BinsArgs {
   float tau;
 };
 
-hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s);
+// per-calibration launchers, one specialization per build of kia_fwd.hip / kia_bwd.hip
+template <int CAL> hipError_t forward_cal(const Problem& p, const FwdArgs& a, hipStream_t s);
+template <int CAL> hipError_t bins_cal(const Problem& p, const BinsArgs& a, hipStream_t s);
+template <int CAL> hipError_t dq_cal(const Problem& p, const BwdArgs& a, hipStream_t s);
+#define KIA_DECLARE_CAL(C)                                                                   \
+  template <> hipError_t forward_cal<C>(const Problem& p, const FwdArgs& a, hipStream_t s); \
+  template <> hipError_t bins_cal<C>(const Problem& p, const BinsArgs& a, hipStream_t s);   \
+  template <> hipError_t dq_cal<C>(const Problem& p, const BwdArgs& a, hipStream_t s);
+KIA_DECLARE_CAL(MINMAX)
+KIA_DECLARE_CAL(FWM)
+KIA_DECLARE_CAL(FWM_FLOOR)
+KIA_DECLARE_CAL(FWM_RES)
+#undef KIA_DECLARE_CAL
+// the dK, dV kernel (independent of the calibration; built with KIA_CAL = 0)
+hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s);
+
+inline hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
+  switch (p.calib) {
+    case MINMAX: return forward_cal<MINMAX>(p, a, s);
+    case FWM: return forward_cal<FWM>(p, a, s);
+    case FWM_FLOOR: return forward_cal<FWM_FLOOR>(p, a, s);
+    default: return forward_cal<FWM_RES>(p, a, s);
+  }
+}
 // stages: bit 0 = dq kernel (dQ and the P, dS tiles), bit 1 = dkdv kernel (dK, dV)
-hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s, int stages);
-hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s);
+inline hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_t s, int stages) {
+  if (stages & 1) {
+    hipError_t e;
+    switch (p.calib) {
+      case MINMAX: e = dq_cal<MINMAX>(p, a, s); break;
+      case FWM: e = dq_cal<FWM>(p, a, s); break;
+      case FWM_FLOOR: e = dq_cal<FWM_FLOOR>(p, a, s); break;
+      default: e = dq_cal<FWM_RES>(p, a, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return (stages & 2) ? launch_dkdv(p, a, s) : hipSuccess;
+}
+inline hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s) {
+  switch (p.calib) {
+    case MINMAX: return bins_cal<MINMAX>(p, a, s);
+    case FWM: return bins_cal<FWM>(p, a, s);
+    case FWM_FLOOR: return bins_cal<FWM_FLOOR>(p, a, s);
+    default: return bins_cal<FWM_RES>(p, a, s);
+  }
+}
 
 }  // namespace kia

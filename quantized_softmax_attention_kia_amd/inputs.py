@@ -69,11 +69,14 @@ class Variant:
     grad: str           # "full" | "detached"
     K: int
     tau: float = 8.0
+    tail: str = "zero"  # FWM tail policy: "zero" | "floor" | "resolved"
 
     @property
     def name(self) -> str:
         ste = "" if self.recon == "lerp" else f"-{self.ste}"
         cal = "minmax" if self.calib == "minmax" else f"fwm{self.tau:g}"
+        if self.tail != "zero":
+            cal += f"-{self.tail}"
         return f"{cal}-{self.recon}{ste}-K{self.K}-{self.grad}"
 
 

@@ -59,6 +59,9 @@ def test_workspace_layout(kb):
     assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
     st, rr, w = ws(kb, params(kb, causal=0))
     assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096 and w == 2 * 2 * 3 * nt * nt * 4096 + rnd(N * 4)
+    for tail in range(3):   # every FWM tail policy has the same layout
+        st, rr2, w2 = ws(kb, params(kb, calib=1, tail=tail))
+        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4)
     for grad in range(5):   # every gradient mode has the same layout
         st, rr2, w2 = ws(kb, params(kb, grad=grad))
         assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4)
@@ -71,6 +74,7 @@ def test_workspace_layout(kb):
     (dict(calib=1, tau=0.0), -1), (dict(calib=1, tau=float("nan")), -1), (dict(calib=2), -1),
     (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=5), -1), (dict(grad=-1), -1), (dict(dtype=7), -1),
     (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1),
+    (dict(tail=1), -1), (dict(tail=2), -1), (dict(calib=1, tail=3), -1), (dict(calib=1, tail=-1), -1),
 ])
 def test_rejects_bad_params(kb, bad, status):
     p = params(kb, **bad)

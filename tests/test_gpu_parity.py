@@ -22,6 +22,9 @@ VARIANTS16 = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest
 # the range_grad ablations: single-channel (max_only, min_only) and the P1 projection
 ABLATIONS = [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
              ("nearest", "prob")) for g in ("max_only", "min_only", "p1")]
+# the FWM tail policies (floored and resolved tails), as (calib, recon, ste, grad, tail)
+TAILS = [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
+         ("nearest", "prob")) for g in ("full", "detached", "p1")]
 
 
 @pytest.fixture(scope="module")
@@ -37,10 +40,15 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _tail(variant):
+    """variant: (calib, recon, ste, grad, K, tau[, tail])"""
+    return variant[6] if len(variant) > 6 else "zero"
+
+
 def gpu_run(kb, variant, q, k, v, do, *, causal=True, scale=0.0, dtype="f32"):
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    cfg = kb.Config(*variant[:4], K=variant[4], tau=variant[5], causal=causal, scale=scale)
+    cfg = kb.Config(*variant[:4], K=variant[4], tau=variant[5], causal=causal, scale=scale, tail=_tail(variant))
     qt, kt, vt, dot = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(tdt) for x in (q, k, v, do))
     o, rowrec, p = kb.forward(cfg, qt, kt, vt)
     dq, dk, dv = kb.backward(p, qt, kt, vt, o, dot, rowrec)
@@ -50,7 +58,7 @@ def gpu_run(kb, variant, q, k, v, do, *, causal=True, scale=0.0, dtype="f32"):
 
 
 def ocfg(variant):
-    return ORC.OracleConfig(*variant[:4], K=variant[4], tau=variant[5])
+    return ORC.OracleConfig(*variant[:4], K=variant[4], tau=variant[5], tail=_tail(variant))
 
 
 def compare_all_heads(variant, q, k, v, do, got, *, causal=True, scale=None):
@@ -109,15 +117,45 @@ def test_small_ablations(kb, variant, shape):
     say("   ", rep)
 
 
-@pytest.mark.parametrize("variant", [("minmax", "lerp"), ("minmax", "nearest"), ("fwm", "lerp"), ("fwm", "nearest")],
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n") + s[6])
+@pytest.mark.parametrize("variant", TAILS, ids=lambda v: "-".join(v))
+def test_small_tail_policies(kb, variant, shape):
+    """Floored and resolved FWM tails: tau = 3 at score std 2 puts many keys below the window."""
+    B, H, T, D, causal, seed, dtype = shape
+    q, k, v, do = make_inputs(B, H, T, D, seed, dtype=dtype, q_scale=2.0)
+    full = variant[:4] + (8, 3.0, variant[4])
+    say(f"[tail] {shape} {full}")
+    got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
+    rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
+    say("   ", rep)
+
+
+@pytest.mark.parametrize("K,tau", [(4, 6.0), (16, 2.0), (64, 1.0)])
+@pytest.mark.parametrize("recon,ste", [("lerp", "prob"), ("nearest", "weight")])
+def test_resolved_grid_depth(kb, recon, ste, K, tau):
+    """Resolved grid far below the window: tau = 1, K = 64 needs more levels than the table holds
+    (103 K / tau > 1024), so keys deeper than the table take the computed grid values."""
+    B, H, T, D, seed = 1, 2, 130, 64, 61
+    q, k, v, do = make_inputs(B, H, T, D, seed, q_scale=6.0)
+    full = ("fwm", recon, ste, "full", K, tau, "resolved")
+    say(f"[resolved depth] {B}x{H}x{T}x{D} seed={seed} {full}")
+    got, _ = gpu_run(kb, full, q, k, v, do)
+    rep = compare_all_heads(full, q, k, v, do, got)
+    say("   ", rep)
+
+
+@pytest.mark.parametrize("variant", [("minmax", "lerp"), ("minmax", "nearest"), ("fwm", "lerp"), ("fwm", "nearest"),
+                                     ("fwm", "lerp", "floor"), ("fwm", "nearest", "floor"),
+                                     ("fwm", "lerp", "resolved"), ("fwm", "nearest", "resolved")],
                          ids=lambda v: "-".join(v))
 @pytest.mark.parametrize("K", [1, 4, 16, 64])
 def test_bins_bitexact(kb, variant, K):
     import torch
     q, k, v, do = make_inputs(1, 2, 150, 64, 21, q_scale=3.0)
-    full = (variant[0], variant[1], "prob", "full", K, 3.0)
+    tail = variant[2] if len(variant) > 2 else "zero"
+    full = (variant[0], variant[1], "prob", "full", K, 3.0, tail)
     say(f"[bins] 1x2x150x64 seed=21 {full}")
-    cfg = kb.Config(*full[:4], K=K, tau=3.0)
+    cfg = kb.Config(*full[:4], K=K, tau=3.0, tail=tail)
     qt, kt, vt = (torch.from_numpy(x).cuda() for x in (q, k, v))
     o, rowrec, p = kb.forward(cfg, qt, kt, vt)
     bins = kb.debug_bins(p, rowrec)

@@ -47,7 +47,8 @@ def run(kb, wl, var, q, k, v, do, detach=False):
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     cfg = kb.Config.of(var)
     if detach:
-        cfg = kb.Config(cfg.calib, cfg.recon, cfg.ste, "detached", cfg.K, cfg.tau, cfg.causal, cfg.scale)
+        import dataclasses
+        cfg = dataclasses.replace(cfg, grad="detached")
     qt, kt, vt, dot = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v, do))
     o, rowrec, p = kb.forward(cfg, qt, kt, vt)
     dq, dk, dv = kb.backward(p, qt, kt, vt, o, dot, rowrec)
@@ -100,6 +101,29 @@ def test_gpt2_ablations_sampled_heads(kb, grad):
         ratio = (dk.sum(dim=2).abs() / dk.abs().sum(dim=2).clamp_min(1e-30)).max().item()
         say(f"    max_h |sum_j dK_j| / sum_j |dK_j| = {ratio:.2e}")
         assert ratio < 1e-4, ratio
+
+
+@pytest.mark.parametrize("tail", ["floor", "resolved"])
+@pytest.mark.parametrize("ste", ["weight", "prob"])
+def test_wide_tail_policies_sampled_heads(kb, tail, ste):
+    """The tail-policy runs of the pages (hard Nearest, K = 4, tau = 6, both surrogates) on the
+    wide-span inputs, where many keys fall below the window: sampled heads against the oracle,
+    and the full gradient's dK sums to zero over each head's keys."""
+    from quantized_softmax_attention_kia_amd.inputs import Variant
+    wl = WORKLOADS["wide"]
+    var = Variant("fwm", "nearest", ste, "full", 4, 6.0, tail)
+    q, k, v, do = inputs("wide")
+    say(f"[wide tail] B={wl.B} H={wl.H} T={wl.T} D={wl.D} seed={wl.seed} {var.name}")
+    got = run(kb, wl, var, q, k, v, do)
+    cfg = ORC.OracleConfig.of(var)
+    for b, h in parity.pick_heads(cfg, q, k, want=2):
+        gh = {key: got[key][b, h].cpu().numpy().astype(np.float64) for key in ("O", "dQ", "dK", "dV")}
+        rep = parity.check_head(cfg, q[b, h], k[b, h], v[b, h], do[b, h], gh)
+        say(f"    head ({b},{h}): {rep}")
+    dk = got["dK"].double()
+    ratio = (dk.sum(dim=2).abs() / dk.abs().sum(dim=2).clamp_min(1e-30)).max().item()
+    say(f"    max_h |sum_j dK_j| / sum_j |dK_j| = {ratio:.2e}")
+    assert ratio < 1e-4, ratio
 
 
 def test_full_and_detached_forward_bitwise_identical(kb):
