@@ -38,7 +38,7 @@
  *    max_only is the full gradient and its min_only the detached one.
  *  - P1: the detached score gradient minus its mean over the row's visible
  *    (causal) keys, tail keys included, so every row sums to zero.
- *  - FWM tail policies (App. D "Definition and experiment", App. C.3 stages):
+ *  - FWM tail policies (App. C.3 tau-selection stages, App. D.4 tail policy):
  *    zero (the paper's FWM: w = 0 below the window); floor (z <- -tau: a key
  *    below the window weighs e^{b_0} and, its score clamped, has no gradient);
  *    resolved (the grid b_r = -tau + r h continued below -tau, r unbounded

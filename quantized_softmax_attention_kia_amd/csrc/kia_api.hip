@@ -68,9 +68,11 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   // resolved grid: table levels below the window down to b <= -104, where e^b rounds to 0 in
   // float, capped at LRES_MAX (keys below the table get their grid values computed)
   pr->lres = 0;
+  pr->res_far = 0;
   if (pr->calib == kia::FWM_RES) {
     const double need = std::ceil((104.0 - (double)p->tau) * (double)p->K / (double)p->tau);
     pr->lres = need <= 0.0 ? 0 : (need >= (double)kia::LRES_MAX ? kia::LRES_MAX : (int)need);
+    pr->res_far = need > (double)kia::LRES_MAX;
   }
   pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
   pr->gk = p->grad == KIA_GRAD_DETACHED ? kia::GK_DETACHED : (p->grad == KIA_GRAD_P1 ? kia::GK_P1 : kia::GK_SUMS);
@@ -165,7 +167,7 @@ kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, co
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.rec = carve(pr, rowrec);
   a.nheads = pr.nheads;
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale; a.lres = pr.lres;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale; a.lres = pr.lres; a.res_far = pr.res_far;
   return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
 }
 
@@ -191,7 +193,7 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   a.dst = reinterpret_cast<float*>(ws + L.ws_off[1]);
   a.rowmean = reinterpret_cast<float*>(ws + L.ws_off[2]);
   a.nheads = pr.nheads;
-  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale; a.lres = pr.lres;
+  a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale; a.lres = pr.lres; a.res_far = pr.res_far;
   a.keepM = pr.keepM; a.keepm = pr.keepm; a.p1 = pr.gk == kia::GK_P1;
   return hip_status(kia::launch_backward(pr, a, static_cast<hipStream_t>(stream), stages), name);
 }

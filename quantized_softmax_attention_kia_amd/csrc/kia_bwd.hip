@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         const int v = 8 * b + j;
         Decision d = decide<CAL>(s[v], rc, K, a.tau);
         if (!(crow(v, 0) <= lim) || (CAL == FWM && d.tail)) d.r = K + 1;
-        const Weights wt = weights_cal<CAL>(d, trow, a.lres, K, a.tau);
+        const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
         const float Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
         const float gam = (gt[v] - Di) * invWg;
         const float dS = gam * Delta;

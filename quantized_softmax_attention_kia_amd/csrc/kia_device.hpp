@@ -553,15 +553,17 @@ __device__ __forceinline__ Weights weights(const Decision& d, const float* trow)
 
 // The same for any calibration.  The FWM tables are shared by the rows (the FWM grid does not
 // depend on the row) and, on the resolved grid, start lres levels below the window: trow[r] for
-// r >= -lres.  A resolved key further below (rare: lres reaches e^{b} < 2^-149 unless K/tau is
-// large) has its grid values computed here.
+// r >= -lres.  When the table reaches b <= -104, where e^b rounds to 0 in float, a key further
+// below reads that zero entry; otherwise (far: the level cap was hit, K/tau large) such a key has
+// its grid values computed here.
 template <int CAL>
-__device__ __forceinline__ Weights weights_cal(const Decision& d, const float* trow, int lres, int K, float tau) {
+__device__ __forceinline__ Weights weights_cal(const Decision& d, const float* trow, int lres, bool far, int K,
+                                               float tau) {
   if (CAL != FWM_RES) return weights(d, trow);
   Weights w;
   w.E0 = trow[max(d.r, -lres)];
   w.E1 = trow[max(d.r + 1, -lres)];
-  if (d.r < -lres) {
+  if (far && d.r < -lres) {
     w.E0 = grid_value<FWM_RES>(0.f, 0.f, K, tau, d.r);
     w.E1 = grid_value<FWM_RES>(0.f, 0.f, K, tau, d.r + 1);
   }

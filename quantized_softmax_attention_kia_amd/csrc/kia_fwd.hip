@@ -463,7 +463,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
             if (CAL == FWM || CAL == FWM_FLOOR) r = r || fabsf((s[v] - M) + a.tau) <= edge;
             risky |= (ok && r) ? (1u << j) : 0u;
           }
-          const Weights wt = weights_cal<CAL>(d, trow, a.lres, K, a.tau);
+          const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
           // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
           const bool keep = ok && (CAL == FWM_FLOOR || !d.tail);
           const float wl = keep ? wt.wL : 0.f;

@@ -48,6 +48,7 @@ struct Problem {
   int gk;                 // GradKind
   int keepM, keepm;       // GK_SUMS: which extremum terms are injected (max_only / min_only drop one)
   int lres;               // FWM_RES: grid levels below the window in the table (0 otherwise)
+  int res_far;            // FWM_RES: the table stops above b = -104 (lres hit LRES_MAX)
 };
 
 struct FwdArgs {
@@ -61,6 +62,7 @@ struct FwdArgs {
   float tau;
   double scale;  // score scale, applied in double to the exact scores
   int lres;      // FWM_RES: grid levels below the window in the table
+  int res_far;   // FWM_RES: keys below the table need computed grid values
 };
 
 struct BwdArgs {
@@ -82,6 +84,7 @@ struct BwdArgs {
   int keepM, keepm;  // GK_SUMS: inject the maximum's / minimum's term
   int p1;            // dkdv: subtract rowmean from the visible dS elements
   int lres;          // FWM_RES: grid levels below the window in the table
+  int res_far;       // FWM_RES: keys below the table need computed grid values
 };
 
 struct BinsArgs {

@@ -17,7 +17,7 @@ detach only the other extremum (the single-channel ablation of App. I); "p1"
 is the detached gradient with a hook on the scores that projects each row's
 gradient onto the zero-sum subspace over its visible keys (App. B "Detach").
 
-FWM tail policies (App. D, App. C.3): "zero" drops keys below the window;
+FWM tail policies (App. C.3, App. D.4): "zero" drops keys below the window;
 "floor" clamps z at -tau, so such a key weighs e^{-tau} and torch's clamp gives
 it no gradient; "resolved" continues the grid b_q = -tau + q h to every integer
 q below the window, with the grid value computed as exp(b_q) for any q.

@@ -16,12 +16,12 @@ and raises AssertionError when the oracle disagrees with:
   * shift invariance of the output (and of dQ for the full gradient);
   * degenerate rows, causal row 0, V = 1, tied extrema, K = 1 affine LERP;
   * the hand-derived fixtures in tests/golden/;
-  * for the FWM tail policies (App. D, App. C.3): floored tail keys weigh e^{-tau}
+  * for the FWM tail policies (App. C.3, App. D.4): floored tail keys weigh e^{-tau}
     and carry no gradient, moving them deeper changes nothing; the resolved grid
     keeps every key within the chord and nearest-centre bounds of e^z and
     converges to softmax as h -> 0 even with a narrow window.
 Source: "Pretraining Transformers with Quantized Softmax in Attention", §3,
-§5.1, App. A, App. B, App. C.2, App. C.3, App. D.
+§5.1, App. A, App. B, App. C.2, App. C.3, App. D.4.
 """
 from __future__ import annotations
 
@@ -40,7 +40,8 @@ VARIANTS = [(c, r, s, g) for c in ("minmax", "fwm") for r in ("lerp", "nearest")
 # the range_grad ablations (App. I single-channel modes, App. B P1 projection)
 VARIANTS += [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
              ("nearest", "prob")) for g in ("max_only", "min_only", "p1")]
-# the FWM tail policies (App. D tau-floor variant, App. C.3 resolved grid)
+# the FWM tail policies (App. D.4: the tau-floor variant, also the floor tail of the App. C.3
+# tau-selection stages, and the resolved grid)
 VARIANTS += [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("lerp", "prob"),
              ("nearest", "weight"), ("nearest", "prob")) for g in ("full", "detached")]
 
