@@ -44,7 +44,7 @@ ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C, OpenMP, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        tmp = _LIB_PATH + ".tmp"
+        tmp = f"{_LIB_PATH}.{os.getpid()}.tmp"   # one per process: concurrent builds do not collide
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
