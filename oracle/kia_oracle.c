@@ -69,12 +69,13 @@
 #endif
 
 enum { KO_MINMAX = 0, KO_FWM = 1 };
-enum { KO_LERP = 0, KO_NEAREST = 1 };
+/* reconstructions; SOFTMAX, EXP_BF16 and EXP_FP8 are the exponential baselines (no grid) */
+enum { KO_LERP = 0, KO_NEAREST = 1, KO_SOFTMAX = 2, KO_EXP_BF16 = 3, KO_EXP_FP8 = 4 };
 enum { KO_WEIGHT_STE = 0, KO_PROB_STE = 1 };
 enum { KO_FULL = 0, KO_DETACHED = 1, KO_MAX_ONLY = 2, KO_MIN_ONLY = 3, KO_P1 = 4 };
 enum { KO_TAIL_ZERO = 0, KO_TAIL_FLOOR = 1, KO_TAIL_RESOLVED = 2 };
 
-enum { FLIP_INTERVAL = 1, FLIP_NEAREST = 2, FLIP_TAIL = 4 };
+enum { FLIP_INTERVAL = 1, FLIP_NEAREST = 2, FLIP_TAIL = 4, FLIP_ROUND = 8, FLIP_ROUND2 = 16 };
 
 enum {
   MUT_NONE = 0,
@@ -99,7 +100,10 @@ enum {
   MUT_ONLY_SWAPPED = 19,    /* max_only keeps the m channel, min_only the M channel */
   MUT_P1_SKIP_TAIL = 20,    /* P1 shifts only the keys inside the FWM window */
   MUT_FLOOR_TAIL_SLOPE = 21, /* floored tail keys keep the slope of the first interval */
-  MUT_RESOLVED_GRID_CLAMP = 22 /* the resolved grid reads the table's end values below the window */
+  MUT_RESOLVED_GRID_CLAMP = 22, /* the resolved grid reads the table's end values below the window */
+  MUT_FP8_TRUNCATES = 23,   /* FP8-rounded exp rounds toward zero */
+  MUT_BF16_GRAD_UNROUNDED = 24, /* BF16-exp backward keeps the fp32 gradient (no bf16 casts) */
+  MUT_FP8_DELTA_ROUNDED = 25  /* FP8-rounded exp backward uses the rounded weight as derivative */
 };
 
 typedef struct {
@@ -147,6 +151,201 @@ static void flag_push(ko_flags_t *f, int row, int key, int kind, double dist) {
   }
 }
 
+/* ---------------------------------------------------------------- exponential baselines
+ * App. B "Softmax" and App. D.5 "Definitions".  Every weight is an exponential of the
+ * row-max-shifted score z = s - M; no grid, no K, no tau:
+ *  - SOFTMAX: w = e^z, the exact derivative dw/dz = w.
+ *  - EXP_BF16: z rounded to bfloat16, the exponential of that value rounded to bfloat16
+ *    (the input rounded before exponentiation, the output after), returned to full
+ *    precision for the normalization.  The backward is the chain rule through the casts
+ *    (a cast passes the gradient, converted to the tensor's format), with the tensors in
+ *    their formats: dL/dw rounded to bfloat16 where it enters the bfloat16 output, times
+ *    the bfloat16 weight (the exponential's derivative is its value), rounded to bfloat16.
+ *  - EXP_FP8: w = e^z rounded to E4M3 (4 exponent bits, bias 7, 3 significand bits,
+ *    subnormals, no infinities), with the identity as the rounding step's derivative, so
+ *    dw/dz = e^z (the unrounded exponential), and the normalization Jacobian at the
+ *    rounded weights.
+ * The row maximum stays on the gradient path in all three: its term -sum_j dL/dz_j goes
+ * to the arg-max key(s), split evenly among ties (it vanishes for SOFTMAX in exact
+ * arithmetic).  There is no minimum term, so max_only is full and min_only detached, as
+ * for FWM.
+ * Readings: roundings are to nearest, ties to even, on the exact value (the exponential
+ * of the rounded bfloat16 input, correctly rounded to bfloat16; e^z correctly rounded to
+ * E4M3).
+ */
+
+/* Round x >= 0 to a binary format with mb stored significand bits and smallest normal
+   exponent emin (subnormals below it): nearest, ties to even.  *pos is x in units of the
+   format's spacing at x (rounding midpoints at pos = k + 1/2); *lo, *hi its two neighbours. */
+static double round_fmt(double x, int mb, int emin, int truncate, double *pos, double *lo, double *hi) {
+  if (x == 0.0) { *pos = 0.0; *lo = *hi = 0.0; return 0.0; }
+  int e;
+  (void)frexp(x, &e);               /* x in [2^(e-1), 2^e) */
+  int E = e - 1 < emin ? emin : e - 1;
+  const double ulp = ldexp(1.0, E - mb);
+  const double q = x / ulp;         /* exact: a power-of-two scaling */
+  const double fl = floor(q);
+  *pos = q; *lo = fl * ulp; *hi = (fl + 1.0) * ulp;
+  return (truncate ? fl : rint(q)) * ulp;   /* rint: nearest, ties to even */
+}
+static double round_signed(double x, int mb, int emin, double *pos, double *alt) {
+  double lo, hi, pq;
+  const double r = round_fmt(fabs(x), mb, emin, 0, &pq, &lo, &hi);
+  if (pos) *pos = pq;
+  if (alt) *alt = copysign(r == lo ? hi : lo, x);
+  return copysign(r, x);
+}
+#define BF16_MB 7
+#define BF16_EMIN (-126)
+#define E4M3_MB 3
+#define E4M3_EMIN (-6)
+
+/* E4M3 byte of a value in [0, 1] that the format represents */
+static int e4m3_code(double w) {
+  if (w <= 0.0) return 0;
+  if (w < ldexp(1.0, E4M3_EMIN)) return (int)(w / ldexp(1.0, E4M3_EMIN - E4M3_MB));   /* subnormal */
+  int e;
+  double f = frexp(w, &e);          /* w = f 2^e, f in [0.5, 1) */
+  const int E = e - 1;              /* w = (1 + m/8) 2^E */
+  const int mant = (int)((2.0 * f - 1.0) * 8.0);
+  return ((E + 7) << 3) | mant;
+}
+/* low byte of the bfloat16 encoding of a value the format represents */
+static int bf16_low_byte(double w) {
+  const float f = (float)w;         /* exact: bfloat16 values are floats */
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  return (int)((b >> 16) & 0xFF);
+}
+
+static void ko_row_exp(const ko_cfg_t *cfg, int n, const double *s, const double *g, const double *gabs,
+                       const uint8_t *flip, double *P, double *dS, double *PL_out,
+                       double *z_out, int32_t *r_out, double *t_out, int32_t *code_out, uint8_t *tail_out,
+                       double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags,
+                       const double *eb, double *amb) {
+  const int mode = cfg->recon, mut = cfg->mutation;
+  double *w = (double *)malloc(sizeof(double) * n);
+  double *de = (double *)malloc(sizeof(double) * n);   /* dw/dz (SOFTMAX, EXP_FP8) */
+  int32_t *code = (int32_t *)malloc(sizeof(int32_t) * n);
+  double M = -INFINITY, m = INFINITY;
+  for (int j = 0; j < n; ++j) {
+    if (s[j] > M) M = s[j];
+    if (s[j] < m) m = s[j];
+  }
+  int amax = -1, amin = -1, nA = 0, nC = 0, ibelowM = -1, iabovem = -1;
+  double belowM = -INFINITY, abovem = INFINITY;
+  for (int j = 0; j < n; ++j) {
+    if (s[j] == M) { if (amax < 0) amax = j; nA++; } else if (s[j] > belowM) { belowM = s[j]; ibelowM = j; }
+    if (s[j] == m) { if (amin < 0) amin = j; nC++; } else if (s[j] < abovem) { abovem = s[j]; iabovem = j; }
+  }
+  const double ebM = eb ? eb[amax] : 0.0, ebm = eb ? eb[amin] : 0.0;
+
+  /* --- forward: the weights --- */
+  for (int j = 0; j < n; ++j) {
+    const double z = s[j] - M;
+    const int kid = key_id ? key_id[j] : j;
+    const uint8_t fl = flip ? flip[j] : 0;
+    const double ez = eb ? eb[j] + ebM : 0.0;      /* how far fp32 scores can move z */
+    code[j] = 0;
+    if (mode == KO_SOFTMAX) {
+      w[j] = exp(z);
+      de[j] = w[j];
+    } else if (mode == KO_EXP_FP8) {
+      double pos, lo, hi;
+      const double we = exp(z);
+      double r = round_fmt(we, E4M3_MB, E4M3_EMIN, mut == MUT_FP8_TRUNCATES, &pos, &lo, &hi);
+      const double dist = fabs(pos - floor(pos) - 0.5);
+      if (flags && dist < fmax(flags->guard, pos * ez)) flag_push(flags, row_id, kid, FLIP_ROUND, dist);
+      if (fl & FLIP_ROUND) r = (r == lo) ? hi : lo;
+      w[j] = r;
+      de[j] = mut == MUT_FP8_DELTA_ROUNDED ? r : we;
+      code[j] = e4m3_code(r);
+    } else {                                      /* EXP_BF16 */
+      double pos, alt;
+      double zb = round_signed(z, BF16_MB, BF16_EMIN, &pos, &alt);
+      double dist = fabs(pos - floor(pos) - 0.5);
+      if (flags && z != 0.0 && dist < fmax(flags->guard, pos * ez / fabs(z)))
+        flag_push(flags, row_id, kid, FLIP_ROUND, dist);
+      if (fl & FLIP_ROUND) zb = alt;
+      double wb = round_signed(exp(zb), BF16_MB, BF16_EMIN, &pos, &alt);
+      dist = fabs(pos - floor(pos) - 0.5);
+      if (flags && dist < flags->guard) flag_push(flags, row_id, kid, FLIP_ROUND2, dist);
+      if (fl & FLIP_ROUND2) wb = alt;
+      w[j] = wb;
+      de[j] = wb;
+      code[j] = bf16_low_byte(wb);
+    }
+  }
+  double W = 0.0;
+  for (int j = 0; j < n; ++j) W += w[j];
+  for (int j = 0; j < n; ++j) {
+    P[j] = w[j] / W;
+    if (PL_out) PL_out[j] = P[j];
+  }
+
+  /* --- backward --- */
+  double a = 0.0, Dsum = 0.0;
+  if (g) {
+    for (int j = 0; j < n; ++j) Dsum += P[j] * g[j];
+    double gmax = 0.0;
+    for (int j = 0; j < n; ++j) gmax = fmax(gmax, gabs ? gabs[j] : fabs(g[j]));
+    double amb_sum = 0.0;
+    for (int j = 0; j < n; ++j) {
+      const double gam = (g[j] - Dsum) / W;     /* dL/dw_j (App. B normalization Jacobian) */
+      if (amb) amb[j] = 0.0;
+      if (mode != KO_EXP_BF16 || mut == MUT_BF16_GRAD_UNROUNDED) {
+        dS[j] = gam * de[j];
+        continue;
+      }
+      double pos, alt;
+      const double gb = round_signed(gam, BF16_MB, BF16_EMIN, &pos, &alt);   /* into the bf16 output */
+      dS[j] = round_signed(gb * w[j], BF16_MB, BF16_EMIN, NULL, NULL);       /* exp's backward, in bf16 */
+      if (amb) {
+        /* a gradient computed in fp32 rounds the other way when it lies within its own error of a
+           rounding midpoint: the change that would make, for the tolerance of a comparison */
+        double lo, hi, pq;
+        (void)round_fmt(fabs(gam), BF16_MB, BF16_EMIN, 0, &pq, &lo, &hi);
+        const double ulp = hi - lo;
+        const double band = 1e-5 * ((gabs ? gabs[j] : fabs(g[j])) + gmax) / W;
+        if (fabs(pq - floor(pq) - 0.5) * ulp < band)
+          amb[j] = fabs(round_signed(alt * w[j], BF16_MB, BF16_EMIN, NULL, NULL) - dS[j]);
+        amb_sum += amb[j];
+      }
+    }
+    const int keepM = cfg->grad == KO_FULL || cfg->grad == KO_MAX_ONLY;
+    if (keepM) {
+      for (int j = 0; j < n; ++j) a -= dS[j];   /* the row maximum's term: z = s - M */
+      for (int j = 0; j < n; ++j)
+        if (s[j] == M) {
+          dS[j] += a / nA;
+          if (amb) amb[j] += amb_sum / nA;
+        }
+    }
+    if (cfg->grad == KO_P1) {
+      double sum = 0.0;
+      for (int j = 0; j < n; ++j) sum += dS[j];
+      for (int j = 0; j < n; ++j) {
+        dS[j] -= sum / n;
+        if (amb) amb[j] += amb_sum / n;
+      }
+    }
+  }
+  if (z_out) for (int j = 0; j < n; ++j) {
+    z_out[j] = s[j] - M; r_out[j] = 0; t_out[j] = 0.0; code_out[j] = code[j]; tail_out[j] = 0;
+  }
+  if (rowd) {
+    rowd[RD_M] = M; rowd[RD_m] = m; rowd[RD_h] = 0.0; rowd[RD_WL] = W; rowd[RD_WN] = W;
+    rowd[RD_a] = a; rowd[RD_b] = 0.0; rowd[RD_gapM] = M - belowM; rowd[RD_gapm] = abovem - m; rowd[RD_D] = Dsum;
+    rowd[RD_tolM] = eb ? ebM + (ibelowM >= 0 ? eb[ibelowM] : 0.0) : 0.0;
+    rowd[RD_tolm] = eb ? ebm + (iabovem >= 0 ? eb[iabovem] : 0.0) : 0.0;
+  }
+  if (rowi) {
+    rowi[RI_amax] = amax; rowi[RI_amin] = amin; rowi[RI_nA] = nA; rowi[RI_nC] = nC; rowi[RI_degenerate] = 0;
+    rowi[RI_amax2] = ibelowM; rowi[RI_amin2] = iabovem;
+  }
+  free(w); free(de); free(code);
+}
+
 /*
  * One attention row.  s[0..n) are the scaled scores of the row's visible keys,
  * g[0..n) the upstream gradient dL/dP_j (may be NULL: forward only).
@@ -157,7 +356,12 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
                         const uint8_t *flip, double *P, double *dS, double *PL_out,
                         double *u_out, int32_t *r_out, double *t_out, int32_t *ell_out, uint8_t *tail_out,
                         double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags,
-                        const double *eb) {
+                        const double *eb, const double *gabs, double *amb) {
+  if (cfg->recon >= KO_SOFTMAX) {
+    ko_row_exp(cfg, n, s, g, gabs, flip, P, dS, PL_out, u_out, r_out, t_out, ell_out, tail_out, rowd, rowi,
+               row_id, key_id, flags, eb, amb);
+    return;
+  }
   const int K = cfg->K;
   const int mut = cfg->mutation;
   const int tailp = cfg->calib == KO_FWM ? cfg->tail : KO_TAIL_ZERO;
@@ -389,7 +593,7 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
   if (cfg->calib == KO_FWM && !(cfg->tau > 0.0)) return -1;
   if (cfg->tail < KO_TAIL_ZERO || cfg->tail > KO_TAIL_RESOLVED || (cfg->calib == KO_MINMAX && cfg->tail != 0)) return -1;
   if (u && !(r && t && ell && tail)) return -1;
-  ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL, NULL);
+  ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL, NULL, NULL, NULL);
   return 0;
 }
 
@@ -406,13 +610,18 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
  * absout: optional [4, T, D]: the same sums with every term replaced by its absolute
  * value (sum_j P|V|, scale sum_j |dS||K|, scale sum_i |dS||Q|, sum_i P|dO|), the
  * scale against which cancellation in an output element is judged.
+ * ambout: optional [2, T, D] (EXP_BF16 only, else zeros): scale sum_j A_ij |K_j| and
+ * scale sum_i A_ij |Q_i|, where A_ij is how much dS_ij changes if its bfloat16 gradient
+ * rounding goes the other way at a position where a gradient computed in fp32 may do so.
+ * Exponential baselines: bins holds the E4M3 byte of the weight (EXP_FP8), the low byte
+ * of the bfloat16 weight (EXP_BF16) or 0 (SOFTMAX) for visible keys.
  */
 int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
             const double *Q, const double *Kt, const double *V, const double *dO,
             double *O, double *dQ, double *dK, double *dV, double *rowd, int32_t *rowi,
             int64_t nflip, const int32_t *flips,
             double guard, int64_t flag_cap, int32_t *flag_pos, double *flag_dist, int64_t *nflags,
-            uint8_t *bins, const uint8_t *row_mask, double *absout, int nthreads) {
+            uint8_t *bins, const uint8_t *row_mask, double *absout, double *ambout, int nthreads) {
   if (!cfg || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
   if (dO && !(dQ && dK && dV)) return -1;
   if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
@@ -445,6 +654,12 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
     }
   }
   if (absout) memset(absout, 0, sizeof(double) * 4 * (size_t)T * D);
+  double *ambK = NULL;
+  if (ambout) memset(ambout, 0, sizeof(double) * 2 * (size_t)T * D);
+  if (ambout && dO) {
+    ambK = (double *)calloc((size_t)nthreads * T * D, sizeof(double));
+    if (!ambK) { free(accK); free(accV); free(absK); free(absV); return -2; }
+  }
   const double dq_scale = (mut == MUT_DQ_NO_SCALE) ? 1.0 : scale;
 
 #ifdef _OPENMP
@@ -464,6 +679,8 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
     double *dS = dO ? (double *)malloc(sizeof(double) * n) : NULL;
     int32_t *kid = (int32_t *)malloc(sizeof(int32_t) * n);
     double *eb = (double *)malloc(sizeof(double) * n);
+    double *gabs = dO ? (double *)malloc(sizeof(double) * n) : NULL;
+    double *amb = (dO && ambout) ? (double *)calloc(n, sizeof(double)) : NULL;
     uint8_t *flip = NULL;
     for (int j = 0; j < n; ++j) {
       kid[j] = j;
@@ -476,9 +693,13 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
       /* one fp32 ulp of the score, 2^-23 |s|, plus the double accumulation's own bound */
       eb[j] = 1.1920928955078125e-07 * fabs(s[j]) + 1e-15 * fabs(scale) * aabs;
       if (dO) {
-        double ga = 0.0;
-        for (int k = 0; k < D; ++k) ga += dO[(size_t)i * D + k] * V[(size_t)j * D + k];
+        double ga = 0.0, gb = 0.0;
+        for (int k = 0; k < D; ++k) {
+          ga += dO[(size_t)i * D + k] * V[(size_t)j * D + k];
+          gb += fabs(dO[(size_t)i * D + k] * V[(size_t)j * D + k]);
+        }
         g[j] = ga;
+        gabs[j] = gb;
       }
     }
     for (int64_t f = 0; f < nflip; ++f) {
@@ -496,13 +717,14 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
       dtail = (uint8_t *)malloc(n);
     }
     ko_row_impl(cfg, n, s, g, flip, P, dS, Pv, du, dr, dt, dl, dtail,
-                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl, eb);
+                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL, i, kid, fl, eb,
+                gabs, amb);
     if (bins) {
       for (int j = 0; j < T; ++j) bins[(size_t)i * T + j] = 255;
       /* bin value: the index (interval r, or Nearest l); on the resolved FWM grid the index + 64,
          clamped below at 0 (indices below -64 share the value 0); 254 tail, 255 not visible */
       for (int j = 0; j < n && j < T; ++j) {
-        int idx = cfg->recon == KO_NEAREST ? dl[j] : dr[j];
+        int idx = (cfg->recon == KO_NEAREST || cfg->recon >= KO_SOFTMAX) ? dl[j] : dr[j];
         if (cfg->calib == KO_FWM && cfg->tail == KO_TAIL_RESOLVED) idx = idx < -64 ? 0 : idx + 64;
         bins[(size_t)i * T + j] = dtail[j] ? 254 : (uint8_t)idx;
       }
@@ -531,6 +753,14 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
           aV[(size_t)j * D + k] += Pv[j] * dO[(size_t)i * D + k];
         }
       }
+      if (amb) {
+        double *cK = ambK + (size_t)tid * T * D;
+        for (int j = 0; j < n; ++j)
+          for (int k = 0; k < D; ++k) {
+            ambout[(size_t)i * D + k] += fabs(scale) * amb[j] * fabs(Kt[(size_t)j * D + k]);
+            cK[(size_t)j * D + k] += fabs(scale) * amb[j] * fabs(Q[(size_t)i * D + k]);
+          }
+      }
       if (absout) {
         double *bK = absK + (size_t)tid * T * D, *bV = absV + (size_t)tid * T * D;
         double *bQ = absout + (size_t)T * D;
@@ -542,7 +772,7 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
           }
       }
     }
-    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip); free(eb);
+    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip); free(eb); free(gabs); free(amb);
   }
   if (dO) {
     for (int th = 0; th < nthreads; ++th)
@@ -557,7 +787,10 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
           absout[3 * (size_t)T * D + x] += absV[(size_t)th * T * D + x];
         }
     }
-    free(accK); free(accV); free(absK); free(absV);
+    if (ambout)
+      for (int th = 0; th < nthreads; ++th)
+        for (size_t x = 0; x < (size_t)T * D; ++x) ambout[(size_t)T * D + x] += ambK[(size_t)th * T * D + x];
+    free(accK); free(accV); free(absK); free(absV); free(ambK);
   }
   if (nflags) *nflags = fl ? fl->count : 0;
   return 0;

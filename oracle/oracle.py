@@ -23,19 +23,22 @@ _SRC = os.path.join(_HERE, "kia_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkia_oracle.so")
 
 CALIB = {"minmax": 0, "fwm": 1}
-RECON = {"lerp": 0, "nearest": 1}
+# softmax, exp_bf16, exp_fp8: the exponential baselines (App. B "Softmax", App. D.5); they ignore
+# calib, K, tau and ste
+RECON = {"lerp": 0, "nearest": 1, "softmax": 2, "exp_bf16": 3, "exp_fp8": 4}
 STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 TAIL = {"zero": 0, "floor": 1, "resolved": 2}
 
-FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL = 1, 2, 4
+FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL, FLIP_ROUND, FLIP_ROUND2 = 1, 2, 4, 8, 16
 MUTATIONS = {
     "drop_rho_delta": 1, "sign_dm": 2, "delta_times_h": 3, "nearest_strict": 4,
     "wste_uses_lerp": 5, "dk_with_do": 6, "tail_inclusive": 7, "no_tie_split": 8,
     "nearest_fwd_lerp": 9, "extrema_all_keys": 10, "dq_no_scale": 11, "no_hsafe": 12,
     "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
     "x_index": 17, "detach_keeps_m": 18, "only_swapped": 19, "p1_skip_tail": 20,
-    "floor_tail_slope": 21, "resolved_grid_clamp": 22,
+    "floor_tail_slope": 21, "resolved_grid_clamp": 22, "fp8_truncates": 23, "bf16_grad_unrounded": 24,
+    "fp8_delta_rounded": 25,
 }
 ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
 ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")
@@ -94,7 +97,8 @@ def _load():
         lib.ko_row.restype = ctypes.c_int
         lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                 dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
-                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up, dp, ctypes.c_int]
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up, dp, dp,
+                                ctypes.c_int]
         lib.ko_head.restype = ctypes.c_int
         assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
         _lib = lib
@@ -143,7 +147,9 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags
     (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible).
     rows: optional list of row indices; only those rows are computed (their contributions alone).
-    absolute: also return abs = {O, dQ, dK, dV}: the same sums of absolute values of the terms."""
+    absolute: also return abs = {O, dQ, dK, dV}: the same sums of absolute values of the terms,
+    and amb = {dQ, dK}: what bfloat16 gradient roundings that may go either way can change
+    (exp_bf16; zero otherwise)."""
     lib = _load()
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
@@ -165,6 +171,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
         rmask = np.zeros(T, np.uint8)
         rmask[np.asarray(list(rows), dtype=np.int64)] = 1
     aout = np.zeros((4, T, D)) if absolute else None
+    amb = np.zeros((2, T, D)) if absolute else None
     c = cfg._c()
     rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
                      _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
@@ -173,7 +180,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
                      fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
                      _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
                      _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), _p(aout, ctypes.c_double),
-                     int(nthreads or default_threads()))
+                     _p(amb, ctypes.c_double), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle head rejected its arguments (rc={rc})")
     nf = int(nfl.value)
@@ -183,7 +190,8 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
     return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
                 flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap,
-                abs=None if aout is None else dict(O=aout[0], dQ=aout[1], dK=aout[2], dV=aout[3]))
+                abs=None if aout is None else dict(O=aout[0], dQ=aout[1], dK=aout[2], dV=aout[3]),
+                amb=None if amb is None else dict(dQ=amb[0], dK=amb[1]))
 
 
 def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):

@@ -21,6 +21,14 @@ FWM tail policies (App. C.3, App. D.4): "zero" drops keys below the window;
 "floor" clamps z at -tau, so such a key weighs e^{-tau} and torch's clamp gives
 it no gradient; "resolved" continues the grid b_q = -tau + q h to every integer
 q below the window, with the grid value computed as exp(b_q) for any q.
+
+Exponential baselines (App. B "Softmax", App. D.5 "Definitions"), written with
+torch's own casts so that the backward is torch's native one: softmax (e^z);
+BF16-exp (z cast to bfloat16, exp evaluated in bfloat16, cast back: autograd
+then carries the gradient through the bfloat16 tensors in bfloat16); FP8-rounded
+exp (e^z cast to float8_e4m3fn and back, plus e^z - sg(e^z), so the forward is
+the rounded value and the derivative that of e^z).  The row maximum stays on the
+gradient path (detached only in the detached, min_only and P1 modes).
 """
 import torch
 
@@ -32,8 +40,30 @@ def _st_clamp01(x):
     return x + (x.clamp(0.0, 1.0) - x).detach()
 
 
+EXP_RECON = ("softmax", "exp_bf16", "exp_fp8")
+
+
+def _exp_probs(s, mask, recon, grad):
+    dt = s.dtype
+    M = torch.where(mask, s, torch.tensor(-float("inf"), dtype=dt)).amax(dim=1, keepdim=True)
+    if grad in ("detached", "p1", "min_only"):
+        M = M.detach()
+    z = torch.where(mask, s - M, torch.zeros_like(s))
+    if recon == "softmax":
+        w = torch.exp(z)
+    elif recon == "exp_bf16":
+        w = torch.exp(z.to(torch.bfloat16)).to(dt)
+    else:
+        we = torch.exp(z)
+        w = we.detach().to(torch.float8_e4m3fn).to(dt) + (we - we.detach())
+    w = torch.where(mask, w, torch.zeros_like(w))
+    return w / w.sum(dim=1, keepdim=True)
+
+
 def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0, tail_policy="zero"):
     """s: [R, n] float64, mask: [R, n] bool (visible keys).  Returns P [R, n]."""
+    if recon in EXP_RECON:
+        return _exp_probs(s, mask, recon, grad)
     dt = s.dtype
     pos_inf = torch.tensor(float("inf"), dtype=dt)
     M = torch.where(mask, s, -pos_inf).amax(dim=1, keepdim=True)

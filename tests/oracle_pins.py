@@ -19,9 +19,13 @@ and raises AssertionError when the oracle disagrees with:
   * for the FWM tail policies (App. C.3, App. D.4): floored tail keys weigh e^{-tau}
     and carry no gradient, moving them deeper changes nothing; the resolved grid
     keeps every key within the chord and nearest-centre bounds of e^z and
-    converges to softmax as h -> 0 even with a narrow window.
+    converges to softmax as h -> 0 even with a narrow window;
+  * for the exponential baselines (App. B "Softmax", App. D.5): torch's native
+    autograd through its own bfloat16 / float8_e4m3fn casts, the textbook softmax
+    gradient, the E4M3 value set (56 nonzero values in (0, 1], underflow below
+    2^-10) and the rounding of each weight to its format.
 Source: "Pretraining Transformers with Quantized Softmax in Attention", §3,
-§5.1, App. A, App. B, App. C.2, App. C.3, App. D.4.
+§5.1, App. A, App. B, App. C.2, App. C.3, App. D.4, App. D.5.
 """
 from __future__ import annotations
 
@@ -44,12 +48,55 @@ VARIANTS += [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "pr
 # tau-selection stages, and the resolved grid)
 VARIANTS += [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("lerp", "prob"),
              ("nearest", "weight"), ("nearest", "prob")) for g in ("full", "detached")]
+# the exponential baselines (App. B "Softmax", App. D.5): no grid; calib, K, tau and ste are ignored
+EXP_RECON = ("softmax", "exp_bf16", "exp_fp8")
+VARIANTS += [("fwm", r, "prob", g) for r in EXP_RECON for g in ("full", "detached", "max_only", "min_only", "p1")]
+
+
+def is_exp(cfg):
+    return cfg.recon in EXP_RECON
+
+
+def max_only_calib(cfg):
+    """FWM and the exponential baselines calibrate on the row maximum alone."""
+    return cfg.calib == "fwm" or is_exp(cfg)
 
 
 def zero_sum_mode(cfg):
-    """Modes whose row score gradients sum to zero: full, P1, and FWM's max_only (FWM has no
-    minimum channel, so max_only is its full gradient)."""
-    return cfg.grad in ("full", "p1") or (cfg.calib == "fwm" and cfg.grad == "max_only")
+    """Modes whose row score gradients sum to zero: full, P1, and max_only where there is no
+    minimum channel (FWM, the exponential baselines: max_only is their full gradient); every
+    mode of softmax."""
+    if cfg.recon == "softmax":
+        return True   # the maximum's term vanishes: softmax is shift invariant in every mode
+    return cfg.grad in ("full", "p1") or (max_only_calib(cfg) and cfg.grad == "max_only")
+
+
+def _fmt_pos(x, mb, emin):
+    """|x| in units of the spacing of a binary format with mb significand bits (smallest normal
+    exponent emin) at |x|, and its distance from a rounding midpoint, in those units."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(x)
+    E = np.maximum(e - 1, emin)
+    q = x / np.ldexp(1.0, E - mb)
+    return q, np.abs(q - np.floor(q) - 0.5)
+
+
+def _exp_near(s, g, res, cfg, guard=1e-4):
+    """True when a rounding of an exponential baseline lies within guard (in units of the target
+    format's spacing) of a midpoint: there the fp32 steps of torch's casts may round the other way."""
+    z = s - s.max()
+    if cfg.recon == "exp_fp8":
+        return bool((_fmt_pos(np.exp(z), 3, -6)[1] < guard).any())
+    if cfg.recon != "exp_bf16":
+        return False
+    q, d = _fmt_pos(z, 7, -126)
+    zb = np.copysign(np.rint(q) * np.ldexp(1.0, np.maximum(np.frexp(np.abs(z))[1] - 1, -126) - 7), z)
+    bad = (d < guard) & (z != 0)
+    bad |= _fmt_pos(np.exp(zb), 7, -126)[1] < guard
+    if g is not None:
+        gam = (g - (res["P"] * g).sum()) / res["WL"]
+        bad |= _fmt_pos(gam, 7, -126)[1] < guard
+    return bool(bad.any())
 
 
 def cfg_of(calib, recon, ste, grad, tail="zero", K=4, tau=8.0, mutation=None):
@@ -92,10 +139,14 @@ def _random_rows(seed, cfg, count=24):
         s = rng.standard_normal(n) * scales[len(rows) % 3]
         g = rng.standard_normal(n)
         res = ORC.row(dataclasses.replace(cfg, mutation=None), s, g)
-        if _near_boundary(res, cfg):
-            continue
-        if cfg.calib == "fwm" and np.any(np.abs(s - s.max() + cfg.tau) < 1e-6):
-            continue
+        if is_exp(cfg):
+            if _exp_near(s, g, res, cfg):
+                continue
+        else:
+            if _near_boundary(res, cfg):
+                continue
+            if cfg.calib == "fwm" and np.any(np.abs(s - s.max() + cfg.tau) < 1e-6):
+                continue
         rows.append((s, g))
     return rows
 
@@ -129,7 +180,7 @@ def pin_autograd_ties(cfg):
             s[0] = s[2] = s.max() - 0.6 * cfg.tau   # keep both in the window
         g = rng.standard_normal(n)
         res = ORC.row(dataclasses.replace(cfg, mutation=None), s, g)
-        if _near_boundary(res, cfg):
+        if _exp_near(s, g, res, cfg) if is_exp(cfg) else _near_boundary(res, cfg):
             continue
         res = ORC.row(cfg, s, g)
         P, dS = AR.row_grad(s, g, *_ar(cfg), tail_policy=cfg.tail)
@@ -149,6 +200,9 @@ def _head_inputs(seed, T, D, qscale=1.0):
 def pin_autograd_head(cfg):
     for seed, T, D, causal, qs in ((1, 24, 8, True, 1.5), (2, 10, 6, False, 3.0), (3, 33, 4, True, 4.0)):
         Q, K, V, dO = _head_inputs(seed, T, D, qs)
+        if is_exp(cfg) and ORC.head(dataclasses.replace(cfg, mutation=None), Q, K, V, dO, causal=causal,
+                                    guard=1e-4, flag_cap=64, nthreads=2)["nflags"]:
+            continue
         res = ORC.head(cfg, Q, K, V, dO, causal=causal, nthreads=2)
         O, dQ, dK, dV = AR.head_grad(Q, K, V, dO, *_ar(cfg), causal=causal, tail_policy=cfg.tail)
         _close(res["O"], O.numpy(), 1e-11, 1e-13, "head O vs autograd")
@@ -184,7 +238,7 @@ def pin_channel_additivity(cfg):
         oth = ORC.row(dataclasses.replace(cfg, grad=other), s, g)["dS"]
         det = ORC.row(dataclasses.replace(cfg, grad="detached", mutation=None), s, g)["dS"]
         full = ORC.row(dataclasses.replace(cfg, grad="full", mutation=None), s, g)["dS"]
-        if cfg.calib == "minmax":
+        if not max_only_calib(cfg):
             _close(got + oth - det, full, 1e-12, 1e-14, "max_only + min_only - detached vs full")
         else:
             _close(got, full if cfg.grad == "max_only" else det, 1e-14, 0.0, f"FWM {cfg.grad}")
@@ -213,6 +267,8 @@ def _weights(res, recon):
 def pin_reconstruction_bounds(cfg):
     """LERP is a chord of the convex e^z: above it, by at most h^2/8 e^{z+h};
     Nearest picks a grid value within h/2 of z in score coordinates."""
+    if is_exp(cfg):
+        return
     for s, g in _random_rows(31, cfg):
         res = ORC.row(cfg, s, g)
         if res["degenerate"]:
@@ -239,6 +295,8 @@ def pin_reconstruction_bounds(cfg):
 
 def pin_nearest_brute_force(cfg):
     """The Nearest index is the grid point closest to z (ties upward), found by brute force."""
+    if is_exp(cfg):
+        return
     for s, g in _random_rows(41, cfg):
         res = ORC.row(cfg, s, g)
         if res["degenerate"]:
@@ -275,7 +333,7 @@ def pin_finite_differences(cfg):
         return float((ORC.head(cfg, Qx, Kx, Vx, None, nthreads=1)["O"] * dO).sum())
 
     targets = [("V", "dV")]
-    if cfg.recon == "lerp" and cfg.grad == "full":
+    if cfg.recon in ("lerp", "softmax") and cfg.grad == "full":
         targets += [("Q", "dQ"), ("K", "dK")]
     for name, gname in targets:
         for _ in range(8):
@@ -338,7 +396,7 @@ def pin_special_cases(cfg):
         assert abs(w[res["amax"]] - 1.0) <= 1e-14, "weight at the argmax is not 1"
         if cfg.calib == "minmax":
             assert abs(w[res["amin"]] - math.exp(res["m"] - res["M"])) <= 1e-14, "weight at the argmin"
-        if cfg.recon == "lerp":
+        if cfg.recon == "lerp" or is_exp(cfg):
             other = dataclasses.replace(cfg, ste="weight" if cfg.ste == "prob" else "prob")
             assert np.array_equal(ORC.row(other, s, g)["dS"], res["dS"]), "STE flag changed LERP"
     if cfg.calib == "minmax" and cfg.recon == "lerp":
@@ -352,6 +410,8 @@ def pin_special_cases(cfg):
 
 def pin_k_limit(cfg):
     """LERP -> softmax as K grows: forward error O(h^2), gradient error O(h) (full)."""
+    if is_exp(cfg):
+        return
     if cfg.recon != "lerp":
         return
     rng = np.random.default_rng(61)
@@ -373,6 +433,8 @@ def pin_k_limit(cfg):
 
 def pin_golden(cfg):
     """Hand-derived fixtures (tests/golden/hand_rows.txt)."""
+    if is_exp(cfg):
+        return
     for case in golden_io.load_cases():
         if case["calib"] != cfg.calib or case.get("tail_policy", "zero") != cfg.tail:
             continue
@@ -399,6 +461,8 @@ def pin_tail_policy(cfg):
     """Floor: a tail key weighs e^{-tau}, has no score gradient, and lowering it further changes
     nothing.  Resolved: nothing is truncated, and a key's weight keeps following e^z below the
     window (LERP within the chord bound, so deeper keys weigh less).  Zero: tail keys weigh 0."""
+    if is_exp(cfg):
+        return
     if cfg.calib != "fwm":
         return
     rng = np.random.default_rng(71)
@@ -430,7 +494,46 @@ def pin_tail_policy(cfg):
             assert w[1] == 0.0 and w[2] == 0.0, "zero-policy tail keys weigh something"
 
 
-PINS = [pin_golden, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
+def pin_exp_weights(cfg):
+    """Exponential baselines: softmax is e^z / sum and its gradient P (g - sum P g) (App. B
+    "Softmax"); the FP8 weight is the E4M3 value nearest e^z, one of the format's 56 nonzero values
+    in (0, 1] (or 0 below 2^-10), with the unrounded e^z as derivative; the BF16 weight is the
+    bfloat16 value nearest exp of the bfloat16 value nearest z (App. D.5 "Definitions")."""
+    if not is_exp(cfg):
+        return
+    # the E4M3 values in (0, 1]: 7 subnormal multiples of 2^-9 and 8 normal values per binade 2^-6 .. 2^-1, plus 1
+    e4m3 = sorted({m * 2.0 ** -9 for m in range(1, 8)} | {(1 + f / 8) * 2.0 ** e for e in range(-6, 0) for f in range(8)}
+                  | {1.0})
+    assert len(e4m3) == 56
+    grid = np.array([0.0] + e4m3)
+    for s, g in _random_rows(83, cfg):
+        res = ORC.row(cfg, s, g)
+        z = s - s.max()
+        w = res["P"] * res["WL"]
+        if cfg.recon == "softmax":
+            e = np.exp(z)
+            _close(res["P"], e / e.sum(), 1e-14, 1e-16, "softmax P")
+            if cfg.grad in ("full", "max_only"):
+                P = e / e.sum()
+                _close(res["dS"], P * (g - (P * g).sum()), 1e-12, 1e-15, "softmax gradient")
+        elif cfg.recon == "exp_fp8":
+            e = np.exp(z)
+            nearest = grid[np.argmin(np.abs(grid[None, :] - e[:, None]), axis=1)]
+            _close(w, nearest, 1e-13, 0.0, "E4M3 weight is the nearest representable value")
+            assert np.all((w == 0) == (e < 2.0 ** -10)), "E4M3 underflow threshold"
+            if cfg.grad == "detached":
+                gam = (g - (res["P"] * g).sum()) / res["WL"]
+                _close(res["dS"], gam * e, 1e-12, 1e-15, "FP8 derivative is the unrounded e^z")
+        else:
+            zb = np.array([float(torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)) for x in z])
+            assert np.all(np.abs(zb - z) <= np.abs(z) * 2.0 ** -8), "bfloat16 input rounding"
+            wb = np.exp(zb)
+            assert np.all(np.abs(w - wb) <= wb * 2.0 ** -8), "bfloat16 output rounding"
+            bits = np.array([np.float32(x).view(np.uint32) for x in w])
+            assert np.all(bits & 0xFFFF == 0), "weights are bfloat16 values"
+
+
+PINS = [pin_golden, pin_exp_weights, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
         pin_two_key,
         pin_reconstruction_bounds, pin_nearest_brute_force, pin_finite_differences, pin_shift_invariance,
         pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit, pin_tail_policy]
