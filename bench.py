@@ -103,6 +103,9 @@ def main() -> int:
                     help="gradient mode of every variant (the headline is full)")
     ap.add_argument("--tail", default="zero", choices=["zero", "floor", "resolved"],
                     help="tail policy of the FWM variants (the headline is zero, the FWM of the pages)")
+    ap.add_argument("--baselines", action="store_true",
+                    help="time the exponential baselines (softmax, BF16-exp, FP8-rounded exp) on the same "
+                         "workload instead of the K-interval variants")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
                          "byte counters)")
@@ -120,6 +123,9 @@ def main() -> int:
     import dataclasses
     wl = WORKLOADS[args.workload]
     variants = [dataclasses.replace(v, tail=args.tail) if v.calib == "fwm" else v for v in wl.variants]
+    if args.baselines:
+        from quantized_softmax_attention_kia_amd.inputs import Variant
+        variants = [Variant("fwm", r, "prob", "full", 4) for r in ("softmax", "exp_bf16", "exp_fp8")]
     log(f"workload {wl.name}: B={wl.B} H={wl.H} T={wl.T} D={wl.D} {wl.dtype} seed={wl.seed}; "
         f"{len(variants)} variants")
     q, k, v, do = wl.inputs()
@@ -208,7 +214,7 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    traffic = read_traffic(kernel_key) if args.grad == "full" and args.tail == "zero" else None
+    traffic = read_traffic(kernel_key) if args.grad == "full" and args.tail == "zero" and not args.baselines else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "

@@ -58,14 +58,31 @@ extern "C" {
 typedef enum {
   KIA_OK = 0,
   KIA_ERR_INVALID_ARG = -1, /* null pointer, bad size or enum value, tau <= 0 under FWM,
-                               a tail policy other than zero under MinMax */
+                               a tail policy other than zero under MinMax or an
+                               exponential baseline */
   KIA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
   KIA_ERR_WORKSPACE = -3,   /* reserved: a buffer smaller than kia_workspace_size asks */
   KIA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } kia_status_t;
 
 typedef enum { KIA_CALIB_MINMAX = 0, KIA_CALIB_FWM = 1 } kia_calib_t;
-typedef enum { KIA_RECON_LERP = 0, KIA_RECON_NEAREST = 1 } kia_recon_t;
+/* LERP and Nearest rebuild weights from the grid; SOFTMAX, EXP_BF16 and EXP_FP8 are the
+   exponential baselines (App. B "Softmax", App. D.5): no grid, so calib, K, tau and ste are
+   ignored (they are still checked) and tail must be ZERO:
+     SOFTMAX   w = e^z, z = s - M;
+     EXP_BF16  z rounded to bfloat16, e^(that) rounded to bfloat16; the backward carries the
+               gradient through the bfloat16 weight in bfloat16 (dL/dw rounded to bfloat16,
+               times the weight, rounded to bfloat16);
+     EXP_FP8   e^z rounded to E4M3 (float8_e4m3fn), derivative e^z (the unrounded exponential);
+   roundings to nearest, ties to even, of the exact values.  The row maximum's term
+   -sum_j dL/dz_j goes to the arg-max key(s) in the full and max_only modes. */
+typedef enum {
+  KIA_RECON_LERP = 0,
+  KIA_RECON_NEAREST = 1,
+  KIA_RECON_SOFTMAX = 2,
+  KIA_RECON_EXP_BF16 = 3,
+  KIA_RECON_EXP_FP8 = 4
+} kia_recon_t;
 /* surrogate placement; ignored under LERP (both give the LERP Jacobian) */
 typedef enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 } kia_ste_t;
 /* full calibration gradient, or one of the range_grad ablations */
@@ -177,7 +194,9 @@ kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void*
  *        (recon = Nearest) or the interval index r in 0..K-1 (recon = LERP);
  *        on the resolved FWM grid (indices may be negative) the index + 64,
  *        with indices below -64 all given 0; 254 for FWM tail keys (zero and
- *        floor policies); 255 for keys the query does not see.
+ *        floor policies); 255 for keys the query does not see.  The exponential
+ *        baselines give the E4M3 byte of the weight (EXP_FP8), the low byte of
+ *        the bfloat16 weight (EXP_BF16) or 0 (SOFTMAX) for visible keys.
  * Costs O(B*H*T*T) bytes; meant for small T.
  */
 kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream);

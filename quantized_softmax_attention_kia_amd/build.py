@@ -16,9 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkia.so")
 # (source, object, defines): the forward and dq kernels are built once per calibration
-# (MinMax, FWM with a zero, floored or resolved tail); the KIA_CAL=0 backward build also
-# holds the dkdv kernel
-NCALIB = 4
+# (MinMax, FWM with a zero, floored or resolved tail, the exponential baselines); the KIA_CAL=0
+# backward build also holds the dkdv kernel
+NCALIB = 5
 SOURCES = [("kia_api.hip", "kia_api.o", [])] + [
     (src, f"{src[:-4]}_c{c}.o", [f"-DKIA_CAL={c}"]) for c in range(NCALIB) for src in ("kia_fwd.hip", "kia_bwd.hip")]
 ARCH = "gfx950"

@@ -37,7 +37,7 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   if (p->K < 1 || p->K > 64) { set_err("K must be in 1..64 (got %d)", p->K); return KIA_ERR_INVALID_ARG; }
   if (p->causal != 0 && p->causal != 1) { set_err("causal must be 0 or 1"); return KIA_ERR_INVALID_ARG; }
   if (p->calib != KIA_CALIB_MINMAX && p->calib != KIA_CALIB_FWM) { set_err("bad calib %d", p->calib); return KIA_ERR_INVALID_ARG; }
-  if (p->recon != KIA_RECON_LERP && p->recon != KIA_RECON_NEAREST) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
+  if (p->recon < KIA_RECON_LERP || p->recon > KIA_RECON_EXP_FP8) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
   if (p->ste != KIA_STE_WEIGHT && p->ste != KIA_STE_PROB) { set_err("bad ste %d", p->ste); return KIA_ERR_INVALID_ARG; }
   if (p->grad < KIA_GRAD_FULL || p->grad > KIA_GRAD_P1) { set_err("bad grad %d", p->grad); return KIA_ERR_INVALID_ARG; }
   if (p->dtype != KIA_F32 && p->dtype != KIA_BF16) { set_err("bad dtype %d", p->dtype); return KIA_ERR_INVALID_ARG; }
@@ -49,6 +49,11 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   if (p->tail < KIA_TAIL_ZERO || p->tail > KIA_TAIL_RESOLVED) { set_err("bad tail %d", p->tail); return KIA_ERR_INVALID_ARG; }
   if (p->calib == KIA_CALIB_MINMAX && p->tail != KIA_TAIL_ZERO) {
     set_err("a tail policy other than zero needs FWM (MinMax has no window)");
+    return KIA_ERR_INVALID_ARG;
+  }
+  const bool expb = p->recon >= KIA_RECON_SOFTMAX;
+  if (expb && p->tail != KIA_TAIL_ZERO) {
+    set_err("the exponential baselines have no window: tail must be zero");
     return KIA_ERR_INVALID_ARG;
   }
   // index ranges the kernels rely on: per-head offsets in int, grid size in int
@@ -63,8 +68,10 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   pr->causal = p->causal;
   pr->tau = p->tau;
   pr->scale = p->scale > 0.f ? (double)p->scale : 1.0 / std::sqrt((double)p->D);
-  pr->calib = p->calib == KIA_CALIB_MINMAX ? kia::MINMAX
-              : (p->tail == KIA_TAIL_FLOOR ? kia::FWM_FLOOR : (p->tail == KIA_TAIL_RESOLVED ? kia::FWM_RES : kia::FWM));
+  pr->calib = expb ? kia::EXPB
+              : p->calib == KIA_CALIB_MINMAX
+                  ? kia::MINMAX
+                  : (p->tail == KIA_TAIL_FLOOR ? kia::FWM_FLOOR : (p->tail == KIA_TAIL_RESOLVED ? kia::FWM_RES : kia::FWM));
   // resolved grid: table levels below the window down to b <= -104, where e^b rounds to 0 in
   // float, capped at LRES_MAX (keys below the table get their grid values computed)
   pr->lres = 0;
@@ -74,10 +81,16 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
     pr->lres = need <= 0.0 ? 0 : (need >= (double)kia::LRES_MAX ? kia::LRES_MAX : (int)need);
     pr->res_far = need > (double)kia::LRES_MAX;
   }
-  pr->mode = p->recon == KIA_RECON_LERP ? kia::LERP : (p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P);
+  switch (p->recon) {
+    case KIA_RECON_LERP: pr->mode = kia::LERP; break;
+    case KIA_RECON_NEAREST: pr->mode = p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P; break;
+    case KIA_RECON_SOFTMAX: pr->mode = kia::EXP32; break;
+    case KIA_RECON_EXP_BF16: pr->mode = kia::EXPBF; break;
+    default: pr->mode = kia::EXPF8; break;
+  }
   pr->gk = p->grad == KIA_GRAD_DETACHED ? kia::GK_DETACHED : (p->grad == KIA_GRAD_P1 ? kia::GK_P1 : kia::GK_SUMS);
   pr->keepM = p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MAX_ONLY;
-  pr->keepm = (p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MIN_ONLY) && p->calib == KIA_CALIB_MINMAX;
+  pr->keepm = (p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MIN_ONLY) && pr->calib == kia::MINMAX;
   pr->bf16 = p->dtype == KIA_BF16;
   return KIA_OK;
 }

@@ -73,7 +73,8 @@ struct DqSmem {
 
 template <int D, int CAL, typename TIn>
 size_t dq_smem_bytes(int K, int lres) {
-  return sizeof(DqSmem<D, nslices<TIn>()>) + sizeof(float) * (CAL == MINMAX ? DQ_BM * (K + 3) : lres + K + 3);
+  return sizeof(DqSmem<D, nslices<TIn>()>) +
+         sizeof(float) * (CAL == MINMAX ? DQ_BM * (K + 3) : (CAL == EXPB ? 0 : lres + K + 3));
 }
 
 // GK: GK_SUMS (full, max_only, min_only: the calibration sums, with the extremum terms that
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const float M = a.rec.M[row], m = a.rec.m[row];
   const int amax = a.rec.amax[row], amin = a.rec.amin[row];
   const int nA = a.rec.nA[row], nC = a.rec.nC[row];
-  const float Wf = (MODE == LERP) ? a.rec.WL[row] : a.rec.WN[row];
+  const float Wf = is_nearest(MODE) ? a.rec.WN[row] : a.rec.WL[row];
   const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
   const float invWf = 1.0f / Wf, invWg = 1.0f / Wg;
 
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
   // MinMax: one table row per query row (zero for rows past T); FWM: one table for all rows, from
   // lres levels below the window (resolved grid) to K (rows past T see no visible key)
-  float* trow;
+  float* trow = tbl;
   if (CAL == MINMAX) {
     trow = tbl + rl * ts;
     for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
-  } else {
+  } else if (CAL != EXPB) {  // the exponential baselines have no grid
     trow = tbl + a.lres;
     for (int i = tid; i <= a.lres + K + 2; i += NT) tbl[i] = i <= a.lres + K ? grid_value<CAL>(M, m, K, a.tau, i - a.lres) : 0.f;
   }
@@ -221,15 +222,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int v = 8 * b + j;
-        Decision d = decide<CAL>(s[v], rc, K, a.tau);
-        if (!(crow(v, 0) <= lim) || (CAL == FWM && d.tail)) d.r = K + 1;
-        const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
-        const float Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
         const float gam = (gt[v] - Di) * invWg;
-        const float dS = gam * Delta;
+        float dS, pw;
+        Decision d;
+        Weights wt;
+        float Delta = 0.f;
+        if constexpr (CAL == EXPB) {
+          // exponential baselines: the weight as the forward took it.  The forward's float form,
+          // where the forward kept it, gave the exact form's value on the stored score; where it
+          // retook it, the stored score is exact.  Here the float form is checked against its
+          // arithmetic alone and the exact form taken where that cannot settle the rounding.
+          // dL/dz = gamma dw/dz, for BF16-exp in bfloat16: gamma rounded where it enters the
+          // bfloat16 weight, the product (exact in float) rounded once more
+          const bool vis = crow(v, 0) <= lim;
+          bool rs = false, re = false;
+          ExpW ew = exp_weight_fast<MODE>(s[v], M, 0.f, &rs, &re);
+          if (rs || re) ew = exp_weight_exact<MODE>(s[v], M);
+          pw = vis ? ew.w : 0.f;
+          if (MODE == EXPBF) dS = vis ? bf16_round(bf16_round(gam) * ew.d) : 0.f;
+          else dS = vis ? gam * ew.d : 0.f;
+        } else {
+          d = decide<CAL>(s[v], rc, K, a.tau);
+          if (!(crow(v, 0) <= lim) || (CAL == FWM && d.tail)) d.r = K + 1;
+          wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
+          Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
+          dS = gam * Delta;
+          pw = is_nearest(MODE) ? wt.wN : wt.wL;
+        }
         ds[j] = dS;
         // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
-        Pw[v * 64 + l] = ((MODE == LERP) ? wt.wL : wt.wN) * invWf;
+        Pw[v * 64 + l] = pw * invWf;
         dSw[v * 64 + l] = dS;
         if (SUMS || P1) hs += dS;
         if (SUMS) {
@@ -518,10 +540,15 @@ static hipError_t dq_gk(const Problem& p, const BwdArgs& a, hipStream_t s) {
 }
 template <int D, int CAL>
 static hipError_t dq_md(const Problem& p, const BwdArgs& a, hipStream_t s) {
-  switch (p.mode) {
-    case LERP: return dq_gk<D, CAL, LERP>(p, a, s);
-    case NEAREST_W: return dq_gk<D, CAL, NEAREST_W>(p, a, s);
-    default: return dq_gk<D, CAL, NEAREST_P>(p, a, s);
+  if constexpr (CAL == EXPB) {
+    if (p.mode == EXPF8) return dq_gk<D, CAL, EXPF8>(p, a, s);
+    return p.mode == EXPBF ? dq_gk<D, CAL, EXPBF>(p, a, s) : dq_gk<D, CAL, EXP32>(p, a, s);
+  } else {
+    switch (p.mode) {
+      case LERP: return dq_gk<D, CAL, LERP>(p, a, s);
+      case NEAREST_W: return dq_gk<D, CAL, NEAREST_W>(p, a, s);
+      default: return dq_gk<D, CAL, NEAREST_P>(p, a, s);
+    }
   }
 }
 template <>

@@ -572,6 +572,114 @@ __device__ __forceinline__ Weights weights_cal(const Decision& d, const float* t
   return w;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Exponential baselines ("Pretraining Transformers with Quantized Softmax in Attention", App. B
+// "Softmax", App. D.5 "Definitions"): w = e^z (softmax), the bfloat16 exponential of z rounded
+// to bfloat16 (BF16-exp), e^z rounded to E4M3 (FP8-rounded exp), z = s - M.  Roundings are to
+// nearest, ties to even, of the exact value.  The fast forms work in float and report when the
+// result may differ from the exact one (a rounding within the error of its float inputs of a
+// midpoint); the exact forms take the score difference and the exponential in double.
+
+// nearest bfloat16 value of a float (ties to even), as a float
+__device__ __forceinline__ float bf16_round(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return __uint_as_float((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);
+}
+// distance of a float from the nearest bfloat16 rounding midpoint, in bfloat16 spacings
+__device__ __forceinline__ float bf16_mid_dist(float x) {
+  return fabsf((float)(__float_as_uint(x) & 0xffffu) - 32768.f) * 0x1p-16f;
+}
+// nearest bfloat16 value of a double (normal range) or of a value in the bfloat16 subnormal range
+__device__ __forceinline__ double bf16_round_d(double x) {
+  if (fabs(x) < 0x1p-126) return rint(x * 0x1p133) * 0x1p-133;
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t r = (b + 0xfffffffffffull + ((b >> 45) & 1ull)) & ~0x1fffffffffffull;
+  return __longlong_as_double((long long)r);
+}
+// nearest E4M3 value (3 significand bits, subnormal multiples of 2^-9) of x in [0, 1]
+__device__ __forceinline__ float e4m3_round(float x) {
+  if (x < 0x1p-6f) return __builtin_rintf(x * 0x1p9f) * 0x1p-9f;
+  const uint32_t b = __float_as_uint(x);
+  return __uint_as_float((b + 0x7ffffu + ((b >> 20) & 1u)) & 0xfff00000u);
+}
+__device__ __forceinline__ float e4m3_mid_dist(float x) {
+  if (x < 0x1p-6f) {
+    const float q = x * 0x1p9f;
+    return fabsf(q - floorf(q) - 0.5f);
+  }
+  return fabsf((float)(__float_as_uint(x) & 0xfffffu) - 524288.f) * 0x1p-20f;
+}
+__device__ __forceinline__ double e4m3_round_d(double x) {
+  if (x < 0x1p-6) return rint(x * 0x1p9) * 0x1p-9;
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t r = (b + 0xffffffffffffull + ((b >> 49) & 1ull)) & ~0x1ffffffffffffull;
+  return __longlong_as_double((long long)r);
+}
+// E4M3 byte of a value the format represents, in [0, 1]
+__device__ __forceinline__ int e4m3_code(float w) {
+  if (w < 0x1p-6f) return (int)(w * 0x1p9f);
+  const uint32_t b = __float_as_uint(w);
+  return (int)((((b >> 23) & 0xffu) - 120u) << 3 | ((b >> 20) & 7u));
+}
+
+struct ExpW {
+  float w;  // the weight
+  float d;  // dw/dz: e^z (softmax: w; FP8: the unrounded exponential; BF16: the bfloat16 weight)
+};
+// fast form: float z, expf.  ez bounds the error of the score behind s (the scores are
+// approximations within ez of the exact ones).  *risky_s is set when the exact form on the exact
+// score may differ, *risky_e when only the exponential's own rounding may (BF16-exp: z's rounding
+// is settled, so the exact form on this score gives the exact value).
+template <int MODE>
+__device__ __forceinline__ ExpW exp_weight_fast(float s, float M, float ez, bool* risky_s, bool* risky_e) {
+  const float z = s - M;
+  ExpW r;
+  *risky_e = false;
+  if (MODE == EXP32) {
+    r.w = __expf(z);
+    r.d = r.w;
+    *risky_s = false;
+  } else if (MODE == EXPF8) {
+    const float e = __expf(z);
+    r.w = e4m3_round(e);
+    r.d = e;
+    // relative error of e: the score's, z's rounding, the exponential's; times at most 16 spacings
+    *risky_s = e4m3_mid_dist(e) < 16.f * (ez + fabsf(z) * 0x1p-23f + 0x1p-20f);
+  } else {
+    const float zb = bf16_round(z);
+    const float e = __expf(zb);
+    r.w = bf16_round(e);
+    r.d = r.w;
+    // z within the score error (plus its own rounding) of a midpoint, in units of z's spacing
+    // (at least |z| 2^-8): dist < 256 ez / |z| + 2^-14, multiplied out; the exponential within its
+    // error (|zb| 2^-23 + 2^-20 of its value) of a midpoint, in units of its spacing (at least
+    // 2^-8 of its value)
+    const float az = fabsf(z);
+    *risky_s = z != 0.f && bf16_mid_dist(z) * az < fmaf(256.f, ez, az * 0x1p-14f);
+    *risky_e = bf16_mid_dist(e) < fmaf(fabsf(zb), 0x1p-15f, 0x1p-12f);
+  }
+  return r;
+}
+// exact form: z = s - M in double (exact for floats), the exponential in double, one rounding
+template <int MODE>
+__device__ __forceinline__ ExpW exp_weight_exact(float s, float M) {
+  const double z = (double)s - (double)M;
+  ExpW r;
+  if (MODE == EXP32) {
+    r.w = __expf((float)z);
+    r.d = r.w;
+  } else if (MODE == EXPF8) {
+    const double e = exp(z);
+    r.w = (float)e4m3_round_d(e);
+    r.d = (float)e;
+  } else {
+    const double e = exp(bf16_round_d(z));
+    r.w = (float)bf16_round_d(e);
+    r.d = r.w;
+  }
+  return r;
+}
+
 // Work order.  The dispatcher hands workgroup b to XCD b % 8.  Each XCD gets a contiguous range
 // of heads (their K, V and score tiles then stay in that XCD's L2) and walks its tiles heaviest
 // first over all of its heads (rank 0 = most work), so the hardware's greedy dispatch balances

@@ -395,11 +395,11 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   const float edge = Erow + a.tau * 0x1p-21f;  // FWM window edge: margin of |(s - M) + tau|
   // MinMax: one table row per query row; FWM: one table for all rows, from lres levels below
   // the window (resolved grid) to K
-  float* trow;
+  float* trow = tbl;
   if (CAL == MINMAX) {
     trow = tbl + c * ts;
     for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
-  } else {
+  } else if (CAL != EXPB) {  // the exponential baselines have no grid
     trow = tbl + a.lres;
     for (int i = threadIdx.x; i <= a.lres + K; i += FWD_NT) tbl[i] = grid_value<CAL>(M, m, K, a.tau, i - a.lres);
   }
@@ -444,6 +444,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       float p[8], pl[8];
       double tL, tN;  // the half tile's weight sums, joined to the row sums once it is settled
       uint32_t risky = 0;
+      uint32_t riske = 0;  // exponential baselines: keys whose weight alone is taken again
       auto weigh = [&](auto masked, auto check) {
         tL = 0.0;
         tN = 0.0;
@@ -451,47 +452,82 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         for (int j = 0; j < 8; ++j) {
           const int v = 8 * b + j, key = k0 + crow(v, g);
           const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
-          // first pass: float arithmetic, checked against the margin; again: the exact decision
-          const Decision d = decltype(check)::value ? decide_fast<CAL>(s[v], rc, K, a.tau)
-                                                    : decide<CAL>(s[v], rc, K, a.tau);
-          if (decltype(check)::value) {
-            // a decision within the score's error bound of a boundary must be taken on the exact
-            // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid)
-            const float dur = CAL == FWM_RES ? fmaf((float)max(-d.r, 0), 0x1p-22f, du) : du;
-            bool r = (d.t < dur && (CAL == FWM_RES || d.r > 0)) || (d.t > 1.f - dur && d.r < K - 1);
-            if (MODE != LERP) r = r || fabsf(d.t - 0.5f) < dur;
-            if (CAL == FWM || CAL == FWM_FLOOR) r = r || fabsf((s[v] - M) + a.tau) <= edge;
-            risky |= (ok && r) ? (1u << j) : 0u;
+          float wl, wn;
+          if constexpr (CAL == EXPB) {
+            // exponential baselines: first pass in float, checked against the score's error bound;
+            // again: the exact rounding
+            bool rs = false, re = false;
+            const ExpW ew = decltype(check)::value ? exp_weight_fast<MODE>(s[v], M, Erow, &rs, &re)
+                                                   : exp_weight_exact<MODE>(s[v], M);
+            if (decltype(check)::value) {
+              risky |= (ok && rs) ? (1u << j) : 0u;
+              riske |= (ok && re && !rs) ? (1u << j) : 0u;
+            }
+            wl = ok ? ew.w : 0.f;
+            wn = wl;
+          } else {
+            // first pass: float arithmetic, checked against the margin; again: the exact decision
+            const Decision d = decltype(check)::value ? decide_fast<CAL>(s[v], rc, K, a.tau)
+                                                      : decide<CAL>(s[v], rc, K, a.tau);
+            if (decltype(check)::value) {
+              // a decision within the score's error bound of a boundary must be taken on the exact
+              // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid)
+              const float dur = CAL == FWM_RES ? fmaf((float)max(-d.r, 0), 0x1p-22f, du) : du;
+              bool r = (d.t < dur && (CAL == FWM_RES || d.r > 0)) || (d.t > 1.f - dur && d.r < K - 1);
+              if (is_nearest(MODE)) r = r || fabsf(d.t - 0.5f) < dur;
+              if (CAL == FWM || CAL == FWM_FLOOR) r = r || fabsf((s[v] - M) + a.tau) <= edge;
+              risky |= (ok && r) ? (1u << j) : 0u;
+            }
+            const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
+            // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
+            const bool keep = ok && (CAL == FWM_FLOOR || !d.tail);
+            wl = keep ? wt.wL : 0.f;
+            wn = keep ? wt.wN : 0.f;
           }
-          const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
-          // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
-          const bool keep = ok && (CAL == FWM_FLOOR || !d.tail);
-          const float wl = keep ? wt.wL : 0.f;
-          const float wn = keep ? wt.wN : 0.f;
           tL += (double)wl;
-          if (MODE != LERP) tN += (double)wn;
-          p[j] = (MODE == LERP) ? wl : wn;
+          if (is_nearest(MODE)) tN += (double)wn;
+          p[j] = is_nearest(MODE) ? wn : wl;
           pl[j] = wl;
         }
       };
       if (full) weigh(std::false_type{}, std::true_type{});
       else weigh(std::true_type{}, std::true_type{});
-      if (__any(risky != 0u)) {
+      if (__any((risky | riske) != 0u)) {
         // rare: the exact scores replace the stored ones (this lane stored them) for every later
-        // pass, and the half tile is weighed again on them
-        uint32_t bits = risky;
+        // pass, and the half tile is weighed again on them (the exponential baselines weigh only
+        // the keys concerned again: their weights do not depend on one another; a key in riske
+        // keeps its score and has its weight taken in exact form)
+        uint32_t bits = risky | riske;
         while (__any(bits != 0u)) {
           const int j = bits ? __builtin_ctz(bits) : 0;
           if (bits) {
-            const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
-            Sw[(8 * b + j) * 64] = xe;
+            float xe = s[8 * b];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) s[8 * b + jj] = jj == j ? xe : s[8 * b + jj];
+            for (int jj = 1; jj < 8; ++jj) xe = jj == j ? s[8 * b + jj] : xe;
+            if ((risky >> j) & 1u) {
+              xe = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
+              Sw[(8 * b + j) * 64] = xe;
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) s[8 * b + jj] = jj == j ? xe : s[8 * b + jj];
+            }
+            if constexpr (CAL == EXPB) {
+              const float we = exp_weight_exact<MODE>(xe, M).w;
+              float old = 0.f;
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                old = jj == j ? p[jj] : old;
+                p[jj] = jj == j ? we : p[jj];
+                pl[jj] = jj == j ? we : pl[jj];
+              }
+              tL += (double)we - (double)old;
+            }
             bits &= bits - 1u;
           }
         }
-        if (full) weigh(std::false_type{}, std::false_type{});
-        else weigh(std::true_type{}, std::false_type{});
+        if constexpr (CAL != EXPB) {
+          if (full) weigh(std::false_type{}, std::false_type{});
+          else weigh(std::true_type{}, std::false_type{});
+        }
       }
       sumL += tL;
       sumN += tN;
@@ -554,9 +590,9 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     sumL += sm.sL[u][c];
     sumN += sm.sN[u][c];
   }
-  const float WLf = (float)sumL, WNf = (MODE == LERP) ? WLf : (float)sumN;
+  const float WLf = (float)sumL, WNf = is_nearest(MODE) ? (float)sumN : WLf;
   if (g == 0) {
-    sm.rowW[c] = (MODE == LERP) ? WLf : WNf;
+    sm.rowW[c] = is_nearest(MODE) ? WNf : WLf;
     sm.rowWL[c] = WLf;
     if (qvalid) {
       const size_t row = (size_t)head * T + qi;
@@ -586,11 +622,12 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 
 template <int D, int CAL, typename TIn>
 size_t fwd_smem_bytes(int K, int lres) {
-  return sizeof(FwdSmem<D, nslices<TIn>()>) + sizeof(float) * (CAL == MINMAX ? BN * (K + 1) : lres + K + 1);
+  return sizeof(FwdSmem<D, nslices<TIn>()>) +
+         sizeof(float) * (CAL == MINMAX ? BN * (K + 1) : (CAL == EXPB ? 0 : lres + K + 1));
 }
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
-template <int CAL, bool NEAREST>
+template <int CAL, int MODE>
 __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, nt = a.rec.nt;
@@ -612,10 +649,19 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
       const bool ok = stored && (!a.causal || key <= qi);
       uint8_t val = 255;
       if (ok) {
-        const Decision d = decide<CAL>(St[v * 64 + l], rc, K, a.tau);
-        const int idx = NEAREST ? d.r + (d.t >= 0.5f ? 1 : 0) : d.r;
-        // resolved grid: the index + 64, indices below -64 sharing the value 0
-        val = d.tail ? 254 : (uint8_t)(CAL == FWM_RES ? max(idx + 64, 0) : idx);
+        if constexpr (CAL == EXPB) {
+          // exponential baselines: the E4M3 byte of the weight (FP8), the low byte of the
+          // bfloat16 weight (BF16), 0 (softmax)
+          const float M = a.rec.M[row];
+          if (MODE == EXPF8) val = (uint8_t)e4m3_code(exp_weight_exact<EXPF8>(St[v * 64 + l], M).w);
+          else if (MODE == EXPBF) val = (uint8_t)(__float_as_uint(exp_weight_exact<EXPBF>(St[v * 64 + l], M).w) >> 16);
+          else val = 0;
+        } else {
+          const Decision d = decide<CAL>(St[v * 64 + l], rc, K, a.tau);
+          const int idx = MODE == LERP ? d.r : d.r + (d.t >= 0.5f ? 1 : 0);
+          // resolved grid: the index + 64, indices below -64 sharing the value 0
+          val = d.tail ? 254 : (uint8_t)(CAL == FWM_RES ? max(idx + 64, 0) : idx);
+        }
       }
       a.bins[(size_t)head * T * T + (size_t)qi * T + key] = val;
     }
@@ -636,10 +682,15 @@ static hipError_t fwd_dt(const Problem& p, const FwdArgs& a, hipStream_t s) {
 }
 template <int D, int CAL>
 static hipError_t fwd_md(const Problem& p, const FwdArgs& a, hipStream_t s) {
-  switch (p.mode) {
-    case LERP: return fwd_dt<D, CAL, LERP>(p, a, s);
-    case NEAREST_W: return fwd_dt<D, CAL, NEAREST_W>(p, a, s);
-    default: return fwd_dt<D, CAL, NEAREST_P>(p, a, s);
+  if constexpr (CAL == EXPB) {
+    if (p.mode == EXPF8) return fwd_dt<D, CAL, EXPF8>(p, a, s);
+    return p.mode == EXPBF ? fwd_dt<D, CAL, EXPBF>(p, a, s) : fwd_dt<D, CAL, EXP32>(p, a, s);
+  } else {
+    switch (p.mode) {
+      case LERP: return fwd_dt<D, CAL, LERP>(p, a, s);
+      case NEAREST_W: return fwd_dt<D, CAL, NEAREST_W>(p, a, s);
+      default: return fwd_dt<D, CAL, NEAREST_P>(p, a, s);
+    }
   }
 }
 template <>
@@ -647,14 +698,19 @@ hipError_t forward_cal<KIA_CAL>(const Problem& p, const FwdArgs& a, hipStream_t 
   return p.D == 128 ? fwd_md<128, KIA_CAL>(p, a, s) : fwd_md<64, KIA_CAL>(p, a, s);
 }
 
-template <int CAL, bool NEAREST>
+template <int CAL, int MODE>
 static hipError_t bins_go(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bins_kernel<CAL, NEAREST>), dim3(p.nheads * a.rec.nt), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bins_kernel<CAL, MODE>), dim3(p.nheads * a.rec.nt), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <>
 hipError_t bins_cal<KIA_CAL>(const Problem& p, const BinsArgs& a, hipStream_t s) {
-  return p.mode == LERP ? bins_go<KIA_CAL, false>(p, a, s) : bins_go<KIA_CAL, true>(p, a, s);
+  if constexpr (KIA_CAL == EXPB) {
+    if (p.mode == EXPF8) return bins_go<KIA_CAL, EXPF8>(p, a, s);
+    return p.mode == EXPBF ? bins_go<KIA_CAL, EXPBF>(p, a, s) : bins_go<KIA_CAL, EXP32>(p, a, s);
+  } else {
+    return p.mode == LERP ? bins_go<KIA_CAL, LERP>(p, a, s) : bins_go<KIA_CAL, NEAREST_W>(p, a, s);
+  }
 }
 
 }  // namespace kia

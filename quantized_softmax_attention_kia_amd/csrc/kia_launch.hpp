@@ -11,13 +11,17 @@ namespace kia {
 // MinMax, and FWM under its three tail policies: keys below the window weigh 0 (FWM), sit on
 // the window edge with weight e^{-tau} and no slope (FWM_FLOOR), or stay on the grid continued
 // below -tau (FWM_RES)
-enum Calib { MINMAX = 0, FWM = 1, FWM_FLOOR = 2, FWM_RES = 3 };
-constexpr int NCALIB = 4;
+// EXPB: the exponential baselines (no grid: the row maximum alone shifts the scores)
+enum Calib { MINMAX = 0, FWM = 1, FWM_FLOOR = 2, FWM_RES = 3, EXPB = 4 };
+constexpr int NCALIB = 5;
 // grid levels below the window held in the FWM_RES table (lower ones are computed on the fly)
 constexpr int LRES_MAX = 1024;
 // reconstruction and surrogate: LERP; Nearest with the Weight-STE point (P^N, W^N);
 // Nearest with the Prob-STE point (P^L, W^L)
-enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2 };
+enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2,
+            // under EXPB: softmax, BF16-exp, FP8-rounded exp
+            EXP32 = 3, EXPBF = 4, EXPF8 = 5 };
+constexpr bool is_nearest(int mode) { return mode == NEAREST_W || mode == NEAREST_P; }
 // backward kernels by gradient mode: the calibration sums (full, max_only, min_only), the
 // detached extrema, or the detached gradient projected onto zero-sum rows (P1)
 enum GradKind { GK_SUMS = 0, GK_DETACHED = 1, GK_P1 = 2 };
@@ -106,6 +110,7 @@ KIA_DECLARE_CAL(MINMAX)
 KIA_DECLARE_CAL(FWM)
 KIA_DECLARE_CAL(FWM_FLOOR)
 KIA_DECLARE_CAL(FWM_RES)
+KIA_DECLARE_CAL(EXPB)
 #undef KIA_DECLARE_CAL
 // the dK, dV kernel (independent of the calibration; built with KIA_CAL = 0)
 hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s);
@@ -115,7 +120,8 @@ inline hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t
     case MINMAX: return forward_cal<MINMAX>(p, a, s);
     case FWM: return forward_cal<FWM>(p, a, s);
     case FWM_FLOOR: return forward_cal<FWM_FLOOR>(p, a, s);
-    default: return forward_cal<FWM_RES>(p, a, s);
+    case FWM_RES: return forward_cal<FWM_RES>(p, a, s);
+    default: return forward_cal<EXPB>(p, a, s);
   }
 }
 // stages: bit 0 = dq kernel (dQ and the P, dS tiles), bit 1 = dkdv kernel (dK, dV)
@@ -126,7 +132,8 @@ inline hipError_t launch_backward(const Problem& p, const BwdArgs& a, hipStream_
       case MINMAX: e = dq_cal<MINMAX>(p, a, s); break;
       case FWM: e = dq_cal<FWM>(p, a, s); break;
       case FWM_FLOOR: e = dq_cal<FWM_FLOOR>(p, a, s); break;
-      default: e = dq_cal<FWM_RES>(p, a, s); break;
+      case FWM_RES: e = dq_cal<FWM_RES>(p, a, s); break;
+      default: e = dq_cal<EXPB>(p, a, s); break;
     }
     if (e != hipSuccess) return e;
   }
@@ -137,7 +144,8 @@ inline hipError_t launch_bins(const Problem& p, const BinsArgs& a, hipStream_t s
     case MINMAX: return bins_cal<MINMAX>(p, a, s);
     case FWM: return bins_cal<FWM>(p, a, s);
     case FWM_FLOOR: return bins_cal<FWM_FLOOR>(p, a, s);
-    default: return bins_cal<FWM_RES>(p, a, s);
+    case FWM_RES: return bins_cal<FWM_RES>(p, a, s);
+    default: return bins_cal<EXPB>(p, a, s);
   }
 }
 

@@ -73,6 +73,8 @@ class Variant:
 
     @property
     def name(self) -> str:
+        if self.recon in ("softmax", "exp_bf16", "exp_fp8"):
+            return f"{self.recon}-{self.grad}"
         ste = "" if self.recon == "lerp" else f"-{self.ste}"
         cal = "minmax" if self.calib == "minmax" else f"fwm{self.tau:g}"
         if self.tail != "zero":

@@ -75,6 +75,7 @@ def test_workspace_layout(kb):
     (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=5), -1), (dict(grad=-1), -1), (dict(dtype=7), -1),
     (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1),
     (dict(tail=1), -1), (dict(tail=2), -1), (dict(calib=1, tail=3), -1), (dict(calib=1, tail=-1), -1),
+    (dict(recon=2, calib=1, tail=1), -1), (dict(recon=4, calib=1, tail=2), -1),
 ])
 def test_rejects_bad_params(kb, bad, status):
     p = params(kb, **bad)

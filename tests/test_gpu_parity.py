@@ -25,6 +25,8 @@ ABLATIONS = [(c, r, s, g) for c in ("minmax", "fwm") for (r, s) in (("lerp", "pr
 # the FWM tail policies (floored and resolved tails), as (calib, recon, ste, grad, tail)
 TAILS = [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("lerp", "prob"), ("nearest", "weight"),
          ("nearest", "prob")) for g in ("full", "detached", "p1")]
+# the exponential baselines (softmax, BF16-exp, FP8-rounded exp); calib, K, tau, ste are ignored
+EXPS = [("fwm", r, "prob", g) for r in ("softmax", "exp_bf16", "exp_fp8") for g in ("full", "detached", "p1")]
 
 
 @pytest.fixture(scope="module")
@@ -130,6 +132,18 @@ def test_small_tail_policies(kb, variant, shape):
     say("   ", rep)
 
 
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n") + s[6])
+@pytest.mark.parametrize("variant", EXPS, ids=lambda v: "-".join(v))
+def test_small_exp_baselines(kb, variant, shape):
+    B, H, T, D, causal, seed, dtype = shape
+    q, k, v, do = make_inputs(B, H, T, D, seed, dtype=dtype, q_scale=2.0)
+    full = variant + (4, 8.0)
+    say(f"[exp baseline] {shape} {full}")
+    got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
+    rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
+    say("   ", rep)
+
+
 @pytest.mark.parametrize("K,tau", [(4, 6.0), (16, 2.0), (64, 1.0)])
 @pytest.mark.parametrize("recon,ste", [("lerp", "prob"), ("nearest", "weight")])
 def test_resolved_grid_depth(kb, recon, ste, K, tau):
@@ -146,7 +160,8 @@ def test_resolved_grid_depth(kb, recon, ste, K, tau):
 
 @pytest.mark.parametrize("variant", [("minmax", "lerp"), ("minmax", "nearest"), ("fwm", "lerp"), ("fwm", "nearest"),
                                      ("fwm", "lerp", "floor"), ("fwm", "nearest", "floor"),
-                                     ("fwm", "lerp", "resolved"), ("fwm", "nearest", "resolved")],
+                                     ("fwm", "lerp", "resolved"), ("fwm", "nearest", "resolved"),
+                                     ("fwm", "softmax"), ("fwm", "exp_bf16"), ("fwm", "exp_fp8")],
                          ids=lambda v: "-".join(v))
 @pytest.mark.parametrize("K", [1, 4, 16, 64])
 def test_bins_bitexact(kb, variant, K):
