@@ -69,8 +69,11 @@
 #endif
 
 enum { KO_MINMAX = 0, KO_FWM = 1 };
-/* reconstructions; SOFTMAX, EXP_BF16 and EXP_FP8 are the exponential baselines (no grid) */
-enum { KO_LERP = 0, KO_NEAREST = 1, KO_SOFTMAX = 2, KO_EXP_BF16 = 3, KO_EXP_FP8 = 4 };
+/* reconstructions; SOFTMAX, EXP_BF16 and EXP_FP8 are the exponential baselines (no grid);
+   BINMEAN weighs each Nearest bin by the mean of e^z over its members, NEAREST_BINMEAN is the
+   strict Nearest forward with the bin-mean backward */
+enum { KO_LERP = 0, KO_NEAREST = 1, KO_SOFTMAX = 2, KO_EXP_BF16 = 3, KO_EXP_FP8 = 4, KO_BINMEAN = 5,
+       KO_NEAREST_BINMEAN = 6 };
 enum { KO_WEIGHT_STE = 0, KO_PROB_STE = 1 };
 enum { KO_FULL = 0, KO_DETACHED = 1, KO_MAX_ONLY = 2, KO_MIN_ONLY = 3, KO_P1 = 4 };
 enum { KO_TAIL_ZERO = 0, KO_TAIL_FLOOR = 1, KO_TAIL_RESOLVED = 2 };
@@ -103,7 +106,9 @@ enum {
   MUT_RESOLVED_GRID_CLAMP = 22, /* the resolved grid reads the table's end values below the window */
   MUT_FP8_TRUNCATES = 23,   /* FP8-rounded exp rounds toward zero */
   MUT_BF16_GRAD_UNROUNDED = 24, /* BF16-exp backward keeps the fp32 gradient (no bf16 casts) */
-  MUT_FP8_DELTA_ROUNDED = 25  /* FP8-rounded exp backward uses the rounded weight as derivative */
+  MUT_FP8_DELTA_ROUNDED = 25, /* FP8-rounded exp backward uses the rounded weight as derivative */
+  MUT_BINMEAN_SUM = 26,     /* a bin weighs the sum of e^z over its members, not the mean */
+  MUT_BINMEAN_OWN_G = 27    /* the bin-mean backward keeps each key's own upstream gradient */
 };
 
 typedef struct {
@@ -357,7 +362,7 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
                         double *u_out, int32_t *r_out, double *t_out, int32_t *ell_out, uint8_t *tail_out,
                         double *rowd, int32_t *rowi, int row_id, const int32_t *key_id, ko_flags_t *flags,
                         const double *eb, const double *gabs, double *amb) {
-  if (cfg->recon >= KO_SOFTMAX) {
+  if (cfg->recon >= KO_SOFTMAX && cfg->recon <= KO_EXP_FP8) {
     ko_row_exp(cfg, n, s, g, gabs, flip, P, dS, PL_out, u_out, r_out, t_out, ell_out, tail_out, rowd, rowi,
                row_id, key_id, flags, eb, amb);
     return;
@@ -365,6 +370,8 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
   const int K = cfg->K;
   const int mut = cfg->mutation;
   const int tailp = cfg->calib == KO_FWM ? cfg->tail : KO_TAIL_ZERO;
+  const int binmean = cfg->recon == KO_BINMEAN || cfg->recon == KO_NEAREST_BINMEAN;
+  const int nearest_bins = cfg->recon == KO_NEAREST || binmean;
   double *E = (double *)malloc(sizeof(double) * (K + 1));
   double *bgrid = (double *)malloc(sizeof(double) * (K + 1));
   double *u = (double *)malloc(sizeof(double) * n);
@@ -439,7 +446,7 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
       if ((tailp == KO_TAIL_RESOLVED || (K >= 2 && kint >= 1)) && kint <= K - 1 && fabs(uj - kint) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_INTERVAL, fabs(uj - kint));
       double khalf = floor(uj) + 0.5;
-      if (cfg->recon == KO_NEAREST && khalf < K && fabs(uj - khalf) < gj)
+      if (nearest_bins && khalf < K && fabs(uj - khalf) < gj)
         flag_push(flags, row_id, key_id ? key_id[j] : j, FLIP_NEAREST, fabs(uj - khalf));
     }
     int rj = (mut == MUT_INTERVAL_ROUND) ? (int)floor(uj + 0.5) : (int)floor(uj);
@@ -486,14 +493,58 @@ static void ko_row_impl(const ko_cfg_t *cfg, int n, const double *s, const doubl
   /* --- normalization (§3) and strict hard forward (App. C.2 (iii)) --- */
   double WL = 0.0, WN = 0.0;
   for (int j = 0; j < n; ++j) { WL += wL[j]; WN += wN[j]; }
-  int nearest_fwd = (cfg->recon == KO_NEAREST) && (mut != MUT_NEAREST_FWD_LERP);
+  int nearest_fwd = (cfg->recon == KO_NEAREST || cfg->recon == KO_NEAREST_BINMEAN) && (mut != MUT_NEAREST_FWD_LERP);
   for (int j = 0; j < n; ++j) {
     P[j] = nearest_fwd ? wN[j] / WN : wL[j] / WL;
     if (PL_out) PL_out[j] = (mut == MUT_DV_WITH_PL) ? wL[j] / WL : P[j];
   }
 
   double a = 0.0, b = 0.0, Dsum = 0.0;
-  if (g) {
+  if (binmean) {
+    /* --- bin-mean reconstruction (§5 and App. I: each bin's weight is the mean of exp over its
+       members, so bin mass is conserved; its backward is the exact derivative, the bins held
+       fixed).  Bins are the Nearest bins l = 0..K of the row's calibration; keys below an FWM
+       window belong to none and weigh 0.  Under NEAREST_BINMEAN (App. I.3) the forward stays
+       the strict Nearest one and only the backward is the bin mean's. --- */
+    double *Sb = (double *)calloc(K + 1, sizeof(double)), *Gb = (double *)calloc(K + 1, sizeof(double));
+    int *nb = (int *)calloc(K + 1, sizeof(int));
+    double *ez = (double *)malloc(sizeof(double) * n);
+    for (int j = 0; j < n; ++j) {
+      ez[j] = tail[j] ? 0.0 : exp(s[j] - M);
+      if (tail[j]) continue;
+      Sb[ell[j]] += ez[j];
+      nb[ell[j]] += 1;
+      if (g) Gb[ell[j]] += g[j];
+    }
+    double WC = 0.0;
+    for (int j = 0; j < n; ++j) {
+      wL[j] = tail[j] ? 0.0 : (mut == MUT_BINMEAN_SUM ? Sb[ell[j]] : Sb[ell[j]] / nb[ell[j]]);
+      WC += wL[j];
+    }
+    WL = WC;                                   /* the bin-mean normalizer, recorded as W^L */
+    for (int j = 0; j < n; ++j) {
+      if (cfg->recon == KO_BINMEAN) P[j] = wL[j] / WC;
+      if (PL_out) PL_out[j] = P[j];            /* dV takes the forward's value */
+    }
+    if (g) {
+      /* dL/ds_k = P^E_k (gbar_{B(k)} - sum_j P^C_j g_j) with P^E_k = e^{z_k} / W^C and gbar_B
+         the mean of g over bin B: the upstream gradient replaced by its bin average */
+      for (int j = 0; j < n; ++j) Dsum += wL[j] / WC * g[j];
+      for (int j = 0; j < n; ++j) {
+        if (tail[j]) { dS[j] = 0.0; continue; }
+        const double gbar = mut == MUT_BINMEAN_OWN_G ? g[j] : Gb[ell[j]] / nb[ell[j]];
+        dS[j] = ez[j] / WC * (gbar - Dsum);
+        gam[j] = (g[j] - Dsum) / WC;
+        Delta[j] = 0.0;
+      }
+      if (cfg->grad == KO_P1) {               /* the rows already sum to zero; kept for form */
+        double sum = 0.0;
+        for (int j = 0; j < n; ++j) sum += dS[j];
+        for (int j = 0; j < n; ++j) dS[j] -= sum / n;
+      }
+    }
+    free(Sb); free(Gb); free(nb); free(ez);
+  } else if (g) {
     /* --- normalization Jacobian (App. B): gamma_j = (g_j - sum_i P_i g_i)/W,
        at (P^L, W^L) for LERP and Prob-STE, at (P^N, W^N) for Weight-STE --- */
     int use_lerp_point = (cfg->recon == KO_LERP) || (cfg->ste == KO_PROB_STE) || (mut == MUT_WSTE_USES_LERP);
@@ -592,6 +643,8 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
   if (!cfg || n < 1 || cfg->K < 1 || !s || !P || (g && !dS)) return -1;
   if (cfg->calib == KO_FWM && !(cfg->tau > 0.0)) return -1;
   if (cfg->tail < KO_TAIL_ZERO || cfg->tail > KO_TAIL_RESOLVED || (cfg->calib == KO_MINMAX && cfg->tail != 0)) return -1;
+  if (cfg->recon < KO_LERP || cfg->recon > KO_NEAREST_BINMEAN) return -1;
+  if (cfg->recon >= KO_BINMEAN && cfg->tail != KO_TAIL_ZERO) return -1;   /* bin mean: zero tail only */
   if (u && !(r && t && ell && tail)) return -1;
   ko_row_impl(cfg, n, s, g, flip, P, dS, NULL, u, r, t, ell, tail, rowd, rowi, 0, NULL, NULL, NULL, NULL, NULL);
   return 0;
@@ -626,6 +679,8 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
   if (dO && !(dQ && dK && dV)) return -1;
   if (cfg->K < 1 || (cfg->calib == KO_FWM && !(cfg->tau > 0.0))) return -1;
   if (cfg->tail < KO_TAIL_ZERO || cfg->tail > KO_TAIL_RESOLVED || (cfg->calib == KO_MINMAX && cfg->tail != 0)) return -1;
+  if (cfg->recon < KO_LERP || cfg->recon > KO_NEAREST_BINMEAN) return -1;
+  if (cfg->recon >= KO_BINMEAN && cfg->tail != KO_TAIL_ZERO) return -1;   /* bin mean: zero tail only */
   const int mut = cfg->mutation;
   ko_flags_t fl_store, *fl = NULL;
   if (flag_cap > 0 && flag_pos && flag_dist) {

@@ -25,7 +25,9 @@ _LIB_PATH = os.path.join(_HERE, "libkia_oracle.so")
 CALIB = {"minmax": 0, "fwm": 1}
 # softmax, exp_bf16, exp_fp8: the exponential baselines (App. B "Softmax", App. D.5); they ignore
 # calib, K, tau and ste
-RECON = {"lerp": 0, "nearest": 1, "softmax": 2, "exp_bf16": 3, "exp_fp8": 4}
+# binmean: each Nearest bin weighs the mean of e^z over its members; nearest_binmean: the strict
+# Nearest forward with the bin-mean backward (App. I.3); both ignore ste
+RECON = {"lerp": 0, "nearest": 1, "softmax": 2, "exp_bf16": 3, "exp_fp8": 4, "binmean": 5, "nearest_binmean": 6}
 STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 TAIL = {"zero": 0, "floor": 1, "resolved": 2}
@@ -38,7 +40,7 @@ MUTATIONS = {
     "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
     "x_index": 17, "detach_keeps_m": 18, "only_swapped": 19, "p1_skip_tail": 20,
     "floor_tail_slope": 21, "resolved_grid_clamp": 22, "fp8_truncates": 23, "bf16_grad_unrounded": 24,
-    "fp8_delta_rounded": 25,
+    "fp8_delta_rounded": 25, "binmean_sum": 26, "binmean_own_g": 27,
 }
 ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
 ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")

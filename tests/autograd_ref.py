@@ -29,6 +29,11 @@ then carries the gradient through the bfloat16 tensors in bfloat16); FP8-rounded
 exp (e^z cast to float8_e4m3fn and back, plus e^z - sg(e^z), so the forward is
 the rounded value and the derivative that of e^z).  The row maximum stays on the
 gradient path (detached only in the detached, min_only and P1 modes).
+
+Bin mean (§5, App. I; App. I.3 for the hybrid): the Nearest bins are taken from
+the detached scores; each in-window key weighs the mean of e^z over its bin (a
+scatter-add of torch.exp); the hybrid returns sg(P^N) + (P^C - sg(P^C)), so its
+forward is the strict Nearest one and its gradient the bin mean's.
 """
 import torch
 
@@ -109,6 +114,19 @@ def row_probs(s, mask, calib, recon, ste, grad, K, tau=8.0, tail_policy="zero"):
     zero = torch.zeros_like(wL)
     wL = torch.where(keep, wL, zero)
     wN = torch.where(keep, wN, zero)
+    if recon in ("binmean", "nearest_binmean"):
+        # bins fixed (detached decisions); values e^{s - M} depend on the scores alone
+        Mv = torch.where(mask, s, -pos_inf).amax(dim=1, keepdim=True).detach()
+        ez = torch.where(keep, torch.exp(torch.where(keep, s - Mv, zero)), zero)
+        bins = torch.where(keep, ell, torch.full_like(ell, K + 1))
+        S = torch.zeros(R, K + 2, dtype=dt).scatter_add(1, bins, ez)
+        cnt = torch.zeros(R, K + 2, dtype=dt).scatter_add(1, bins, keep.to(dt))
+        wC = torch.where(keep, S.gather(1, bins) / cnt.gather(1, bins).clamp_min(1.0), zero)
+        PC = wC / wC.sum(dim=1, keepdim=True)
+        if recon == "binmean":
+            return PC
+        PN = (wN / wN.sum(dim=1, keepdim=True)).detach()
+        return PN + (PC - PC.detach())
     if recon == "lerp":
         return wL / wL.sum(dim=1, keepdim=True)
     if ste == "weight":

@@ -40,9 +40,9 @@ def load_cases(name="hand_rows.txt"):
             if key == "case":
                 cur = {"case": val}
                 cases.append(cur)
-            elif key in ("calib", "tail_policy"):
+            elif key in ("calib", "tail_policy", "recon"):
                 cur[key] = val
             else:
                 vals = [_eval(v) for v in val.split(",")]
-                cur[key] = vals if len(vals) > 1 or key in ("s", "u", "r", "t", "ell", "wL", "wN", "tail") else vals[0]
+                cur[key] = vals if len(vals) > 1 or key in ("s", "u", "r", "t", "ell", "wL", "wN", "wC", "tail") else vals[0]
     return cases

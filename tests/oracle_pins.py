@@ -51,6 +51,9 @@ VARIANTS += [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in 
 # the exponential baselines (App. B "Softmax", App. D.5): no grid; calib, K, tau and ste are ignored
 EXP_RECON = ("softmax", "exp_bf16", "exp_fp8")
 VARIANTS += [("fwm", r, "prob", g) for r in EXP_RECON for g in ("full", "detached", "max_only", "min_only", "p1")]
+# bin-mean reconstruction and the Nearest-forward / bin-mean-backward hybrid (§5, App. I)
+BINMEAN = ("binmean", "nearest_binmean")
+VARIANTS += [(c, r, "prob", g) for c in ("minmax", "fwm") for r in BINMEAN for g in ("full", "detached", "p1")]
 
 
 def is_exp(cfg):
@@ -66,8 +69,8 @@ def zero_sum_mode(cfg):
     """Modes whose row score gradients sum to zero: full, P1, and max_only where there is no
     minimum channel (FWM, the exponential baselines: max_only is their full gradient); every
     mode of softmax."""
-    if cfg.recon == "softmax":
-        return True   # the maximum's term vanishes: softmax is shift invariant in every mode
+    if cfg.recon in ("softmax",) + BINMEAN:
+        return True   # no extremum term: shift invariant in every mode
     return cfg.grad in ("full", "p1") or (max_only_calib(cfg) and cfg.grad == "max_only")
 
 
@@ -220,7 +223,9 @@ def pin_zero_sum(cfg):
         res = ORC.row(cfg, s, g)
         tot, mag = abs(res["dS"].sum()), np.abs(res["dS"]).sum()
         if zero_sum_mode(cfg):
-            assert tot <= 1e-12 * mag + 1e-300, f"zero-sum violated: {tot} vs {mag}"
+            # rounding of O(1) terms: an absolute 1e-15 besides the relative bound (a row's
+            # gradient can be tiny when its bins average the upstream gradient away)
+            assert tot <= 1e-12 * mag + 1e-15, f"zero-sum violated: {tot} vs {mag}"
         elif tot > 1e-6 * mag:
             nonzero += 1
     if not zero_sum_mode(cfg):
@@ -267,7 +272,7 @@ def _weights(res, recon):
 def pin_reconstruction_bounds(cfg):
     """LERP is a chord of the convex e^z: above it, by at most h^2/8 e^{z+h};
     Nearest picks a grid value within h/2 of z in score coordinates."""
-    if is_exp(cfg):
+    if is_exp(cfg) or cfg.recon == "binmean":   # bin means: pin_binmean
         return
     for s, g in _random_rows(31, cfg):
         res = ORC.row(cfg, s, g)
@@ -333,7 +338,7 @@ def pin_finite_differences(cfg):
         return float((ORC.head(cfg, Qx, Kx, Vx, None, nthreads=1)["O"] * dO).sum())
 
     targets = [("V", "dV")]
-    if cfg.recon in ("lerp", "softmax") and cfg.grad == "full":
+    if cfg.recon in ("lerp", "softmax", "binmean") and cfg.grad == "full":
         targets += [("Q", "dQ"), ("K", "dK")]
     for name, gname in targets:
         for _ in range(8):
@@ -393,6 +398,8 @@ def pin_special_cases(cfg):
         res = ORC.row(cfg, s, g)
         w = _weights(res, cfg.recon)
         assert abs(res["P"].sum() - 1.0) <= 1e-14, "probabilities do not sum to 1"
+        if cfg.recon == "binmean":
+            continue   # the arg-max key's bin is averaged; pin_binmean covers it
         assert abs(w[res["amax"]] - 1.0) <= 1e-14, "weight at the argmax is not 1"
         if cfg.calib == "minmax":
             assert abs(w[res["amin"]] - math.exp(res["m"] - res["M"])) <= 1e-14, "weight at the argmin"
@@ -438,6 +445,8 @@ def pin_golden(cfg):
     for case in golden_io.load_cases():
         if case["calib"] != cfg.calib or case.get("tail_policy", "zero") != cfg.tail:
             continue
+        if (case.get("recon") == "binmean") != (cfg.recon == "binmean"):
+            continue
         c = dataclasses.replace(cfg, K=int(case["K"]), tau=float(case.get("tau", cfg.tau)))
         s = np.array(case["s"], dtype=np.float64)
         g = np.linspace(-1.0, 1.0, len(s))
@@ -447,9 +456,9 @@ def pin_golden(cfg):
         assert list(res["r"]) == [int(x) for x in case["r"]], f"{name}: r"
         _close(res["t"], case["t"], 0.0, 1e-15, f"{name}: t")
         assert list(res["tail"].astype(int)) == [int(x) for x in case["tail"]], f"{name}: tail"
-        if c.recon == "nearest":
+        if c.recon != "lerp":
             assert list(res["ell"]) == [int(x) for x in case["ell"]], f"{name}: ell"
-        w = np.array(case["wL" if c.recon == "lerp" else "wN"])
+        w = np.array(case["wC"] if c.recon == "binmean" else case["wL" if c.recon == "lerp" else "wN"])
         _close(res["P"], w / w.sum(), 1e-14, 1e-16, f"{name}: P")
         for key in ("M", "m", "h"):
             assert abs(res[key] - case[key]) <= 1e-15, f"{name}: {key}"
@@ -533,7 +542,48 @@ def pin_exp_weights(cfg):
             assert np.all(bits & 0xFFFF == 0), "weights are bfloat16 values"
 
 
-PINS = [pin_golden, pin_exp_weights, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
+def pin_binmean(cfg):
+    """Bin mean (§5, App. I): every in-window key of a bin weighs the mean of e^z over the bin,
+    so bin mass is conserved (sum_j w^C_j = sum_j e^{z_j}); with every bin a singleton it is
+    softmax; its score gradient divided by e^{z_k}/W^C is constant within a bin (the upstream
+    gradient replaced by its bin average).  The hybrid (App. I.3) has the strict Nearest forward
+    bit for bit and the bin mean's backward bit for bit."""
+    if cfg.recon not in BINMEAN:
+        return
+    for s, g in _random_rows(97, cfg, count=12):
+        res = ORC.row(cfg, s, g)
+        bm = ORC.row(dataclasses.replace(cfg, recon="binmean"), s, g)
+        if cfg.recon == "nearest_binmean":
+            near = ORC.row(dataclasses.replace(cfg, recon="nearest", mutation=None), s, g)
+            assert np.array_equal(res["P"], near["P"]), "hybrid forward differs from Nearest"
+            assert np.array_equal(res["dS"], bm["dS"]), "hybrid backward differs from the bin mean's"
+            continue
+        z = s - s.max()
+        keep = ~res["tail"]
+        w = res["P"] * res["WL"]
+        _close(w.sum(), np.exp(z[keep]).sum(), 1e-13, 0.0, "bin mass conservation")
+        ratio = np.zeros_like(z)
+        ratio[keep] = res["dS"][keep] / (np.exp(z[keep]) / res["WL"])
+        for b in np.unique(res["ell"][keep]):
+            mem = keep & (res["ell"] == b)
+            e = np.exp(z[mem])
+            _close(w[mem], np.full(mem.sum(), e.mean()), 1e-13, 0.0, f"bin {b} weight is the mean of e^z")
+            if cfg.grad in ("full", "detached"):
+                _close(ratio[mem], np.full(mem.sum(), ratio[mem][0]), 1e-9, 1e-12, f"bin {b} gradient contrast")
+    # singleton bins: softmax (MinMax with K far above the number of keys)
+    if cfg.calib == "minmax":
+        s = np.random.default_rng(5).standard_normal(6) * 2.0
+        g = np.random.default_rng(6).standard_normal(6)
+        res = ORC.row(dataclasses.replace(cfg, K=4096), s, g)
+        if len(set(res["ell"].tolist())) == 6:
+            e = np.exp(s - s.max()); P = e / e.sum()
+            if cfg.recon == "binmean":   # the hybrid's forward is Nearest's
+                _close(res["P"], P, 1e-13, 1e-16, "singleton bins give softmax")
+            if cfg.grad == "full":
+                _close(res["dS"], P * (g - (P * g).sum()), 1e-10, 1e-14, "singleton bins give the softmax gradient")
+
+
+PINS = [pin_golden, pin_exp_weights, pin_binmean, pin_autograd_rows, pin_autograd_ties, pin_autograd_head, pin_zero_sum, pin_channel_additivity,
         pin_two_key,
         pin_reconstruction_bounds, pin_nearest_brute_force, pin_finite_differences, pin_shift_invariance,
         pin_degenerate_and_causal_edges, pin_special_cases, pin_k_limit, pin_tail_policy]
