@@ -103,6 +103,9 @@ def main() -> int:
                     help="gradient mode of every variant (the headline is full)")
     ap.add_argument("--tail", default="zero", choices=["zero", "floor", "resolved"],
                     help="tail policy of the FWM variants (the headline is zero, the FWM of the pages)")
+    ap.add_argument("--binmean", action="store_true",
+                    help="time bin mean and the Nearest-forward / bin-mean-backward hybrid (MinMax and FWM, "
+                         "K = 4) on the same workload instead of the K-interval variants")
     ap.add_argument("--baselines", action="store_true",
                     help="time the exponential baselines (softmax, BF16-exp, FP8-rounded exp) on the same "
                          "workload instead of the K-interval variants")
@@ -126,6 +129,9 @@ def main() -> int:
     if args.baselines:
         from quantized_softmax_attention_kia_amd.inputs import Variant
         variants = [Variant("fwm", r, "prob", "full", 4) for r in ("softmax", "exp_bf16", "exp_fp8")]
+    if args.binmean:
+        from quantized_softmax_attention_kia_amd.inputs import Variant
+        variants = [Variant(c, r, "prob", "full", 4) for c in ("minmax", "fwm") for r in ("binmean", "nearest_binmean")]
     log(f"workload {wl.name}: B={wl.B} H={wl.H} T={wl.T} D={wl.D} {wl.dtype} seed={wl.seed}; "
         f"{len(variants)} variants")
     q, k, v, do = wl.inputs()
@@ -214,7 +220,8 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    traffic = read_traffic(kernel_key) if args.grad == "full" and args.tail == "zero" and not args.baselines else None
+    headline = args.grad == "full" and args.tail == "zero" and not args.baselines and not args.binmean
+    traffic = read_traffic(kernel_key) if headline else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "

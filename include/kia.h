@@ -60,7 +60,7 @@ typedef enum {
   KIA_ERR_INVALID_ARG = -1, /* null pointer, bad size or enum value, tau <= 0 under FWM,
                                a tail policy other than zero under MinMax or an
                                exponential baseline */
-  KIA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
+  KIA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64, 128}, K > 8 for bin mean */
   KIA_ERR_WORKSPACE = -3,   /* reserved: a buffer smaller than kia_workspace_size asks */
   KIA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } kia_status_t;
@@ -76,12 +76,21 @@ typedef enum { KIA_CALIB_MINMAX = 0, KIA_CALIB_FWM = 1 } kia_calib_t;
      EXP_FP8   e^z rounded to E4M3 (float8_e4m3fn), derivative e^z (the unrounded exponential);
    roundings to nearest, ties to even, of the exact values.  The row maximum's term
    -sum_j dL/dz_j goes to the arg-max key(s) in the full and max_only modes. */
+/* BINMEAN (§5, App. I): each Nearest bin l = 0..K of the row's calibration weighs the mean of
+   e^z over its members (bin mass conserved; keys below an FWM window belong to no bin); its
+   backward is the exact derivative with the bins fixed: dL/ds_k = e^{z_k}/W^C (gbar_b(k) -
+   sum_j P_j g_j), gbar_b the mean of dL/dP over bin b; the extrema add nothing.
+   NEAREST_BINMEAN (App. I.3): the strict Nearest forward (P^N) with BINMEAN's backward.
+   Both ignore ste, take the zero tail only and are built for K <= 8 (KIA_ERR_UNSUPPORTED
+   above); full, detached, max_only and min_only give the same gradient, P1 projects it. */
 typedef enum {
   KIA_RECON_LERP = 0,
   KIA_RECON_NEAREST = 1,
   KIA_RECON_SOFTMAX = 2,
   KIA_RECON_EXP_BF16 = 3,
-  KIA_RECON_EXP_FP8 = 4
+  KIA_RECON_EXP_FP8 = 4,
+  KIA_RECON_BINMEAN = 5,
+  KIA_RECON_NEAREST_BINMEAN = 6
 } kia_recon_t;
 /* surrogate placement; ignored under LERP (both give the LERP Jacobian) */
 typedef enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 } kia_ste_t;
@@ -191,7 +200,8 @@ kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void*
  *  rowrec: the record written by kia_forward with the same params (its stored
  *        scores and row extrema decide the bins).
  *  bins: device uint8 [B,H,T,T]: for visible keys the Nearest index l in 0..K
- *        (recon = Nearest) or the interval index r in 0..K-1 (recon = LERP);
+ *        (recon = Nearest and the bin-mean modes) or the interval index r in 0..K-1
+ *        (recon = LERP);
  *        on the resolved FWM grid (indices may be negative) the index + 64,
  *        with indices below -64 all given 0; 254 for FWM tail keys (zero and
  *        floor policies); 255 for keys the query does not see.  The exponential

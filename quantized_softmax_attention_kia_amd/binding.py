@@ -20,7 +20,7 @@ KIA_OK = 0
 STATUS = {0: "KIA_OK", -1: "KIA_ERR_INVALID_ARG", -2: "KIA_ERR_UNSUPPORTED", -3: "KIA_ERR_WORKSPACE",
           -4: "KIA_ERR_HIP"}
 CALIB = {"minmax": 0, "fwm": 1}
-RECON = {"lerp": 0, "nearest": 1, "softmax": 2, "exp_bf16": 3, "exp_fp8": 4}
+RECON = {"lerp": 0, "nearest": 1, "softmax": 2, "exp_bf16": 3, "exp_fp8": 4, "binmean": 5, "nearest_binmean": 6}
 STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}

@@ -37,7 +37,7 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
   if (p->K < 1 || p->K > 64) { set_err("K must be in 1..64 (got %d)", p->K); return KIA_ERR_INVALID_ARG; }
   if (p->causal != 0 && p->causal != 1) { set_err("causal must be 0 or 1"); return KIA_ERR_INVALID_ARG; }
   if (p->calib != KIA_CALIB_MINMAX && p->calib != KIA_CALIB_FWM) { set_err("bad calib %d", p->calib); return KIA_ERR_INVALID_ARG; }
-  if (p->recon < KIA_RECON_LERP || p->recon > KIA_RECON_EXP_FP8) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
+  if (p->recon < KIA_RECON_LERP || p->recon > KIA_RECON_NEAREST_BINMEAN) { set_err("bad recon %d", p->recon); return KIA_ERR_INVALID_ARG; }
   if (p->ste != KIA_STE_WEIGHT && p->ste != KIA_STE_PROB) { set_err("bad ste %d", p->ste); return KIA_ERR_INVALID_ARG; }
   if (p->grad < KIA_GRAD_FULL || p->grad > KIA_GRAD_P1) { set_err("bad grad %d", p->grad); return KIA_ERR_INVALID_ARG; }
   if (p->dtype != KIA_F32 && p->dtype != KIA_BF16) { set_err("bad dtype %d", p->dtype); return KIA_ERR_INVALID_ARG; }
@@ -51,10 +51,19 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
     set_err("a tail policy other than zero needs FWM (MinMax has no window)");
     return KIA_ERR_INVALID_ARG;
   }
-  const bool expb = p->recon >= KIA_RECON_SOFTMAX;
+  const bool expb = p->recon >= KIA_RECON_SOFTMAX && p->recon <= KIA_RECON_EXP_FP8;
   if (expb && p->tail != KIA_TAIL_ZERO) {
     set_err("the exponential baselines have no window: tail must be zero");
     return KIA_ERR_INVALID_ARG;
+  }
+  const bool binmean = p->recon == KIA_RECON_BINMEAN || p->recon == KIA_RECON_NEAREST_BINMEAN;
+  if (binmean && p->tail != KIA_TAIL_ZERO) {
+    set_err("bin mean takes the zero tail only");
+    return KIA_ERR_INVALID_ARG;
+  }
+  if (binmean && p->K > kia::BINM_MAXB - 1) {
+    set_err("bin mean is built for K <= %d (got %d)", kia::BINM_MAXB - 1, p->K);
+    return KIA_ERR_UNSUPPORTED;
   }
   // index ranges the kernels rely on: per-head offsets in int, grid size in int
   if (p->T > (1 << 20)) { set_err("T=%lld exceeds 2^20", (long long)p->T); return KIA_ERR_UNSUPPORTED; }
@@ -86,7 +95,9 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
     case KIA_RECON_NEAREST: pr->mode = p->ste == KIA_STE_WEIGHT ? kia::NEAREST_W : kia::NEAREST_P; break;
     case KIA_RECON_SOFTMAX: pr->mode = kia::EXP32; break;
     case KIA_RECON_EXP_BF16: pr->mode = kia::EXPBF; break;
-    default: pr->mode = kia::EXPF8; break;
+    case KIA_RECON_EXP_FP8: pr->mode = kia::EXPF8; break;
+    case KIA_RECON_BINMEAN: pr->mode = kia::BINM; break;
+    default: pr->mode = kia::NEARB; break;
   }
   pr->gk = p->grad == KIA_GRAD_DETACHED ? kia::GK_DETACHED : (p->grad == KIA_GRAD_P1 ? kia::GK_P1 : kia::GK_SUMS);
   pr->keepM = p->grad == KIA_GRAD_FULL || p->grad == KIA_GRAD_MAX_ONLY;

@@ -71,10 +71,14 @@ struct DqSmem {
   // row of lres + K + 3 floats
 };
 
-template <int D, int CAL, typename TIn>
+__host__ __device__ constexpr int dq_table_floats(int CAL, int K, int lres) {
+  return CAL == MINMAX ? DQ_BM * (K + 3) : (CAL == EXPB ? 0 : lres + K + 3);
+}
+// bin-mean modes: after the grid table, per row the bins' means of e^z and of g
+template <int D, int CAL, int MODE, typename TIn>
 size_t dq_smem_bytes(int K, int lres) {
   return sizeof(DqSmem<D, nslices<TIn>()>) +
-         sizeof(float) * (CAL == MINMAX ? DQ_BM * (K + 3) : (CAL == EXPB ? 0 : lres + K + 3));
+         sizeof(float) * (dq_table_floats(CAL, K, lres) + (is_binmean(MODE) ? 2 * DQ_BM * BINM_MAXB : 0));
 }
 
 // GK: GK_SUMS (full, max_only, min_only: the calibration sums, with the extremum terms that
@@ -173,16 +177,77 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     for (int nb = 0; nb < D / 32; ++nb) pk[nb] = zero16();
   }
 
-  PairRegs<D, TIn, NT> kr;  // K rows of the next key tile, staged as the workgroup's K^T slices
-  RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
-  kr.load(Kp, 0, T);
-  vr.load(Vp, 0, T);
+  constexpr bool BM = is_binmean(MODE);
   // stored scores of a tile: query c, key k0 + crow(v, g); loaded one tile ahead
   auto load_s = [&](int kt, float (&dst)[16]) {
     const float* St = Sh + tile_index(qtw, kt, a.rec.nt, a.causal) * 1024 + l;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dst[v] = St[v * 64];
   };
+
+  // bin-mean modes (§5, App. I): a first sweep sums, per Nearest bin of the row, e^{s - M}, the
+  // member count and the upstream gradient g (keys below an FWM window belong to no bin), per
+  // lane in registers and then over the row's two lanes; per row it keeps the bins' means of e^z
+  // and of g, W^C = sum_b S_b and D^C = sum_j P^C_j g_j, for dS_k = e^{z_k} / W^C (gbar_b(k) - D^C)
+  float* bmean = tbl + dq_table_floats(CAL, K, a.lres) + rl * BINM_MAXB;  // [DQ_BM][BINM_MAXB]
+  float* bgbar = bmean + DQ_BM * BINM_MAXB;
+  float invWC = 0.f, DC = 0.f;
+  if constexpr (BM) {
+    float bs[BINM_MAXB], bn[BINM_MAXB], bg[BINM_MAXB];
+#pragma unroll
+    for (int q = 0; q < BINM_MAXB; ++q) { bs[q] = 0.f; bn[q] = 0.f; bg[q] = 0.f; }
+    RowRegs<D, TIn, NT> vp;
+    vp.load(Vp, 0, T);
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int k0 = kt * BN;
+      __syncthreads();
+      vp.template store<NS>(sm.VN);
+      __syncthreads();
+      if (kt + 1 < ntiles) vp.load(Vp, k0 + BN, T);
+      if (!active(kt)) continue;
+      float s[16];
+      load_s(kt, s);
+      f16v gt = zero16();
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), dos[kb], gt);
+      const int lim = (qvalid ? (a.causal ? min(qi, T - 1) : T - 1) : -1) - k0 - 4 * g;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const Decision d = decide<CAL>(s[v], rc, K, a.tau);
+        const bool in = crow(v, 0) <= lim && !d.tail;
+        const int ell = d.r + (d.t >= 0.5f ? 1 : 0);
+        const float x = __expf(s[v] - M);
+#pragma unroll
+        for (int q = 0; q < BINM_MAXB; ++q) {
+          const bool hit = in && ell == q;
+          bs[q] += hit ? x : 0.f;
+          bn[q] += hit ? 1.f : 0.f;
+          bg[q] += hit ? gt[v] : 0.f;
+        }
+      }
+    }
+    float WC = 0.f, GC = 0.f;
+#pragma unroll
+    for (int q = 0; q < BINM_MAXB; ++q) {
+      bs[q] += __shfl_xor(bs[q], 32);
+      bn[q] += __shfl_xor(bn[q], 32);
+      bg[q] += __shfl_xor(bg[q], 32);
+      const float mean = bn[q] > 0.f ? bs[q] / bn[q] : 0.f, gbar = bn[q] > 0.f ? bg[q] / bn[q] : 0.f;
+      WC += bs[q];
+      GC = fmaf(bs[q], gbar, GC);
+      if (g == 0) {
+        bmean[q] = mean;
+        bgbar[q] = gbar;
+      }
+    }
+    invWC = WC > 0.f ? 1.f / WC : 0.f;
+    DC = GC * invWC;
+  }
+
+  PairRegs<D, TIn, NT> kr;  // K rows of the next key tile, staged as the workgroup's K^T slices
+  RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
+  kr.load(Kp, 0, T);
+  if (!BM) vr.load(Vp, 0, T);
   float snext[16];
   if (active(0)) load_s(0, snext);
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -195,19 +260,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     if (kt + 1 < ntiles && active(kt + 1)) load_s(kt + 1, snext);
     __syncthreads();
     kr.template store_t<NS>(sm.KT);
-    vr.template store<NS>(sm.VN);
+    if (!BM) vr.template store<NS>(sm.VN);
     __syncthreads();
     if (kt + 1 < ntiles) {
       kr.load(Kp, k0 + BN, T);
-      vr.load(Vp, k0 + BN, T);
+      if (!BM) vr.load(Vp, k0 + BN, T);
     }
     if (!act) continue;
     float* Pw = Ph + to;
     float* dSw = dSh + to;
     // (dO V^T)^T as bf16 slice products: register v holds g = dO_i . V_j for query c, key k0 + crow(v, g)
     f16v gt = zero16();
+    if (!BM) {
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), dos[kb], gt);
+      for (int kb = 0; kb < D / 16; ++kb) gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), dos[kb], gt);
+    }
     // half tiles (keys crow(v, g), v = 8 b .. 8 b + 7): decisions, weights and dS, then their share of
     // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g)).  A key
     // that is not visible, or in the FWM tail, takes the table's two zero entries (r = K + 1): its
@@ -227,7 +294,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         Decision d;
         Weights wt;
         float Delta = 0.f;
-        if constexpr (CAL == EXPB) {
+        if constexpr (BM) {
+          // bin mean: dS_k = e^{z_k} / W^C (gbar_b(k) - D^C); the forward's weight is the bin's
+          // mean (bin mean) or the grid value at the Nearest index (the hybrid)
+          d = decide<CAL>(s[v], rc, K, a.tau);
+          const bool in = crow(v, 0) <= lim && !d.tail;
+          const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), BINM_MAXB - 1);
+          dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
+          if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
+          else pw = in ? weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau).wN : 0.f;
+        } else if constexpr (CAL == EXPB) {
           // exponential baselines: the weight as the forward took it.  The forward's float form,
           // where the forward kept it, gave the exact form's value on the stored score; where it
           // retook it, the stored score is exact.  Here the float form is checked against its
@@ -522,7 +598,7 @@ hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s) {
 template <int D, int CAL, int MODE, int GK, typename TIn>
 static hipError_t dq_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
-  const size_t smem = dq_smem_bytes<D, CAL, TIn>(p.K, p.lres);
+  const size_t smem = dq_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
   hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
   return hipGetLastError();
 }
@@ -547,7 +623,17 @@ static hipError_t dq_md(const Problem& p, const BwdArgs& a, hipStream_t s) {
     switch (p.mode) {
       case LERP: return dq_gk<D, CAL, LERP>(p, a, s);
       case NEAREST_W: return dq_gk<D, CAL, NEAREST_W>(p, a, s);
-      default: return dq_gk<D, CAL, NEAREST_P>(p, a, s);
+      case NEAREST_P: return dq_gk<D, CAL, NEAREST_P>(p, a, s);
+      default:
+        // bin mean and the hybrid: no extremum terms (their values do not depend on the
+        // extrema), so only the detached and P1 kernels
+        if constexpr (CAL == MINMAX || CAL == FWM) {
+          if (p.mode == BINM)
+            return p.gk == GK_P1 ? dq_dt<D, CAL, BINM, GK_P1>(p, a, s) : dq_dt<D, CAL, BINM, GK_DETACHED>(p, a, s);
+          return p.gk == GK_P1 ? dq_dt<D, CAL, NEARB, GK_P1>(p, a, s) : dq_dt<D, CAL, NEARB, GK_DETACHED>(p, a, s);
+        } else {
+          return hipErrorInvalidValue;
+        }
     }
   }
 }

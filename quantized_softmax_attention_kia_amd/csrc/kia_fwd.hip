@@ -394,9 +394,87 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f + (float)(K + 1) * 0x1p-22f;
   const float edge = Erow + a.tau * 0x1p-21f;  // FWM window edge: margin of |(s - M) + tau|
   // MinMax: one table row per query row; FWM: one table for all rows, from lres levels below
-  // the window (resolved grid) to K
+  // the window (resolved grid) to K; bin mean: one row per query row holding the bin means
   float* trow = tbl;
-  if (CAL == MINMAX) {
+  if constexpr (MODE == BINM) {
+    // ---- bin mean (§5, App. I): a pass over the row's stored scores settles every Nearest
+    // decision as pass 2 will (float decisions checked against the bound, exact scores patched in
+    // where it cannot settle them, then the half tile decided in double), and sums e^{s - M} and
+    // the member count of each bin, per lane in registers; the sums meet per row in a fixed order
+    // and the table then holds each bin's mean, so pass 2 runs as Nearest on it.  Keys below an
+    // FWM window belong to no bin.
+    trow = tbl + c * ts;
+    float bs[BINM_MAXB], bn[BINM_MAXB];
+#pragma unroll
+    for (int q = 0; q < BINM_MAXB; ++q) { bs[q] = 0.f; bn[q] = 0.f; }
+    for (int kt = w; kt < ntiles; kt += FWD_NW) {
+      const int k0 = kt * BN;
+      float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+      float s[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint32_t risky = 0, okm = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = 8 * b + j, key = k0 + crow(v, g);
+          const bool ok = qvalid && key < T && (!a.causal || key <= qi);
+          const Decision d = decide_fast<CAL>(s[v], rc, K, a.tau);
+          bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1) || fabsf(d.t - 0.5f) < du;
+          if (CAL == FWM) r = r || fabsf((s[v] - M) + a.tau) <= edge;
+          risky |= (ok && r) ? (1u << j) : 0u;
+          okm |= ok ? (1u << j) : 0u;
+        }
+        const bool redo = __any(risky != 0u);
+        uint32_t bits = risky;
+        while (__any(bits != 0u)) {
+          const int j = bits ? __builtin_ctz(bits) : 0;
+          if (bits) {
+            const float xe = exact_score<D, TIn>(qrow, Kp + (size_t)(k0 + crow(8 * b + j, g)) * D, a.scale);
+            Sw[(8 * b + j) * 64] = xe;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) s[8 * b + jj] = jj == j ? xe : s[8 * b + jj];
+            bits &= bits - 1u;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = 8 * b + j;
+          const Decision d = redo ? decide<CAL>(s[v], rc, K, a.tau) : decide_fast<CAL>(s[v], rc, K, a.tau);
+          const int ell = d.r + (d.t >= 0.5f ? 1 : 0);
+          const bool in = ((okm >> j) & 1u) && !d.tail;
+          const float x = __expf(s[v] - M);
+#pragma unroll
+          for (int q = 0; q < BINM_MAXB; ++q) {
+            bs[q] += (in && ell == q) ? x : 0.f;
+            bn[q] += (in && ell == q) ? 1.f : 0.f;
+          }
+        }
+      }
+    }
+    // the row's two lanes of each wave, then the two waves in order
+    float* part = reinterpret_cast<float*>(sm.wave[0]);  // [wave][row][bin][sum, count]
+#pragma unroll
+    for (int q = 0; q < BINM_MAXB; ++q) {
+      bs[q] += __shfl_xor(bs[q], 32);
+      bn[q] += __shfl_xor(bn[q], 32);
+      if (g == 0) {
+        part[((w * BN + c) * BINM_MAXB + q) * 2] = bs[q];
+        part[((w * BN + c) * BINM_MAXB + q) * 2 + 1] = bn[q];
+      }
+    }
+    __syncthreads();
+    for (int q = g + 2 * w; q <= K; q += 2 * FWD_NW) {
+      float S = 0.f, n = 0.f;
+#pragma unroll
+      for (int u = 0; u < FWD_NW; ++u) {
+        S += part[((u * BN + c) * BINM_MAXB + q) * 2];
+        n += part[((u * BN + c) * BINM_MAXB + q) * 2 + 1];
+      }
+      trow[q] = n > 0.f ? S / n : 0.f;
+    }
+  } else if (CAL == MINMAX) {
     trow = tbl + c * ts;
     for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
   } else if (CAL != EXPB) {  // the exponential baselines have no grid
@@ -620,11 +698,13 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   }
 }
 
-template <int D, int CAL, typename TIn>
+template <int D, int CAL, int MODE, typename TIn>
 size_t fwd_smem_bytes(int K, int lres) {
   return sizeof(FwdSmem<D, nslices<TIn>()>) +
-         sizeof(float) * (CAL == MINMAX ? BN * (K + 1) : (CAL == EXPB ? 0 : lres + K + 1));
+         sizeof(float) * (CAL == MINMAX || MODE == BINM ? BN * (K + 1) : (CAL == EXPB ? 0 : lres + K + 1));
 }
+static_assert(sizeof(float) * 2 * BINM_MAXB * BN * FWD_NW <= FWD_NW * fwd_wave_bytes<64, 1>(),
+              "bin-mean partial sums fit the V^T staging area");
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
 template <int CAL, int MODE>
@@ -672,7 +752,7 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
 template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + BN - 1) / BN;
-  const size_t smem = fwd_smem_bytes<D, CAL, TIn>(p.K, p.lres);
+  const size_t smem = fwd_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
   hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
 }
@@ -689,7 +769,11 @@ static hipError_t fwd_md(const Problem& p, const FwdArgs& a, hipStream_t s) {
     switch (p.mode) {
       case LERP: return fwd_dt<D, CAL, LERP>(p, a, s);
       case NEAREST_W: return fwd_dt<D, CAL, NEAREST_W>(p, a, s);
-      default: return fwd_dt<D, CAL, NEAREST_P>(p, a, s);
+      case NEAREST_P: return fwd_dt<D, CAL, NEAREST_P>(p, a, s);
+      case BINM:
+        if constexpr (CAL == MINMAX || CAL == FWM) return fwd_dt<D, CAL, BINM>(p, a, s);
+        else return hipErrorInvalidValue;
+      default: return fwd_dt<D, CAL, NEAREST_W>(p, a, s);  // NEARB: the strict Nearest forward
     }
   }
 }

@@ -20,8 +20,16 @@ constexpr int LRES_MAX = 1024;
 // Nearest with the Prob-STE point (P^L, W^L)
 enum Mode { LERP = 0, NEAREST_W = 1, NEAREST_P = 2,
             // under EXPB: softmax, BF16-exp, FP8-rounded exp
-            EXP32 = 3, EXPBF = 4, EXPF8 = 5 };
-constexpr bool is_nearest(int mode) { return mode == NEAREST_W || mode == NEAREST_P; }
+            EXP32 = 3, EXPBF = 4, EXPF8 = 5,
+            // bin mean (each Nearest bin weighs the mean of e^z over its members), and the strict
+            // Nearest forward with the bin-mean backward (its forward runs as NEAREST_W)
+            BINM = 6, NEARB = 7 };
+constexpr bool is_nearest(int mode) {
+  return mode == NEAREST_W || mode == NEAREST_P || mode == BINM || mode == NEARB;
+}
+constexpr bool is_binmean(int mode) { return mode == BINM || mode == NEARB; }
+// bins of the bin-mean modes: at most 9 (K <= 8), kept per lane in registers
+constexpr int BINM_MAXB = 9;
 // backward kernels by gradient mode: the calibration sums (full, max_only, min_only), the
 // detached extrema, or the detached gradient projected onto zero-sum rows (P1)
 enum GradKind { GK_SUMS = 0, GK_DETACHED = 1, GK_P1 = 2 };

@@ -75,7 +75,7 @@ class Variant:
     def name(self) -> str:
         if self.recon in ("softmax", "exp_bf16", "exp_fp8"):
             return f"{self.recon}-{self.grad}"
-        ste = "" if self.recon == "lerp" else f"-{self.ste}"
+        ste = "" if self.recon in ("lerp", "binmean", "nearest_binmean") else f"-{self.ste}"
         cal = "minmax" if self.calib == "minmax" else f"fwm{self.tau:g}"
         if self.tail != "zero":
             cal += f"-{self.tail}"

@@ -72,10 +72,11 @@ def test_workspace_layout(kb):
 @pytest.mark.parametrize("bad,status", [
     (dict(K=0), -1), (dict(K=65), -1), (dict(D=48), -2), (dict(D=0), -1), (dict(T=-1), -1),
     (dict(calib=1, tau=0.0), -1), (dict(calib=1, tau=float("nan")), -1), (dict(calib=2), -1),
-    (dict(recon=5), -1), (dict(ste=-1), -1), (dict(grad=5), -1), (dict(grad=-1), -1), (dict(dtype=7), -1),
+    (dict(recon=9), -1), (dict(ste=-1), -1), (dict(grad=5), -1), (dict(grad=-1), -1), (dict(dtype=7), -1),
     (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1),
     (dict(tail=1), -1), (dict(tail=2), -1), (dict(calib=1, tail=3), -1), (dict(calib=1, tail=-1), -1),
     (dict(recon=2, calib=1, tail=1), -1), (dict(recon=4, calib=1, tail=2), -1),
+    (dict(recon=5, K=9), -2), (dict(recon=6, K=64), -2), (dict(recon=5, calib=1, tail=1), -1), (dict(recon=7), -1),
 ])
 def test_rejects_bad_params(kb, bad, status):
     p = params(kb, **bad)

@@ -27,6 +27,9 @@ TAILS = [("fwm", r, s, g, tp) for tp in ("floor", "resolved") for (r, s) in (("l
          ("nearest", "prob")) for g in ("full", "detached", "p1")]
 # the exponential baselines (softmax, BF16-exp, FP8-rounded exp); calib, K, tau, ste are ignored
 EXPS = [("fwm", r, "prob", g) for r in ("softmax", "exp_bf16", "exp_fp8") for g in ("full", "detached", "p1")]
+# bin mean and the Nearest-forward / bin-mean-backward hybrid (built for K <= 8)
+BINMEANS = [(c, r, "prob", g) for c in ("minmax", "fwm") for r in ("binmean", "nearest_binmean")
+            for g in ("full", "detached", "p1")]
 
 
 @pytest.fixture(scope="module")
@@ -142,6 +145,36 @@ def test_small_exp_baselines(kb, variant, shape):
     got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
     rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
     say("   ", rep)
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + ("c" if s[4] else "n") + s[6])
+@pytest.mark.parametrize("variant", BINMEANS, ids=lambda v: "-".join(v))
+def test_small_binmean(kb, variant, shape):
+    B, H, T, D, causal, seed, dtype = shape
+    q, k, v, do = make_inputs(B, H, T, D, seed, dtype=dtype, q_scale=2.0)
+    full = variant + (4, 5.0)
+    say(f"[bin mean] {shape} {full}")
+    got, _ = gpu_run(kb, full, q, k, v, do, causal=causal, dtype=dtype)
+    rep = compare_all_heads(full, q, k, v, do, got, causal=causal)
+    say("   ", rep)
+
+
+@pytest.mark.parametrize("variant", [("minmax", "binmean"), ("fwm", "binmean"), ("fwm", "nearest_binmean")],
+                         ids=lambda v: "-".join(v))
+@pytest.mark.parametrize("K", [1, 2, 8])
+def test_binmean_bins_and_sizes(kb, variant, K):
+    """Bin mean at K = 1, 2, 8 (the largest built): bins bit-exact and outputs at parity."""
+    import torch
+    q, k, v, do = make_inputs(1, 2, 150, 64, 22, q_scale=3.0)
+    full = (variant[0], variant[1], "prob", "full", K, 3.0)
+    say(f"[bin mean K] 1x2x150x64 seed=22 {full}")
+    got, (qt, kt, rowrec, p) = gpu_run(kb, full, q, k, v, do)
+    bins = kb.debug_bins(p, rowrec)
+    torch.cuda.synchronize()
+    bins = bins.cpu().numpy()
+    for h in range(2):
+        say("   ", parity.check_bins(ocfg(full), q[0, h], k[0, h], bins[0, h]))
+    say("   ", compare_all_heads(full, q, k, v, do, got))
 
 
 @pytest.mark.parametrize("K,tau", [(4, 6.0), (16, 2.0), (64, 1.0)])

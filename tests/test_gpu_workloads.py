@@ -147,6 +147,27 @@ def test_gpt2_exp_baselines_sampled_heads(kb, recon):
     assert ratio < 1e-4, ratio
 
 
+@pytest.mark.parametrize("recon", ["binmean", "nearest_binmean"])
+def test_gpt2_binmean_sampled_heads(kb, recon):
+    """Bin mean and the hybrid at the benchmark shape (FWM, K = 4, the pages' setting): sampled heads
+    against the oracle; every head's dK sums to zero over its keys."""
+    from quantized_softmax_attention_kia_amd.inputs import Variant
+    wl = WORKLOADS["gpt2"]
+    var = Variant("fwm", recon, "prob", "full", 4)
+    q, k, v, do = inputs("gpt2")
+    say(f"[gpt2 bin mean] B={wl.B} H={wl.H} T={wl.T} D={wl.D} seed={wl.seed} {recon}")
+    got = run(kb, wl, var, q, k, v, do)
+    cfg = ORC.OracleConfig.of(var)
+    for b, h in parity.pick_heads(cfg, q, k, want=2):
+        gh = {key: got[key][b, h].cpu().numpy().astype(np.float64) for key in ("O", "dQ", "dK", "dV")}
+        rep = parity.check_head(cfg, q[b, h], k[b, h], v[b, h], do[b, h], gh)
+        say(f"    head ({b},{h}): {rep}")
+    dk = got["dK"].double()
+    ratio = (dk.sum(dim=2).abs() / dk.abs().sum(dim=2).clamp_min(1e-30)).max().item()
+    say(f"    max_h |sum_j dK_j| / sum_j |dK_j| = {ratio:.2e}")
+    assert ratio < 1e-4, ratio
+
+
 def test_full_and_detached_forward_bitwise_identical(kb):
     wl = WORKLOADS["wide"]
     q, k, v, do = inputs("wide")
