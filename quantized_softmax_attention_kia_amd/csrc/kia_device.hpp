@@ -1,11 +1,12 @@
 // Device-side building blocks of the K-interval attention kernels for gfx950.
 //
-// Scores are computed once, in the forward, on the fp64 MFMA (products of fp32
-// inputs are exact in double, the sum is accumulated in double and the scale
-// applied in double) and rounded once to fp32; the forward stores them as
-// 32 x 32 tiles that every later pass reads back.  Calibration, grid tables and
-// bin decisions go through the functions below in every kernel, so all kernels
-// take the same decisions on the same stored scores.
+// Scores are computed once, in the forward, as bf16 slice products on the matrix
+// pipe with a rigorous error bound, and recomputed exactly (double products and
+// sums, one rounding to fp32) wherever that bound could change an extremum or a
+// decision; the forward stores them as 32 x 32 tiles that every later pass reads
+// back.  Calibration, grid tables and decisions go through the functions below
+// in every kernel, so all kernels take the same decisions on the same stored
+// scores.
 //
 // Operator: "Pretraining Transformers with Quantized Softmax in Attention",
 // §3 (Objects and calibration; Reconstruction) and App. A (edge cases).
@@ -20,17 +21,12 @@ namespace kia {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4v __attribute__((ext_vector_type(4)));
-typedef double d4v __attribute__((ext_vector_type(4)));
 
 constexpr int KMAX = 64;
 constexpr float DEGENERATE_EPS = 1e-12f;
 
 // ---------------------------------------------------------------------------------------------
-// 32x32x2 fp32 MFMA.  Operands: lane l supplies A[l%32][l/32] and B[l/32][l%32].
-// Accumulator: lane l, register v holds C[crow(v, l/32)][l%32].
-__device__ __forceinline__ f16v mfma32(float a, float b, f16v c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
+// 32x32 MFMA accumulator layout: lane l, register v holds C[crow(v, l/32)][l%32].
 __device__ __forceinline__ int crow(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
 __device__ __forceinline__ f16v zero16() {
@@ -38,12 +34,6 @@ __device__ __forceinline__ f16v zero16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
-}
-
-// 16x16x4 fp64 MFMA.  Operands: lane l supplies A[l%16][l/16] and B[l/16][l%16].
-// Accumulator: lane l, register v holds C[4v + l/16][l%16].
-__device__ __forceinline__ d4v mfma64(double a, double b, d4v c) {
-  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -298,115 +288,6 @@ __device__ __forceinline__ Split8 load_bt(const __bf16* xt, int b, int n) {
     r.l = rd(p + 2 * D * TP);
   }
   return r;
-}
-
-// Dimension order of a score dot product: MFMA step 4q+e takes dims 8q+e (lanes 0-31)
-// and 8q+4+e (lanes 32-63).  A lane's register operand for its own row holds, at index
-// 4q+e, dim 8q + 4(l/32) + e.
-template <int D, typename T>
-__device__ __forceinline__ void load_row_operand(float (&reg)[D / 2], const T* row, bool valid, float mul) {
-  const int g = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int q = 0; q < D / 8; ++q) {
-    f4v x = valid ? Ld<T>::four(row + 8 * q + 4 * g) : f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) reg[4 * q + e] = x[e] * mul;
-  }
-}
-
-// Tile product over the head dimension: C[a][b] = sum_d Arows[a][d] * Brow_b[d], where the
-// A rows (32 of them, stride ld floats) sit in LDS and lane l's register operand holds its
-// own B row (l%32).  Used for the dO V^T products (g_ij = dO_i . V_j).
-template <int D>
-__device__ __forceinline__ f16v tile_dot(const float* arows, int ld, const float (&breg)[D / 2]) {
-  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-  const float* row = arows + c * ld + 4 * g;
-  f16v acc = zero16();
-#pragma unroll
-  for (int q = 0; q < D / 8; ++q) {
-    f4v a = *reinterpret_cast<const f4v*>(row + 8 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma32(a[e], breg[4 * q + e], acc);
-  }
-  return acc;
-}
-
-// The same product with both operands in LDS: C[a][b] = sum_d Arows[a][d] * Brows[b][d].
-template <int D>
-__device__ __forceinline__ f16v tile_dot_lds(const float* arows, const float* brows, int ld) {
-  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-  const float* ra = arows + c * ld + 4 * g;
-  const float* rb = brows + c * ld + 4 * g;
-  f16v acc = zero16();
-#pragma unroll
-  for (int q = 0; q < D / 8; ++q) {
-    const f4v x = *reinterpret_cast<const f4v*>(ra + 8 * q);
-    const f4v y = *reinterpret_cast<const f4v*>(rb + 8 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma32(x[e], y[e], acc);
-  }
-  return acc;
-}
-
-// The same product with A's rows in registers: lane l holds row l%32 of A at the dims
-// 8q + 4(l/32) .. + 3 (q < D/8) and B's rows sit in LDS.
-template <int D>
-__device__ __forceinline__ f16v tile_dot_ra(const f4v (&arow)[D / 8], const float* brows, int ld) {
-  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-  const float* rb = brows + c * ld + 4 * g;
-  f16v acc = zero16();
-#pragma unroll
-  for (int q = 0; q < D / 8; ++q) {
-    const f4v y = *reinterpret_cast<const f4v*>(rb + 8 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma32(arow[q][e], y[e], acc);
-  }
-  return acc;
-}
-
-// Scores of one 32 (query) x 32 (key) tile in double: four 16x16 sub-tiles of S^T = K Q^T.
-// K rows (32, stride ld floats) sit in LDS; qr holds the lane's query operand:
-// qr[qb * (D/4) + 4j + e] = Q[16 qb + l%16][16 j + 4 (l/16) + e] (MFMA step 4j + e).
-// acc[kb][qb] register v = sum_d K[16 kb + 4 v + l/16][d] * Q[16 qb + l%16][d], exact products
-// accumulated in double.
-template <int D>
-__device__ __forceinline__ void score_tile_f64(const float* krows, int ld, const float (&qr)[D / 2],
-                                               d4v (&acc)[2][2]) {
-  const int l = threadIdx.x & 63, G = l >> 4, c = l & 15;
-  const float* r0 = krows + c * ld + 4 * G;
-  const float* r1 = krows + (16 + c) * ld + 4 * G;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) acc[kb][qb] = d4v{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    const f4v k0 = *reinterpret_cast<const f4v*>(r0 + 16 * j);
-    const f4v k1 = *reinterpret_cast<const f4v*>(r1 + 16 * j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double a0 = k0[e], a1 = k1[e];
-      const double b0 = qr[4 * j + e], b1 = qr[D / 4 + 4 * j + e];
-      acc[0][0] = mfma64(a0, b0, acc[0][0]);
-      acc[0][1] = mfma64(a0, b1, acc[0][1]);
-      acc[1][0] = mfma64(a1, b0, acc[1][0]);
-      acc[1][1] = mfma64(a1, b1, acc[1][1]);
-    }
-  }
-}
-
-// out[nb] += sum_v coef[v] * Brows[crow(v, g)][32 nb + l%32]: contracts the 32-long side
-// of an accumulator-layout tile (coef) with 32 LDS rows (stride ld).  Gives O += P V,
-// dQ += dS K, dV += P^T dO and dK += dS^T Q depending on which tile layout coef is in.
-template <int D>
-__device__ __forceinline__ void tile_accum(f16v (&out)[D / 32], const f16v& coef, const float* brows, int ld) {
-  const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float* row = brows + crow(v, g) * ld + c;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) out[nb] = mfma32(coef[v], row[32 * nb], out[nb]);
-  }
 }
 
 // The wave's index in its workgroup, as a wave-uniform (scalar) value.
@@ -696,34 +577,5 @@ __device__ __forceinline__ void block_work(int nheads, int& head, int& rank) {
     head = b % nheads;
   }
 }
-
-// Stage rows of a [T, D] head tensor through registers: each of NT staging threads (thread
-// threadIdx.x % NT) holds CH = 32*D/4/NT float4 chunks of a 32-row tile (rows row0.., zero past
-// nrows).
-template <int D, int NT, typename T>
-struct TileRegs {
-  static constexpr int CH = 32 * D / 4 / NT;
-  f4v x[CH];
-  __device__ __forceinline__ void load(const T* src, int row0, int nrows) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int id = threadIdx.x % NT + i * NT;
-      const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
-      const int gr = row0 + r;
-      x[i] = f4v{0.f, 0.f, 0.f, 0.f};
-      if (gr < nrows) x[i] = Ld<T>::four(src + (size_t)gr * D + c4);
-    }
-  }
-  __device__ __forceinline__ void store(float* dst, int ld, float mul) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int id = threadIdx.x % NT + i * NT;
-      const int r = id / (D / 4), c4 = (id % (D / 4)) * 4;
-      f4v y = x[i];
-      if (mul != 1.0f) y *= mul;
-      *reinterpret_cast<f4v*>(dst + r * ld + c4) = y;
-    }
-  }
-};
 
 }  // namespace kia
