@@ -214,7 +214,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const Decision d = decide<CAL>(s[v], rc, K, a.tau);
-        const bool in = crow(v, 0) <= lim && !d.tail;
+        const bool in = (crow(v, 0) <= lim) & !d.tail;
         const int ell = d.r + (d.t >= 0.5f ? 1 : 0);
         const float x = __expf(s[v] - M);
 #pragma unroll
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           // bin mean: dS_k = e^{z_k} / W^C (gbar_b(k) - D^C); the forward's weight is the bin's
           // mean (bin mean) or the grid value at the Nearest index (the hybrid)
           d = decide<CAL>(s[v], rc, K, a.tau);
-          const bool in = crow(v, 0) <= lim && !d.tail;
+          const bool in = (crow(v, 0) <= lim) & !d.tail;
           const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), BINM_MAXB - 1);
           dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
           if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           else dS = vis ? gam * ew.d : 0.f;
         } else {
           d = decide<CAL>(s[v], rc, K, a.tau);
-          if (!(crow(v, 0) <= lim) || (CAL == FWM && d.tail)) d.r = K + 1;
+          if ((crow(v, 0) > lim) | (CAL == FWM && d.tail)) d.r = K + 1;
           wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
           Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
           dS = gam * Delta;

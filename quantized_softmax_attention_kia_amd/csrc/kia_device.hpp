@@ -411,9 +411,10 @@ __device__ __forceinline__ Decision decide_fast(float s, const RowCal& rc, int K
     d.tail = z < -tau;
     u = (fmaxf(z, -tau) + tau) * rc.inv_hf;
   }
-  const int r = min(max((int)floorf(u), 0), K - 1);
-  d.r = r;
-  d.t = __builtin_amdgcn_fmed3f(u - (float)r, 0.f, 1.f);
+  // the interval index clamped in float (one med3), then converted once
+  const float rf = __builtin_amdgcn_fmed3f(floorf(u), 0.f, (float)(K - 1));
+  d.r = (int)rf;
+  d.t = __builtin_amdgcn_fmed3f(u - rf, 0.f, 1.f);
   return d;
 }
 // Reconstructed weights of one key (§3 "Reconstruction"), from the row's grid table.

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         const float x = acc[v] * scale_f;
         const int key = k0 + crow(v, g);
         St[v * 64] = x;
-        const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
+        const bool ok = !decltype(masked)::value || (qvalid & (key < T) & (!a.causal | (key <= qi)));
         if (ok) {
           track<CAL>(ex, x, k0 + crow(v, 0));
           amx = fmaxf(amx, aacc[v]);
@@ -419,11 +419,11 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int v = 8 * b + j, key = k0 + crow(v, g);
-          const bool ok = qvalid && key < T && (!a.causal || key <= qi);
+          const bool ok = qvalid & (key < T) & (!a.causal | (key <= qi));
           const Decision d = decide_fast<CAL>(s[v], rc, K, a.tau);
-          bool r = (d.t < du && d.r > 0) || (d.t > 1.f - du && d.r < K - 1) || fabsf(d.t - 0.5f) < du;
-          if (CAL == FWM) r = r || fabsf((s[v] - M) + a.tau) <= edge;
-          risky |= (ok && r) ? (1u << j) : 0u;
+          bool r = ((d.t < du) & (d.r > 0)) | ((d.t > 1.f - du) & (d.r < K - 1)) | (fabsf(d.t - 0.5f) < du);
+          if (CAL == FWM) r |= fabsf((s[v] - M) + a.tau) <= edge;
+          risky |= (ok & r) ? (1u << j) : 0u;
           okm |= ok ? (1u << j) : 0u;
         }
         const bool redo = __any(risky != 0u);
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
           const int v = 8 * b + j;
           const Decision d = redo ? decide<CAL>(s[v], rc, K, a.tau) : decide_fast<CAL>(s[v], rc, K, a.tau);
           const int ell = d.r + (d.t >= 0.5f ? 1 : 0);
-          const bool in = ((okm >> j) & 1u) && !d.tail;
+          const bool in = ((okm >> j) & 1u) & !d.tail;
           const float x = __expf(s[v] - M);
 #pragma unroll
           for (int q = 0; q < BINM_MAXB; ++q) {
@@ -520,16 +520,19 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         __builtin_amdgcn_sched_barrier(0);
       }
       float p[8], pl[8];
-      double tL, tN;  // the half tile's weight sums, joined to the row sums once it is settled
+      // the half tile's weight sums: eight positive terms summed in float (error at most 7 u of
+      // the half tile's sum, no absorption across the row), joined to the row sums in double once
+      // the half tile is settled
+      float tL, tN;
       uint32_t risky = 0;
       uint32_t riske = 0;  // exponential baselines: keys whose weight alone is taken again
       auto weigh = [&](auto masked, auto check) {
-        tL = 0.0;
-        tN = 0.0;
+        tL = 0.f;
+        tN = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int v = 8 * b + j, key = k0 + crow(v, g);
-          const bool ok = !decltype(masked)::value || (qvalid && key < T && (!a.causal || key <= qi));
+          const bool ok = !decltype(masked)::value || (qvalid & (key < T) & (!a.causal | (key <= qi)));
           float wl, wn;
           if constexpr (CAL == EXPB) {
             // exponential baselines: first pass in float, checked against the score's error bound;
@@ -549,12 +552,13 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
                                                       : decide<CAL>(s[v], rc, K, a.tau);
             if (decltype(check)::value) {
               // a decision within the score's error bound of a boundary must be taken on the exact
-              // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid)
+              // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid).
+              // Bitwise operators: every test is cheap, and short-circuit forms become branches.
               const float dur = CAL == FWM_RES ? fmaf((float)max(-d.r, 0), 0x1p-22f, du) : du;
-              bool r = (d.t < dur && (CAL == FWM_RES || d.r > 0)) || (d.t > 1.f - dur && d.r < K - 1);
-              if (is_nearest(MODE)) r = r || fabsf(d.t - 0.5f) < dur;
-              if (CAL == FWM || CAL == FWM_FLOOR) r = r || fabsf((s[v] - M) + a.tau) <= edge;
-              risky |= (ok && r) ? (1u << j) : 0u;
+              bool r = ((d.t < dur) & (CAL == FWM_RES || d.r > 0)) | ((d.t > 1.f - dur) & (d.r < K - 1));
+              if (is_nearest(MODE)) r |= fabsf(d.t - 0.5f) < dur;
+              if (CAL == FWM || CAL == FWM_FLOOR) r |= fabsf((s[v] - M) + a.tau) <= edge;
+              risky |= (ok & r) ? (1u << j) : 0u;
             }
             const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
             // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
@@ -562,8 +566,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
             wl = keep ? wt.wL : 0.f;
             wn = keep ? wt.wN : 0.f;
           }
-          tL += (double)wl;
-          if (is_nearest(MODE)) tN += (double)wn;
+          tL += wl;
+          if (is_nearest(MODE)) tN += wn;
           p[j] = is_nearest(MODE) ? wn : wl;
           pl[j] = wl;
         }
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
                 p[jj] = jj == j ? we : p[jj];
                 pl[jj] = jj == j ? we : pl[jj];
               }
-              tL += (double)we - (double)old;
+              tL += we - old;
             }
             bits &= bits - 1u;
           }
@@ -607,8 +611,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
           else weigh(std::true_type{}, std::false_type{});
         }
       }
-      sumL += tL;
-      sumN += tN;
+      sumL += (double)tL;
+      sumN += (double)tN;
       if (MODE == NEAREST_P) {
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
