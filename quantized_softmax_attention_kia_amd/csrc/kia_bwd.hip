@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS>));
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
-  const int T = a.T, K = a.K, ts = K + 3;  // grid table row: e^{b_0} .. e^{b_K}, then two zeros
+  const int T = a.T, K = a.K;  // grid table: e^{b_0} .. e^{b_K}, then two zeros
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
   int head, rank;
   block_work(a.nheads, head, rank);
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   // lres levels below the window (resolved grid) to K (rows past T see no visible key)
   float* trow = tbl;
   if (CAL == MINMAX) {
-    trow = tbl + rl * ts;
-    for (int r = g; r <= K + 2; r += 2) trow[r] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
+    trow = tbl + rl;  // interval-major: entry r of row rl at r * DQ_BM + rl
+    for (int r = g; r <= K + 2; r += 2) trow[r * DQ_BM] = qvalid && r <= K ? grid_value<CAL>(M, m, K, a.tau, r) : 0.f;
   } else if (CAL != EXPB) {  // the exponential baselines have no grid
     trow = tbl + a.lres;
     for (int i = tid; i <= a.lres + K + 2; i += NT) tbl[i] = i <= a.lres + K ? grid_value<CAL>(M, m, K, a.tau, i - a.lres) : 0.f;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), BINM_MAXB - 1);
           dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
           if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
-          else pw = in ? weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau).wN : 0.f;
+          else pw = in ? weights_cal<CAL, CAL == MINMAX ? DQ_BM : 1>(d, trow, a.lres, a.res_far != 0, K, a.tau).wN : 0.f;
         } else if constexpr (CAL == EXPB) {
           // exponential baselines: the weight as the forward took it.  The forward's float form,
           // where the forward kept it, gave the exact form's value on the stored score; where it
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         } else {
           d = decide<CAL>(s[v], rc, K, a.tau);
           if ((crow(v, 0) > lim) | (CAL == FWM && d.tail)) d.r = K + 1;
-          wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
+          wt = weights_cal<CAL, CAL == MINMAX ? DQ_BM : 1>(d, trow, a.lres, a.res_far != 0, K, a.tau);
           Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
           dS = gam * Delta;
           pw = is_nearest(MODE) ? wt.wN : wt.wL;

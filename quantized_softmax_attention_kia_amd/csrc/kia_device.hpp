@@ -424,10 +424,14 @@ struct Weights {
   float wN;      // Nearest: E0 or E1 at index r + 1[t >= 1/2]
 };
 
+// Grid value r of the row sits at trow[r * ST]: ST = 1 for a table of its own (FWM: one for all
+// rows), ST = rows per workgroup for the per-row MinMax tables, kept interval-major so that the
+// rows of a wave read distinct LDS banks whatever their intervals.
+template <int ST = 1>
 __device__ __forceinline__ Weights weights(const Decision& d, const float* trow) {
   Weights w;
-  w.E0 = trow[d.r];
-  w.E1 = trow[d.r + 1];
+  w.E0 = trow[d.r * ST];
+  w.E1 = trow[(d.r + 1) * ST];
   w.wL = fmaf(d.t, w.E1 - w.E0, w.E0);
   w.wN = (d.t >= 0.5f) ? w.E1 : w.E0;
   return w;
@@ -438,10 +442,10 @@ __device__ __forceinline__ Weights weights(const Decision& d, const float* trow)
 // r >= -lres.  When the table reaches b <= -104, where e^b rounds to 0 in float, a key further
 // below reads that zero entry; otherwise (far: the level cap was hit, K/tau large) such a key has
 // its grid values computed here.
-template <int CAL>
+template <int CAL, int ST = 1>
 __device__ __forceinline__ Weights weights_cal(const Decision& d, const float* trow, int lres, bool far, int K,
                                                float tau) {
-  if (CAL != FWM_RES) return weights(d, trow);
+  if (CAL != FWM_RES) return weights<ST>(d, trow);
   Weights w;
   w.E0 = trow[max(d.r, -lres)];
   w.E1 = trow[max(d.r + 1, -lres)];

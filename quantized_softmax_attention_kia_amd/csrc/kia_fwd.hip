@@ -183,7 +183,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   FwdSmem<D, NS>& sm = *reinterpret_cast<FwdSmem<D, NS>*>(smem_raw);
   float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D, NS>));
   const int w = wave_id(), l = threadIdx.x & 63, g = l >> 5, c = l & 31;
-  const int T = a.T, K = a.K, ts = K + 1, nt = a.rec.nt;
+  const int T = a.T, K = a.K, nt = a.rec.nt;
   int head, rank;
   block_work(a.nheads, head, rank);
   const int qt = a.causal ? nt - 1 - rank : rank;  // rank 0: the latest query tile, the most keys
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     // the member count of each bin, per lane in registers; the sums meet per row in a fixed order
     // and the table then holds each bin's mean, so pass 2 runs as Nearest on it.  Keys below an
     // FWM window belong to no bin.
-    trow = tbl + c * ts;
+    trow = tbl + c;
     float bs[BINM_MAXB], bn[BINM_MAXB];
 #pragma unroll
     for (int q = 0; q < BINM_MAXB; ++q) { bs[q] = 0.f; bn[q] = 0.f; }
@@ -472,11 +472,11 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         S += part[((u * BN + c) * BINM_MAXB + q) * 2];
         n += part[((u * BN + c) * BINM_MAXB + q) * 2 + 1];
       }
-      trow[q] = n > 0.f ? S / n : 0.f;
+      trow[q * BN] = n > 0.f ? S / n : 0.f;
     }
   } else if (CAL == MINMAX) {
-    trow = tbl + c * ts;
-    for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r] = grid_value<CAL>(M, m, K, a.tau, r);
+    trow = tbl + c;  // interval-major: entry r of row c at r * BN + c
+    for (int r = g + 2 * w; r <= K; r += 2 * FWD_NW) trow[r * BN] = grid_value<CAL>(M, m, K, a.tau, r);
   } else if (CAL != EXPB) {  // the exponential baselines have no grid
     trow = tbl + a.lres;
     for (int i = threadIdx.x; i <= a.lres + K; i += FWD_NT) tbl[i] = grid_value<CAL>(M, m, K, a.tau, i - a.lres);
@@ -560,7 +560,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
               if (CAL == FWM || CAL == FWM_FLOOR) r |= fabsf((s[v] - M) + a.tau) <= edge;
               risky |= (ok & r) ? (1u << j) : 0u;
             }
-            const Weights wt = weights_cal<CAL>(d, trow, a.lres, a.res_far != 0, K, a.tau);
+            constexpr int ST = (CAL == MINMAX || MODE == BINM) ? BN : 1;
+            const Weights wt = weights_cal<CAL, ST>(d, trow, a.lres, a.res_far != 0, K, a.tau);
             // a floored tail key keeps the weight of the window edge (r = 0, t = 0)
             const bool keep = ok && (CAL == FWM_FLOOR || !d.tail);
             wl = keep ? wt.wL : 0.f;
