@@ -64,9 +64,9 @@ def make_inputs(B: int, H: int, T: int, D: int, seed: int, *, dtype: str = "f32"
 class Variant:
     """One operator configuration: calibration x reconstruction x surrogate x gradient mode."""
     calib: str          # "minmax" | "fwm"
-    recon: str          # "lerp" | "nearest"
-    ste: str            # "weight" | "prob" (ignored for LERP)
-    grad: str           # "full" | "detached"
+    recon: str          # "lerp" | "nearest" | "softmax" | "exp_bf16" | "exp_fp8" | "binmean" | "nearest_binmean"
+    ste: str            # "weight" | "prob" (Nearest only)
+    grad: str           # "full" | "detached" | "max_only" | "min_only" | "p1"
     K: int
     tau: float = 8.0
     tail: str = "zero"  # FWM tail policy: "zero" | "floor" | "resolved"

@@ -330,9 +330,13 @@ def test_explicit_scale(kb):
     compare_all_heads(variant, q, k, v, do, got, scale=0.125)
 
 
-def test_deterministic(kb):
-    q, k, v, do = make_inputs(2, 2, 130, 64, 44)
-    variant = ("minmax", "nearest", "prob", "full", 4, 8.0)
+@pytest.mark.parametrize("variant", [("minmax", "nearest", "prob", "full", 4, 8.0),
+                                     ("fwm", "lerp", "prob", "p1", 8, 3.0, "resolved"),
+                                     ("fwm", "exp_bf16", "prob", "full", 4, 8.0),
+                                     ("minmax", "binmean", "prob", "full", 4, 8.0)], ids=lambda v: "-".join(map(str, v)))
+def test_deterministic(kb, variant):
+    """Repeated calls give bit-identical outputs: every sum runs in a fixed order (no atomics)."""
+    q, k, v, do = make_inputs(2, 2, 130, 64, 44, q_scale=2.0)
     say(f"[determinism] {variant}")
     a, _ = gpu_run(kb, variant, q, k, v, do)
     b, _ = gpu_run(kb, variant, q, k, v, do)

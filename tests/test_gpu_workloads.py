@@ -168,6 +168,26 @@ def test_gpt2_binmean_sampled_heads(kb, recon):
     assert ratio < 1e-4, ratio
 
 
+@pytest.mark.parametrize("var", [("fwm", "nearest", "weight", "full", 4, 6.0, "resolved"),
+                                 ("fwm", "softmax", "prob", "full", 4, 8.0, "zero"),
+                                 ("minmax", "binmean", "prob", "full", 8, 8.0, "zero")],
+                         ids=lambda v: f"{v[0]}-{v[1]}-{v[6]}")
+def test_long_context_new_modes(kb, var):
+    """The long-context workload (T = 8192, D = 128, 1% outlier keys) under a resolved FWM tail,
+    the softmax baseline and bin mean: one sampled head against the oracle."""
+    from quantized_softmax_attention_kia_amd.inputs import Variant
+    wl = WORKLOADS["long"]
+    v = Variant(*var)
+    q, k, vv, do = inputs("long")
+    say(f"[long new modes] B={wl.B} H={wl.H} T={wl.T} D={wl.D} seed={wl.seed} {v.name}")
+    got = run(kb, wl, v, q, k, vv, do)
+    cfg = ORC.OracleConfig.of(v)
+    for b, h in parity.pick_heads(cfg, q, k, want=1):
+        gh = {key: got[key][b, h].cpu().numpy().astype(np.float64) for key in ("O", "dQ", "dK", "dV")}
+        rep = parity.check_head(cfg, q[b, h], k[b, h], vv[b, h], do[b, h], gh)
+        say(f"    head ({b},{h}): {rep}")
+
+
 def test_full_and_detached_forward_bitwise_identical(kb):
     wl = WORKLOADS["wide"]
     q, k, v, do = inputs("wide")
