@@ -307,7 +307,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   const bool twoM = CAL == MINMAX && oneM && loc.mx2 >= thrM, twom = CAL == MINMAX && onem && loc.mn2 <= thrm;
   auto exact_pair = [&](bool dM, int kM, bool dm, int km) {
     // exact scores of a max and a min candidate (either may be absent), patched in
-    float xM_, xm_;
+    float xM_ = 0.f, xm_ = 0.f;  // (under FWM there is no min candidate: xm_ stays unused)
     const int kM_ = dM ? kM : km, km_ = dm ? km : kM;
     if (CAL == MINMAX) exact_score2<D, TIn>(qrow, Kp + (size_t)kM_ * D, Kp + (size_t)km_ * D, a.scale, xM_, xm_);
     else xM_ = exact_score<D, TIn>(qrow, Kp + (size_t)kM_ * D, a.scale);
