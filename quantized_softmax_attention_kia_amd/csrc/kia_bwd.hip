@@ -25,9 +25,9 @@
 //               the stored scores, and after the sweep adds alpha_i = a_i/nA_i and
 //               beta_i = b_i/nC_i into dS at the row's extremum keys (each element is patched
 //               by the lane that wrote it).
-//   dkdv kernel (key-major, 64 keys per workgroup): dV += P^T dO, dK += dS^T Q from those
-//               tiles, each transposed by its wave through LDS: no decisions, no row
-//               records, no atomics.
+//   dkdv kernel (key-major, 128 keys per workgroup, four waves of 32 that share each staged
+//               query tile): dV += P^T dO, dK += dS^T Q from those tiles: no decisions, no
+//               row records, no atomics.
 // Both sweep their tiles while the next tile's operands are already being loaded.
 // Built once per calibration: KIA_CAL (a kia::Calib value) selects the dq kernels this build
 // supplies; the build with KIA_CAL = 0 also supplies the dkdv kernel.
@@ -40,11 +40,13 @@
 
 namespace kia {
 
-constexpr int NW = 2;         // waves per workgroup
-constexpr int NT = 64 * NW;   // threads per workgroup
+constexpr int NW = 2;         // waves per dq workgroup
+constexpr int NT = 64 * NW;   // threads per dq workgroup
 constexpr int BN = 32;        // keys per tile (dq kernel) / queries per tile (dkdv kernel)
 constexpr int DQ_BM = 32 * NW;  // query rows per dq workgroup
-constexpr int KV_BN = 32 * NW;  // key rows per dkdv workgroup
+constexpr int KV_NW = 4;        // waves per dkdv workgroup: one staged query tile serves four key tiles
+constexpr int KV_NT = 64 * KV_NW;
+constexpr int KV_BN = 32 * KV_NW;  // key rows per dkdv workgroup
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p);
 template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
@@ -492,7 +494,7 @@ __device__ __forceinline__ void kv_load(KvTile<P1>& t, const BwdArgs& a, size_t 
 
 // P1: subtract each query row's mean of the detached dS from its visible elements.
 template <int D, typename TIn, bool P1>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int NS = nslices<TIn>();
   __shared__ KvSmem<D, NS> sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const int qt_first = a.causal ? kb0 / BN : 0;
   // the workgroup's Q and dO rows of the next query tile, staged through LDS as bf16 slices;
   // the wave's P and dS of a tile, in two buffers taken in turn
-  PairRegs<D, TIn> qr, dr;
+  PairRegs<D, TIn, KV_NT> qr, dr;
   KvTile<P1> t0, t1;
   auto stage = [&](int qt) {
     __syncthreads();
@@ -586,8 +588,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 template <int D, typename TIn>
 static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nkt = (p.T + KV_BN - 1) / KV_BN;
-  if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false>), dim3(p.nheads * nkt), dim3(NT), 0, s, a);
+  if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true>), dim3(p.nheads * nkt), dim3(KV_NT), 0, s, a);
+  else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false>), dim3(p.nheads * nkt), dim3(KV_NT), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s) {
