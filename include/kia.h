@@ -145,9 +145,15 @@ typedef struct {
  *    the hard P^N for Nearest) and dS[B*H][tiles][1024] (the unscaled score
  *    gradients, extremum terms included; under P1 the detached ones, before the
  *    projection), then float rowmean[N] (P1: each row's mean of dS over its
- *    visible keys).  Within a tile of S, P or dS, element
+ *    visible keys), then float ptab[N][K+2].  Within a tile of S, P or dS, element
  *    (query row a, key column b of the tile) sits at float offset v*64 + a + 32*g,
  *    where b = 8*(v/4) + 4*g + v%4.
+ *    Where every P of a row is one of K+1 table values times 1/W (recon Nearest,
+ *    bin mean or the hybrid, with MinMax or with FWM and the zero or floored
+ *    tail), the P array holds instead one byte per element, at byte offset
+ *    (tile * 1024 + the element's offset above): the index j of its value
+ *    ptab[row][j] (j = K+1, whose value is 0, for keys the query does not see
+ *    and for FWM tail keys); the rest of the P array is unused.
  * Either output pointer may be NULL.  Returns KIA_ERR_INVALID_ARG or
  * KIA_ERR_UNSUPPORTED for parameters kia_forward would reject.
  */

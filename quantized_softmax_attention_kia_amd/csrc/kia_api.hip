@@ -111,7 +111,7 @@ struct Layout {
   size_t rowrec_bytes;
   int nt;
   size_t tiles_per_head;
-  size_t ws_off[3];
+  size_t ws_off[4];
   size_t ws_bytes;
 };
 
@@ -135,6 +135,8 @@ Layout layout(const kia::Problem& pr) {
   o += tile_bytes;
   L.ws_off[2] = o;                       // per-row mean of the detached dS (P1)
   o += round_up(N * 4);
+  L.ws_off[3] = o;                       // per-row table of P values by index (coded P tiles)
+  o += round_up(N * (size_t)(pr.K + 2) * 4);
   L.ws_bytes = o;
   return L;
 }
@@ -216,6 +218,9 @@ static kia_status_t backward_stages(const kia_params_t* p, const void* q, const 
   a.pt = reinterpret_cast<float*>(ws + L.ws_off[0]);
   a.dst = reinterpret_cast<float*>(ws + L.ws_off[1]);
   a.rowmean = reinterpret_cast<float*>(ws + L.ws_off[2]);
+  a.pcode = reinterpret_cast<uint8_t*>(ws + L.ws_off[0]);
+  a.ptab = reinterpret_cast<float*>(ws + L.ws_off[3]);
+  a.pc = kia::p_coded(pr.calib, pr.mode);
   a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = (float)pr.scale; a.lres = pr.lres; a.res_far = pr.res_far;
   a.keepM = pr.keepM; a.keepm = pr.keepm; a.p1 = pr.gk == kia::GK_P1;

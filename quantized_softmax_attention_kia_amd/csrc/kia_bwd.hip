@@ -90,6 +90,7 @@ size_t dq_smem_bytes(int K, int lres) {
 template <int D, int CAL, int MODE, int GK, typename TIn>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dq_kernel(BwdArgs a) {
   constexpr bool SUMS = GK == GK_SUMS, P1 = GK == GK_P1;
+  constexpr bool PC = p_coded(CAL, MODE);  // P written as table indices beside the row's table
   constexpr int NS = nslices<TIn>();
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const size_t tbase = (size_t)head * a.rec.tiles_per_head;
   const float* Sh = a.rec.S + tbase * 1024;
   float* Ph = a.pt + tbase * 1024;
+  uint8_t* Pch = a.pcode + tbase * 1024;
   float* dSh = a.dst + tbase * 1024;
   auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
@@ -246,6 +248,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     DC = GC * invWC;
   }
 
+  if constexpr (PC) {
+    // the row's P by table index (bin means under bin mean, else the grid), index K + 1 zero
+    if (qvalid) {
+      float* pr = a.ptab + row * (size_t)(K + 2);
+      for (int j = g; j <= K + 1; j += 2) {
+        float e = 0.f;
+        if (j <= K) e = MODE == BINM ? bmean[j] : trow[j * (CAL == MINMAX ? DQ_BM : 1)];
+        pr[j] = e * invWf;
+      }
+    }
+  }
+
   PairRegs<D, TIn, NT> kr;  // K rows of the next key tile, staged as the workgroup's K^T slices
   RowRegs<D, TIn, NT> vr;   // V rows of the next key tile, staged as natural-layout slices
   kr.load(Kp, 0, T);
@@ -270,6 +284,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     }
     if (!act) continue;
     float* Pw = Ph + to;
+    uint8_t* Pcw = Pch + to;
     float* dSw = dSh + to;
     // (dO V^T)^T as bf16 slice products: register v holds g = dO_i . V_j for query c, key k0 + crow(v, g)
     f16v gt = zero16();
@@ -293,6 +308,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         const int v = 8 * b + j;
         const float gam = (gt[v] - Di) * invWg;
         float dS, pw;
+        int code = 0;  // PC: the index of pw in the row's table
         Decision d;
         Weights wt;
         float Delta = 0.f;
@@ -303,6 +319,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           const bool in = (crow(v, 0) <= lim) & !d.tail;
           const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), BINM_MAXB - 1);
           dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
+          code = in ? ell : K + 1;
           if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
           else pw = in ? weights_cal<CAL, CAL == MINMAX ? DQ_BM : 1>(d, trow, a.lres, a.res_far != 0, K, a.tau).wN : 0.f;
         } else if constexpr (CAL == EXPB) {
@@ -326,10 +343,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
           dS = gam * Delta;
           pw = is_nearest(MODE) ? wt.wN : wt.wL;
+          code = d.r > K ? K + 1 : d.r + (d.t >= 0.5f ? 1 : 0);  // wN is the table's entry there
         }
         ds[j] = dS;
         // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
-        Pw[v * 64 + l] = pw * invWf;
+        if constexpr (PC) Pcw[v * 64 + l] = (uint8_t)code;
+        else Pw[v * 64 + l] = pw * invWf;
         dSw[v * 64 + l] = dS;
         if (SUMS || P1) hs += dS;
         if (SUMS) {
@@ -458,29 +477,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 
 // ============================================================================ dkdv kernel
 
-template <int D, int NS>
+// rows of a query tile times the longest table of P values by index (K <= 64)
+constexpr int KV_PT = BN * 66;
+template <int D, int NS, bool PC>
 struct KvSmem {
   __bf16 QT[NS * D * TP];   // Q^T of the query tile, bf16 slices
   __bf16 dOT[NS * D * TP];  // dO^T of the query tile
+  float pt[PC ? KV_PT : 1];  // coded P: the query tile's rows of P values by index
 };
 
 // Lane (c, g) loads, for its key c of the wave's key tile, the stored P and dS of the queries
 // crow(v, g) (v = 0..15): in a stored tile they sit at v_c * 64 + 32 g_c + (query) with
 // c = crow(v_c, g_c), so they form four aligned runs of four floats.
 // Under P1 the tile also carries the rows' means of the detached dS (queries crow(v, g)).
-template <bool P1>
+// Coded P (PC): the same runs hold one byte per element, four to a 32-bit word.
+template <bool P1, bool PC>
 struct KvTile {
-  f4v p[4], ds[4];
+  f4v p[PC ? 1 : 4], ds[4];
+  uint32_t pc[PC ? 4 : 1];
   float mean[P1 ? 16 : 1];
 };
-template <bool P1>
-__device__ __forceinline__ void kv_load(KvTile<P1>& t, const BwdArgs& a, size_t tbase, int head, int qt, int ktw) {
+template <bool P1, bool PC>
+__device__ __forceinline__ void kv_load(KvTile<P1, PC>& t, const BwdArgs& a, size_t tbase, int head, int qt,
+                                        int ktw) {
   const int l = threadIdx.x & 63, g = l >> 5, c = l & 31;
   const size_t to = (tbase + tile_index(qt, ktw, a.rec.nt, a.causal)) * 1024 +
                     (4 * (c >> 3) + (c & 3)) * 64 + 32 * ((c >> 2) & 1) + 4 * g;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    t.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
+    if (PC) t.pc[q] = *reinterpret_cast<const uint32_t*>(a.pcode + to + 8 * q);
+    else t.p[q] = *reinterpret_cast<const f4v*>(a.pt + to + 8 * q);
     t.ds[q] = *reinterpret_cast<const f4v*>(a.dst + to + 8 * q);
   }
   if (P1) {
@@ -493,10 +519,11 @@ __device__ __forceinline__ void kv_load(KvTile<P1>& t, const BwdArgs& a, size_t 
 }
 
 // P1: subtract each query row's mean of the detached dS from its visible elements.
-template <int D, typename TIn, bool P1>
+// PC: P arrives as table indices and is looked up in the query rows' tables (staged with Q, dO).
+template <int D, typename TIn, bool P1, bool PC>
 __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int NS = nslices<TIn>();
-  __shared__ KvSmem<D, NS> sm;
+  __shared__ KvSmem<D, NS, PC> sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, nt = a.rec.nt;
   int head, kt;
@@ -517,24 +544,55 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
   // the workgroup's Q and dO rows of the next query tile, staged through LDS as bf16 slices;
   // the wave's P and dS of a tile, in two buffers taken in turn
   PairRegs<D, TIn, KV_NT> qr, dr;
-  KvTile<P1> t0, t1;
+  KvTile<P1, PC> t0, t1;
+  // coded P: the query tile's table rows are contiguous (rows past T are never looked up)
+  constexpr int PT_PER = PC ? (KV_PT + KV_NT - 1) / KV_NT : 1;
+  const int K2 = a.K + 2;
+  float ptr[PT_PER];
+  auto pt_load = [&](int qt) {
+    const float* src = a.ptab + ((size_t)head * T + (size_t)qt * BN) * K2;
+    const int n = min(BN, T - qt * BN) * K2;
+#pragma unroll
+    for (int u = 0; u < PT_PER; ++u) {
+      const int i = tid + u * KV_NT;
+      ptr[u] = i < n ? src[i] : 0.f;
+    }
+  };
+  if (PC && qt_first < nt) pt_load(qt_first);
   auto stage = [&](int qt) {
     __syncthreads();
     qr.template store_t<NS>(sm.QT);
     dr.template store_t<NS>(sm.dOT);
+    if (PC) {
+#pragma unroll
+      for (int u = 0; u < PT_PER; ++u) {
+        const int i = tid + u * KV_NT;
+        if (i < BN * K2) sm.pt[i] = ptr[u];
+      }
+    }
     __syncthreads();
     if (qt + 1 < nt) {
       qr.load(Qp, (qt + 1) * BN, T);
       dr.load(dOp, (qt + 1) * BN, T);
+      if (PC) pt_load(qt + 1);
     }
   };
-  auto contract = [&](const KvTile<P1>& t, int qt) {
+  auto contract = [&](const KvTile<P1, PC>& t, int qt) {
     // element (query crow(v, g), key c) of P and dS; zero where masked
     float p[16], ds[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { p[4 * q + e] = t.p[q][e]; ds[4 * q + e] = t.ds[q][e]; }
+      for (int e = 0; e < 4; ++e) {
+        if (PC) {
+          // query 8 q + 4 g + e of the tile: index K + 1 (masked, tail) is P = 0
+          const int code = (int)((t.pc[q] >> (8 * e)) & 0xffu);
+          p[4 * q + e] = code <= a.K ? sm.pt[(8 * q + 4 * g + e) * K2 + code] : 0.f;
+        } else {
+          p[4 * q + e] = t.p[q][e];
+        }
+        ds[4 * q + e] = t.ds[q][e];
+      }
     if (P1) {
       // the query row's mean of the detached dS comes off every visible element
       const int key = kw0 + c;
@@ -557,15 +615,15 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
   if (qt_first < nt) {
     qr.load(Qp, qt_first * BN, T);
     dr.load(dOp, qt_first * BN, T);
-    if (active(qt_first)) kv_load<P1>(t0, a, tbase, head, qt_first, ktw);
+    if (active(qt_first)) kv_load<P1, PC>(t0, a, tbase, head, qt_first, ktw);
   }
   for (int qt = qt_first; qt < nt; qt += 2) {
     stage(qt);
-    if (qt + 1 < nt && active(qt + 1)) kv_load<P1>(t1, a, tbase, head, qt + 1, ktw);
+    if (qt + 1 < nt && active(qt + 1)) kv_load<P1, PC>(t1, a, tbase, head, qt + 1, ktw);
     if (active(qt)) contract(t0, qt);
     if (qt + 1 >= nt) break;
     stage(qt + 1);
-    if (qt + 2 < nt && active(qt + 2)) kv_load<P1>(t0, a, tbase, head, qt + 2, ktw);
+    if (qt + 2 < nt && active(qt + 2)) kv_load<P1, PC>(t0, a, tbase, head, qt + 2, ktw);
     if (active(qt + 1)) contract(t1, qt + 1);
   }
 #pragma unroll
@@ -588,8 +646,14 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
 template <int D, typename TIn>
 static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nkt = (p.T + KV_BN - 1) / KV_BN;
-  if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true>), dim3(p.nheads * nkt), dim3(KV_NT), 0, s, a);
-  else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false>), dim3(p.nheads * nkt), dim3(KV_NT), 0, s, a);
+  const dim3 grid(p.nheads * nkt), block(KV_NT);
+  if (a.pc) {
+    if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false, true>), grid, block, 0, s, a);
+  } else {
+    if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s) {

@@ -28,6 +28,13 @@ constexpr bool is_nearest(int mode) {
   return mode == NEAREST_W || mode == NEAREST_P || mode == BINM || mode == NEARB;
 }
 constexpr bool is_binmean(int mode) { return mode == BINM || mode == NEARB; }
+// The forward's normalized weight P reaches the dkdv kernel as a float per element, or, where
+// every P of a row is one of K + 1 table values times 1/W (the Nearest forward, bin mean and the
+// hybrid, under MinMax or FWM with a zero or floored tail), as a one-byte table index per element
+// (K + 1: P = 0) beside each row's table of the K + 2 values.
+constexpr bool p_coded(int calib, int mode) {
+  return is_nearest(mode) && (calib == MINMAX || calib == FWM || calib == FWM_FLOOR);
+}
 // bins of the bin-mean modes: at most 9 (K <= 8), kept per lane in registers
 constexpr int BINM_MAXB = 9;
 // backward kernels by gradient mode: the calibration sums (full, max_only, min_only), the
@@ -89,6 +96,9 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* pt;     // key-major tiles of the forward's P, written by the dq kernel
+  uint8_t* pcode;  // the same tiles as table indices, one byte per element (pc: p_coded)
+  float* ptab;     // pc: per row, the K + 2 values of P by index (the last is 0)
+  int pc;
   float* dst;    // key-major tiles of dS (extremum terms included), written by the dq kernel
   float* rowmean;  // P1: per row, the mean of the detached dS over the visible keys (dq writes it)
   int T, K, causal;

@@ -52,19 +52,23 @@ def test_workspace_layout(kb):
     rnd = lambda x: (x + 255) // 256 * 256
     nt = (100 + 31) // 32
     tiles = 2 * 3 * nt * (nt + 1) // 2 * 4096        # stored causal score tiles
+    tab = rnd(N * (4 + 2) * 4)    # per row, the K + 2 values of a coded P
     st, rr, w = ws(kb, params(kb))
-    # key-major P and dS tiles, then the per-row P1 means
-    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles + rnd(N * 4)
+    # key-major P and dS tiles, the per-row P1 means, the per-row tables of coded P
+    assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles + rnd(N * 4) + tab
     st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
     assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
     st, rr, w = ws(kb, params(kb, causal=0))
-    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096 and w == 2 * 2 * 3 * nt * nt * 4096 + rnd(N * 4)
+    assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096
+    assert w == 2 * 2 * 3 * nt * nt * 4096 + rnd(N * 4) + tab
+    st, rr, w = ws(kb, params(kb, K=64))
+    assert st == 0 and w == 2 * tiles + rnd(N * 4) + rnd(N * 66 * 4)
     for tail in range(3):   # every FWM tail policy has the same layout
         st, rr2, w2 = ws(kb, params(kb, calib=1, tail=tail))
-        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4)
+        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4) + tab
     for grad in range(5):   # every gradient mode has the same layout
         st, rr2, w2 = ws(kb, params(kb, grad=grad))
-        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4)
+        assert st == 0 and rr2 == 8 * rnd(N * 4) + tiles and w2 == 2 * tiles + rnd(N * 4) + tab
     st, rr, w = ws(kb, params(kb, B=0))
     assert st == 0 and rr == 0
 
