@@ -349,7 +349,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
         const int kt = kt0 + i * FWD_NW;
-        uint32_t bits = cand[i] | (cand[i] >> 16);
+        uint32_t bits = (cand[i] | (cand[i] >> 16)) & 0xffffu;  // elements v = 0..15 of the tile
         while (bits) {
           const int v = __builtin_ctz(bits);
           bits &= bits - 1u;
