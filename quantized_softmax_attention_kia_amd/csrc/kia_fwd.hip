@@ -45,11 +45,11 @@ constexpr int FWD_NT = 64 * FWD_NW;
 constexpr int BN = 32;               // keys per tile, query rows per workgroup
 
 
-// Approximate extrema of the keys one lane stored: the three largest values and the keys of the
-// first two, likewise for the smallest.  Keys reach a lane in increasing order.
-struct Lane3 {
-  float mx, mx2, mx3, mn, mn2, mn3;
-  int ax, ax2, an, an2;
+// Approximate extrema of the keys one lane stored: the two largest values and the key of the
+// largest, likewise for the smallest.  Keys reach a lane in increasing order.
+struct Lane2 {
+  float mx, mx2, mn, mn2;
+  int ax, an;
 };
 // Exact extrema of a row over the stored scores: value, first key, count of ties.
 struct XExt {
@@ -129,24 +129,18 @@ __device__ __forceinline__ bf8v bf_abs(bf8v v) {
   return r;
 }
 
-// With mx >= mx2 >= mx3 the new second and third values are medians of (x, mx, mx2) and
-// (x, mx2, mx3); likewise for the minimum.  A value equal to the extremum keeps the earlier key
-// and becomes the second (a tie).  The minimum is tracked for MinMax only (FWM calibrates on the
-// maximum alone); under FWM only the first key and the second value are kept.
+// With mx >= mx2 the new second value is the median of (x, mx, mx2); likewise for the minimum.
+// A value equal to the extremum keeps the earlier key and becomes the second (a tie).  The minimum
+// is tracked for MinMax only (FWM calibrates on the maximum alone).  One key per side is enough:
+// a lane whose second value is also a candidate rescans its tiles (near ties, rare).
 template <int CAL>
-__device__ __forceinline__ void track(Lane3& e, float x, int key) {
+__device__ __forceinline__ void track(Lane2& e, float x, int key) {
   const bool g1 = x > e.mx;
-  if (CAL == MINMAX) {
-    e.ax2 = g1 ? e.ax : (x > e.mx2 ? key : e.ax2);
-    e.mx3 = __builtin_amdgcn_fmed3f(x, e.mx2, e.mx3);
-  }
   e.ax = g1 ? key : e.ax;
   e.mx2 = __builtin_amdgcn_fmed3f(x, e.mx, e.mx2);
   e.mx = fmaxf(x, e.mx);
   if (CAL == MINMAX) {
     const bool l1 = x < e.mn;
-    e.an2 = l1 ? e.an : (x < e.mn2 ? key : e.an2);
-    e.mn3 = __builtin_amdgcn_fmed3f(x, e.mn2, e.mn3);
     e.an = l1 ? key : e.an;
     e.mn2 = __builtin_amdgcn_fmed3f(x, e.mn, e.mn2);
     e.mn = fminf(x, e.mn);
@@ -218,8 +212,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     }
   }
   // keys are tracked without the lane's 4 g (crow(v, g) = crow(v, 0) + 4 g), a wave-uniform value
-  Lane3 ex{-INFINITY, -INFINITY, -INFINITY, INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4,
-           INT_MAX - 4, INT_MAX - 4};
+  Lane2 ex{-INFINITY, -INFINITY, INFINITY, INFINITY, INT_MAX - 4, INT_MAX - 4};
   float amx = 0.f;  // largest sum of |q_h| |k_h| over the row's visible keys
   // one key tile: its scores from the K operand kr (slice products), stored, and tracked
   auto score_tile = [&](int kt, const RowOp<D, TIn>& kr) {
@@ -267,10 +260,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     score_tile(kt + FWD_NW, kr1);
   }
   ex.ax += 4 * g;
-  ex.ax2 += 4 * g;
   ex.an += 4 * g;
-  ex.an2 += 4 * g;
-  const Lane3& loc = ex;  // this lane's own extrema: keys whose scores it stored
+  const Lane2& loc = ex;  // this lane's own extrema: keys whose scores it stored
   // the row's approximate extrema and error bound: lanes of a row, then the waves, in LDS
   {
     const float rmx = fmaxf(loc.mx, __shfl_xor(loc.mx, 32)), rmn = fminf(loc.mn, __shfl_xor(loc.mn, 32));
@@ -295,16 +286,15 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 
   // ---- exact extrema.  Every key whose exact score can attain the row maximum (minimum) has a
   // stored score within 2 Erow of the approximate one: a candidate.  Each lane recomputes its own
-  // candidates exactly (MinMax: up to two per side, whose keys it kept; FWM: one) and patches the
-  // elements it stored; a lane holding more (rare) rescans its tiles for them.  First index and
-  // tie count are then taken over exact values.
+  // candidate exactly (one per side, whose key it kept) and patches the element it stored; a lane
+  // holding more (near ties, rare) rescans its tiles for them.  First index and tie count are then
+  // taken over exact values.
   const float thrM = rowmx - 2.f * Erow, thrm = rowmn + 2.f * Erow;
   XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
-  // number of candidates of each side that this lane's kept keys cover (FWM keeps one key)
-  const bool scanM = qvalid && (CAL == MINMAX ? loc.mx3 >= thrM : loc.mx2 >= thrM);
-  const bool scanm = CAL == MINMAX && qvalid && loc.mn3 <= thrm;
+  // whether this lane's kept key covers its candidates of each side, or it has to rescan
+  const bool scanM = qvalid && loc.mx2 >= thrM;
+  const bool scanm = CAL == MINMAX && qvalid && loc.mn2 <= thrm;
   const bool oneM = qvalid && loc.mx >= thrM && !scanM, onem = CAL == MINMAX && qvalid && loc.mn <= thrm && !scanm;
-  const bool twoM = CAL == MINMAX && oneM && loc.mx2 >= thrM, twom = CAL == MINMAX && onem && loc.mn2 <= thrm;
   auto exact_pair = [&](bool dM, int kM, bool dm, int km) {
     // exact scores of a max and a min candidate (either may be absent), patched in
     float xM_ = 0.f, xm_ = 0.f;  // (under FWM there is no min candidate: xm_ stays unused)
@@ -321,9 +311,6 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     }
   };
   if (oneM || onem) exact_pair(oneM, loc.ax, onem, loc.an);
-  if (CAL == MINMAX && __any(twoM || twom)) {
-    if (twoM || twom) exact_pair(twoM, loc.ax2, twom, loc.an2);
-  }
   if (__any(scanM || scanm)) {
     constexpr int TB = 4;  // tiles per batch of loads
     for (int kt0 = w; kt0 < ntiles; kt0 += TB * FWD_NW) {
