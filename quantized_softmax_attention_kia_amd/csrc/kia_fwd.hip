@@ -476,7 +476,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
   // the next V tile is loaded while this one computes, except under Nearest with Prob-STE,
-  // whose second output accumulator takes those registers
+  // whose second output accumulator takes those registers: there the tile's own V is loaded
+  // first, arrives while both half tiles are weighed, and is staged before their products
   constexpr bool VPRE = MODE != NEAREST_P;
   PairRegs<D, TIn, 64> vr;
   if (VPRE && w < ntiles) vr.load(Vp, w * BN, T);
@@ -487,15 +488,19 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     float s[16];  // this lane's scores of the tile, as it stored them in pass 1
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
-    vr.template store_t<NS>(VT);
-    wave_lds_sync();
-    if (VPRE && kt + FWD_NW < ntiles) vr.load(Vp, k0 + FWD_NW * BN, T);  // next V tile in flight
+    if (VPRE) {
+      vr.template store_t<NS>(VT);
+      wave_lds_sync();
+      if (kt + FWD_NW < ntiles) vr.load(Vp, k0 + FWD_NW * BN, T);  // next V tile in flight
+    }
     const bool full = full_tile(kt);
     // each tile's P V (bf16 slice products on the matrix pipe) goes into a fresh accumulator,
     // then into the running sum: the long accumulation chain then holds one add per tile
     f16v ot[D / 32], otl[D / 32];
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) { ot[nb] = zero16(); otl[nb] = zero16(); }
+    // without the prefetch: the weights of both half tiles, kept until V is staged
+    float pa[VPRE ? 1 : 2][8], pla[VPRE ? 1 : 2][8];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {  // half tiles: keys crow(v, g) for v = 8b .. 8b+7
       // the half tile's V^T operands are read from LDS first, so that their latency overlaps the
@@ -601,15 +606,27 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
       sumL += (double)tL;
       sumN += (double)tN;
-      if (MODE == NEAREST_P) {
+      if constexpr (!VPRE) {
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
+        for (int j = 0; j < 8; ++j) { pa[b][j] = p[j]; pla[b][j] = pl[j]; }
+        continue;
       }
       const Split8 ps = split8(p);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
-      if (MODE == NEAREST_P) {
-        const Split8 psl = split8(pl);
+    }
+    if constexpr (!VPRE) {
+      vr.template store_t<NS>(VT);
+      wave_lds_sync();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        Split8 vb[D / 32];
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
+        const Split8 ps = split8(pa[b]);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
+        const Split8 psl = split8(pla[b]);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) otl[nb] = mfma_split<NS>(psl, vb[nb], otl[nb]);
       }
