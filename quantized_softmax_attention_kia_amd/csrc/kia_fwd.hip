@@ -259,6 +259,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     if (kt + 2 * FWD_NW < ntiles) kr0.load(Kp, (kt + 2 * FWD_NW) * BN + c, T);
     score_tile(kt + FWD_NW, kr1);
   }
+  // pass 2's first V tile, loaded while the extrema are settled (not under Nearest with Prob-STE,
+  // which loads each tile's V in its own step)
+  PairRegs<D, TIn, 64> vr;
+  if (MODE != NEAREST_P && w < ntiles) vr.load(Vp, w * BN, T);
   ex.ax += 4 * g;
   ex.an += 4 * g;
   const Lane2& loc = ex;  // this lane's own extrema: keys whose scores it stored
@@ -479,8 +483,6 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // whose second output accumulator takes those registers: there the tile's own V is loaded
   // first, arrives while both half tiles are weighed, and is staged before their products
   constexpr bool VPRE = MODE != NEAREST_P;
-  PairRegs<D, TIn, 64> vr;
-  if (VPRE && w < ntiles) vr.load(Vp, w * BN, T);
   for (int kt = w; kt < ntiles; kt += FWD_NW) {
     const int k0 = kt * BN;
     if (!VPRE) vr.load(Vp, k0, T);
