@@ -452,21 +452,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     sm.amin[rl] = qvalid ? amin : 0;
   }
   __syncthreads();
+  // the extremum keys' K rows of all 16 rows first (every row records valid keys, so no load
+  // waits behind a row test), then the stores
+  constexpr int NX = SUMS ? 16 : 1, NXM = SUMS && CAL == MINMAX ? 16 : 1;
+  float xa[NX][D / 32], xb[NXM][D / 32];
+  if (SUMS) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r2 = 32 * w + crow(v, g);
+      const TIn* ka = Kp + (size_t)sm.amax[r2] * D + c;
+      const TIn* kb = Kp + (size_t)sm.amin[r2] * D + c;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        xa[v][nb] = ld1<TIn>(ka + 32 * nb);
+        if (CAL == MINMAX) xb[v][nb] = ld1<TIn>(kb + 32 * nb);
+      }
+    }
+  }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int qrow = qw0 + crow(v, g);
     if (qrow < T) {
       const int r2 = 32 * w + crow(v, g);
       const float al = sm.alpha[r2], be = sm.beta[r2];
-      const TIn* ka = Kp + (size_t)sm.amax[r2] * D + c;
-      const TIn* kb = Kp + (size_t)sm.amin[r2] * D + c;
       float* out = a.dq + hb + (size_t)qrow * D + c;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
         float val = dq[nb][v];
         if (SUMS) {
-          val = fmaf(al, ld1<TIn>(ka + 32 * nb), val);
-          if (CAL == MINMAX) val = fmaf(be, ld1<TIn>(kb + 32 * nb), val);
+          val = fmaf(al, xa[v][nb], val);
+          if (CAL == MINMAX) val = fmaf(be, xb[v][nb], val);
         }
         if (P1) val = fmaf(-sm.mean[r2], pk[nb][v], val);
         out[32 * nb] = val * a.scale;
