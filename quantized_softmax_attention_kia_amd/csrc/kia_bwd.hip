@@ -120,6 +120,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   float* dSh = a.dst + tbase * 1024;
   auto active = [&](int kt) { return qw0 < T && (!a.causal || kt * BN <= qlast_w); };
 
+  // the row's loads first (record, the rows of O and dO), so that their latencies overlap;
+  // rows past T read row 0 of the head and are zeroed or never used
+  const float M = a.rec.M[row], m = a.rec.m[row];
+  const int amax = a.rec.amax[row], amin = a.rec.amin[row];
+  const int nA = a.rec.nA[row], nC = a.rec.nC[row];
+  const float Wf = is_nearest(MODE) ? a.rec.WN[row] : a.rec.WL[row];
+  const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
+  f4v xo[D / 8], yo[D / 8];
+  {
+    const int qc = qvalid ? qi : 0;
+    const float* X = ((MODE == NEAREST_P) ? a.rec.OL : a.o) + hb + (size_t)qc * D + 4 * g;
+    const TIn* Y = dOp + (size_t)qc * D + 4 * g;
+#pragma unroll
+    for (int q = 0; q < D / 8; ++q) {
+      xo[q] = *reinterpret_cast<const f4v*>(X + 8 * q);
+      yo[q] = Ld<TIn>::four(Y + 8 * q);
+    }
+  }
   // the lane's dO row as bf16 slices, columns 16 kb + 8 g ..: the B operand of every g = V dO^T
   Split8 dos[D / 16];
   {
@@ -128,30 +146,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) dos[kb] = dr.split(kb);
   }
-
-  // row record of the forward
-  const float M = a.rec.M[row], m = a.rec.m[row];
-  const int amax = a.rec.amax[row], amin = a.rec.amin[row];
-  const int nA = a.rec.nA[row], nC = a.rec.nC[row];
-  const float Wf = is_nearest(MODE) ? a.rec.WN[row] : a.rec.WL[row];
-  const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
   const float invWf = 1.0f / Wf, invWg = 1.0f / Wg;
 
   // D_i = dO_i . O_i (O^L_i for Nearest with Prob-STE): sum_j P_j g_j at the normalization point
   float Di;
   {
-    const float* X = ((MODE == NEAREST_P) ? a.rec.OL : a.o) + hb + (size_t)qi * D + 4 * g;
-    const TIn* Y = dOp + (size_t)qi * D + 4 * g;
     double part = 0.0;
-    if (qvalid) {
 #pragma unroll
-      for (int q = 0; q < D / 8; ++q) {
-        const f4v x = *reinterpret_cast<const f4v*>(X + 8 * q);
-        const f4v y = Ld<TIn>::four(Y + 8 * q);
+    for (int q = 0; q < D / 8; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fma((double)y[e], (double)x[e], part);
-      }
-    }
+      for (int e = 0; e < 4; ++e) part = fma((double)yo[q][e], (double)xo[q][e], part);
+    if (!qvalid) part = 0.0;
     Di = (float)(part + __shfl_xor(part, 32));
   }
 

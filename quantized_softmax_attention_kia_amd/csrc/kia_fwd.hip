@@ -200,6 +200,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // the stored tiles, so pass 2 reads back exactly what this lane wrote.
   const float scale_f = (float)a.scale;
   const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + hb + (size_t)(qvalid ? qi : 0) * D;
+  // two K operand buffers in turn: the next tile's K is in flight while this one computes (the
+  // first is requested before the Q row, so both loads overlap)
+  RowOp<D, TIn> kr0, kr1;
+  if (w < ntiles) kr0.load(Kp, w * BN + c, T);
   Split8 qs[D / 16];
   bf8v qa[D / 16];
   {
@@ -249,9 +253,6 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     if (full_tile(kt)) epilogue(std::false_type{});
     else epilogue(std::true_type{});
   };
-  // two operand buffers in turn: the next tile's K is in flight while this one computes
-  RowOp<D, TIn> kr0, kr1;
-  if (w < ntiles) kr0.load(Kp, w * BN + c, T);
   for (int kt = w; kt < ntiles; kt += 2 * FWD_NW) {
     if (kt + FWD_NW < ntiles) kr1.load(Kp, (kt + FWD_NW) * BN + c, T);
     score_tile(kt, kr0);
