@@ -263,6 +263,25 @@ def test_tied_extrema(kb):
         compare_all_heads(full, q, k, v, do, got)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_tied_extrema_in_one_lane(kb, dtype):
+    """Copies of one key 64 apart fall to the same wave and lane for every row that sees them: that
+    lane holds up to nine tied candidates of the maximum (and, for another key, of the minimum) and
+    rescans its ten tiles in batches; D = 128.  The changes keep K exact in bf16 (x4, negation)."""
+    q, k, v, do = make_inputs(1, 2, 600, 128, 73, dtype=dtype, q_scale=2.0)
+    k[0, :, 3] *= 4.0
+    k[0, :, 20] = -k[0, :, 3]
+    for j in range(1, 9):
+        k[0, :, 3 + 64 * j] = k[0, :, 3]
+        k[0, :, 20 + 64 * j] = k[0, :, 20]
+    for variant in [("minmax", "lerp", "prob", "full"), ("minmax", "nearest", "weight", "full"),
+                    ("fwm", "nearest", "prob", "full")]:
+        full = variant + (4, 8.0)
+        say(f"[lane-ties] 1x2x600x128 {dtype} seed=73 {full}")
+        got, _ = gpu_run(kb, full, q, k, v, do, dtype=dtype)
+        compare_all_heads(full, q, k, v, do, got)
+
+
 def grid_inputs(seed, B, H, T, D, rel):
     """Q, K on the integers -2..2 times (1 + rel N(0,1)): the scores sit on a coarse grid (and the
     row extrema and interval boundaries with them) up to a perturbation of relative size rel."""
