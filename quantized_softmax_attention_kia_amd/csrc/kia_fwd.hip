@@ -5,8 +5,9 @@
 // does not apply.  A workgroup owns 32 query rows of one head (heaviest first); its
 // FWD_NW waves split the visible key tiles between them (wave w takes every
 // FWD_NW-th), so the longest rows do not hold the whole kernel back, and sweep them
-// twice, loading the next tile while they compute the current one; partial results
-// meet in LDS, in a fixed order:
+// twice, loading the next tile while they compute the current one (pass 2 under Nearest
+// with Prob-STE loads each tile's V while it weighs that tile); partial results meet in
+// LDS, in a fixed order:
 //   pass 1  scores of each 32 x 32 tile as bf16 slice products on the matrix pipe
 //           (K operands loaded straight from memory into registers) with a
 //           rigorous error bound per row, stored for every later pass; the row
