@@ -87,7 +87,7 @@ size_t dq_smem_bytes(int K, int lres) {
 // a.keepM / a.keepm select), GK_DETACHED, or GK_P1 (detached; each row's dS mean over its visible
 // keys is recorded for the dkdv kernel and taken out of dQ through the sum of the visible K rows).
 // At D = 64 the register budget is held to two waves per SIMD.
-template <int D, int CAL, int MODE, int GK, typename TIn>
+template <int D, int CAL, int MODE, int GK, typename TIn, int NB = BINM_MAXB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dq_kernel(BwdArgs a) {
   constexpr bool SUMS = GK == GK_SUMS, P1 = GK == GK_P1;
   constexpr bool PC = p_coded(CAL, MODE);  // P written as table indices beside the row's table
@@ -202,9 +202,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   float* bgbar = bmean + DQ_BM * BINM_MAXB;
   float invWC = 0.f, DC = 0.f;
   if constexpr (BM) {
-    float bs[BINM_MAXB], bn[BINM_MAXB], bg[BINM_MAXB];
+    float bs[NB], bn[NB], bg[NB];
 #pragma unroll
-    for (int q = 0; q < BINM_MAXB; ++q) { bs[q] = 0.f; bn[q] = 0.f; bg[q] = 0.f; }
+    for (int q = 0; q < NB; ++q) { bs[q] = 0.f; bn[q] = 0.f; bg[q] = 0.f; }
     RowRegs<D, TIn, NT> vp;
     vp.load(Vp, 0, T);
     for (int kt = 0; kt < ntiles; ++kt) {
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         const int ell = d.r + (d.t >= 0.5f ? 1 : 0);
         const float x = __expf(s[v] - M);
 #pragma unroll
-        for (int q = 0; q < BINM_MAXB; ++q) {
+        for (int q = 0; q < NB; ++q) {
           const bool hit = in && ell == q;
           bs[q] += hit ? x : 0.f;
           bn[q] += hit ? 1.f : 0.f;
@@ -235,9 +235,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         }
       }
     }
-    float WC = 0.f, GC = 0.f;
+    float WC = 0.f, GC = 0.f;  // bins past K hold nothing: NB of them cover every member
 #pragma unroll
-    for (int q = 0; q < BINM_MAXB; ++q) {
+    for (int q = 0; q < NB; ++q) {
       bs[q] += __shfl_xor(bs[q], 32);
       bn[q] += __shfl_xor(bn[q], 32);
       bg[q] += __shfl_xor(bg[q], 32);
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           // mean (bin mean) or the grid value at the Nearest index (the hybrid)
           d = decide<CAL>(s[v], rc, K, a.tau);
           const bool in = (crow(v, 0) <= lim) & !d.tail;
-          const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), BINM_MAXB - 1);
+          const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), NB - 1);
           dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
           code = in ? ell : K + 1;
           if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
@@ -685,7 +685,10 @@ template <int D, int CAL, int MODE, int GK, typename TIn>
 static hipError_t dq_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
   const size_t smem = dq_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
-  hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+  if (is_binmean(MODE) && p.K < BINM_SMALLB)
+    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE, int GK>

@@ -170,8 +170,8 @@ __device__ __forceinline__ void xext_merge(XExt& a, int lanemask, bool is_max) {
   xext_combine(a, b, is_max);
 }
 
-// At D = 64 the register budget is held to two waves per SIMD.
-template <int D, int CAL, int MODE, typename TIn>
+// At D = 64 the register budget is held to two waves per SIMD.  NB: bins held under bin mean.
+template <int D, int CAL, int MODE, typename TIn, int NB = BINM_MAXB>
 __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
   constexpr int NS = nslices<TIn>();
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -397,9 +397,9 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     // and the table then holds each bin's mean, so pass 2 runs as Nearest on it.  Keys below an
     // FWM window belong to no bin.
     trow = tbl + c;
-    float bs[BINM_MAXB], bn[BINM_MAXB];
+    float bs[NB], bn[NB];
 #pragma unroll
-    for (int q = 0; q < BINM_MAXB; ++q) { bs[q] = 0.f; bn[q] = 0.f; }
+    for (int q = 0; q < NB; ++q) { bs[q] = 0.f; bn[q] = 0.f; }
     for (int kt = w; kt < ntiles; kt += FWD_NW) {
       const int k0 = kt * BN;
       float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
           const bool in = ((okm >> j) & 1u) & !d.tail;
           const float x = __expf(s[v] - M);
 #pragma unroll
-          for (int q = 0; q < BINM_MAXB; ++q) {
+          for (int q = 0; q < NB; ++q) {
             bs[q] += (in && ell == q) ? x : 0.f;
             bn[q] += (in && ell == q) ? 1.f : 0.f;
           }
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     // the row's two lanes of each wave, then the two waves in order
     float* part = reinterpret_cast<float*>(sm.wave[0]);  // [wave][row][bin][sum, count]
 #pragma unroll
-    for (int q = 0; q < BINM_MAXB; ++q) {
+    for (int q = 0; q < NB; ++q) {
       bs[q] += __shfl_xor(bs[q], 32);
       bn[q] += __shfl_xor(bn[q], 32);
       if (g == 0) {
@@ -766,7 +766,10 @@ template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + BN - 1) / BN;
   const size_t smem = fwd_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
-  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+  if (MODE == BINM && p.K < BINM_SMALLB)
+    hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE>

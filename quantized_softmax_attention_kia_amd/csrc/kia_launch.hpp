@@ -37,6 +37,9 @@ constexpr bool p_coded(int calib, int mode) {
 }
 // bins of the bin-mean modes: at most 9 (K <= 8), kept per lane in registers
 constexpr int BINM_MAXB = 9;
+// bins held when K <= 4 (the bin-mean kernels are also built for this count: fewer registers and
+// per-key compares); LDS layouts keep the BINM_MAXB stride
+constexpr int BINM_SMALLB = 5;
 // backward kernels by gradient mode: the calibration sums (full, max_only, min_only), the
 // detached extrema, or the detached gradient projected onto zero-sum rows (P1)
 enum GradKind { GK_SUMS = 0, GK_DETACHED = 1, GK_P1 = 2 };
