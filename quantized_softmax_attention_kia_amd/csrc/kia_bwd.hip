@@ -685,10 +685,13 @@ template <int D, int CAL, int MODE, int GK, typename TIn>
 static hipError_t dq_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
   const size_t smem = dq_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
-  if (is_binmean(MODE) && p.K < BINM_SMALLB)
-    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
-  else
-    hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+  if constexpr (is_binmean(MODE)) {
+    if (p.K < BINM_SMALLB) {
+      hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((dq_kernel<D, CAL, MODE, GK, TIn>), dim3(p.nheads * nqt), dim3(NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE, int GK>

@@ -485,13 +485,19 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // whose second output accumulator takes those registers: there the tile's own V is loaded
   // first, arrives while both half tiles are weighed, and is staged before their products
   constexpr bool VPRE = MODE != NEAREST_P;
+  float s[16];  // this lane's scores of the tile, as it stored them in pass 1
+  auto load_scores = [&](int kt) {
+    const float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = St[v * 64];
+  };
+  // without the V prefetch, the next tile's scores are requested once this tile is weighed
+  if (!VPRE && w < ntiles) load_scores(w);
   for (int kt = w; kt < ntiles; kt += FWD_NW) {
     const int k0 = kt * BN;
     if (!VPRE) vr.load(Vp, k0, T);
     float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
-    float s[16];  // this lane's scores of the tile, as it stored them in pass 1
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = Sw[v * 64];
+    if (VPRE) load_scores(kt);
     if (VPRE) {
       vr.template store_t<NS>(VT);
       wave_lds_sync();
@@ -620,6 +626,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
     }
     if constexpr (!VPRE) {
+      if (kt + FWD_NW < ntiles) load_scores(kt + FWD_NW);
       vr.template store_t<NS>(VT);
       wave_lds_sync();
 #pragma unroll
@@ -766,10 +773,13 @@ template <int D, int CAL, int MODE, typename TIn>
 static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + BN - 1) / BN;
   const size_t smem = fwd_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
-  if (MODE == BINM && p.K < BINM_SMALLB)
-    hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+  if constexpr (MODE == BINM) {
+    if (p.K < BINM_SMALLB) {
+      hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
 }
 template <int D, int CAL, int MODE>
