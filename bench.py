@@ -50,9 +50,9 @@ def sources_digest() -> str:
 
 
 def read_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic.md), or None
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic_gpt2_fwd_bwd.md), or None
     when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_fwd_bwd.md")
     if not os.path.exists(path):
         return None
     digest = sources_digest()
