@@ -114,8 +114,8 @@ def main() -> int:
                          "byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the operator shards over batch x heads with no exchange, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the implementation runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the operator would shard over batch x heads with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np
