@@ -540,7 +540,8 @@ __device__ __forceinline__ void kv_load(KvTile<P1, PC>& t, const BwdArgs& a, siz
 
 // P1: subtract each query row's mean of the detached dS from its visible elements.
 // PC: P arrives as table indices and is looked up in the query rows' tables (staged with Q, dO).
-template <int D, typename TIn, bool P1, bool PC>
+// PT1: the query tile's table rows fit one element per thread (K <= 6).
+template <int D, typename TIn, bool P1, bool PC, bool PT1 = false>
 __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void dkdv_kernel(BwdArgs a) {
   constexpr int NS = nslices<TIn>();
   __shared__ KvSmem<D, NS, PC> sm;
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
   PairRegs<D, TIn, KV_NT> qr, dr;
   KvTile<P1, PC> t0, t1;
   // coded P: the query tile's table rows are contiguous (rows past T are never looked up)
-  constexpr int PT_PER = PC ? (KV_PT + KV_NT - 1) / KV_NT : 1;
+  constexpr int PT_PER = PC && !PT1 ? (KV_PT + KV_NT - 1) / KV_NT : 1;
   const int K2 = a.K + 2;
   float ptr[PT_PER];
   auto pt_load = [&](int qt) {
@@ -667,7 +668,10 @@ template <int D, typename TIn>
 static hipError_t dkdv_go(const Problem& p, const BwdArgs& a, hipStream_t s) {
   const int nkt = (p.T + KV_BN - 1) / KV_BN;
   const dim3 grid(p.nheads * nkt), block(KV_NT);
-  if (a.pc) {
+  if (a.pc && BN * (p.K + 2) <= KV_NT) {
+    if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false, true, true>), grid, block, 0, s, a);
+  } else if (a.pc) {
     if (a.p1) hipLaunchKernelGGL((dkdv_kernel<D, TIn, true, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((dkdv_kernel<D, TIn, false, true>), grid, block, 0, s, a);
   } else {
