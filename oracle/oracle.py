@@ -32,18 +32,11 @@ STE = {"weight": 0, "prob": 1}
 GRAD = {"full": 0, "detached": 1, "max_only": 2, "min_only": 3, "p1": 4}
 TAIL = {"zero": 0, "floor": 1, "resolved": 2}
 
+# flip kinds: the other valid decision at a flagged position (kia_oracle.c, "Flags and flips")
 FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL, FLIP_ROUND, FLIP_ROUND2 = 1, 2, 4, 8, 16
-MUTATIONS = {
-    "drop_rho_delta": 1, "sign_dm": 2, "delta_times_h": 3, "nearest_strict": 4,
-    "wste_uses_lerp": 5, "dk_with_do": 6, "tail_inclusive": 7, "no_tie_split": 8,
-    "nearest_fwd_lerp": 9, "extrema_all_keys": 10, "dq_no_scale": 11, "no_hsafe": 12,
-    "interval_round": 13, "gamma_sign": 14, "dv_with_pl": 15, "fwm_grid_shift": 16,
-    "x_index": 17, "detach_keeps_m": 18, "only_swapped": 19, "p1_skip_tail": 20,
-    "floor_tail_slope": 21, "resolved_grid_clamp": 22, "fp8_truncates": 23, "bf16_grad_unrounded": 24,
-    "fp8_delta_rounded": 25, "binmean_sum": 26, "binmean_own_g": 27,
-}
-ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "gapM", "gapm", "D", "tolM", "tolm")
-ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate", "amax2", "amin2")
+FLIP_GRAD, FLIP_TIE_MAX, FLIP_TIE_MIN = 32, 64, 128
+ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "D")
+ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate")
 
 
 def build(force: bool = False) -> str:
@@ -58,8 +51,8 @@ def build(force: bool = False) -> str:
 
 class _Cfg(ctypes.Structure):
     _fields_ = [("calib", ctypes.c_int32), ("recon", ctypes.c_int32), ("ste", ctypes.c_int32),
-                ("grad", ctypes.c_int32), ("K", ctypes.c_int32), ("mutation", ctypes.c_int32),
-                ("tau", ctypes.c_double), ("tail", ctypes.c_int32)]
+                ("grad", ctypes.c_int32), ("K", ctypes.c_int32), ("tau", ctypes.c_double),
+                ("tail", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -70,7 +63,7 @@ class OracleConfig:
     grad: str = "full"
     K: int = 4
     tau: float = 8.0
-    mutation: str | None = None
+    mutation: str | None = None   # a planted mistake (oracle/mutants.py): runs that mutant library
     tail: str = "zero"   # FWM tail policy: zero, floor or resolved
 
     @classmethod
@@ -80,17 +73,21 @@ class OracleConfig:
 
     def _c(self) -> _Cfg:
         return _Cfg(CALIB[self.calib], RECON[self.recon], STE[self.ste], GRAD[self.grad],
-                    int(self.K), MUTATIONS[self.mutation] if self.mutation else 0, float(self.tau),
-                    TAIL[self.tail])
+                    int(self.K), float(self.tau), TAIL[self.tail])
 
 
-_lib = None
+_libs = {}
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        lib = ctypes.CDLL(build())
+def _load(mutation=None):
+    """The oracle library, or with `mutation` the mutant library that plants that mistake."""
+    if mutation not in _libs:
+        if mutation is None:
+            path = build()
+        else:
+            from oracle import mutants
+            path = mutants.build_mutant(mutation)
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
         up = ctypes.POINTER(ctypes.c_uint8)
@@ -99,12 +96,12 @@ def _load():
         lib.ko_row.restype = ctypes.c_int
         lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                 dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
-                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up, dp, dp,
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up,
                                 ctypes.c_int]
         lib.ko_head.restype = ctypes.c_int
         assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
-        _lib = lib
-    return _lib
+        _libs[mutation] = lib
+    return _libs[mutation]
 
 
 def _p(a, ct):
@@ -120,9 +117,9 @@ def row(cfg: OracleConfig, s, g=None, flip=None):
     """One row of visible scores s (already scaled) with upstream dL/dP g.
 
     Returns a dict: P, dS (None if g is None), u, r, t, ell, tail and the row
-    record fields (M, m, h, WL, WN, a, b, gapM, gapm, D, amax, amin, nA, nC, degenerate).
+    record fields (M, m, h, WL, WN, a, b, D, amax, amin, nA, nC, degenerate).
     """
-    lib = _load()
+    lib = _load(cfg.mutation)
     s = np.ascontiguousarray(s, dtype=np.float64)
     n = s.shape[0]
     g = None if g is None else np.ascontiguousarray(g, dtype=np.float64)
@@ -145,14 +142,14 @@ def row(cfg: OracleConfig, s, g=None, flip=None):
 
 
 def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=None,
-         guard=0.0, flag_cap=0, bins=False, rows=None, absolute=False, nthreads=None):
+         guard=0.0, flag_cap=0, bins=False, rows=None, nthreads=None):
     """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags
     (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible).
-    rows: optional list of row indices; only those rows are computed (their contributions alone).
-    absolute: also return abs = {O, dQ, dK, dV}: the same sums of absolute values of the terms,
-    and amb = {dQ, dK}: what bfloat16 gradient roundings that may go either way can change
-    (exp_bf16; zero otherwise)."""
-    lib = _load()
+    flips: (row, key, kind) triples at which the other valid decision is taken.
+    flag_cap > 0: also return the flagged positions (row, key, kind) and their distances from
+    the boundary, within `guard` or the fp32 representation bound of the scores.
+    rows: optional list of row indices; only those rows are computed (their contributions alone)."""
+    lib = _load(cfg.mutation)
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
     V = np.ascontiguousarray(V, dtype=np.float64)
@@ -172,8 +169,6 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     if rows is not None:
         rmask = np.zeros(T, np.uint8)
         rmask[np.asarray(list(rows), dtype=np.int64)] = 1
-    aout = np.zeros((4, T, D)) if absolute else None
-    amb = np.zeros((2, T, D)) if absolute else None
     c = cfg._c()
     rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
                      _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
@@ -181,8 +176,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
                      _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32),
                      fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
                      _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
-                     _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), _p(aout, ctypes.c_double),
-                     _p(amb, ctypes.c_double), int(nthreads or default_threads()))
+                     _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle head rejected its arguments (rc={rc})")
     nf = int(nfl.value)
@@ -191,9 +185,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     rowd = {k: rd[:, i].copy() for i, k in enumerate(ROWD_FIELDS)}
     rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
     return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
-                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap,
-                abs=None if aout is None else dict(O=aout[0], dQ=aout[1], dK=aout[2], dV=aout[3]),
-                amb=None if amb is None else dict(dQ=amb[0], dK=amb[1]))
+                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap)
 
 
 def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):

@@ -3,6 +3,7 @@ check that each planted mistake is caught by at least one pin."""
 import pytest
 
 import oracle_pins as OP
+from oracle import mutants
 
 IDS = ["-".join(v) for v in OP.VARIANTS]
 
@@ -20,7 +21,7 @@ def test_pins_other_K(oracle_mod, variant, K):
         pin(OP.cfg_of(*variant, K=K, tau=5.0))
 
 
-@pytest.mark.parametrize("mutation", sorted(OP.ORC.MUTATIONS))
+@pytest.mark.parametrize("mutation", sorted(mutants.MUTANTS))
 def test_planted_mistake_is_caught(oracle_mod, mutation):
     caught = []
     for variant in OP.VARIANTS:
