@@ -132,7 +132,9 @@ typedef struct {
  *    Layout (offsets are multiples of 256 bytes), N = B*H*T, nt = ceil(T/32):
  *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N];
  *      (m, amin and nC belong to MinMax; under FWM m = M and amin = nC = 0)
- *      float OL[N*D] (Nearest + Prob-STE only);
+ *      float OL[N*D] (Nearest + Prob-STE: the output O^L; BF16-exp: the residual
+ *        O - o of the double output whose float o is the kernel's output, and then WN
+ *        holds W's residual, W = WL + WN; other modes: absent);
  *      float S[B*H][tiles][1024]: the scores s_ij = scale * Q_i . K_j as floats, in
  *        32 x 32 tiles (query tile, key tile); tiles = nt(nt+1)/2 when causal
  *        (key tile <= query tile), nt^2 otherwise.  About 2 T^2 bytes per head

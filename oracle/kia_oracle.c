@@ -62,14 +62,23 @@
  *    rounds dL/dw to bfloat16 where it enters the bfloat16 weight, then the
  *    product with the weight; FP8 rounds e^z to E4M3 with e^z as derivative.
  *
+ * Scores.  The pages run the attention operator in fp32 (App. C.1 "Numerics
+ * and hardware"): a score is an fp32 number.  With cfg.score_fp32 the oracle
+ * takes it as the product sum Q_i . K_j formed in double (exact products of the
+ * fp32 or bf16 inputs), scaled, and rounded once to fp32; every later step works
+ * in double on those values, so row extrema, ties and every decision are those
+ * of correctly rounded fp32 scores.  Without it the double sum is used as is
+ * (the method in exact arithmetic, for checks against derivatives).
+ *
  * Flags and flips (apparatus).  A decision of the method (an interval, a
- * Nearest rounding, the FWM tail edge, a rounding to bfloat16 / E4M3, which key
- * attains a row extremum) can go either way when the operator runs on fp32
- * scores: the flag list names the positions within `guard` of the decision's
- * boundary (in the decision's own units) or within what representing the
- * scores in fp32 can move there; a flip asks the oracle to take the other
- * decision at a named position.  This is how a test checks that a result
- * computed in fp32 is one of the answers that are correct at that precision.
+ * Nearest rounding, the FWM tail edge, a rounding to bfloat16 / E4M3) within
+ * `guard` of its boundary (in the decision's own units), and a score whose
+ * double product sum lies within its own rounding bound of an fp32 midpoint
+ * (so that another correct summation order rounds it the other way), can go
+ * either way: the flag list names those positions, and a flip asks the oracle
+ * to take the other decision (the other fp32 neighbour of the score) there.
+ * This is how a test checks that a result is one of the answers that are
+ * correct at that precision.
  */
 #include <math.h>
 #include <stdint.h>
@@ -97,14 +106,15 @@ enum {
   FLIP_ROUND = 8,      /* FP8: the other E4M3 neighbour of e^z; BF16: of z */
   FLIP_ROUND2 = 16,    /* BF16: the other bfloat16 neighbour of e^(rounded z) */
   FLIP_GRAD = 32,      /* BF16: the other bfloat16 neighbour of dL/dw */
-  FLIP_TIE_MAX = 64,   /* the key ties the row maximum */
-  FLIP_TIE_MIN = 128   /* the key ties the row minimum */
+  FLIP_SCORE = 64      /* the other fp32 neighbour of the score */
 };
 
 typedef struct {
   int32_t calib, recon, ste, grad, K;
   double tau;
-  int32_t tail;   /* FWM tail policy (KO_TAIL_*); zero for MinMax */
+  int32_t tail;        /* FWM tail policy (KO_TAIL_*); zero for MinMax */
+  int32_t score_fp32;  /* ko_head: 1 rounds each score to fp32 (the operator's precision), 0 keeps
+                          the double product sum (the method in exact arithmetic) */
 } ko_cfg_t;
 
 #define DEGENERATE_EPS 1e-12
@@ -489,42 +499,13 @@ static void flag_push(ko_flags_t *f, int row, int key, int kind, double dist) {
   }
 }
 
-/* Keys whose score may round, in fp32, to the same value as the row maximum (minimum) although
-   the exact scores differ: eb bounds how far representing a score in fp32 moves it. */
-static void ko_flag_ties(const ko_cfg_t *cfg, int n, const double *s, const double *eb, const ko_ext_t *x,
-                         const uint8_t *inA, const uint8_t *inC, int row_id, ko_flags_t *f) {
-  const int minmax = cfg->calib == KO_MINMAX && cfg->recon < KO_SOFTMAX;
-  for (int j = 0; j < n; ++j) {
-    const double gM = x->M - s[j], gm = s[j] - x->m;
-    if (!inA[j] && gM <= eb[j] + eb[x->amax]) flag_push(f, row_id, j, FLIP_TIE_MAX, gM);
-    if (minmax && !inC[j] && gm <= eb[j] + eb[x->amin]) flag_push(f, row_id, j, FLIP_TIE_MIN, gm);
-  }
-}
-
-/* A key flipped into a tie joins the set of keys attaining the extremum. */
-static void ko_flip_ties(int n, const uint8_t *flip, ko_ext_t *x, uint8_t *inA, uint8_t *inC) {
-  for (int j = 0; j < n; ++j) {
-    if ((flip[j] & FLIP_TIE_MAX) && !inA[j]) {
-      inA[j] = 1; x->nA++;
-      if (j < x->amax) x->amax = j;
-    }
-    if ((flip[j] & FLIP_TIE_MIN) && !inC[j]) {
-      inC[j] = 1; x->nC++;
-      if (j < x->amin) x->amin = j;
-    }
-  }
-}
-
-/* Decisions within the guard (in interval widths) of a boundary, or within the change of u that
-   representing the score and the row extrema in fp32 can cause, when that is larger. */
-static void ko_flag_decision(const ko_cfg_t *cfg, const ko_ext_t *x, const ko_cal_t *c, double s, double ebj,
-                             const double *eb, const ko_dec_t *d, int row_id, int key, ko_flags_t *f) {
+/* Decisions within the guard (in interval widths) of a boundary. */
+static void ko_flag_decision(const ko_cfg_t *cfg, const ko_ext_t *x, const ko_cal_t *c, double s,
+                             const ko_dec_t *d, int row_id, int key, ko_flags_t *f) {
   const int K = cfg->K;
   const int resolved = cfg->calib == KO_FWM && cfg->tail == KO_TAIL_RESOLVED;
   const int nearest_bins = cfg->recon == KO_NEAREST || cfg->recon == KO_BINMEAN || cfg->recon == KO_NEAREST_BINMEAN;
-  const double eu = cfg->calib == KO_MINMAX ? (ebj + 2.0 * eb[x->amin] + eb[x->amax]) / c->h
-                                            : (ebj + eb[x->amax]) / c->h;
-  const double gj = eu > f->guard ? eu : f->guard;
+  const double gj = f->guard;
   if (cfg->calib == KO_FWM && !resolved && fabs(s - x->M + cfg->tau) / c->h < gj)
     flag_push(f, row_id, key, FLIP_TAIL, fabs(s - x->M + cfg->tau) / c->h);
   const double kint = floor(d->u + 0.5);
@@ -563,17 +544,17 @@ static void ko_flip_decision(const ko_cfg_t *cfg, uint8_t bits, ko_dec_t *d) {
 }
 
 /* Exponential baselines: roundings within the guard (in spacings of the target format) of a
-   midpoint, or within what the fp32 representation of the scores (ez, the error of z) can move. */
-static void ko_flag_exp(const ko_cfg_t *cfg, const ko_xdec_t *d, double ez, int row_id, int key, ko_flags_t *f) {
+   midpoint (z = s - M is exact in double for fp32 scores). */
+static void ko_flag_exp(const ko_cfg_t *cfg, const ko_xdec_t *d, int row_id, int key, ko_flags_t *f) {
   double pos, lo, hi, alt;
   if (cfg->recon == KO_EXP_FP8) {
     (void)round_fmt(exp(d->z), E4M3_MB, E4M3_EMIN, &pos, &lo, &hi);
     const double dist = fabs(pos - floor(pos) - 0.5);
-    if (dist < fmax(f->guard, pos * ez)) flag_push(f, row_id, key, FLIP_ROUND, dist);
+    if (dist < f->guard) flag_push(f, row_id, key, FLIP_ROUND, dist);
   } else if (cfg->recon == KO_EXP_BF16) {
     const double zb = round_signed(d->z, BF16_MB, BF16_EMIN, &pos, &alt);
     double dist = fabs(pos - floor(pos) - 0.5);
-    if (d->z != 0.0 && dist < fmax(f->guard, pos * ez / fabs(d->z))) flag_push(f, row_id, key, FLIP_ROUND, dist);
+    if (d->z != 0.0 && dist < f->guard) flag_push(f, row_id, key, FLIP_ROUND, dist);
     (void)round_fmt(exp(zb), BF16_MB, BF16_EMIN, &pos, &lo, &hi);
     dist = fabs(pos - floor(pos) - 0.5);
     if (dist < f->guard) flag_push(f, row_id, key, FLIP_ROUND2, dist);
@@ -627,18 +608,15 @@ typedef struct {
 /*
  * One attention row: the method's steps in order, with the apparatus between them.
  *  s[0..n): the scaled scores of the row's visible keys; g: dL/dP_j (NULL: forward only);
- *  flip: per-key flip bits (NULL: none); eb, flags: per-key fp32 representation bound of the
- *  scores and the flag list (both NULL: no flags).  Outputs P, Pv (probabilities for dV),
- *  dS (if g), key decisions, the row record.
+ *  flip: per-key flip bits (NULL: none); flags: the flag list (NULL: no flags).  Outputs P, Pv
+ *  (probabilities for dV), dS (if g), key decisions, the row record.
  */
 static void ko_row_run(const ko_cfg_t *cfg, int n, const double *s, const double *g, const uint8_t *flip,
-                       const double *eb, ko_flags_t *flags, int row_id, const int32_t *key_id,
+                       ko_flags_t *flags, int row_id, const int32_t *key_id,
                        double *P, double *Pv, double *dS, const ko_keyout_t *ko, double *rowd, int32_t *rowi) {
   uint8_t *inA = (uint8_t *)malloc(n), *inC = (uint8_t *)malloc(n);
   ko_ext_t x;
   ko_extrema(n, s, &x, inA, inC);
-  if (flags) ko_flag_ties(cfg, n, s, eb, &x, inA, inC, row_id, flags);
-  if (flip) ko_flip_ties(n, flip, &x, inA, inC);
   ko_sums_t sum = {0.0, 0.0, 0.0, 0.0, 0.0};
   double h = 0.0;
   int degenerate = 0;
@@ -647,7 +625,7 @@ static void ko_row_run(const ko_cfg_t *cfg, int n, const double *s, const double
     ko_xdec_t *d = (ko_xdec_t *)malloc(sizeof(ko_xdec_t) * n);
     for (int j = 0; j < n; ++j) {
       ko_exp_decide(cfg, s[j] - x.M, &d[j]);
-      if (flags) ko_flag_exp(cfg, &d[j], eb[j] + eb[x.amax], row_id, key_id[j], flags);
+      if (flags) ko_flag_exp(cfg, &d[j], row_id, key_id[j], flags);
       if (flip && flip[j]) ko_flip_exp(cfg, flip[j], &d[j]);
     }
     double W = 0.0;
@@ -679,7 +657,7 @@ static void ko_row_run(const ko_cfg_t *cfg, int n, const double *s, const double
     ko_dec_t *d = (ko_dec_t *)malloc(sizeof(ko_dec_t) * n);
     for (int j = 0; j < n; ++j) {
       ko_decide(cfg, &x, &c, s[j], &d[j]);
-      if (flags) ko_flag_decision(cfg, &x, &c, s[j], eb[j], eb, &d[j], row_id, key_id[j], flags);
+      if (flags) ko_flag_decision(cfg, &x, &c, s[j], &d[j], row_id, key_id[j], flags);
       if (flip && flip[j]) ko_flip_decision(cfg, flip[j], &d[j]);
     }
     ko_finish_grid(cfg, n, s, g, &x, &c, d, inA, inC, P, Pv, dS, &sum);
@@ -729,7 +707,7 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
   if (u && !(r && t && ell && tail)) return -1;
   double *Pv = (double *)malloc(sizeof(double) * n);
   ko_keyout_t ko = {u, t, r, ell, NULL, tail};
-  ko_row_run(cfg, n, s, g, flip, NULL, NULL, 0, NULL, P, Pv, dS, &ko, rowd, rowi);
+  ko_row_run(cfg, n, s, g, flip, NULL, 0, NULL, P, Pv, dS, &ko, rowd, rowi);
   free(Pv);
   return 0;
 }
@@ -746,13 +724,14 @@ int ko_row(const ko_cfg_t *cfg, int n, const double *s, const double *g, const u
  * bfloat16 weight (EXP_BF16) or 0 (SOFTMAX).
  * row_mask: optional [T]; rows with 0 are skipped (their O, dQ rows stay 0 and they add nothing
  * to dK, dV), so a caller can get the contributions of chosen rows alone.
+ * scores: optional [T, T]: the fp32 scores of the visible keys (0 elsewhere).
  */
 int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
             const double *Q, const double *Kt, const double *V, const double *dO,
             double *O, double *dQ, double *dK, double *dV, double *rowd, int32_t *rowi,
             int64_t nflip, const int32_t *flips,
             double guard, int64_t flag_cap, int32_t *flag_pos, double *flag_dist, int64_t *nflags,
-            uint8_t *bins, const uint8_t *row_mask, int nthreads) {
+            uint8_t *bins, const uint8_t *row_mask, double *scores, int nthreads) {
   if (!ko_cfg_ok(cfg) || T < 1 || D < 1 || !Q || !Kt || !V || !O) return -1;
   if (dO && !(dQ && dK && dV)) return -1;
   ko_flags_t fl_store, *fl = NULL;
@@ -792,9 +771,14 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
     double *Pv = (double *)malloc(sizeof(double) * n);
     double *dS = dO ? (double *)malloc(sizeof(double) * n) : NULL;
     int32_t *kid = (int32_t *)malloc(sizeof(int32_t) * n);
-    double *eb = fl ? (double *)malloc(sizeof(double) * n) : NULL;
     int32_t *code = bins ? (int32_t *)malloc(sizeof(int32_t) * n) : NULL;
     uint8_t *flip = NULL;
+    for (int64_t f = 0; f < nflip; ++f) {
+      if (flips[3 * f] == i && flips[3 * f + 1] >= 0 && flips[3 * f + 1] < n) {
+        if (!flip) flip = (uint8_t *)calloc(n, 1);
+        flip[flips[3 * f + 1]] |= (uint8_t)flips[3 * f + 2];
+      }
+    }
     for (int j = 0; j < n; ++j) {
       kid[j] = j;
       double acc = 0.0, aabs = 0.0;
@@ -802,24 +786,31 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
         acc += Q[(size_t)i * D + k] * Kt[(size_t)j * D + k];
         aabs += fabs(Q[(size_t)i * D + k] * Kt[(size_t)j * D + k]);
       }
-      s[j] = scale * acc;
-      /* how far representing the score in fp32 can move it: one fp32 ulp, 2^-23 |s|, plus the
-         double accumulation's own bound */
-      if (eb) eb[j] = 1.1920928955078125e-07 * fabs(s[j]) + 1e-15 * fabs(scale) * aabs;
+      s[j] = cfg->score_fp32 ? (double)(float)(scale * acc) : scale * acc;   /* fp32 score (App. C.1) */
+      if (cfg->score_fp32 && (fl || (flip && (flip[j] & FLIP_SCORE)))) {
+        /* the double sum errs by at most 2 D 2^-53 sum|q k| and the scaling by 2^-53 |s|; a
+           summation in another order (the same bound) may round to the other fp32 neighbour
+           when the exact value is that close to a midpoint */
+        const double x = scale * acc;
+        const double bound = (4.0 * D + 4.0) * 0x1p-53 * fabs(scale) * aabs;
+        const float lo = (float)x <= x ? (float)x : nextafterf((float)x, -INFINITY);
+        const float hi = nextafterf(lo, INFINITY);
+        const double mid = 0.5 * ((double)lo + (double)hi);
+        if (fl && fabs(x - mid) <= bound) flag_push(fl, i, j, FLIP_SCORE, fabs(x - mid));
+        if (flip && (flip[j] & FLIP_SCORE)) s[j] = s[j] == (double)lo ? (double)hi : (double)lo;
+      }
       if (dO) {
         double ga = 0.0;
         for (int k = 0; k < D; ++k) ga += dO[(size_t)i * D + k] * V[(size_t)j * D + k];
         g[j] = ga;                                          /* g_j = dL/dP_j = dO_i . V_j */
       }
     }
-    for (int64_t f = 0; f < nflip; ++f) {
-      if (flips[3 * f] == i && flips[3 * f + 1] >= 0 && flips[3 * f + 1] < n) {
-        if (!flip) flip = (uint8_t *)calloc(n, 1);
-        flip[flips[3 * f + 1]] |= (uint8_t)flips[3 * f + 2];
-      }
+    if (scores) {
+      for (int j = 0; j < T; ++j) scores[(size_t)i * T + j] = 0.0;
+      for (int j = 0; j < n; ++j) scores[(size_t)i * T + j] = s[j];
     }
     ko_keyout_t ko = {NULL, NULL, NULL, NULL, code, NULL};
-    ko_row_run(cfg, n, s, g, flip, eb, fl, i, kid, P, Pv, dS, &ko,
+    ko_row_run(cfg, n, s, g, flip, fl, i, kid, P, Pv, dS, &ko,
                rowd ? rowd + (size_t)i * RD_N : NULL, rowi ? rowi + (size_t)i * RI_N : NULL);
     if (bins) {
       for (int j = 0; j < T; ++j) bins[(size_t)i * T + j] = 255;
@@ -838,7 +829,7 @@ int ko_head(const ko_cfg_t *cfg, int T, int D, int causal, double scale,
         }
       }
     }
-    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip); free(eb); free(code);
+    free(s); free(g); free(P); free(Pv); free(dS); free(kid); free(flip); free(code);
   }
   if (dO) {
     for (int th = 0; th < nthreads; ++th)

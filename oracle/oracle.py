@@ -34,7 +34,7 @@ TAIL = {"zero": 0, "floor": 1, "resolved": 2}
 
 # flip kinds: the other valid decision at a flagged position (kia_oracle.c, "Flags and flips")
 FLIP_INTERVAL, FLIP_NEAREST, FLIP_TAIL, FLIP_ROUND, FLIP_ROUND2 = 1, 2, 4, 8, 16
-FLIP_GRAD, FLIP_TIE_MAX, FLIP_TIE_MIN = 32, 64, 128
+FLIP_GRAD, FLIP_SCORE = 32, 64
 ROWD_FIELDS = ("M", "m", "h", "WL", "WN", "a", "b", "D")
 ROWI_FIELDS = ("amax", "amin", "nA", "nC", "degenerate")
 
@@ -52,7 +52,7 @@ def build(force: bool = False) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("calib", ctypes.c_int32), ("recon", ctypes.c_int32), ("ste", ctypes.c_int32),
                 ("grad", ctypes.c_int32), ("K", ctypes.c_int32), ("tau", ctypes.c_double),
-                ("tail", ctypes.c_int32)]
+                ("tail", ctypes.c_int32), ("score_fp32", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -65,6 +65,9 @@ class OracleConfig:
     tau: float = 8.0
     mutation: str | None = None   # a planted mistake (oracle/mutants.py): runs that mutant library
     tail: str = "zero"   # FWM tail policy: zero, floor or resolved
+    # scores rounded once to fp32, the precision the pages run the operator in (App. C.1); False
+    # keeps the double product sums (the method in exact arithmetic)
+    score_fp32: bool = True
 
     @classmethod
     def of(cls, v, mutation=None):
@@ -73,7 +76,7 @@ class OracleConfig:
 
     def _c(self) -> _Cfg:
         return _Cfg(CALIB[self.calib], RECON[self.recon], STE[self.ste], GRAD[self.grad],
-                    int(self.K), float(self.tau), TAIL[self.tail])
+                    int(self.K), float(self.tau), TAIL[self.tail], int(bool(self.score_fp32)))
 
 
 _libs = {}
@@ -96,7 +99,7 @@ def _load(mutation=None):
         lib.ko_row.restype = ctypes.c_int
         lib.ko_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                 dp, dp, dp, dp, dp, dp, dp, dp, dp, ip,
-                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up,
+                                ctypes.c_int64, ip, ctypes.c_double, ctypes.c_int64, ip, dp, lp, up, up, dp,
                                 ctypes.c_int]
         lib.ko_head.restype = ctypes.c_int
         assert lib.ko_rowd_n() == len(ROWD_FIELDS) and lib.ko_rowi_n() == len(ROWI_FIELDS)
@@ -142,13 +145,14 @@ def row(cfg: OracleConfig, s, g=None, flip=None):
 
 
 def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=None,
-         guard=0.0, flag_cap=0, bins=False, rows=None, nthreads=None):
+         guard=0.0, flag_cap=0, bins=False, rows=None, scores=False, nthreads=None):
     """One head: Q, K, V, dO are [T, D].  Returns dict O, dQ, dK, dV, rowd, rowi, flags
     (and bins [T, T] uint8 when bins=True: Nearest index / interval index, 254 tail, 255 invisible).
     flips: (row, key, kind) triples at which the other valid decision is taken.
     flag_cap > 0: also return the flagged positions (row, key, kind) and their distances from
     the boundary, within `guard` or the fp32 representation bound of the scores.
-    rows: optional list of row indices; only those rows are computed (their contributions alone)."""
+    rows: optional list of row indices; only those rows are computed (their contributions alone).
+    scores: also return the fp32 scores the method ran on ([T, T], 0 where a key is not visible)."""
     lib = _load(cfg.mutation)
     Q = np.ascontiguousarray(Q, dtype=np.float64)
     K = np.ascontiguousarray(K, dtype=np.float64)
@@ -169,6 +173,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     if rows is not None:
         rmask = np.zeros(T, np.uint8)
         rmask[np.asarray(list(rows), dtype=np.int64)] = 1
+    smap = np.zeros((T, T)) if scores else None
     c = cfg._c()
     rc = lib.ko_head(ctypes.byref(c), T, D, int(bool(causal)), scale,
                      _p(Q, ctypes.c_double), _p(K, ctypes.c_double), _p(V, ctypes.c_double), _p(dO, ctypes.c_double),
@@ -176,7 +181,8 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
                      _p(rd, ctypes.c_double), _p(ri, ctypes.c_int32),
                      fl.shape[0], _p(fl, ctypes.c_int32), float(guard), int(flag_cap),
                      _p(fpos, ctypes.c_int32), _p(fdist, ctypes.c_double), ctypes.byref(nfl),
-                     _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), int(nthreads or default_threads()))
+                     _p(bmap, ctypes.c_uint8), _p(rmask, ctypes.c_uint8), _p(smap, ctypes.c_double),
+                     int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle head rejected its arguments (rc={rc})")
     nf = int(nfl.value)
@@ -185,7 +191,7 @@ def head(cfg: OracleConfig, Q, K, V, dO=None, *, causal=True, scale=None, flips=
     rowd = {k: rd[:, i].copy() for i, k in enumerate(ROWD_FIELDS)}
     rowi = {k: ri[:, i].copy() for i, k in enumerate(ROWI_FIELDS)}
     return dict(O=O, dQ=dQ, dK=dK, dV=dV, rowd=rowd, rowi=rowi, nflags=nf,
-                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap)
+                flags=fpos[:kept][order], flag_dist=fdist[:kept][order], bins=bmap, scores=smap)
 
 
 def forward_backward(cfg: OracleConfig, q, k, v, do=None, *, causal=True, scale=None, heads=None, nthreads=None):

@@ -109,13 +109,38 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_inputs(p: Params, *tensors):
+_DTYPE_OF = {v: k for k, v in DTYPE.items()}
+
+
+def _check_inputs(p: Params, *tensors, outputs=(), rowrec=None, workspace=None):
+    """Every input [B,H,T,D], contiguous, of the params' dtype, on one GPU; every output the same
+    shape in float32 on that GPU; the record and workspace at least the sizes the library asks for.
+    The kernels read buffers through raw pointers: a mismatch here would be an out-of-bounds access."""
     shape = (p.B, p.H, p.T, p.D)
+    want = _DTYPE_OF.get(p.dtype)
+    dev = tensors[0].device if tensors else None
     for t in tensors:
-        if not t.is_cuda:
-            raise ValueError("tensors must be on the GPU")
         if tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"expected contiguous [B,H,T,D]={shape}, got {tuple(t.shape)}")
+        if t.dtype != want:
+            raise ValueError(f"expected {want} inputs (params dtype), got {t.dtype}")
+    for t in outputs:
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous float32 [B,H,T,D]={shape}, got {t.dtype} {tuple(t.shape)}")
+    bufs = []
+    if rowrec is not None or workspace is not None:
+        rr, ws = kia_workspace_size(p)
+        for name, buf, need in (("rowrec", rowrec, rr), ("workspace", workspace, ws)):
+            if buf is None:
+                continue
+            if buf.numel() * buf.element_size() < need or not buf.is_contiguous():
+                raise ValueError(f"{name} holds {buf.numel() * buf.element_size()} bytes; {need} needed")
+            bufs.append(buf)
+    for t in list(tensors) + [x for x in outputs if x is not None] + bufs:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
 
 
 def kia_workspace_size(p: Params):
@@ -126,29 +151,34 @@ def kia_workspace_size(p: Params):
 
 
 def kia_forward(p: Params, q, k, v, o, rowrec, stream=None) -> None:
-    _check_inputs(p, q, k, v)
+    _check_inputs(p, q, k, v, outputs=(o,), rowrec=rowrec)
     _check(_lib.kia_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(rowrec), _stream(stream)))
 
 
 def kia_backward(p: Params, q, k, v, o, d_o, rowrec, dq, dk, dv, workspace, stream=None) -> None:
-    _check_inputs(p, q, k, v, d_o)
+    _check_inputs(p, q, k, v, d_o, outputs=(o, dq, dk, dv), rowrec=rowrec, workspace=workspace)
     _check(_lib.kia_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowrec),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
 
 
 def kia_backward_dq(p: Params, q, k, v, o, d_o, rowrec, dq, workspace, stream=None) -> None:
-    _check_inputs(p, q, k, v, d_o)
+    _check_inputs(p, q, k, v, d_o, outputs=(o, dq), rowrec=rowrec, workspace=workspace)
     _check(_lib.kia_backward_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowrec),
                                 _ptr(dq), _ptr(workspace), _stream(stream)))
 
 
 def kia_backward_dkdv(p: Params, q, k, v, d_o, rowrec, dk, dv, workspace, stream=None) -> None:
-    _check_inputs(p, q, k, v, d_o)
+    _check_inputs(p, q, k, v, d_o, outputs=(dk, dv), rowrec=rowrec, workspace=workspace)
     _check(_lib.kia_backward_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(rowrec),
                                   _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
 
 
 def kia_debug_bins(p: Params, rowrec, bins, stream=None) -> None:
+    rr, _ = kia_workspace_size(p)
+    if rowrec.numel() * rowrec.element_size() < rr:
+        raise ValueError(f"rowrec holds {rowrec.numel() * rowrec.element_size()} bytes; {rr} needed")
+    if bins.dtype != torch.uint8 or bins.numel() < p.B * p.H * p.T * p.T or bins.device != rowrec.device:
+        raise ValueError("bins must be uint8 [B,H,T,T] on the record's GPU")
     _check(_lib.kia_debug_bins(ctypes.byref(p), _ptr(rowrec), _ptr(bins), _stream(stream)))
 
 

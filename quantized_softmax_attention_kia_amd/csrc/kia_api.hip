@@ -121,7 +121,7 @@ Layout layout(const kia::Problem& pr) {
   size_t o = 0;
   for (int i = 0; i < 8; ++i) { L.off[i] = o; o += round_up(N * 4); }
   L.off[8] = o;
-  if (pr.mode == kia::NEAREST_P) o += round_up(N * pr.D * 4);
+  if (pr.mode == kia::NEAREST_P || pr.mode == kia::EXPBF) o += round_up(N * pr.D * 4);
   L.nt = (pr.T + 31) / 32;
   L.tiles_per_head = pr.causal ? (size_t)L.nt * (L.nt + 1) / 2 : (size_t)L.nt * L.nt;
   L.off[9] = o;
@@ -153,7 +153,7 @@ kia::RowRec carve(const kia::Problem& pr, void* base) {
   r.nC = reinterpret_cast<int32_t*>(b + L.off[5]);
   r.WN = reinterpret_cast<float*>(b + L.off[6]);
   r.WL = reinterpret_cast<float*>(b + L.off[7]);
-  r.OL = pr.mode == kia::NEAREST_P ? reinterpret_cast<float*>(b + L.off[8]) : nullptr;
+  r.OL = pr.mode == kia::NEAREST_P || pr.mode == kia::EXPBF ? reinterpret_cast<float*>(b + L.off[8]) : nullptr;
   r.S = reinterpret_cast<float*>(b + L.off[9]);
   r.nt = L.nt;
   r.tiles_per_head = L.tiles_per_head;

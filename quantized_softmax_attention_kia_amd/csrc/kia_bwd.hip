@@ -63,10 +63,18 @@ __device__ __forceinline__ int stored_offset(int a, int b) {
 __device__ __forceinline__ int stored_lane_group(int b) { return (b >> 2) & 1; }
 
 // ============================================================================ dq kernel
-template <int D, int NS>
+// BF16-exp forms g = dO V^T in double (fp64 MFMA): V rows as floats, row stride D + 4 (operand
+// reads free of bank conflicts), and each wave's 32 x 32 tile of g, transposed through LDS
+template <int D> constexpr int vns() { return D + 4; }
+template <int D, int NS, bool F64>
+constexpr int dq_vn_elems() {
+  return F64 && 2 * BN * vns<D>() > NS * BN * np<D>() ? 2 * BN * vns<D>() : NS * BN * np<D>();
+}
+template <int D, int NS, bool F64>
 struct DqSmem {
   __align__(16) __bf16 KT[NS * D * TP];         // K^T of the key tile, bf16 slices (dQ += dS K)
-  __align__(16) __bf16 VN[NS * BN * np<D>()];   // V rows of the key tile, bf16 slices (g = V dO^T)
+  __align__(16) __bf16 VN[dq_vn_elems<D, NS, F64>()];  // V rows of the key tile, bf16 slices (g = V dO^T)
+  double GX[F64 ? NW : 1][F64 ? 32 * 33 : 1];
   float alpha[DQ_BM], beta[DQ_BM], mean[DQ_BM];
   int amax[DQ_BM], amin[DQ_BM];
   // followed in dynamic LDS by the grid table: MinMax DQ_BM rows x (K + 3) floats, FWM one
@@ -79,7 +87,7 @@ __host__ __device__ constexpr int dq_table_floats(int CAL, int K, int lres) {
 // bin-mean modes: after the grid table, per row the bins' means of e^z and of g
 template <int D, int CAL, int MODE, typename TIn>
 size_t dq_smem_bytes(int K, int lres) {
-  return sizeof(DqSmem<D, nslices<TIn>()>) +
+  return sizeof(DqSmem<D, nslices<TIn>(), MODE == EXPBF>) +
          sizeof(float) * (dq_table_floats(CAL, K, lres) + (is_binmean(MODE) ? 2 * DQ_BM * BINM_MAXB : 0));
 }
 
@@ -92,9 +100,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   constexpr bool SUMS = GK == GK_SUMS, P1 = GK == GK_P1;
   constexpr bool PC = p_coded(CAL, MODE);  // P written as table indices beside the row's table
   constexpr int NS = nslices<TIn>();
+  // BF16-exp: dL/dw is rounded to bfloat16, so it is formed from exact parts: g in double (fp64
+  // MFMA), D_i from the forward's double output (O and its residual), W from its float and residual
+  constexpr bool F64 = MODE == EXPBF;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  DqSmem<D, NS>& sm = *reinterpret_cast<DqSmem<D, NS>*>(smem_raw);
-  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS>));
+  DqSmem<D, NS, F64>& sm = *reinterpret_cast<DqSmem<D, NS, F64>*>(smem_raw);
+  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(DqSmem<D, NS, F64>));
+  float* VF = reinterpret_cast<float*>(sm.VN);  // F64: V rows as floats
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K;  // grid table: e^{b_0} .. e^{b_K}, then two zeros
   const int nqt = (T + DQ_BM - 1) / DQ_BM;
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const int nA = a.rec.nA[row], nC = a.rec.nC[row];
   const float Wf = is_nearest(MODE) ? a.rec.WN[row] : a.rec.WL[row];
   const float Wg = (MODE == NEAREST_W) ? a.rec.WN[row] : a.rec.WL[row];
-  f4v xo[D / 8], yo[D / 8];
+  f4v xo[D / 8], yo[D / 8], xr[F64 ? D / 8 : 1];  // xr: F64, the residual of O
   {
     const int qc = qvalid ? qi : 0;
     const float* X = ((MODE == NEAREST_P) ? a.rec.OL : a.o) + hb + (size_t)qc * D + 4 * g;
@@ -136,6 +148,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     for (int q = 0; q < D / 8; ++q) {
       xo[q] = *reinterpret_cast<const f4v*>(X + 8 * q);
       yo[q] = Ld<TIn>::four(Y + 8 * q);
+      if (F64) xr[q] = *reinterpret_cast<const f4v*>(a.rec.OL + hb + (size_t)qc * D + 4 * g + 8 * q);
+    }
+  }
+  const double Wgd = F64 ? (double)Wg + (double)a.rec.WN[row] : (double)Wg;
+  // F64: the A operand of g = dO V^T, dO[qw0 + 16 qh + l%16][4 s + l/16] (zero past T)
+  float doA[F64 ? 2 : 1][F64 ? D / 4 : 1];
+  if constexpr (F64) {
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int r = qw0 + 16 * qh + (l & 15);
+#pragma unroll
+      for (int s4 = 0; s4 < D / 4; ++s4) doA[qh][s4] = r < T ? Ld<TIn>::one(dOp + (size_t)r * D + 4 * s4 + (l >> 4)) : 0.f;
     }
   }
   // the lane's dO row as bf16 slices, columns 16 kb + 8 g ..: the B operand of every g = V dO^T
@@ -150,14 +174,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 
   // D_i = dO_i . O_i (O^L_i for Nearest with Prob-STE): sum_j P_j g_j at the normalization point
   float Di;
+  double Did;  // F64: in double, from O and its residual
   {
     double part = 0.0;
 #pragma unroll
     for (int q = 0; q < D / 8; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part = fma((double)yo[q][e], (double)xo[q][e], part);
+      for (int e = 0; e < 4; ++e) {
+        part = fma((double)yo[q][e], (double)xo[q][e], part);
+        if (F64) part = fma((double)yo[q][e], (double)xr[q][e], part);
+      }
     if (!qvalid) part = 0.0;
-    Di = (float)(part + __shfl_xor(part, 32));
+    Did = part + __shfl_xor(part, 32);
+    Di = (float)Did;
   }
 
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
@@ -178,6 +207,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   const bool blockties = __syncthreads_or(rowties);
 
   double acc_a = 0.0, sds = 0.0;  // calibration sums of the row (terms of both signs)
+  // A row whose maximum is attained by one key: that key's own score gradient gamma Delta and the
+  // maximum's calibration term alpha cancel (the key's own dw/dM is -Delta at t = 1), so both are
+  // formed together from the other keys' terms, without that cancellation.  The key stays out of
+  // the sums and of the dQ products; xself / xown keep its own gamma Delta and gamma K (Delta +
+  // dw/dM), and after the sweep its coefficient (self plus alpha) goes into dS and dQ at once.
+  const bool xrow = SUMS && qvalid && !flat && nA == 1;
+  float xself = 0.f, xown = 0.f;
   f16v dq[D / 32], pk[P1 ? D / 32 : 1];  // pk: P1 only, the sum of the visible K rows
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) dq[nb] = zero16();
@@ -197,14 +233,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   // bin-mean modes (§5, App. I): a first sweep sums, per Nearest bin of the row, e^{s - M}, the
   // member count and the upstream gradient g (keys below an FWM window belong to no bin), per
   // lane in registers and then over the row's two lanes; per row it keeps the bins' means of e^z
-  // and of g, W^C = sum_b S_b and D^C = sum_j P^C_j g_j, for dS_k = e^{z_k} / W^C (gbar_b(k) - D^C)
+  // and, for dS_k = e^{z_k} / W^C (gbar_b(k) - D^C), the differences gbar_b - D^C (W^C = sum_b S_b,
+  // D^C = sum_j P^C_j g_j).  The sums are kept in double: D^C is a weighted mean of the bins' mean
+  // gradients, which can be large beside the differences it is taken from
   float* bmean = tbl + dq_table_floats(CAL, K, a.lres) + rl * BINM_MAXB;  // [DQ_BM][BINM_MAXB]
-  float* bgbar = bmean + DQ_BM * BINM_MAXB;
-  float invWC = 0.f, DC = 0.f;
+  float* bgd = bmean + DQ_BM * BINM_MAXB;
+  float invWC = 0.f;
   if constexpr (BM) {
-    float bs[NB], bn[NB], bg[NB];
+    double bs[NB], bg[NB];
+    float bn[NB];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) { bs[q] = 0.f; bn[q] = 0.f; bg[q] = 0.f; }
+    for (int q = 0; q < NB; ++q) { bs[q] = 0.0; bn[q] = 0.f; bg[q] = 0.0; }
     RowRegs<D, TIn, NT> vp;
     vp.load(Vp, 0, T);
     for (int kt = 0; kt < ntiles; ++kt) {
@@ -229,28 +268,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
           const bool hit = in && ell == q;
-          bs[q] += hit ? x : 0.f;
+          bs[q] += hit ? (double)x : 0.0;
           bn[q] += hit ? 1.f : 0.f;
-          bg[q] += hit ? gt[v] : 0.f;
+          bg[q] += hit ? (double)gt[v] : 0.0;
         }
       }
     }
-    float WC = 0.f, GC = 0.f;  // bins past K hold nothing: NB of them cover every member
+    double WC = 0.0, GC = 0.0, gbar[NB];  // bins past K hold nothing: NB of them cover every member
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       bs[q] += __shfl_xor(bs[q], 32);
       bn[q] += __shfl_xor(bn[q], 32);
       bg[q] += __shfl_xor(bg[q], 32);
-      const float mean = bn[q] > 0.f ? bs[q] / bn[q] : 0.f, gbar = bn[q] > 0.f ? bg[q] / bn[q] : 0.f;
+      gbar[q] = bn[q] > 0.f ? bg[q] / (double)bn[q] : 0.0;
       WC += bs[q];
-      GC = fmaf(bs[q], gbar, GC);
-      if (g == 0) {
-        bmean[q] = mean;
-        bgbar[q] = gbar;
+      GC = fma(bs[q], gbar[q], GC);
+    }
+    const double DC = WC > 0.0 ? GC / WC : 0.0;
+    if (g == 0) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        bmean[q] = bn[q] > 0.f ? (float)(bs[q] / (double)bn[q]) : 0.f;
+        bgd[q] = (float)(gbar[q] - DC);
       }
     }
-    invWC = WC > 0.f ? 1.f / WC : 0.f;
-    DC = GC * invWC;
+    invWC = WC > 0.0 ? (float)(1.0 / WC) : 0.f;
   }
 
   if constexpr (PC) {
@@ -281,7 +323,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     if (kt + 1 < ntiles && active(kt + 1)) load_s(kt + 1, snext);
     __syncthreads();
     kr.template store_t<NS>(sm.KT);
-    if (!BM) vr.template store<NS>(sm.VN);
+    if (F64) vr.store_f32(VF, vns<D>());
+    else if (!BM) vr.template store<NS>(sm.VN);
     __syncthreads();
     if (kt + 1 < ntiles) {
       kr.load(Kp, k0 + BN, T);
@@ -293,9 +336,38 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     float* dSw = dSh + to;
     // (dO V^T)^T as bf16 slice products: register v holds g = dO_i . V_j for query c, key k0 + crow(v, g)
     f16v gt = zero16();
-    if (!BM) {
+    if (!BM && !F64) {
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) gt = mfma_split<NS, NS>(load_an<D, NS>(sm.VN, c, kb), dos[kb], gt);
+    }
+    // F64: g in double, block (qh, kh) element i at query 16 qh + l/16 + 4 i, key 16 kh + l%16, then
+    // through LDS to the lane's own elements (query c, key crow(v, g))
+    double g64[F64 ? 16 : 1];
+    if constexpr (F64) {
+      d4v gx[2][2];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) { gx[qh][0] = zero4d(); gx[qh][1] = zero4d(); }
+#pragma unroll
+      for (int s4 = 0; s4 < D / 4; ++s4) {
+        const int d = 4 * s4 + (l >> 4);
+        const double b0 = VF[(l & 15) * vns<D>() + d], b1 = VF[(16 + (l & 15)) * vns<D>() + d];
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          gx[qh][0] = mfma_f64(doA[qh][s4], b0, gx[qh][0]);
+          gx[qh][1] = mfma_f64(doA[qh][s4], b1, gx[qh][1]);
+        }
+      }
+      double* G = sm.GX[w];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) G[(16 * qh + (l >> 4) + 4 * i) * 33 + 16 * kh + (l & 15)] = gx[qh][kh][i];
+      wave_lds_sync();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) g64[v] = G[c * 33 + crow(v, g)];
+      wave_lds_sync();  // read before the next tile's g is written
     }
     // half tiles (keys crow(v, g), v = 8 b .. 8 b + 7): decisions, weights and dS, then their share of
     // dQ += dS K as bf16 slice products (dS in the A layout: query c, keys crow(8 b + e, g)).  A key
@@ -303,6 +375,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
     // weight, slope, dS and calibration terms are then exactly zero.  A floored tail key keeps the
     // window edge's weight and has no slope, hence no dS and no calibration term.
     const int lim = (qvalid ? (a.causal ? min(qi, T - 1) : T - 1) : -1) - k0 - 4 * g;  // crow(v, 0) <= lim
+    // at D = 128 (one wave per SIMD, registers to spare) each key tile's dS K goes into a fresh
+    // accumulator that joins the running dQ once: a long row (T = 8192: 256 key tiles) then takes one
+    // rounding of its running sum per tile instead of one per slice product
+    constexpr bool FRESH = D == 128 && !P1;
+    f16v tq[FRESH ? D / 32 : 1];
+    if (FRESH) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) tq[nb] = zero16();
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float ds[8];
@@ -323,7 +404,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           d = decide<CAL>(s[v], rc, K, a.tau);
           const bool in = (crow(v, 0) <= lim) & !d.tail;
           const int ell = min(d.r + (d.t >= 0.5f ? 1 : 0), NB - 1);
-          dS = in ? __expf(s[v] - M) * invWC * (bgbar[ell] - DC) : 0.f;
+          dS = in ? __expf(s[v] - M) * invWC * bgd[ell] : 0.f;
           code = in ? ell : K + 1;
           if (MODE == BINM) pw = in ? bmean[ell] : 0.f;
           else pw = in ? weights_cal<CAL, CAL == MINMAX ? DQ_BM : 1>(d, trow, a.lres, a.res_far != 0, K, a.tau).wN : 0.f;
@@ -339,37 +420,52 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
           ExpW ew = exp_weight_fast<MODE>(s[v], M, 0.f, &rs, &re);
           if (rs || re) ew = exp_weight_exact<MODE>(s[v], M);
           pw = vis ? ew.w : 0.f;
-          if (MODE == EXPBF) dS = vis ? bf16_round(bf16_round(gam) * ew.d) : 0.f;
-          else dS = vis ? gam * ew.d : 0.f;
+          if constexpr (F64) {
+            // dL/dw in double, rounded once to bfloat16 (exact parts: the rounding is the exact
+            // value's wherever that lies farther than double rounding error from a midpoint)
+            const float gb = (float)bf16_round_d((g64[v] - Did) / Wgd);
+            dS = vis ? bf16_round(gb * ew.d) : 0.f;
+          } else {
+            dS = vis ? gam * ew.d : 0.f;
+          }
         } else {
           d = decide<CAL>(s[v], rc, K, a.tau);
           if ((crow(v, 0) > lim) | (CAL == FWM && d.tail)) d.r = K + 1;
           wt = weights_cal<CAL, CAL == MINMAX ? DQ_BM : 1>(d, trow, a.lres, a.res_far != 0, K, a.tau);
-          Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : (wt.E1 - wt.E0) * rc.inv_hf;
+          Delta = (CAL == FWM_FLOOR && d.tail) ? 0.f : wt.E0 * rc.slope;
           dS = gam * Delta;
           pw = is_nearest(MODE) ? wt.wN : wt.wL;
           code = d.r > K ? K + 1 : d.r + (d.t >= 0.5f ? 1 : 0);  // wN is the table's entry there
         }
-        ds[j] = dS;
         // the forward's normalized weight: P^L for LERP, the hard P^N for Nearest
         if constexpr (PC) Pcw[v * 64 + l] = (uint8_t)code;
         else Pw[v * 64 + l] = pw * invWf;
         dSw[v * 64 + l] = dS;
-        if (SUMS || P1) hs += dS;
+        if (P1) hs += dS;
         if (SUMS) {
+          const bool xk = xrow & (k0 + crow(v, g) == amax);  // the row's only arg-max key
+          xself += xk ? dS : 0.f;
+          hs += xk ? 0.f : dS;
           if (CAL == MINMAX) {
             const float rf = (float)d.r;
             // K * dw/dM = (r - K) w + t e^{b_{r+1}} - kappa (r + t) Delta
             const float dMk = fmaf(rf - (float)K, wt.wL, d.t * wt.E1) - rc.kappa * (rf + d.t) * Delta;
-            ha = fmaf(gam, dMk, ha);
+            ha = fmaf(gam, xk ? 0.f : dMk, ha);
+            // K (Delta + dw/dM) = (K - kappa (r + t)) Delta + (r - K) w + t e^{b_{r+1}}: 0 at t = 1
+            if (xk) xown += gam * fmaf((float)K - rc.kappa * (rf + d.t), Delta, fmaf(rf - (float)K, wt.wL, d.t * wt.E1));
           }
+          dS = xk ? 0.f : dS;
         }
+        ds[j] = dS;
       }
       if (SUMS || P1) sds += (double)hs;
       if (SUMS && CAL == MINMAX) acc_a += (double)ha;
       const Split8 dss = split8(ds);
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) dq[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.KT, b, 32 * nb + c), dq[nb]);
+      for (int nb = 0; nb < D / 32; ++nb) {
+        if (FRESH) tq[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.KT, b, 32 * nb + c), tq[nb]);
+        else dq[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.KT, b, 32 * nb + c), dq[nb]);
+      }
       if (P1) {
         // the sum of the row's visible K rows, for the mean's share of dQ: a 0 / 1 mask (exact in
         // bf16) times the K^T slices
@@ -382,6 +478,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) pk[nb] = mfma_split<NS, 1>(ms, load_bt<D, NS>(sm.KT, b, 32 * nb + c), pk[nb]);
       }
+    }
+    if (FRESH) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) dq[nb] += tq[nb];
     }
   }
 
@@ -397,8 +497,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
   if (SUMS) {
     acc_a += __shfl_xor(acc_a, 32);
     sds += __shfl_xor(sds, 32);
+    xself += __shfl_xor(xself, 32);  // the other lane of the row holds 0
+    xown += __shfl_xor(xown, 32);
     if (inject) {
-      if (CAL == MINMAX) {
+      if (xrow) {
+        // alpha here is the arg-max key's whole coefficient: its own gamma Delta plus the
+        // maximum's term (or its own term alone when that term is dropped)
+        if (CAL == MINMAX) {
+          const double comb = (acc_a + (double)xown) / (double)K;
+          alpha = a.keepM ? (float)comb : xself;
+          beta = a.keepm ? (float)((-sds - comb) / (double)nC) : 0.f;
+        } else {
+          alpha = a.keepM ? (float)(-sds) : xself;
+        }
+      } else if (CAL == MINMAX) {
         const double A = acc_a / (double)K;
         const double Bm = -sds - A;
         alpha = a.keepM ? (float)(A / (double)nA) : 0.f;
@@ -407,11 +519,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 
         alpha = a.keepM ? (float)(-sds / (double)nA) : 0.f;
       }
     }
-    // dS of the first arg-max / arg-min key of the row gains alpha / beta, added by the lane
-    // that stored the element (program order makes its own store visible to it)
-    if (inject && a.keepM && g == stored_lane_group(amax % BN)) {
+    // dS of the first arg-max / arg-min key of the row gains alpha / beta (the arg-max key of an
+    // xrow row takes its coefficient), written by the lane that stored the element (program order
+    // makes its own store visible to it)
+    if (inject && (a.keepM || xrow) && g == stored_lane_group(amax % BN)) {
       float* e = dSh + tile_index(qtw, amax / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amax % BN);
-      *e = *e + alpha;
+      *e = xrow ? alpha : *e + alpha;
     }
     if (CAL == MINMAX && inject && a.keepm && g == stored_lane_group(amin % BN)) {
       float* e = dSh + tile_index(qtw, amin / BN, a.rec.nt, a.causal) * 1024 + stored_offset(c, amin % BN);
@@ -557,9 +670,24 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
   const size_t tbase = (size_t)head * a.rec.tiles_per_head;
   auto active = [&](int qt) { return kw0 < T && (!a.causal || ktw <= qt); };  // wave-uniform
 
-  f16v dk[D / 32], dv[D / 32];
+  // At D = 128 (long rows) the running sums are kept in double: a key that carries much of the
+  // probability of many rows sums terms far larger than its result (dV_j = sum_i P_ij dO_i with P
+  // near 1 in hundreds of rows), and float roundings of a running sum of 8192 rows would reach the
+  // result.  Each query tile's products go into one fresh float accumulator, first dV's and then
+  // dK's, and join the double sums once per tile.  (P1 keeps the float sums: its extra operands
+  // leave no registers for them.)
+  constexpr bool DSUM = D == 128 && !P1;
+  f16v dk[DSUM ? 1 : D / 32], dv[DSUM ? 1 : D / 32];
+  double dkd[DSUM ? D / 32 : 1][DSUM ? 16 : 1], dvd[DSUM ? D / 32 : 1][DSUM ? 16 : 1];
+  if constexpr (DSUM) {
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = zero16(); dv[nb] = zero16(); }
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { dkd[nb][v] = 0.0; dvd[nb][v] = 0.0; }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = zero16(); dv[nb] = zero16(); }
+  }
 
   const int qt_first = a.causal ? kb0 / BN : 0;
   // the workgroup's Q and dO rows of the next query tile, staged through LDS as bf16 slices;
@@ -623,14 +751,57 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
         if (query < T && key < T && (!a.causal || key <= query)) ds[v] -= t.mean[v];
       }
     }
+    if constexpr (DSUM) {
+      f16v tf[D / 32];
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) tf[nb] = zero16();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const Split8 ps = split8(p + 8 * b);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) tf[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), tf[nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { dvd[nb][v] += (double)tf[nb][v]; tf[nb][v] = 0.f; }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const Split8 dss = split8(ds + 8 * b);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) tf[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), tf[nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dkd[nb][v] += (double)tf[nb][v];
+      return;
+    }
+    // at D = 128 under P1 each query tile's products go into a fresh accumulator that joins the
+    // float running sums once per tile
+    constexpr bool FRESH = D == 128;
+    f16v tv[FRESH ? D / 32 : 1], tk[FRESH ? D / 32 : 1];
+    if (FRESH) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) { tv[nb] = zero16(); tk[nb] = zero16(); }
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const Split8 ps = split8(p + 8 * b), dss = split8(ds + 8 * b);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
-        dv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), dv[nb]);
-        dk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), dk[nb]);
+        if (FRESH) {
+          tv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), tv[nb]);
+          tk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), tk[nb]);
+        } else {
+          dv[nb] = mfma_split<NS>(ps, load_bt<D, NS>(sm.dOT, b, 32 * nb + c), dv[nb]);
+          dk[nb] = mfma_split<NS>(dss, load_bt<D, NS>(sm.QT, b, 32 * nb + c), dk[nb]);
+        }
       }
+    }
+    if (FRESH) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) { dv[nb] += tv[nb]; dk[nb] += tk[nb]; }
     }
   };
   if (qt_first < nt) {
@@ -655,8 +826,13 @@ __global__ __launch_bounds__(KV_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ?
       float* pv = a.dv + hb + (size_t)key * D + c;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) {
-        pk[32 * nb] = dk[nb][v] * a.scale;
-        pv[32 * nb] = dv[nb][v];
+        if constexpr (DSUM) {
+          pk[32 * nb] = (float)(dkd[nb][v] * a.scale);
+          pv[32 * nb] = (float)dvd[nb][v];
+        } else {
+          pk[32 * nb] = dk[nb][v] * a.scale;
+          pv[32 * nb] = dv[nb][v];
+        }
       }
     }
   }

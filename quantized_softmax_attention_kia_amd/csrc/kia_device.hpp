@@ -51,8 +51,10 @@ __device__ __forceinline__ size_t tile_index(int qt, int kt, int nt, int causal)
 template <typename T> struct Ld;
 template <> struct Ld<float> {
   __device__ static f4v four(const float* p) { return *reinterpret_cast<const f4v*>(p); }
+  __device__ static float one(const float* p) { return *p; }
 };
 template <> struct Ld<uint16_t> {
+  __device__ static float one(const uint16_t* p) { return __uint_as_float(((uint32_t)*p) << 16); }
   __device__ static f4v four(const uint16_t* p) {
     uint2 raw = *reinterpret_cast<const uint2*>(p);
     f4v r;
@@ -76,6 +78,15 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f16v mfma_bf16(bf8v a, bf8v b, f16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// fp64 MFMA (16x16x4): lane l supplies A[l%16][l/16] and B[l/16][l%16]; element i of lane l of
+// the accumulator is C[l/16 + 4 i][l%16].  Products and sums in double: operands that are floats
+// (fp32 or bf16 inputs, bfloat16 weights) multiply exactly.
+typedef double d4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ d4v mfma_f64(double a, double b, d4v c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ d4v zero4d() { return d4v{0.0, 0.0, 0.0, 0.0}; }
 
 // Number of bf16 slices that represent an input element exactly enough: bf16 inputs are exact.
 template <typename TIn> constexpr int nslices() { return sizeof(TIn) == 2 ? 1 : 3; }
@@ -177,6 +188,59 @@ struct PairRegs {
       }
     }
   }
+  // the two rows in their natural layout as floats, X[r * stride + d] (stride a multiple of 4)
+  __device__ __forceinline__ void store_f32(float* x, int stride) const {
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      float* p = x + (2 * rp) * stride + cg * CW + 4 * j;
+      *reinterpret_cast<f4v*>(p) = f4v{x0[4 * j], x0[4 * j + 1], x0[4 * j + 2], x0[4 * j + 3]};
+      *reinterpret_cast<f4v*>(p + stride) = f4v{x1[4 * j], x1[4 * j + 1], x1[4 * j + 2], x1[4 * j + 3]};
+    }
+  }
+};
+
+// bf16 inputs: the rows stay packed as loaded (two bf16 to a word), half the registers of the
+// float form; they are exact bf16 values, so the transposed store only moves their halves
+template <int D, int NTH>
+struct PairRegs<D, uint16_t, NTH> {
+  static constexpr int CW = D * 16 / NTH;
+  uint32_t x0[CW / 2], x1[CW / 2];  // columns 2 i (low half) and 2 i + 1 (high half)
+  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows) {
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
+    const int r0 = row0 + 2 * rp;
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      const uint2 a = r0 < nrows ? *reinterpret_cast<const uint2*>(src + (size_t)r0 * D + cg * CW + 4 * j) : uint2{0u, 0u};
+      const uint2 b = r0 + 1 < nrows ? *reinterpret_cast<const uint2*>(src + (size_t)(r0 + 1) * D + cg * CW + 4 * j)
+                                     : uint2{0u, 0u};
+      x0[2 * j] = a.x; x0[2 * j + 1] = a.y;
+      x1[2 * j] = b.x; x1[2 * j + 1] = b.y;
+    }
+  }
+  template <int NS>
+  __device__ __forceinline__ void store_t(__bf16* xt) const {
+    static_assert(NS == 1, "bf16 inputs are one slice");
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
+    uint32_t* w = reinterpret_cast<uint32_t*>(xt);
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int at = ((cg * CW + j) * TP + 2 * rp) >> 1;
+      const uint32_t a = (j & 1) ? x0[j >> 1] >> 16 : x0[j >> 1] & 0xffffu;
+      const uint32_t b = (j & 1) ? x1[j >> 1] & 0xffff0000u : x1[j >> 1] << 16;
+      w[at] = a | b;
+    }
+  }
+  __device__ __forceinline__ void store_f32(float* x, int stride) const {
+    const int t = threadIdx.x % NTH, rp = t & 15, cg = t >> 4;
+#pragma unroll
+    for (int j = 0; j < CW / 4; ++j) {
+      float* p = x + (2 * rp) * stride + cg * CW + 4 * j;
+      *reinterpret_cast<f4v*>(p) = f4v{bf16_lo(x0[2 * j]), bf16_hi(x0[2 * j]), bf16_lo(x0[2 * j + 1]), bf16_hi(x0[2 * j + 1])};
+      *reinterpret_cast<f4v*>(p + stride) =
+          f4v{bf16_lo(x1[2 * j]), bf16_hi(x1[2 * j]), bf16_lo(x1[2 * j + 1]), bf16_hi(x1[2 * j + 1])};
+    }
+  }
 };
 
 // A 32-row tile staged in its natural layout as NS bf16 slices, XN[s][r * NP + d], for A / B
@@ -213,6 +277,45 @@ struct RowRegs {
         *reinterpret_cast<bf8v*>(o + 64 * np<D>()) = sp.l;
       }
     }
+  }
+  // the row in its natural layout as floats, X[r * stride + d] (stride a multiple of 4)
+  __device__ __forceinline__ void store_f32(float* xs, int stride) const {
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j)
+      *reinterpret_cast<f4v*>(xs + r * stride + c0 + 4 * j) = f4v{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+  }
+};
+
+// bf16 inputs: the row stays packed as loaded (two bf16 to a word)
+template <int D, int NTH>
+struct RowRegs<D, uint16_t, NTH> {
+  static constexpr int PER = 32 * D / NTH;
+  uint32_t x[PER / 2];
+  __device__ __forceinline__ void load(const uint16_t* src, int row0, int nrows) {
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+    const int gr = row0 + r;
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const uint2 a = gr < nrows ? *reinterpret_cast<const uint2*>(src + (size_t)gr * D + c0 + 4 * j) : uint2{0u, 0u};
+      x[2 * j] = a.x;
+      x[2 * j + 1] = a.y;
+    }
+  }
+  template <int NS>
+  __device__ __forceinline__ void store(__bf16* xn) const {
+    static_assert(NS == 1, "bf16 inputs are one slice");
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+#pragma unroll
+    for (int j = 0; j < PER / 8; ++j)
+      *reinterpret_cast<uint4*>(xn + r * np<D>() + c0 + 8 * j) = uint4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+  }
+  __device__ __forceinline__ void store_f32(float* xs, int stride) const {
+    const int t = threadIdx.x % NTH, r = t / (D / PER), c0 = (t % (D / PER)) * PER;
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j)
+      *reinterpret_cast<f4v*>(xs + r * stride + c0 + 4 * j) =
+          f4v{bf16_lo(x[2 * j]), bf16_hi(x[2 * j]), bf16_lo(x[2 * j + 1]), bf16_hi(x[2 * j + 1])};
   }
 };
 
@@ -261,7 +364,7 @@ template <int D> struct RowOp<D, uint16_t> {
   }
   __device__ __forceinline__ Split8 split(int kb) const {
     Split8 s;
-    __builtin_memcpy(&s.h, &x[kb], 16);
+    s.h = __builtin_bit_cast(bf8v, x[kb]);
     return s;
   }
 };
@@ -306,11 +409,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 // u of a key is formed in double from its stored fp32 score: with K up to 64, u reaches K and
 // an fp32 u would lose the low bits of the local position t.
 struct RowCal {
-  double origin;  // score at u = 0: m (MinMax) or M (FWM: u is measured from M - tau)
+  // u is measured down from the row maximum, u = K - (M - s)/h (the maximum's own weight is then
+  // exactly the top grid value); the degenerate MinMax branch measures it up from m (h = 1)
+  double origin;  // m (MinMax) or M
+  float top_f;    // M
   double inv_h;   // 1/h
-  float inv_hf;   // 1/h rounded to float (secant slopes)
+  float inv_hf;   // 1/h rounded to float
   float kappa;    // 1 on the regular MinMax branch (h depends on M, m), 0 on the degenerate one
   float origin_f; // the origin as a float (m or M: exact)
+  // Secant slope over the grid value: Delta_r = (e^{b_{r+1}} - e^{b_r}) / h = e^{b_r} expm1(b_{r+1} -
+  // b_r) / h, and the grid step b_{r+1} - b_r is the same for every r ((M - m)/K, or tau/K).  The
+  // difference of two fp32 grid values would lose about (e^step - 1)^-1 ulps when the step is
+  // small (K/tau = 64: 64 ulps); the factor formed in double keeps Delta within 2 ulps.
+  float slope;
 };
 
 template <int CAL>
@@ -323,13 +434,17 @@ __device__ __forceinline__ RowCal row_calibration(float M, float m, int K, float
     rc.origin = (double)m;
     rc.inv_h = 1.0 / h;
     rc.kappa = deg ? 0.0f : 1.0f;
+    rc.slope = (float)(expm1(span / (double)K) / h);
   } else {
+    const double h = (double)tau / (double)K;
     rc.origin = (double)M;
     rc.inv_h = (double)K / (double)tau;
     rc.kappa = 1.0f;
+    rc.slope = (float)(expm1(h) / h);
   }
   rc.inv_hf = (float)rc.inv_h;
   rc.origin_f = CAL == MINMAX ? m : M;
+  rc.top_f = M;
   return rc;
 }
 
@@ -361,21 +476,21 @@ __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, flo
   Decision d;
   double u;
   if (CAL == FWM_RES) {  // App. D.4: the grid continues below -tau, nothing is clipped below
-    const double z = (double)s - rc.origin;
+    const double z = (double)s - (double)rc.top_f;
     d.tail = false;
-    u = (fmin(z, 0.0) + (double)tau) * rc.inv_h;
+    u = (double)K + fmin(z, 0.0) * rc.inv_h;
     const int r = min((int)fmax(floor(u), (double)RES_RMIN), K - 1);
     d.r = r;
     d.t = (float)fmin(fmax(u - (double)r, 0.0), 1.0);
     return d;
   }
   if (CAL == MINMAX) {
-    u = ((double)s - rc.origin) * rc.inv_h;
+    u = rc.kappa != 0.f ? (double)K - ((double)rc.top_f - (double)s) * rc.inv_h : (double)s - rc.origin;
     d.tail = false;
   } else {
-    const double z = (double)s - rc.origin;
+    const double z = (double)s - (double)rc.top_f;
     d.tail = z < -(double)tau;
-    u = (fmax(z, -(double)tau) + (double)tau) * rc.inv_h;
+    u = (double)K + fmax(z, -(double)tau) * rc.inv_h;
   }
   int r = (int)floor(u);
   r = min(max(r, 0), K - 1);
@@ -388,28 +503,30 @@ __device__ __forceinline__ Decision decide(float s, const RowCal& rc, int K, flo
 // of the (at most four) roundings on the way to u errs by at most 2^-24 of a quantity below
 // (K + 1) interval widths, so this u is within (K + 1) 2^-22 of decide()'s: a decision whose t
 // is farther than that from 0, 1 (interior boundaries) and 1/2 (Nearest) is decide()'s, and so
-// is the FWM tail flag when |(s - M) + tau| (in float) exceeds tau 2^-21.
+// is the FWM tail flag when |(s - M) + tau| (in float) exceeds tau 2^-21.  Measured from the
+// maximum, the error shrinks toward the top of the grid (K - u widths times a few 2^-24), where
+// the weights are largest, and vanishes at the maximum itself.
 // On the resolved grid |u| is not bounded by K + 1: the caller widens the margin by |r| 2^-22.
 template <int CAL>
 __device__ __forceinline__ Decision decide_fast(float s, const RowCal& rc, int K, float tau) {
   Decision d;
   float u;
   if (CAL == FWM_RES) {
-    const float z = s - rc.origin_f;
+    const float z = s - rc.top_f;
     d.tail = false;
-    u = (fminf(z, 0.f) + tau) * rc.inv_hf;
+    u = fmaf(fminf(z, 0.f), rc.inv_hf, (float)K);
     const int r = min((int)floorf(fmaxf(u, (float)RES_RMIN)), K - 1);
     d.r = r;
     d.t = __builtin_amdgcn_fmed3f(u - (float)r, 0.f, 1.f);
     return d;
   }
   if (CAL == MINMAX) {
-    u = (s - rc.origin_f) * rc.inv_hf;
+    u = rc.kappa != 0.f ? fmaf(s - rc.top_f, rc.inv_hf, (float)K) : s - rc.origin_f;
     d.tail = false;
   } else {
-    const float z = s - rc.origin_f;
+    const float z = s - rc.top_f;
     d.tail = z < -tau;
-    u = (fmaxf(z, -tau) + tau) * rc.inv_hf;
+    u = fmaf(fmaxf(z, -tau), rc.inv_hf, (float)K);
   }
   // the interval index clamped in float (one med3), then converted once
   const float rf = __builtin_amdgcn_fmed3f(floorf(u), 0.f, (float)(K - 1));

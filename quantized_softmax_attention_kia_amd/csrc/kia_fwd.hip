@@ -24,7 +24,8 @@
 //           pass decides as on exact scores) -> LERP / Nearest weight from the table
 //           (no exp) -> row sums W^L, W^N -> O += w V as bf16 slice products on the
 //           matrix pipe, V^T staged in LDS by the wave (and O^L += w^L V for Nearest
-//           with Prob-STE) -> O = num / W (the strict hard forward for Nearest).  Row sums are kept in double and each tile's P V is summed
+//           with Prob-STE; BF16-exp multiplies in double on the fp64 MFMA and stores O
+//           with its residual) -> O = num / W (the strict hard forward for Nearest).  Row sums are kept in double and each tile's P V is summed
 //           into a fresh accumulator before joining the running O, so the
 //           precision of O (which the backward's D_i = dO . O amplifies) does not
 //           decay with T.
@@ -44,6 +45,10 @@ namespace kia {
 constexpr int FWD_NW = 2;            // waves per workgroup, splitting the key tiles of a query tile
 constexpr int FWD_NT = 64 * FWD_NW;
 constexpr int BN = 32;               // keys per tile, query rows per workgroup
+// A key that carries P >= 1/HEAVY_INV of its row is heavy: its score is recomputed exactly after
+// pass 2 and its weight corrected, up to HMAX keys per lane
+constexpr double HEAVY_INV = 16.0;
+constexpr int HMAX = 4;
 
 
 // Approximate extrema of the keys one lane stored: the two largest values and the key of the
@@ -58,18 +63,29 @@ struct XExt {
   int k, n;
 };
 
-template <int D, int NS>
-constexpr int fwd_wave_bytes() {  // per wave: V^T slices of its key tile, later its partial O
-  return NS * D * TP * 2 > D / 32 * 4096 ? NS * D * TP * 2 : D / 32 * 4096;
+// BF16-exp multiplies its weights by V in double (fp64 MFMA): V as floats, row stride VFS, and
+// the tile's weights, row stride PTS (strides that keep the operand reads free of bank conflicts)
+template <int D> constexpr int vfs() { return D + 16; }
+constexpr int PTS = 36;
+
+template <int D, int NS, bool F64>
+constexpr int fwd_wave_bytes() {  // per wave: V of its key tile (as staged), later its partial O
+  // (the partial O in double at D = 128 and under BF16-exp)
+  return F64 ? (32 * vfs<D>() * 4 + 32 * PTS * 4 > 32 * D * 8 ? 32 * vfs<D>() * 4 + 32 * PTS * 4 : 32 * D * 8)
+             : (NS * D * TP * 2 > D / 32 * (D == 128 ? 8192 : 4096) ? NS * D * TP * 2 : D / 32 * (D == 128 ? 8192 : 4096));
 }
 
-template <int D, int NS>
+template <int D, int NS, bool F64>
 struct FwdSmem {
-  __align__(16) unsigned char wave[FWD_NW][fwd_wave_bytes<D, NS>()];
+  __align__(16) unsigned char wave[FWD_NW][fwd_wave_bytes<D, NS, F64>()];
   float rmx[FWD_NW][BN], rmn[FWD_NW][BN], amx[FWD_NW][BN];
   XExt xM[FWD_NW][BN], xm[FWD_NW][BN];
   double sL[FWD_NW][BN], sN[FWD_NW][BN];
   float rowW[BN], rowWL[BN];
+  double rowWd[BN], rowWLd[BN];  // the row sums in double: O's normalizer, and W^L
+  // heavy keys retaken after pass 2: per lane up to HMAX (key, change of the continuous weight)
+  int hn[FWD_NW][64], hk[FWD_NW][64][HMAX];
+  float hd[FWD_NW][64][HMAX];
   // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
 };
 
@@ -91,10 +107,10 @@ constexpr double acc_c() {
 
 // The exact score of one (query, key) pair: products and sum in double, scale in double,
 // rounded once to fp32 -- the value the bound is measured against.
-template <int D, typename TIn>
+template <int D, typename TIn, int UNROLL = 8>
 __device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, double scale) {
   double acc = 0.0;
-#pragma unroll 8
+#pragma unroll UNROLL
   for (int d = 0; d < D; d += 4) {
     const f4v x = Ld<TIn>::four(qrow + d), y = Ld<TIn>::four(krow + d);
 #pragma unroll
@@ -174,9 +190,19 @@ __device__ __forceinline__ void xext_merge(XExt& a, int lanemask, bool is_max) {
 template <int D, int CAL, int MODE, typename TIn, int NB = BINM_MAXB>
 __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
   constexpr int NS = nslices<TIn>();
+  // BF16-exp: the weights are bfloat16 values, taken exactly, and their products with V are summed
+  // in double (fp64 MFMA) with the row sums, so that the output carries double precision (O and its
+  // residual): the backward's D_i = dO_i . O_i is then exact enough to round dL/dw to bfloat16 as
+  // the exact values do
+  constexpr bool F64 = MODE == EXPBF;
+  // At D = 128 (long rows; one wave per SIMD, registers to spare) the running sum of O (of O^L
+  // under Nearest with Prob-STE, whose D_i = dO_i . O^L_i the backward amplifies; O itself stays
+  // in float) is kept in double: a row of 8192 keys adds 128 fresh tile products into it, and
+  // float roundings of the running sum would reach D_i at about 1e-6 relative
+  constexpr bool DRUN = D == 128 && !F64;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  FwdSmem<D, NS>& sm = *reinterpret_cast<FwdSmem<D, NS>*>(smem_raw);
-  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D, NS>));
+  FwdSmem<D, NS, F64>& sm = *reinterpret_cast<FwdSmem<D, NS, F64>*>(smem_raw);
+  float* tbl = reinterpret_cast<float*>(smem_raw + sizeof(FwdSmem<D, NS, F64>));
   const int w = wave_id(), l = threadIdx.x & 63, g = l >> 5, c = l & 31;
   const int T = a.T, K = a.K, nt = a.rec.nt;
   int head, rank;
@@ -190,6 +216,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   const int ntiles = a.causal ? qt + 1 : nt;  // wave w takes key tiles w, w + FWD_NW, ...
   float* Sh = a.rec.S + (size_t)head * a.rec.tiles_per_head * 1024;
   __bf16* VT = reinterpret_cast<__bf16*>(sm.wave[w]);
+  float* VF = reinterpret_cast<float*>(sm.wave[w]);  // F64: V as floats, then the weights
+  float* PT = VF + 32 * vfs<D>();
   // a tile whose every (query, key) pair is visible needs no masks
   auto full_tile = [&](int kt) { return kt * BN + BN <= T && q0 + BN <= T && (!a.causal || kt < qt); };
   auto stored_at = [&](int key) {  // where the lane that stored (qi, key) keeps it
@@ -385,6 +413,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // the error bound in interval widths, with room for the float arithmetic of decide_fast and the
   // rounding of t itself
   const float du = 1.01f * Erow * rc.inv_hf + 0x1p-20f + (float)(K + 1) * 0x1p-22f;
+
   const float edge = Erow + a.tau * 0x1p-21f;  // FWM window edge: margin of |(s - M) + tau|
   // MinMax: one table row per query row; FWM: one table for all rows, from lres levels below
   // the window (resolved grid) to K; bin mean: one row per query row holding the bin means
@@ -481,6 +510,20 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   f16v o[D / 32], ol[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { o[nb] = zero16(); ol[nb] = zero16(); }
+  // DRUN: the running sum in double, in the layout of o
+  double od[DRUN ? D / 32 : 1][DRUN ? 16 : 1];
+  if constexpr (DRUN) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) od[nb][v] = 0.0;
+  }
+  // F64: the double accumulator, element i of block (qh, nb): row 16 qh + l/16 + 4 i, column 16 nb + l%16
+  d4v o64[F64 ? 2 : 1][F64 ? D / 16 : 1];
+  if constexpr (F64) {
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) { o64[0][nb] = zero4d(); o64[1][nb] = zero4d(); }
+  }
   // the next V tile is loaded while this one computes, except under Nearest with Prob-STE,
   // whose second output accumulator takes those registers: there the tile's own V is loaded
   // first, arrives while both half tiles are weighed, and is staged before their products
@@ -499,16 +542,21 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
     if (VPRE) load_scores(kt);
     if (VPRE) {
-      vr.template store_t<NS>(VT);
+      if constexpr (F64) vr.store_f32(VF, vfs<D>());
+      else vr.template store_t<NS>(VT);
       wave_lds_sync();
       if (kt + FWD_NW < ntiles) vr.load(Vp, k0 + FWD_NW * BN, T);  // next V tile in flight
     }
     const bool full = full_tile(kt);
     // each tile's P V (bf16 slice products on the matrix pipe) goes into a fresh accumulator,
     // then into the running sum: the long accumulation chain then holds one add per tile
-    f16v ot[D / 32], otl[D / 32];
+    // (DRUN under Nearest with Prob-STE: O^L's tile product reuses ot once O's has joined o)
+    constexpr int NOTL = MODE == NEAREST_P && !DRUN ? D / 32 : 1;
+    f16v ot[D / 32], otl[NOTL];
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) { ot[nb] = zero16(); otl[nb] = zero16(); }
+    for (int nb = 0; nb < D / 32; ++nb) ot[nb] = zero16();
+#pragma unroll
+    for (int nb = 0; nb < NOTL; ++nb) otl[nb] = zero16();
     // without the prefetch: the weights of both half tiles, kept until V is staged
     float pa[VPRE ? 1 : 2][8], pla[VPRE ? 1 : 2][8];
 #pragma unroll
@@ -516,7 +564,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       // the half tile's V^T operands are read from LDS first, so that their latency overlaps the
       // weighing (not under Nearest with Prob-STE, whose second accumulator takes the registers)
       Split8 vb[D / 32];
-      if (MODE != NEAREST_P) {
+      if (MODE != NEAREST_P && !F64) {
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
         __builtin_amdgcn_sched_barrier(0);
@@ -525,7 +573,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       // the half tile's weight sums: eight positive terms summed in float (error at most 7 u of
       // the half tile's sum, no absorption across the row), joined to the row sums in double once
       // the half tile is settled
-      float tL, tN;
+      std::conditional_t<F64, double, float> tL, tN;  // F64: the exact weights' sums in double
       uint32_t risky = 0;
       uint32_t riske = 0;  // exponential baselines: keys whose weight alone is taken again
       auto weigh = [&](auto masked, auto check) {
@@ -549,9 +597,12 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
             wl = ok ? ew.w : 0.f;
             wn = wl;
           } else {
-            // first pass: float arithmetic, checked against the margin; again: the exact decision
-            const Decision d = decltype(check)::value ? decide_fast<CAL>(s[v], rc, K, a.tau)
-                                                      : decide<CAL>(s[v], rc, K, a.tau);
+            // first pass: float arithmetic, checked against the margin.  Again (a half tile with a key
+            // the margin could not settle): that key's decision in double on its exact score, the
+            // others' as before (so that a key's weight is always the float form on its stored score
+            // unless that score was retaken)
+            const bool exact_d = !decltype(check)::value && ((risky >> j) & 1u);
+            const Decision d = exact_d ? decide<CAL>(s[v], rc, K, a.tau) : decide_fast<CAL>(s[v], rc, K, a.tau);
             if (decltype(check)::value) {
               // a decision within the score's error bound of a boundary must be taken on the exact
               // score (interior boundaries: 1 .. K-1, every integer below K on the resolved grid).
@@ -604,7 +655,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
                 p[jj] = jj == j ? we : p[jj];
                 pl[jj] = jj == j ? we : pl[jj];
               }
-              tL += we - old;
+              tL += (decltype(tL))we - (decltype(tL))old;
             }
             bits &= bits - 1u;
           }
@@ -621,31 +672,77 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         for (int j = 0; j < 8; ++j) { pa[b][j] = p[j]; pla[b][j] = pl[j]; }
         continue;
       }
+      if constexpr (F64) {  // the tile's weights as rows of queries
+#pragma unroll
+        for (int j = 0; j < 8; ++j) PT[c * PTS + crow(8 * b + j, g)] = p[j];
+        continue;
+      }
       const Split8 ps = split8(p);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
+    }
+    if constexpr (F64) {
+      // O += P V in double: A = the weights (query l%16 of the block, key 4 s4 + l/16), B = V
+      wave_lds_sync();
+      const int m16 = l & 15, k4 = l >> 4;
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4) {
+        const int kk = 4 * s4 + k4;
+        const double a0 = PT[m16 * PTS + kk], a1 = PT[(16 + m16) * PTS + kk];
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+          const double bv = VF[kk * vfs<D>() + 16 * nb + m16];
+          o64[0][nb] = mfma_f64(a0, bv, o64[0][nb]);
+          o64[1][nb] = mfma_f64(a1, bv, o64[1][nb]);
+        }
+      }
     }
     if constexpr (!VPRE) {
       if (kt + FWD_NW < ntiles) load_scores(kt + FWD_NW);
       vr.template store_t<NS>(VT);
       wave_lds_sync();
+      if constexpr (DRUN) {
+        // O's product, into o; then O^L's in the same registers, into the double running sum
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        Split8 vb[D / 32];
+        for (int b = 0; b < 2; ++b) {
+          const Split8 ps = split8(pa[b]);
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
-        const Split8 ps = split8(pa[b]);
+          for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+        }
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
-        const Split8 psl = split8(pla[b]);
+        for (int nb = 0; nb < D / 32; ++nb) { o[nb] += ot[nb]; ot[nb] = zero16(); }
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) otl[nb] = mfma_split<NS>(psl, vb[nb], otl[nb]);
+        for (int b = 0; b < 2; ++b) {
+          const Split8 psl = split8(pla[b]);
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(psl, load_bt<D, NS>(VT, b, 32 * nb + c), ot[nb]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          Split8 vb[D / 32];
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) vb[nb] = load_bt<D, NS>(VT, b, 32 * nb + c);
+          const Split8 ps = split8(pa[b]);
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
+          const Split8 psl = split8(pla[b]);
+#pragma unroll
+          for (int nb = 0; nb < NOTL; ++nb) otl[nb] = mfma_split<NS>(psl, vb[nb], otl[nb]);
+        }
       }
     }
+    if constexpr (DRUN) {
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) {
-      o[nb] += ot[nb];
-      if (MODE == NEAREST_P) ol[nb] += otl[nb];
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) od[nb][v] += (double)ot[nb][v];
+    } else if constexpr (!F64) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) {
+        o[nb] += ot[nb];
+        if (MODE == NEAREST_P) ol[nb] += otl[nb % NOTL];
+      }
     }
     wave_lds_sync();  // this tile's V^T reads come before the next tile's staging
   }
@@ -656,6 +753,92 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   if (g == 0) {
     sm.sL[w][c] = sumL;
     sm.sN[w][c] = sumN;
+  }
+
+  // ---- heavy keys.  The faster scores are within Erow of the exact ones, and every decision is
+  // the exact scores' one, but a key that carries much of its row's probability passes a few fp32
+  // ulps of score error into the output and, through D_i = dO_i . O_i, into every score gradient
+  // of the row (the row maximum's calibration term and the outputs with cancelling terms are the
+  // most sensitive).  Once the row sums are known, a row whose largest probability can reach
+  // 1/HEAVY_INV (every weight is at most 1, so W <= HEAVY_INV) recomputes the exact score of each
+  // key that can carry that much (its LERP weight is at most e^{z + h}: z >= ln(W / HEAVY_INV) - h),
+  // patches it into the stored tile for the backward, and records the change of its continuous
+  // weight (w^L, or softmax's e^z) for the output.  Bin mean sums its bins before pass 2 and keeps
+  // its faster scores; the rounded exponentials (BF16-exp, FP8) have taken every weight exactly.
+  constexpr bool HEAVY = MODE != BINM && MODE != EXPBF && MODE != EXPF8;
+  int nh_any = 0;
+  if constexpr (HEAVY) {
+    __syncthreads();
+    double WLr = 0.0, WNr = 0.0;
+#pragma unroll
+    for (int u = 0; u < FWD_NW; ++u) {
+      WLr += sm.sL[u][c];
+      WNr += sm.sN[u][c];
+    }
+    const double Wmin = is_nearest(MODE) ? fmin(WLr, WNr) : WLr;
+    const bool maybe = qvalid && Wmin <= HEAVY_INV;
+    const double hgrid = CAL == EXPB ? 0.0 : 1.0 / rc.inv_h;
+    const float s_thr = maybe ? (float)((double)M + log(Wmin / HEAVY_INV) - hgrid) - Erow : INFINITY;
+    int nh = 0;
+    if (__any(maybe)) {
+      for (int kt = w; kt < ntiles; kt += FWD_NW) {
+        const int k0 = kt * BN;
+        float* Sw = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + crow(v, g);
+          const bool ok = maybe & (key < T) & (!a.causal | (key <= qi));
+          const float x = Sw[v * 64];
+          // the extremum keys' stored scores are exact already
+          bits |= (ok && x >= s_thr && x != M) ? (1u << v) : 0u;
+        }
+        while (__any(bits != 0u)) {
+          const int j = bits ? __builtin_ctz(bits) : 0;
+          if (bits) {
+            bits &= bits - 1u;
+            const float old = Sw[j * 64];
+            const int key = k0 + crow(j, g);
+            // the key's probability under either normalizer, from its faster score (a margin of
+            // 1e-3 for that score's error)
+            bool heavy;
+            if constexpr (CAL == EXPB) {
+              heavy = (double)__expf(old - M) * (HEAVY_INV * (1.0 + 1e-3)) >= WLr;
+            } else {
+              constexpr int ST = CAL == MINMAX ? BN : 1;
+              const Weights w0 = weights_cal<CAL, ST>(decide<CAL>(old, rc, K, a.tau), trow, a.lres, a.res_far != 0,
+                                                       K, a.tau);
+              heavy = (double)w0.wL * (HEAVY_INV * (1.0 + 1e-3)) >= WLr ||
+                      (is_nearest(MODE) && (double)w0.wN * (HEAVY_INV * (1.0 + 1e-3)) >= WNr);
+            }
+            // (a lean form: the output accumulators are live here)
+            const float xe = heavy && nh < HMAX ? exact_score<D, TIn, 2>(qrow, Kp + (size_t)key * D, a.scale) : old;
+            if (xe != old) {
+              // the change of the continuous weight, computed as pass 2 computed the old one (the
+              // decision itself is the same: pass 2 settled it against the bound)
+              float dw = 0.f;
+              if constexpr (MODE == EXP32) {
+                dw = __expf(xe - M) - __expf(old - M);
+              } else if constexpr (MODE == LERP || MODE == NEAREST_P) {
+                // pass 2 weighed the key with the float decision on its stored score
+                constexpr int ST = CAL == MINMAX ? BN : 1;
+                const Decision d0 = decide_fast<CAL>(old, rc, K, a.tau), d1 = decide<CAL>(xe, rc, K, a.tau);
+                const bool keep = CAL == FWM_FLOOR || !d0.tail;
+                dw = keep ? weights_cal<CAL, ST>(d1, trow, a.lres, a.res_far != 0, K, a.tau).wL -
+                                weights_cal<CAL, ST>(d0, trow, a.lres, a.res_far != 0, K, a.tau).wL
+                          : 0.f;
+              }
+              Sw[j * 64] = xe;  // stored by this lane in pass 1
+              sm.hk[w][l][nh] = key;
+              sm.hd[w][l][nh] = dw;
+              ++nh;
+            }
+          }
+        }
+      }
+    }
+    sm.hn[w][l] = nh;
+    nh_any = nh;
   }
   float* part = reinterpret_cast<float*>(sm.wave[w]);  // this wave's V^T is no longer read
   auto gather = [&](f16v (&acc)[D / 32]) {
@@ -678,8 +861,57 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
     }
   };
-  gather(o);
-  if (MODE == NEAREST_P) gather(ol);
+  // whether any lane of the workgroup retook a heavy key (a barrier, which also orders the slots)
+  const bool anyheavy = HEAVY && __syncthreads_or(nh_any);
+  if constexpr (F64) {
+    double* pd = reinterpret_cast<double*>(sm.wave[w]);
+    __syncthreads();
+    if (w > 0) {
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pd[((qh * (D / 16) + nb) * 4 + i) * 64 + l] = o64[qh][nb][i];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int u = 1; u < FWD_NW; ++u) {
+        const double* op = reinterpret_cast<const double*>(sm.wave[u]);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o64[qh][nb][i] += op[((qh * (D / 16) + nb) * 4 + i) * 64 + l];
+      }
+    }
+  } else if constexpr (DRUN) {
+    double* pd = reinterpret_cast<double*>(sm.wave[w]);
+    __syncthreads();
+    if (w > 0) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pd[(nb * 16 + v) * 64 + l] = od[nb][v];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int u = 1; u < FWD_NW; ++u) {
+        const double* op = reinterpret_cast<const double*>(sm.wave[u]);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) od[nb][v] += op[(nb * 16 + v) * 64 + l];
+      }
+    }
+    if (MODE == NEAREST_P) gather(o);
+  } else {
+    gather(o);
+    if (MODE == NEAREST_P) gather(ol);
+  }
   if (w != 0) return;
   sumL = sm.sL[0][c];
   sumN = sm.sN[0][c];
@@ -688,17 +920,69 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     sumL += sm.sL[u][c];
     sumN += sm.sN[u][c];
   }
+  if (HEAVY && (MODE == LERP || MODE == EXP32 || MODE == NEAREST_P) && anyheavy) {
+    // the heavy keys' weight changes, in a fixed order (waves, lanes, slots): into the continuous
+    // row sum (W^L, softmax's W) and into the output rows (O, or O^L under Nearest with Prob-STE).
+    // Lane (c, g) holds output row crow(v, g) of the tile at columns 32 nb + c.
+    f16v(&acc)[D / 32] = MODE == NEAREST_P ? ol : o;  // DRUN: od
+    for (int u = 0; u < FWD_NW; ++u)
+      for (int hl = 0; hl < 64; ++hl) {
+        const int n = sm.hn[u][hl];
+        const int r = hl & 31, gr = (r >> 2) & 1, vr_ = 4 * (r >> 3) + (r & 3);  // crow(vr_, gr) == r
+        for (int x = 0; x < n; ++x) {
+          const int key = sm.hk[u][hl][x];
+          const float dw = sm.hd[u][hl][x];
+          if (c == r) sumL += (double)dw;
+          float vv[D / 32];
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) vv[nb] = Ld<TIn>::one(Vp + (size_t)key * D + 32 * nb + c);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (v == vr_ && g == gr) {
+#pragma unroll
+              for (int nb = 0; nb < D / 32; ++nb) {
+                if (DRUN) od[nb][v] = fma((double)dw, (double)vv[nb], od[nb][v]);
+                else acc[nb][v] = fmaf(dw, vv[nb], acc[nb][v]);
+              }
+            }
+        }
+      }
+  }
   const float WLf = (float)sumL, WNf = is_nearest(MODE) ? (float)sumN : WLf;
   if (g == 0) {
     sm.rowW[c] = is_nearest(MODE) ? WNf : WLf;
     sm.rowWL[c] = WLf;
+    sm.rowWd[c] = is_nearest(MODE) ? sumN : sumL;
+    sm.rowWLd[c] = sumL;
     if (qvalid) {
       const size_t row = (size_t)head * T + qi;
-      a.rec.WN[row] = WNf;
+      // F64: W^N holds the residual of W, so that W^L + W^N is the double sum
+      a.rec.WN[row] = F64 ? (float)(sumL - (double)WLf) : WNf;
       a.rec.WL[row] = WLf;
     }
   }
   wave_lds_sync();
+  if constexpr (F64) {
+    // O = num / W in double, stored as its float and the residual (in the O^L slot of the record)
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * qh + (l >> 4) + 4 * i, qrow = q0 + r;
+        if (qrow < T) {
+          const double Wd = sm.rowWd[r];
+          const size_t at = hb + (size_t)qrow * D + (l & 15);
+#pragma unroll
+          for (int nb = 0; nb < D / 16; ++nb) {
+            const double ov = o64[qh][nb][i] / Wd;
+            const float hi = (float)ov;
+            a.o[at + 16 * nb] = hi;
+            a.rec.OL[at + 16 * nb] = (float)(ov - (double)hi);
+          }
+        }
+      }
+    return;
+  }
   // O = num / W; lane l holds rows crow(v, g) of the tile and columns 32 nb + c
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -706,13 +990,26 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     if (qrow < T) {
       const float inv = 1.0f / sm.rowW[crow(v, g)];
       float* orow = a.o + hb + (size_t)qrow * D + c;
+      if (DRUN && MODE != NEAREST_P) {
+        // the double sum over the double row sum, rounded once
+        const double Wd = sm.rowWd[crow(v, g)];
 #pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) orow[32 * nb] = o[nb][v] * inv;
+        for (int nb = 0; nb < D / 32; ++nb) orow[32 * nb] = (float)(od[nb][v] / Wd);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) orow[32 * nb] = o[nb][v] * inv;
+      }
       if (MODE == NEAREST_P) {
         const float invl = 1.0f / sm.rowWL[crow(v, g)];
         float* olrow = a.rec.OL + hb + (size_t)qrow * D + c;
+        if (DRUN) {
+          const double Wd = sm.rowWLd[crow(v, g)];
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) olrow[32 * nb] = ol[nb][v] * invl;
+          for (int nb = 0; nb < D / 32; ++nb) olrow[32 * nb] = (float)(od[nb][v] / Wd);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) olrow[32 * nb] = ol[nb][v] * invl;
+        }
       }
     }
   }
@@ -720,10 +1017,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 
 template <int D, int CAL, int MODE, typename TIn>
 size_t fwd_smem_bytes(int K, int lres) {
-  return sizeof(FwdSmem<D, nslices<TIn>()>) +
+  return sizeof(FwdSmem<D, nslices<TIn>(), MODE == EXPBF>) +
          sizeof(float) * (CAL == MINMAX || MODE == BINM ? BN * (K + 1) : (CAL == EXPB ? 0 : lres + K + 1));
 }
-static_assert(sizeof(float) * 2 * BINM_MAXB * BN * FWD_NW <= FWD_NW * fwd_wave_bytes<64, 1>(),
+static_assert(sizeof(float) * 2 * BINM_MAXB * BN * FWD_NW <= FWD_NW * fwd_wave_bytes<64, 1, false>(),
               "bin-mean partial sums fit the V^T staging area");
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.

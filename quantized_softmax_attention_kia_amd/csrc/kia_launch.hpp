@@ -54,7 +54,7 @@ struct RowRec {
   int32_t* nC;
   float* WN;
   float* WL;
-  float* OL;  // [N, D], Nearest + Prob-STE only (else nullptr)
+  float* OL;  // [N, D]: Nearest + Prob-STE O^L, BF16-exp O's residual (else nullptr)
   float* S;   // stored score tiles: per head, tiles_per_head tiles of 1024 floats
   int nt;     // number of 32-row tiles along T
   size_t tiles_per_head;

@@ -103,7 +103,8 @@ def _exp_near(s, g, res, cfg, guard=1e-4):
 
 
 def cfg_of(calib, recon, ste, grad, tail="zero", K=4, tau=8.0, mutation=None):
-    return ORC.OracleConfig(calib, recon, ste, grad, K, tau, mutation, tail)
+    # the pins check the method in exact arithmetic: double scores, not rounded to fp32
+    return ORC.OracleConfig(calib, recon, ste, grad, K, tau, mutation, tail, score_fp32=False)
 
 
 def _resolved(cfg):

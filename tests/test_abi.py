@@ -58,6 +58,8 @@ def test_workspace_layout(kb):
     assert st == 0 and rr == 8 * rnd(N * 4) + tiles and w == 2 * tiles + rnd(N * 4) + tab
     st, rr, w = ws(kb, params(kb, recon=1, ste=1))   # Nearest + Prob-STE keeps O^L
     assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
+    st, rr, w = ws(kb, params(kb, recon=3))   # BF16-exp keeps the residual of its double output
+    assert st == 0 and rr == 8 * rnd(N * 4) + rnd(N * 64 * 4) + tiles
     st, rr, w = ws(kb, params(kb, causal=0))
     assert st == 0 and rr == 8 * rnd(N * 4) + 2 * 3 * nt * nt * 4096
     assert w == 2 * 2 * 3 * nt * nt * 4096 + rnd(N * 4) + tab
@@ -105,3 +107,29 @@ def test_empty_problem_is_ok_without_buffers(kb):
         assert kb._lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) == 0
         assert kb._lib.kia_backward(ctypes.byref(p), *([None] * 11)) == 0
     assert kb._lib.kia_forward(None, None, None, None, None, None, None) == -1
+
+
+def test_binding_rejects_mismatched_buffers(kb):
+    """The binding refuses, before any GPU work, inputs whose dtype differs from the params' (the
+    kernels would read a bf16 buffer as float, past its end), outputs that are not float32, and a
+    record or workspace smaller than kia_workspace_size asks for."""
+    import torch
+    cfg = kb.Config()
+    p = kb.make_params(cfg, (1, 2, 40, 64), torch.float32)
+    f32 = torch.zeros((1, 2, 40, 64), dtype=torch.float32)
+    b16 = torch.zeros((1, 2, 40, 64), dtype=torch.bfloat16)
+    rr, wsb = kb.kia_workspace_size(p)
+    rec = torch.zeros(rr, dtype=torch.uint8)
+    work = torch.zeros(wsb, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="inputs"):
+        kb.kia_forward(p, f32, b16, b16, f32, rec)
+    with pytest.raises(ValueError, match="float32"):
+        kb.kia_forward(p, f32, f32, f32, b16, rec)
+    with pytest.raises(ValueError, match="rowrec"):
+        kb.kia_forward(p, f32, f32, f32, f32, rec[: rr - 1])
+    with pytest.raises(ValueError, match="workspace"):
+        kb.kia_backward(p, f32, f32, f32, f32, f32, rec, f32, f32, f32, work[: wsb - 256])
+    with pytest.raises(ValueError, match="inputs"):
+        kb.kia_backward(p, f32, f32, f32, f32, b16, rec, f32, f32, f32, work)
+    with pytest.raises(ValueError, match="GPU"):      # every size right: only the device is wrong here
+        kb.kia_forward(p, f32, f32, f32, f32, rec)

@@ -2,11 +2,9 @@
 
 The harness must accept a result that differs from the oracle only by the other valid
 decision at a flagged position (an interval or Nearest boundary, the FWM window edge, a
-near tie of a row extremum, a bfloat16 rounding), and reject results with a planted
-arithmetic mistake or a flipped decision at a position the oracle did not flag.  The flag
-list itself is pinned against a direct computation: every decision that rounding the
-scores to fp32 changes is flagged, and nothing is flagged farther from its boundary than
-the fp32 bound (or the guard) allows."""
+bfloat16 rounding, an fp32 score at a rounding midpoint), and reject results with a planted
+arithmetic mistake, a tie the fp32 scores do not have, or a flipped decision at a position
+the oracle did not flag.  The scores themselves are pinned by exact rational arithmetic."""
 import numpy as np
 import pytest
 
@@ -59,36 +57,30 @@ def test_rejects_planted_error(mutation):
 
 
 @pytest.mark.parametrize("calib", ["minmax", "fwm"])
-def test_near_tie_is_a_flip_not_an_exclusion(calib):
-    """A key within the fp32 bound of the row maximum may tie it in fp32: the harness accepts
-    the split extremum gradient through a flip, with every element compared; a key farther away
-    than the bound is not flagged, and a split there is rejected."""
+def test_ties_are_ties_of_fp32_scores(calib):
+    """A key whose score rounds to the same fp32 value as the row maximum ties it (the extremum
+    gradient is split between them); one an fp32 ulp below does not, and a result that splits the
+    gradient there is rejected.  Every element is compared."""
     cfg, q, k, v, do = _setup(calib, "lerp", T=120, K=4, qs=2.0)
     i = 100
-    s = (q[i].astype(np.float64) @ k[: i + 1].astype(np.float64).T) / 8.0
-    j0 = int(np.argmax(s))
-    j1 = int(np.argsort(s)[-2])
-    # move key j1 so that its exact score is one part in 1e8 below the row maximum: inside the
-    # fp32 bound (2 ulps), hence a legitimate fp32 tie
-    kk = k.astype(np.float64).copy()
-    kk[j1] = kk[j0] * (1.0 - 1e-8)
-    ref = ORC.head(cfg, q, kk, v, do, guard=parity.GUARD, flag_cap=100000)
-    flags, _ = parity.relevant_flags(ref, cfg)
-    tie = [tuple(int(x) for x in f) for f in flags if f[0] == i and f[1] == j1 and f[2] == ORC.FLIP_TIE_MAX]
-    assert tie, "near tie not flagged"
-    alt = ORC.head(cfg, q, kk, v, do, flips=np.array(tie))
-    got = _outputs(alt)
-    assert any(parity.bad_mask(got[key], ref[key]).any() for key in ("dQ", "dK")), "tie flip changes nothing"
-    rep = parity.check_head(cfg, q, kk, v, do, got)
-    assert rep["flips"] == tie and rep["elements"] == 4 * q.size
-    # 1e-5 below the maximum: far outside the fp32 bound, so no flag and the split is rejected
-    kk[j1] = kk[j0] * (1.0 - 1e-5)
-    ref = ORC.head(cfg, q, kk, v, do, guard=parity.GUARD, flag_cap=100000)
-    flags, _ = parity.relevant_flags(ref, cfg)
-    assert not any(f[0] == i and f[1] == j1 and f[2] == ORC.FLIP_TIE_MAX for f in flags)
-    alt = ORC.head(cfg, q, kk, v, do, flips=np.array([(i, j1, ORC.FLIP_TIE_MAX)]))
+    sc = ORC.head(cfg, q, k, v, do, scores=True)["scores"][i, : i + 1]
+    j0 = int(np.argmax(sc))
+    j1 = int(np.argsort(sc)[-2])
+    tie = k.astype(np.float64).copy()
+    tie[j1] = tie[j0]                         # the same fp32 score: a tie
+    assert ORC.head(cfg, q, tie, v, do)["rowi"]["nA"][i] == 2
+    near = tie.copy()
+    near[j1] = tie[j0] * (1.0 - 2.0 ** -20)   # a few fp32 ulps below: no tie
+    ref = ORC.head(cfg, q, near, v, do, guard=parity.GUARD, flag_cap=100000, scores=True)
+    assert ref["rowi"]["nA"][i] == 1 and ref["scores"][i, j1] < ref["scores"][i, j0]
+    # a result whose row i splits the maximum's term between j0 and j1 as a tie would (row i's
+    # contributions computed with the tie, every other row as the reference has it)
+    tied_i = ORC.head(cfg, q, tie, v, do, rows=[i])
+    ref_i = ORC.head(cfg, q, near, v, do, rows=[i])
+    got = {key: ref[key] + (tied_i[key] - ref_i[key]) for key in parity.KEYS}
+    assert parity.bad_mask(got["dK"], ref["dK"]).any(), "the split changes nothing"
     with pytest.raises(AssertionError):
-        parity.check_head(cfg, q, kk, v, do, _outputs(alt))
+        parity.check_head(cfg, q, near, v, do, got)
 
 
 def test_bf16_gradient_rounding_at_unflagged_position_is_rejected():
@@ -119,61 +111,48 @@ def test_bf16_gradient_rounding_at_unflagged_position_is_rejected():
     assert rejected >= 1, "no single-ulp gradient rounding was large enough to test"
 
 
-def _row_decisions(cfg, s):
-    r = ORC.row(cfg, s)
-    return r["r"], r["ell"], r["tail"], r["amax"], r["nA"], r["amin"], r["nC"]
+def _exact_f32(x):
+    """The fp32 value nearest the rational x, ties to even (no double rounding)."""
+    from fractions import Fraction
+    d = float(x)                              # correctly rounded double
+    f = np.float32(d)
+    lo = f if Fraction(float(f)) <= x else np.nextafter(f, np.float32(-np.inf))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (Fraction(float(lo)) + Fraction(float(hi))) / 2
+    if x < mid:
+        return float(lo)
+    if x > mid:
+        return float(hi)
+    return float(lo) if (lo.view(np.uint32) & 1) == 0 else float(hi)
 
 
-@pytest.mark.parametrize("calib,recon,K", [("minmax", "nearest", 4), ("minmax", "lerp", 16), ("fwm", "nearest", 8),
-                                           ("fwm", "lerp", 32)])
-def test_fp32_guard_covers_and_is_tight(calib, recon, K):
-    """The flag list against a direct computation.  Each row's scores are rounded to fp32 and the
-    decisions retaken on them: every decision that changes (interval, Nearest index, window edge,
-    extremum tie) is flagged.  With the guard at 0 every flagged position lies within the fp32
-    bound of its boundary, recomputed here from its definition: one fp32 ulp of the score and of
-    the extrema u is measured from, over the interval width."""
-    cfg = ORC.OracleConfig(calib, recon, "prob", "full", K, 3.0)
-    # coarse inputs put many scores near boundaries: integers -2..2 times (1 + 3e-7 N(0,1))
-    rng = np.random.default_rng(11)
-    T, D = 160, 64
-    q = rng.integers(-2, 3, (T, D)) * (1.0 + 3e-7 * rng.standard_normal((T, D)))
-    k = rng.integers(-2, 3, (T, D)) * (1.0 + 3e-7 * rng.standard_normal((T, D)))
+def test_scores_are_correctly_rounded_fp32():
+    """The scores the oracle runs on are the exact product sums, scaled and rounded once to fp32
+    (checked with exact rational arithmetic), except where the oracle flags that its double sum
+    lies within its own rounding bound of an fp32 midpoint; a value exactly at a midpoint is
+    flagged, and the flip takes the other fp32 neighbour."""
+    from fractions import Fraction
+    rng = np.random.default_rng(2)
+    T, D = 24, 16
+    q = rng.standard_normal((T, D)).astype(np.float32).astype(np.float64)
+    k = rng.standard_normal((T, D)).astype(np.float32).astype(np.float64)
     v = rng.standard_normal((T, D))
-    ref = ORC.head(cfg, q, k, v, None, guard=0.0, flag_cap=1 << 20)
-    flags = ref["flags"]
-    fl = {(int(a), int(b), int(c)) for a, b, c in flags}
-    flagged_pos = {(a, b) for a, b, _ in fl}
-    changed = 0
-    scale = 1.0 / np.sqrt(D)
-    ulp = 2.0 ** -23
-    for i in range(1, T):
-        s = scale * (q[i] @ k[: i + 1].T)
-        s32 = s.astype(np.float32).astype(np.float64)
-        a = _row_decisions(cfg, s)
-        b = _row_decisions(cfg, s32)
-        ell_differs = (a[1] != b[1]) if recon == "nearest" else np.zeros_like(a[1], dtype=bool)
-        for j in np.flatnonzero((a[0] != b[0]) | ell_differs | (a[2] != b[2])):
-            changed += 1
-            assert (i, int(j)) in flagged_pos, f"decision ({i}, {j}) changed by fp32 scores but not flagged"
-        if b[4] > a[4]:   # an fp32 tie of the maximum the exact scores do not have
-            for j in np.flatnonzero(s32 == s32.max()):
-                if j != a[3]:
-                    changed += 1
-                    assert (i, int(j), ORC.FLIP_TIE_MAX) in fl, f"fp32 tie ({i}, {j}) not flagged"
-        # tightness: every flag of this row within the fp32 bound of its boundary
-        M, m = s.max(), s.min()
-        h = (M - m) / K if calib == "minmax" else cfg.tau / K
-        for (ii, j, kind), dist in zip(map(tuple, flags), ref["flag_dist"]):
-            if ii != i:
-                continue
-            ebj = ulp * abs(s[j]) + 1e-15 * scale * np.abs(q[i] * k[j]).sum()
-            ebM = ulp * abs(M) + 1e-15 * scale * np.abs(q[i] * k[int(np.argmax(s))]).sum()
-            ebm = ulp * abs(m) + 1e-15 * scale * np.abs(q[i] * k[int(np.argmin(s))]).sum()
-            if kind in (ORC.FLIP_TIE_MAX, ORC.FLIP_TIE_MIN):
-                assert dist <= ebj + (ebM if kind == ORC.FLIP_TIE_MAX else ebm) + 1e-300
-            else:
-                bound = (ebj + 2 * ebm + ebM) / h if calib == "minmax" else (ebj + ebM) / h
-                assert dist < bound * (1 + 1e-9), f"flag ({i}, {j}) at {dist} beyond the fp32 bound {bound}"
-    assert changed > 0, "the inputs produced no decision that fp32 scores change"
-    # the flagged set is a small part of the pairs, so flips cannot explain arbitrary errors
-    assert len(flagged_pos) < 0.05 * T * (T + 1) / 2
+    scale = 0.3                               # not a power of two: the scaling rounds too
+    cfg = ORC.OracleConfig("minmax", "lerp", "prob", "full", 4, 8.0)
+    ref = ORC.head(cfg, q, k, v, None, scale=scale, guard=0.0, flag_cap=1000, scores=True)
+    flagged = {(int(a), int(b)) for a, b, kind in ref["flags"] if kind == ORC.FLIP_SCORE}
+    fs = Fraction(scale)
+    for i in range(T):
+        for j in range(i + 1):
+            exact = fs * sum(Fraction(q[i, d]) * Fraction(k[j, d]) for d in range(D))
+            if (i, j) not in flagged:
+                assert ref["scores"][i, j] == _exact_f32(exact), (i, j)
+    # an exact midpoint between 1 and 1 + 2^-23: 1 + 2^-24, rounded to even (1.0), is flagged
+    q2 = np.zeros((2, 4)); k2 = np.zeros((2, 4))
+    q2[1, :2] = [1.0, 2.0 ** -12]; k2[1, :2] = [1.0, 2.0 ** -12]; k2[0, 0] = 0.5
+    r = ORC.head(cfg, q2, k2, np.ones((2, 4)), None, scale=1.0, guard=0.0, flag_cap=10, scores=True)
+    assert r["scores"][1, 1] == 1.0
+    assert (1, 1, ORC.FLIP_SCORE) in {tuple(int(x) for x in f) for f in r["flags"]}
+    r2 = ORC.head(cfg, q2, k2, np.ones((2, 4)), None, scale=1.0, flips=np.array([(1, 1, ORC.FLIP_SCORE)]),
+                  scores=True)
+    assert r2["scores"][1, 1] == 1.0 + 2.0 ** -23
