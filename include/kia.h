@@ -203,6 +203,26 @@ kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void*
                                void* workspace, void* stream);
 
 /*
+ * kia_backward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing: its workspace is a built-in
+ * device array of KIA_NOALLOC_WS_BYTES per GPU, which each GPU the library runs
+ * on holds until the process ends.
+ *  Arguments as for kia_backward, without `workspace`.
+ *  Returns KIA_ERR_WORKSPACE, launching nothing, when these params need more
+ *  workspace (bwd_ws_bytes of kia_workspace_size) than the built-in array holds:
+ *  call kia_backward with a workspace of your own instead.
+ * Every call on one GPU uses that GPU's one array, which keeps what the last call
+ * left there (nothing in it needs to start cleared: every element a call reads,
+ * it wrote first).  Calls that overlap on one GPU (on different streams, or from
+ * different host threads without ordering) race on it: serialize them.
+ */
+#define KIA_NOALLOC_WS_BYTES ((size_t)64 << 20)
+kia_status_t kia_backward_noalloc(const kia_params_t* p, const void* q, const void* k, const void* v,
+                                  const float* o, const void* d_o, const void* rowrec,
+                                  float* dq, float* dk, float* dv, void* stream);
+
+/*
  * Test hook: the reconstruction decision of every (query, key) pair as the
  * kernels take it, for bit-exact comparison of bin decisions.
  *  rowrec: the record written by kia_forward with the same params (its stored

@@ -43,7 +43,8 @@ class Params(ctypes.Structure):
 
 
 EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
-           "kia_debug_bins", "kia_status_string", "kia_last_error")
+           "kia_backward_noalloc", "kia_debug_bins", "kia_status_string", "kia_last_error")
+NOALLOC_WS_BYTES = 64 << 20  # KIA_NOALLOC_WS_BYTES
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -57,9 +58,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kia_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kia_backward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_debug_bins.argtypes = [P, vp, vp, vp]
     for f in ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
-              "kia_debug_bins"):
+              "kia_backward_noalloc", "kia_debug_bins"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kia_status_string.argtypes = [ctypes.c_int]
     lib.kia_status_string.restype = ctypes.c_char_p
@@ -171,6 +173,14 @@ def kia_backward_dkdv(p: Params, q, k, v, d_o, rowrec, dk, dv, workspace, stream
     _check_inputs(p, q, k, v, d_o, outputs=(dk, dv), rowrec=rowrec, workspace=workspace)
     _check(_lib.kia_backward_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(rowrec),
                                   _ptr(dk), _ptr(dv), _ptr(workspace), _stream(stream)))
+
+
+def kia_backward_noalloc(p: Params, q, k, v, o, d_o, rowrec, dq, dk, dv, stream=None) -> None:
+    """kia_backward on the library's built-in workspace (no allocation; params whose workspace
+    exceeds NOALLOC_WS_BYTES raise KIA_ERR_WORKSPACE)."""
+    _check_inputs(p, q, k, v, d_o, outputs=(o, dq, dk, dv), rowrec=rowrec)
+    _check(_lib.kia_backward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowrec),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def kia_debug_bins(p: Params, rowrec, bins, stream=None) -> None:

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -170,6 +171,45 @@ bool empty(const kia::Problem& pr) { return pr.nheads == 0 || pr.T == 0; }
 
 }  // namespace
 
+// The built-in workspace of kia_backward_noalloc.  Each GPU holds its own copy of this array
+// (at its own address) from the library's load until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels are given the device address that
+// hipGetSymbolAddress returns for the current device, taken once per device and kept below.
+static __device__ __align__(256) unsigned char scratch[KIA_NOALLOC_WS_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[SCRATCH_MAX_DEVICES];
+
+// The device address of the current device's copy of `scratch` (looked up on its first use).
+kia_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "kia_backward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) {
+    set_err("kia_backward_noalloc: device %d is beyond the %d this library keeps an address for", dev,
+            SCRATCH_MAX_DEVICES);
+    return KIA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "kia_backward_noalloc: hipGetSymbolAddress");
+    if (!ptr) {
+      set_err("kia_backward_noalloc: hipGetSymbolAddress gave a null address");
+      return KIA_ERR_HIP;
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return KIA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, size_t* bwd_ws_bytes) {
@@ -244,6 +284,25 @@ kia_status_t kia_backward_dkdv(const kia_params_t* p, const void* q, const void*
                                void* workspace, void* stream) {
   return backward_stages(p, q, k, v, nullptr, d_o, rowrec, nullptr, dk, dv, workspace, stream, 2,
                          "kia_backward_dkdv");
+}
+
+kia_status_t kia_backward_noalloc(const kia_params_t* p, const void* q, const void* k, const void* v,
+                                  const float* o, const void* d_o, const void* rowrec, float* dq, float* dk,
+                                  float* dv, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = check_params(p, &pr);
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  const Layout L = layout(pr);
+  if (L.ws_bytes > KIA_NOALLOC_WS_BYTES) {
+    set_err("kia_backward_noalloc: these params need %zu bytes of workspace, above the built-in %zu "
+            "(call kia_backward with a workspace)", L.ws_bytes, (size_t)KIA_NOALLOC_WS_BYTES);
+    return KIA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != KIA_OK) return st;
+  return backward_stages(p, q, k, v, o, d_o, rowrec, dq, dk, dv, ws, stream, 3, "kia_backward_noalloc");
 }
 
 kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream) {
