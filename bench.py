@@ -33,7 +33,7 @@ METRIC = "K-interval attn fwd+bwd TFLOP/s & % MFMA peak, B=8 H=12 T=1024 d=64 ca
 FP32_MFMA_PEAK = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 BF16_MFMA_PEAK = 2500.0
 # algorithmic flops per causal pair, in units of D, per kernel
-ALG_PER_PAIR = {"fwd": 4, "dq": 2, "dkdv": 6}
+ALG_PER_PAIR = {"fwd": 4, "dq": 4, "dkdv": 4}
 KERNEL_SOURCES = ["kia_device.hpp", "kia_launch.hpp", "kia_fwd.hip", "kia_bwd.hip", "kia_api.hip"]
 
 

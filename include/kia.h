@@ -239,8 +239,9 @@ kia_status_t kia_backward_noalloc(const kia_params_t* p, const void* q, const vo
  */
 kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream);
 
-/* Static string naming a status code. */
-const char* kia_status_string(kia_status_t status);
+/* Static string naming a status code: a kia_status_t value, or any other int
+ * ("KIA_ERR_UNKNOWN"). */
+const char* kia_status_string(int status);
 
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* kia_last_error(void);

@@ -318,7 +318,7 @@ kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* 
   return hip_status(kia::launch_bins(pr, a, static_cast<hipStream_t>(stream)), "kia_debug_bins launch");
 }
 
-const char* kia_status_string(kia_status_t s) {
+const char* kia_status_string(int s) {
   switch (s) {
     case KIA_OK: return "KIA_OK";
     case KIA_ERR_INVALID_ARG: return "KIA_ERR_INVALID_ARG";
