@@ -33,8 +33,8 @@ METRIC = "K-interval attn fwd+bwd TFLOP/s & % MFMA peak, B=8 H=12 T=1024 d=64 ca
 FP32_MFMA_PEAK = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 BF16_MFMA_PEAK = 2500.0
 # algorithmic flops per causal pair, in units of D, per kernel
-ALG_PER_PAIR = {"fwd": 4, "dq": 4, "dkdv": 4}
-KERNEL_SOURCES = ["kia_device.hpp", "kia_launch.hpp", "kia_fwd.hip", "kia_bwd.hip", "kia_api.hip"]
+ALG_PER_PAIR = {"fwd": 4, "dq": 4, "dkdv": 4, "bwd": 8}
+KERNEL_SOURCES = ["kia_device.hpp", "kia_launch.hpp", "kia_fwd.hip", "kia_bwd.hip", "kia_api.hip", "kia_flash.hip"]
 
 
 def log(*a):
@@ -107,8 +107,9 @@ def main() -> int:
                     help="time bin mean and the Nearest-forward / bin-mean-backward hybrid (MinMax and FWM, "
                          "K = 4) on the same workload instead of the K-interval variants")
     ap.add_argument("--baselines", action="store_true",
-                    help="time the exponential baselines (softmax, BF16-exp, FP8-rounded exp) on the same "
-                         "workload instead of the K-interval variants")
+                    help="time the one-pass (online-rescale) exact softmax beside the K-interval variants and "
+                         "the exponential baselines (softmax, BF16-exp, FP8-rounded exp) on the two-pass "
+                         "pipeline, on the same workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
                          "byte counters)")
@@ -128,7 +129,8 @@ def main() -> int:
     variants = [dataclasses.replace(v, tail=args.tail) if v.calib == "fwm" else v for v in wl.variants]
     if args.baselines:
         from quantized_softmax_attention_kia_amd.inputs import Variant
-        variants = [Variant("fwm", r, "prob", "full", 4) for r in ("softmax", "exp_bf16", "exp_fp8")]
+        variants = variants + [Variant("fwm", r, "prob", "full", 4) for r in ("softmax", "exp_bf16", "exp_fp8")]
+        variants.append("flash-softmax")
     if args.binmean:
         from quantized_softmax_attention_kia_amd.inputs import Variant
         variants = [Variant(c, r, "prob", "full", 4) for c in ("minmax", "fwm") for r in ("binmean", "nearest_binmean")]
@@ -142,13 +144,24 @@ def main() -> int:
 
     runs = []
     for var in variants:
+        if var == "flash-softmax":
+            cfg = kb.Config("fwm", "softmax", "prob", "full", 4)
+            p = kb.make_params(cfg, qt.shape, tdt)
+            runs.append(dict(
+                name="flash-softmax", kind="flash", p=p,
+                o=torch.empty(qt.shape, device=dev, dtype=torch.float32),
+                rowstats=torch.empty(3 * wl.B * wl.H * wl.T, device=dev, dtype=torch.float32),
+                dq=torch.empty(qt.shape, device=dev, dtype=torch.float32),
+                dk=torch.empty(qt.shape, device=dev, dtype=torch.float32),
+                dv=torch.empty(qt.shape, device=dev, dtype=torch.float32)))
+            continue
         cfg = kb.Config.of(var)
         if args.grad != cfg.grad:
             cfg = dataclasses.replace(cfg, grad=args.grad)
         p = kb.make_params(cfg, qt.shape, tdt)
         rr, ws = kb.kia_workspace_size(p)
         runs.append(dict(
-            name=var.name if args.grad == "full" else f"{var.name}:{args.grad}", p=p,
+            name=var.name if args.grad == "full" else f"{var.name}:{args.grad}", kind="kia", p=p,
             o=torch.empty(qt.shape, device=dev, dtype=torch.float32),
             rowrec=torch.empty(max(rr, 1), device=dev, dtype=torch.uint8),
             dq=torch.empty(qt.shape, device=dev, dtype=torch.float32),
@@ -158,6 +171,17 @@ def main() -> int:
 
     def one_step(events=None):
         for i, r in enumerate(runs):
+            if r["kind"] == "flash":
+                if events is not None:
+                    events[i][0].record(stream)
+                kb.kia_flash_forward(r["p"], qt, kt, vt, r["o"], r["rowstats"], stream)
+                if events is not None:
+                    events[i][1].record(stream)
+                kb.kia_flash_backward(r["p"], qt, kt, vt, r["o"], dot, r["rowstats"], r["dq"], r["dk"], r["dv"], stream)
+                if events is not None:
+                    events[i][2].record(stream)
+                    events[i][3].record(stream)
+                continue
             if events is not None:
                 events[i][0].record(stream)
             kb.kia_forward(r["p"], qt, kt, vt, r["o"], r["rowrec"], stream)
@@ -203,17 +227,31 @@ def main() -> int:
     # per-kernel average launch durations from the events
     per = {}
     for i, r in enumerate(runs):
-        durs = {"fwd": [], "dq": [], "dkdv": []}
+        stages = ("fwd", "bwd") if r["kind"] == "flash" else ("fwd", "dq", "dkdv")
+        durs = {st: [] for st in stages}
         for s in range(args.steps):
             e = ev[s][i]
             durs["fwd"].append(e[0].elapsed_time(e[1]))
-            durs["dq"].append(e[1].elapsed_time(e[2]))
-            durs["dkdv"].append(e[2].elapsed_time(e[3]))
+            if r["kind"] == "flash":
+                durs["bwd"].append(e[1].elapsed_time(e[2]))
+            else:
+                durs["dq"].append(e[1].elapsed_time(e[2]))
+                durs["dkdv"].append(e[2].elapsed_time(e[3]))
         per[r["name"]] = {kname: float(np.mean(x)) for kname, x in durs.items()}
     for name, d in per.items():
         tot = sum(d.values())
-        log(f"  {name:32s} fwd {d['fwd']:.3f} ms  dq {d['dq']:.3f} ms  dkdv {d['dkdv']:.3f} ms  "
-            f"total {tot:.3f} ms  -> {alg_flops_variant / (tot * 1e-3) / 1e12:.1f} TFLOP/s")
+        log(f"  {name:32s} " + "  ".join(f"{st} {x:.3f} ms" for st, x in d.items()) +
+            f"  total {tot:.3f} ms  -> {alg_flops_variant / (tot * 1e-3) / 1e12:.1f} TFLOP/s")
+    baselines = None
+    if args.baselines:
+        fl = sum(per["flash-softmax"].values())
+        kint = [n for n, r in zip(per, runs) if r["kind"] == "kia" and r["p"].recon in (0, 1)]
+        baselines = {"flash_softmax_ms": round(fl, 4),
+                     "flash_softmax_tflops": round(alg_flops_variant / (fl * 1e-3) / 1e12, 3),
+                     "time_over_flash_softmax": {n: round(sum(per[n].values()) / fl, 3) for n in per
+                                                 if n != "flash-softmax"}}
+        log(f"one-pass exact softmax {fl:.3f} ms; K-interval variants take "
+            + ", ".join(f"{sum(per[n].values()) / fl:.2f}x" for n in kint) + " of it")
     # dominant kernel: the (variant, stage) launch with the largest average duration
     dom_var, dom_stage = max(((n, st) for n in per for st in per[n]), key=lambda x: per[x[0]][x[1]])
     dom_ms = per[dom_var][dom_stage]
@@ -230,7 +268,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample ...")
-        cpu = cpu_baseline(variants, q, k, v, do, args.cpu_seconds, args.grad)
+        cpu = cpu_baseline([x for x in variants if not isinstance(x, str)], q, k, v, do, args.cpu_seconds, args.grad)
         log(f"cpu baseline {cpu}")
 
     line = {
@@ -248,6 +286,7 @@ def main() -> int:
             "slowest_variant": {"name": slowest, "tflops": round(slowest_tflops, 3),
                                 "ms": round(sum(per[slowest].values()), 4)},
             "kernel_ms": {n: {k2: round(x, 4) for k2, x in d.items()} for n, d in per.items()},
+            "baselines": baselines,
         },
         "roofline": {"bound": "mfma", "kernel": kernel_key, "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

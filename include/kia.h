@@ -223,6 +223,30 @@ kia_status_t kia_backward_noalloc(const kia_params_t* p, const void* q, const vo
                                   float* dq, float* dk, float* dv, void* stream);
 
 /*
+ * One-pass exact softmax attention (App. B "Softmax"), FlashAttention-style: the
+ * same-hardware speed reference for the K-interval operator.  The forward sweeps
+ * the keys once with a running row maximum, rescaling the running weight sum and
+ * output when it grows (the exponential is shift-invariant, so the probabilities
+ * are those of the row maximum's shift); the backward recomputes the scores tile
+ * by tile.  Memory beyond the inputs and outputs is O(T): nothing T x T is stored.
+ *  p: params->recon must be KIA_RECON_SOFTMAX (KIA_ERR_UNSUPPORTED otherwise);
+ *     calib, K, tau, ste, grad and tail are checked as for kia_forward and do not
+ *     change the result (softmax's row-maximum term is zero).
+ *  q, k, v, d_o: device, [B,H,T,D] of params->dtype.  o: device float32 [B,H,T,D].
+ *  rowstats: device float[3*B*H*T], caller-owned: per row the shift M and weight
+ *     sum W the forward ends with (written by kia_flash_forward, read by
+ *     kia_flash_backward), then D_i = dO_i . O_i (written and read by
+ *     kia_flash_backward).
+ *  dq, dk, dv: device float32 [B,H,T,D], written.
+ * The forward's o and rowstats must be passed unchanged to the backward.
+ */
+kia_status_t kia_flash_forward(const kia_params_t* p, const void* q, const void* k, const void* v, float* o,
+                               float* rowstats, void* stream);
+kia_status_t kia_flash_backward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                                const float* o, const void* d_o, float* rowstats, float* dq, float* dk,
+                                float* dv, void* stream);
+
+/*
  * Test hook: the reconstruction decision of every (query, key) pair as the
  * kernels take it, for bit-exact comparison of bin decisions.
  *  rowrec: the record written by kia_forward with the same params (its stored

@@ -43,7 +43,8 @@ class Params(ctypes.Structure):
 
 
 EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
-           "kia_backward_noalloc", "kia_debug_bins", "kia_status_string", "kia_last_error")
+           "kia_backward_noalloc", "kia_flash_forward", "kia_flash_backward", "kia_debug_bins",
+           "kia_status_string", "kia_last_error")
 NOALLOC_WS_BYTES = 64 << 20  # KIA_NOALLOC_WS_BYTES
 
 
@@ -59,9 +60,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kia_backward_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kia_flash_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.kia_flash_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_debug_bins.argtypes = [P, vp, vp, vp]
     for f in ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
-              "kia_backward_noalloc", "kia_debug_bins"):
+              "kia_backward_noalloc", "kia_flash_forward", "kia_flash_backward", "kia_debug_bins"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kia_status_string.argtypes = [ctypes.c_int]
     lib.kia_status_string.restype = ctypes.c_char_p
@@ -181,6 +184,48 @@ def kia_backward_noalloc(p: Params, q, k, v, o, d_o, rowrec, dq, dk, dv, stream=
     _check_inputs(p, q, k, v, d_o, outputs=(o, dq, dk, dv), rowrec=rowrec)
     _check(_lib.kia_backward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowrec),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def _check_rowstats(p: Params, rowstats):
+    need = 3 * p.B * p.H * p.T
+    if rowstats.dtype != torch.float32 or rowstats.numel() < need or not rowstats.is_contiguous():
+        raise ValueError(f"rowstats must be contiguous float32 with at least {need} elements")
+
+
+def kia_flash_forward(p: Params, q, k, v, o, rowstats, stream=None) -> None:
+    """The one-pass exact-softmax forward (p.recon must be softmax)."""
+    _check_inputs(p, q, k, v, outputs=(o,))
+    _check_rowstats(p, rowstats)
+    if rowstats.device != q.device:
+        raise ValueError("rowstats on another device")
+    _check(_lib.kia_flash_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(rowstats),
+                                  _stream(stream)))
+
+
+def kia_flash_backward(p: Params, q, k, v, o, d_o, rowstats, dq, dk, dv, stream=None) -> None:
+    _check_inputs(p, q, k, v, d_o, outputs=(o, dq, dk, dv))
+    _check_rowstats(p, rowstats)
+    if rowstats.device != q.device:
+        raise ValueError("rowstats on another device")
+    _check(_lib.kia_flash_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(rowstats),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def flash_forward(cfg: Config, q, k, v, stream=None):
+    """Allocate O and the row statistics with torch and run kia_flash_forward.  Returns (o, rowstats, params)."""
+    p = make_params(cfg, q.shape, q.dtype)
+    o = torch.empty(q.shape, device=q.device, dtype=torch.float32)
+    rowstats = torch.empty(max(3 * p.B * p.H * p.T, 1), device=q.device, dtype=torch.float32)
+    kia_flash_forward(p, q, k, v, o, rowstats, stream)
+    return o, rowstats, p
+
+
+def flash_backward(p: Params, q, k, v, o, d_o, rowstats, stream=None):
+    dq = torch.empty(q.shape, device=q.device, dtype=torch.float32)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    kia_flash_backward(p, q, k, v, o, d_o, rowstats, dq, dk, dv, stream)
+    return dq, dk, dv
 
 
 def kia_debug_bins(p: Params, rowrec, bins, stream=None) -> None:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libkia.so")
 # (MinMax, FWM with a zero, floored or resolved tail, the exponential baselines); the KIA_CAL=0
 # backward build also holds the dkdv kernel
 NCALIB = 5
-SOURCES = [("kia_api.hip", "kia_api.o", [])] + [
+SOURCES = [("kia_api.hip", "kia_api.o", []), ("kia_flash.hip", "kia_flash.o", [])] + [
     (src, f"{src[:-4]}_c{c}.o", [f"-DKIA_CAL={c}"]) for c in range(NCALIB) for src in ("kia_fwd.hip", "kia_bwd.hip")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

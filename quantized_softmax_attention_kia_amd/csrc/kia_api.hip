@@ -305,6 +305,52 @@ kia_status_t kia_backward_noalloc(const kia_params_t* p, const void* q, const vo
   return backward_stages(p, q, k, v, o, d_o, rowrec, dq, dk, dv, ws, stream, 3, "kia_backward_noalloc");
 }
 
+static kia_status_t flash_params(const kia_params_t* p, kia::Problem* pr, const char* name) {
+  kia_status_t st = check_params(p, pr);
+  if (st != KIA_OK) return st;
+  if (p->recon != KIA_RECON_SOFTMAX) {
+    set_err("%s: the one-pass kernels compute exact softmax (recon %d given)", name, p->recon);
+    return KIA_ERR_UNSUPPORTED;
+  }
+  return KIA_OK;
+}
+
+kia_status_t kia_flash_forward(const kia_params_t* p, const void* q, const void* k, const void* v, float* o,
+                               float* rowstats, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = flash_params(p, &pr, "kia_flash_forward");
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  if (!q || !k || !v || !o || !rowstats) { set_err("kia_flash_forward: null buffer"); return KIA_ERR_INVALID_ARG; }
+  const size_t N = (size_t)pr.nheads * pr.T;
+  kia::FlashArgs a{};
+  a.nheads = pr.nheads;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.rowM = rowstats; a.rowW = rowstats + N; a.rowD = rowstats + 2 * N;
+  a.T = pr.T; a.causal = pr.causal; a.scale = (float)pr.scale; a.scale_d = pr.scale;
+  return hip_status(kia::launch_flash_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_flash_forward launch");
+}
+
+kia_status_t kia_flash_backward(const kia_params_t* p, const void* q, const void* k, const void* v, const float* o,
+                                const void* d_o, float* rowstats, float* dq, float* dk, float* dv, void* stream) {
+  kia::Problem pr;
+  kia_status_t st = flash_params(p, &pr, "kia_flash_backward");
+  if (st != KIA_OK) return st;
+  if (empty(pr)) return KIA_OK;
+  if (!q || !k || !v || !o || !d_o || !rowstats || !dq || !dk || !dv) {
+    set_err("kia_flash_backward: null buffer");
+    return KIA_ERR_INVALID_ARG;
+  }
+  const size_t N = (size_t)pr.nheads * pr.T;
+  kia::FlashArgs a{};
+  a.nheads = pr.nheads;
+  a.q = q; a.k = k; a.v = v; a.dO = d_o; a.o = const_cast<float*>(o);
+  a.rowM = rowstats; a.rowW = rowstats + N; a.rowD = rowstats + 2 * N;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.T = pr.T; a.causal = pr.causal; a.scale = (float)pr.scale; a.scale_d = pr.scale;
+  return hip_status(kia::launch_flash_backward(pr, a, static_cast<hipStream_t>(stream)), "kia_flash_backward launch");
+}
+
 kia_status_t kia_debug_bins(const kia_params_t* p, const void* rowrec, uint8_t* bins, void* stream) {
   kia::Problem pr;
   kia_status_t st = check_params(p, &pr);

@@ -369,6 +369,20 @@ template <int D> struct RowOp<D, uint16_t> {
   }
 };
 
+// The exact score of one (query, key) pair: products and sum in double, scale in double,
+// rounded once to fp32 -- the value the bound is measured against.
+template <int D, typename TIn, int UNROLL = 8>
+__device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, double scale) {
+  double acc = 0.0;
+#pragma unroll UNROLL
+  for (int d = 0; d < D; d += 4) {
+    const f4v x = Ld<TIn>::four(qrow + d), y = Ld<TIn>::four(krow + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fma((double)x[e], (double)y[e], acc);
+  }
+  return (float)(scale * acc);
+}
+
 // B operand slices for k-block b (rows 16b .. 16b+15) and output column n of the transposed tile.
 // Lane (n, g) supplies rows 16b + 4g + (0..3) and 16b + 8 + 4g + (0..3): the rows that the
 // accumulator-layout coefficients v = 8b .. 8b+7 of lane (., g) stand for (crow(v, g)).

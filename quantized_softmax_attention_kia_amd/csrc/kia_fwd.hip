@@ -105,20 +105,6 @@ constexpr double acc_c() {
   return NS == 3 ? 1.01 * (1.008 * (D - 1) + 0.04 * D + 8.1) * 0x1p-24 : 1.01 * (D + 4) * 0x1p-24;
 }
 
-// The exact score of one (query, key) pair: products and sum in double, scale in double,
-// rounded once to fp32 -- the value the bound is measured against.
-template <int D, typename TIn, int UNROLL = 8>
-__device__ __forceinline__ float exact_score(const TIn* qrow, const TIn* krow, double scale) {
-  double acc = 0.0;
-#pragma unroll UNROLL
-  for (int d = 0; d < D; d += 4) {
-    const f4v x = Ld<TIn>::four(qrow + d), y = Ld<TIn>::four(krow + d);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fma((double)x[e], (double)y[e], acc);
-  }
-  return (float)(scale * acc);
-}
-
 // Exact scores of one query against two keys in one sweep (the loads of both in flight together).
 template <int D, typename TIn>
 __device__ __forceinline__ void exact_score2(const TIn* qrow, const TIn* k1, const TIn* k2, double scale,

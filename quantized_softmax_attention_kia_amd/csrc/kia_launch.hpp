@@ -112,6 +112,26 @@ struct BwdArgs {
   int res_far;       // FWM_RES: keys below the table need computed grid values
 };
 
+// The one-pass exponential baselines (kia_flash.hip): per row the shift M of the scores and the
+// weight sum W the forward ends with, and D_i = dO_i . O_i, which the dq kernel writes for dkdv.
+struct FlashArgs {
+  int nheads;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  float* o;        // forward: written; backward: read
+  float* rowM;
+  float* rowW;
+  float* rowD;
+  float* dq;
+  float* dk;
+  float* dv;
+  int T, causal;
+  float scale;
+  double scale_d;  // the same scale in double, for exact scores
+};
+
 struct BinsArgs {
   RowRec rec;
   uint8_t* bins;
@@ -135,6 +155,9 @@ KIA_DECLARE_CAL(EXPB)
 #undef KIA_DECLARE_CAL
 // the dK, dV kernel (independent of the calibration; built with KIA_CAL = 0)
 hipError_t launch_dkdv(const Problem& p, const BwdArgs& a, hipStream_t s);
+
+hipError_t launch_flash_forward(const Problem& p, const FlashArgs& a, hipStream_t s);
+hipError_t launch_flash_backward(const Problem& p, const FlashArgs& a, hipStream_t s);
 
 inline hipError_t launch_forward(const Problem& p, const FwdArgs& a, hipStream_t s) {
   switch (p.calib) {
