@@ -14,4 +14,6 @@ KIA_STUB(FWM_FLOOR)
 KIA_STUB(FWM_RES)
 KIA_STUB(EXPB)
 hipError_t launch_dkdv(const Problem&, const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_flash_forward(const Problem&, const FlashArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_flash_backward(const Problem&, const FlashArgs&, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace kia

@@ -87,7 +87,13 @@ for kw in bad:
     assert lib.kia_backward(ctypes.byref(p), *([None] * 11)) != 0
     assert lib.kia_backward_noalloc(ctypes.byref(p), *([None] * 10)) != 0
     assert lib.kia_debug_bins(ctypes.byref(p), None, None, None) != 0
+    assert lib.kia_flash_forward(ctypes.byref(p), None, None, None, None, None, None) != 0
+    assert lib.kia_flash_backward(ctypes.byref(p), *([None] * 10)) != 0
     lib.kia_last_error()
+# the one-pass kernels compute softmax only; null buffers are rejected
+assert lib.kia_flash_forward(ctypes.byref(params()), None, None, None, None, None, None) == -2
+assert lib.kia_flash_forward(ctypes.byref(params(recon=2, calib=1)), None, None, None, None, None, None) == -1
+assert lib.kia_flash_backward(ctypes.byref(params(recon=2, calib=1)), *([None] * 10)) == -1
 # valid params, null buffers: rejected before any launch
 p = params()
 assert lib.kia_forward(ctypes.byref(p), None, None, None, None, None, None) != 0
