@@ -33,7 +33,7 @@ METRIC = "K-interval attn fwd+bwd TFLOP/s & % MFMA peak, B=8 H=12 T=1024 d=64 ca
 FP32_MFMA_PEAK = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 BF16_MFMA_PEAK = 2500.0
 # algorithmic flops per causal pair, in units of D, per kernel
-ALG_PER_PAIR = {"fwd": 4, "dq": 4, "dkdv": 4, "bwd": 8}
+ALG_PER_PAIR = {"fwd": 4, "dq": 4, "dkdv": 4, "bwd": 8, "fwd1": 2, "fwd2": 2}
 KERNEL_SOURCES = ["kia_device.hpp", "kia_launch.hpp", "kia_fwd.hip", "kia_bwd.hip", "kia_api.hip", "kia_flash.hip"]
 
 
@@ -110,6 +110,9 @@ def main() -> int:
                     help="time the one-pass (online-rescale) exact softmax beside the K-interval variants and "
                          "the exponential baselines (softmax, BF16-exp, FP8-rounded exp) on the two-pass "
                          "pipeline, on the same workload")
+    ap.add_argument("--split-forward", action="store_true",
+                    help="run the forward as its two launches (kia_forward_scores: scores and exact extrema; "
+                         "kia_forward_weights: calibration, reconstruction, normalization, P V) and time each")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size reference for HBM "
                          "byte counters)")
@@ -184,7 +187,13 @@ def main() -> int:
                 continue
             if events is not None:
                 events[i][0].record(stream)
-            kb.kia_forward(r["p"], qt, kt, vt, r["o"], r["rowrec"], stream)
+            if args.split_forward:
+                kb.kia_forward_scores(r["p"], qt, kt, vt, r["rowrec"], stream)
+                if events is not None:
+                    events[i][4].record(stream)
+                kb.kia_forward_weights(r["p"], qt, kt, vt, r["o"], r["rowrec"], stream)
+            else:
+                kb.kia_forward(r["p"], qt, kt, vt, r["o"], r["rowrec"], stream)
             if events is not None:
                 events[i][1].record(stream)
             kb.kia_backward_dq(r["p"], qt, kt, vt, r["o"], dot, r["rowrec"], r["dq"], r["ws"], stream)
@@ -209,7 +218,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [[[mk() for _ in range(4)] for _ in runs] for _ in range(args.steps)]
+    ev = [[[mk() for _ in range(5)] for _ in runs] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -227,11 +236,16 @@ def main() -> int:
     # per-kernel average launch durations from the events
     per = {}
     for i, r in enumerate(runs):
-        stages = ("fwd", "bwd") if r["kind"] == "flash" else ("fwd", "dq", "dkdv")
+        split = args.split_forward and r["kind"] == "kia"
+        stages = ("fwd", "bwd") if r["kind"] == "flash" else (("fwd1", "fwd2") if split else ("fwd",)) + ("dq", "dkdv")
         durs = {st: [] for st in stages}
         for s in range(args.steps):
             e = ev[s][i]
-            durs["fwd"].append(e[0].elapsed_time(e[1]))
+            if split:
+                durs["fwd1"].append(e[0].elapsed_time(e[4]))
+                durs["fwd2"].append(e[4].elapsed_time(e[1]))
+            else:
+                durs["fwd"].append(e[0].elapsed_time(e[1]))
             if r["kind"] == "flash":
                 durs["bwd"].append(e[1].elapsed_time(e[2]))
             else:
@@ -258,7 +272,8 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    headline = args.grad == "full" and args.tail == "zero" and not args.baselines and not args.binmean
+    headline = (args.grad == "full" and args.tail == "zero" and not args.baselines and not args.binmean
+                and not args.split_forward)
     traffic = read_traffic(kernel_key) if headline else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12

@@ -130,8 +130,9 @@ typedef struct {
  *    per row the extrema, their first index and tie counts, W^N, W^L, for
  *    Nearest with Prob-STE the LERP output O^L, and the scores themselves.
  *    Layout (offsets are multiples of 256 bytes), N = B*H*T, nt = ceil(T/32):
- *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N];
- *      (m, amin and nC belong to MinMax; under FWM m = M and amin = nC = 0)
+ *      float M[N], m[N]; int32 amax[N], amin[N], nA[N], nC[N]; float WN[N], WL[N], E[N];
+ *      (m, amin and nC belong to MinMax; under FWM m = M and amin = nC = 0; E: the
+ *      rigorous bound on the error of each stored score of the row, below)
  *      float OL[N*D] (Nearest + Prob-STE: the output O^L; BF16-exp: the residual
  *        O - o of the double output whose float o is the kernel's output, and then WN
  *        holds W's residual, W = WL + WN; other modes: absent);
@@ -171,6 +172,24 @@ kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, siz
  */
 kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
                          float* o, void* rowrec, void* stream);
+
+/*
+ * The two halves of kia_forward as separate launches, for callers that time,
+ * profile or schedule them apart (kia_forward runs both in one launch and writes
+ * the same bits):
+ *  kia_forward_scores  (first): the scores (stored in rowrec), the exact row
+ *                      extrema, their first indices and tie counts, and the score
+ *                      bounds E; o is not touched.
+ *  kia_forward_weights (second): calibration, grid tables, reconstruction,
+ *                      normalization and P V from what the first left in rowrec;
+ *                      writes o and the rest of the record.
+ * Same stream, same params, same rowrec, weights after scores.  Arguments as for
+ * kia_forward.
+ */
+kia_status_t kia_forward_scores(const kia_params_t* p, const void* q, const void* k, const void* v, void* rowrec,
+                                void* stream);
+kia_status_t kia_forward_weights(const kia_params_t* p, const void* q, const void* k, const void* v, float* o,
+                                 void* rowrec, void* stream);
 
 /*
  * Backward pass (App. B): gradients of L = sum(dO * O) for the operator and

@@ -42,7 +42,7 @@ class Params(ctypes.Structure):
                 ("tail", ctypes.c_int32)]
 
 
-EXPORTS = ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
+EXPORTS = ("kia_workspace_size", "kia_forward", "kia_forward_scores", "kia_forward_weights", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
            "kia_backward_noalloc", "kia_flash_forward", "kia_flash_backward", "kia_debug_bins",
            "kia_status_string", "kia_last_error")
 NOALLOC_WS_BYTES = 64 << 20  # KIA_NOALLOC_WS_BYTES
@@ -56,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER(Params)
     lib.kia_workspace_size.argtypes = [P, sz, sz]
     lib.kia_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.kia_forward_scores.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.kia_forward_weights.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.kia_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_backward_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -63,8 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kia_flash_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.kia_flash_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kia_debug_bins.argtypes = [P, vp, vp, vp]
-    for f in ("kia_workspace_size", "kia_forward", "kia_backward", "kia_backward_dq", "kia_backward_dkdv",
-              "kia_backward_noalloc", "kia_flash_forward", "kia_flash_backward", "kia_debug_bins"):
+    for f in ("kia_workspace_size", "kia_forward", "kia_forward_scores", "kia_forward_weights", "kia_backward",
+              "kia_backward_dq", "kia_backward_dkdv", "kia_backward_noalloc", "kia_flash_forward",
+              "kia_flash_backward", "kia_debug_bins"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kia_status_string.argtypes = [ctypes.c_int]
     lib.kia_status_string.restype = ctypes.c_char_p
@@ -158,6 +161,17 @@ def kia_workspace_size(p: Params):
 def kia_forward(p: Params, q, k, v, o, rowrec, stream=None) -> None:
     _check_inputs(p, q, k, v, outputs=(o,), rowrec=rowrec)
     _check(_lib.kia_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(rowrec), _stream(stream)))
+
+
+def kia_forward_scores(p: Params, q, k, v, rowrec, stream=None) -> None:
+    _check_inputs(p, q, k, v, rowrec=rowrec)
+    _check(_lib.kia_forward_scores(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rowrec), _stream(stream)))
+
+
+def kia_forward_weights(p: Params, q, k, v, o, rowrec, stream=None) -> None:
+    _check_inputs(p, q, k, v, outputs=(o,), rowrec=rowrec)
+    _check(_lib.kia_forward_weights(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(rowrec),
+                                    _stream(stream)))
 
 
 def kia_backward(p: Params, q, k, v, o, d_o, rowrec, dq, dk, dv, workspace, stream=None) -> None:

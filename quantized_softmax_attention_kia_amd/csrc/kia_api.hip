@@ -108,7 +108,7 @@ kia_status_t check_params(const kia_params_t* p, kia::Problem* pr) {
 }
 
 struct Layout {
-  size_t off[10];
+  size_t off[11];
   size_t rowrec_bytes;
   int nt;
   size_t tiles_per_head;
@@ -120,12 +120,12 @@ Layout layout(const kia::Problem& pr) {
   Layout L;
   const size_t N = (size_t)pr.nheads * pr.T;
   size_t o = 0;
-  for (int i = 0; i < 8; ++i) { L.off[i] = o; o += round_up(N * 4); }
-  L.off[8] = o;
+  for (int i = 0; i < 9; ++i) { L.off[i] = o; o += round_up(N * 4); }
+  L.off[9] = o;
   if (pr.mode == kia::NEAREST_P || pr.mode == kia::EXPBF) o += round_up(N * pr.D * 4);
   L.nt = (pr.T + 31) / 32;
   L.tiles_per_head = pr.causal ? (size_t)L.nt * (L.nt + 1) / 2 : (size_t)L.nt * L.nt;
-  L.off[9] = o;
+  L.off[10] = o;
   o += (size_t)pr.nheads * L.tiles_per_head * 1024 * 4;
   L.rowrec_bytes = o;
   o = 0;
@@ -154,8 +154,9 @@ kia::RowRec carve(const kia::Problem& pr, void* base) {
   r.nC = reinterpret_cast<int32_t*>(b + L.off[5]);
   r.WN = reinterpret_cast<float*>(b + L.off[6]);
   r.WL = reinterpret_cast<float*>(b + L.off[7]);
-  r.OL = pr.mode == kia::NEAREST_P || pr.mode == kia::EXPBF ? reinterpret_cast<float*>(b + L.off[8]) : nullptr;
-  r.S = reinterpret_cast<float*>(b + L.off[9]);
+  r.E = reinterpret_cast<float*>(b + L.off[8]);
+  r.OL = pr.mode == kia::NEAREST_P || pr.mode == kia::EXPBF ? reinterpret_cast<float*>(b + L.off[9]) : nullptr;
+  r.S = reinterpret_cast<float*>(b + L.off[10]);
   r.nt = L.nt;
   r.tiles_per_head = L.tiles_per_head;
   return r;
@@ -222,19 +223,35 @@ kia_status_t kia_workspace_size(const kia_params_t* p, size_t* rowrec_bytes, siz
   return KIA_OK;
 }
 
-kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
-                         float* o, void* rowrec, void* stream) {
+static kia_status_t forward_phase(const kia_params_t* p, const void* q, const void* k, const void* v, float* o,
+                                  void* rowrec, void* stream, int phase, const char* name) {
   kia::Problem pr;
   kia_status_t st = check_params(p, &pr);
   if (st != KIA_OK) return st;
   if (empty(pr)) return KIA_OK;
-  if (!q || !k || !v || !o || !rowrec) { set_err("kia_forward: null buffer"); return KIA_ERR_INVALID_ARG; }
+  if (!q || !k || !v || (phase != 1 && !o) || !rowrec) { set_err("%s: null buffer", name); return KIA_ERR_INVALID_ARG; }
   kia::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.rec = carve(pr, rowrec);
   a.nheads = pr.nheads;
   a.T = pr.T; a.K = pr.K; a.causal = pr.causal; a.tau = pr.tau; a.scale = pr.scale; a.lres = pr.lres; a.res_far = pr.res_far;
-  return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), "kia_forward launch");
+  a.phase = phase;
+  return hip_status(kia::launch_forward(pr, a, static_cast<hipStream_t>(stream)), name);
+}
+
+kia_status_t kia_forward(const kia_params_t* p, const void* q, const void* k, const void* v,
+                         float* o, void* rowrec, void* stream) {
+  return forward_phase(p, q, k, v, o, rowrec, stream, 0, "kia_forward");
+}
+
+kia_status_t kia_forward_scores(const kia_params_t* p, const void* q, const void* k, const void* v, void* rowrec,
+                                void* stream) {
+  return forward_phase(p, q, k, v, nullptr, rowrec, stream, 1, "kia_forward_scores");
+}
+
+kia_status_t kia_forward_weights(const kia_params_t* p, const void* q, const void* k, const void* v, float* o,
+                                 void* rowrec, void* stream) {
+  return forward_phase(p, q, k, v, o, rowrec, stream, 2, "kia_forward_weights");
 }
 
 static kia_status_t backward_stages(const kia_params_t* p, const void* q, const void* k, const void* v,

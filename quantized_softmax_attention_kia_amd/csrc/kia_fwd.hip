@@ -173,7 +173,9 @@ __device__ __forceinline__ void xext_merge(XExt& a, int lanemask, bool is_max) {
 }
 
 // At D = 64 the register budget is held to two waves per SIMD.  NB: bins held under bin mean.
-template <int D, int CAL, int MODE, typename TIn, int NB = BINM_MAXB>
+// PHASE: 0 the whole forward; 1 pass 1 and the exact extrema only (the stored scores and the row
+// record's extrema and score bounds); 2 the rest, from what phase 1 stored.
+template <int D, int CAL, int MODE, typename TIn, int NB = BINM_MAXB, int PHASE = 0>
 __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fwd_kernel(FwdArgs a) {
   constexpr int NS = nslices<TIn>();
   // BF16-exp: the weights are bfloat16 values, taken exactly, and their products with V are summed
@@ -210,11 +212,21 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     return tile_index(qt, key / BN, nt, a.causal) * 1024 + (4 * ((key & 31) >> 3) + (key & 3)) * 64 + l;
   };
 
+  const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + hb + (size_t)(qvalid ? qi : 0) * D;
+  PairRegs<D, TIn, 64> vr;  // V rows of pass 2's tiles
+  // the row's exact extrema (FWM: m = M) and the error bound of its stored scores
+  float M, m, Erow;
+  if constexpr (PHASE == 2) {
+    const size_t row = (size_t)head * T + (qvalid ? qi : 0);
+    M = qvalid ? a.rec.M[row] : -INFINITY;
+    m = qvalid ? a.rec.m[row] : (CAL == MINMAX ? INFINITY : -INFINITY);
+    Erow = qvalid ? a.rec.E[row] : 1e-30f;
+    if (MODE != NEAREST_P && w < ntiles) vr.load(Vp, w * BN, T);
+  } else {
   // ---- pass 1: scores (bf16 slice products) stored once; approximate row extrema
   // lane (c, g) holds query q0 + c and, in register v of a tile, key k0 + crow(v, g): the order of
   // the stored tiles, so pass 2 reads back exactly what this lane wrote.
   const float scale_f = (float)a.scale;
-  const TIn* qrow = reinterpret_cast<const TIn*>(a.q) + hb + (size_t)(qvalid ? qi : 0) * D;
   // two K operand buffers in turn: the next tile's K is in flight while this one computes (the
   // first is requested before the Q row, so both loads overlap)
   RowOp<D, TIn> kr0, kr1;
@@ -277,8 +289,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   }
   // pass 2's first V tile, loaded while the extrema are settled (not under Nearest with Prob-STE,
   // which loads each tile's V in its own step)
-  PairRegs<D, TIn, 64> vr;
-  if (MODE != NEAREST_P && w < ntiles) vr.load(Vp, w * BN, T);
+  if (PHASE == 0 && MODE != NEAREST_P && w < ntiles) vr.load(Vp, w * BN, T);
   ex.ax += 4 * g;
   ex.an += 4 * g;
   const Lane2& loc = ex;  // this lane's own extrema: keys whose scores it stored
@@ -302,14 +313,15 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     amx = fmaxf(amx, sm.amx[v][c]);
   }
   // error bound of the row's scores, and of u in interval widths (below)
-  const float Erow = (float)(a.scale * acc_c<D, NS>()) * amx + 1e-30f;
+  const float Er = (float)(a.scale * acc_c<D, NS>()) * amx + 1e-30f;
+  Erow = Er;
 
   // ---- exact extrema.  Every key whose exact score can attain the row maximum (minimum) has a
   // stored score within 2 Erow of the approximate one: a candidate.  Each lane recomputes its own
   // candidate exactly (one per side, whose key it kept) and patches the element it stored; a lane
   // holding more (near ties, rare) rescans its tiles for them.  First index and tie count are then
   // taken over exact values.
-  const float thrM = rowmx - 2.f * Erow, thrm = rowmn + 2.f * Erow;
+  const float thrM = rowmx - 2.f * Er, thrm = rowmn + 2.f * Er;
   XExt yM{-INFINITY, INT_MAX, 0}, ym{INFINITY, INT_MAX, 0};
   // whether this lane's kept key covers its candidates of each side, or it has to rescan
   const bool scanM = qvalid && loc.mx2 >= thrM;
@@ -383,7 +395,8 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     if (CAL == MINMAX) xext_combine(xm, sm.xm[v][c], false);
   }
   if (CAL != MINMAX) xm = xM;  // FWM: no minimum (recorded as M)
-  const float M = xM.v, m = xm.v;
+  M = xM.v;
+  m = xm.v;
   if (w == 0 && g == 0 && qvalid) {
     const size_t row = (size_t)head * T + qi;
     a.rec.M[row] = M;
@@ -392,7 +405,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     a.rec.amin[row] = CAL == MINMAX ? xm.k : 0;
     a.rec.nA[row] = xM.n;
     a.rec.nC[row] = CAL == MINMAX ? xm.n : 0;
+    a.rec.E[row] = Er;
   }
+  }  // pass 1
+  if constexpr (PHASE == 1) return;
 
   // ---- calibration and grid table (K+1 exponentials per row), shared by the waves
   const RowCal rc = row_calibration<CAL>(M, m, K, a.tau);
@@ -1052,18 +1068,28 @@ __global__ __launch_bounds__(256) void bins_kernel(BinsArgs a) {
 }
 
 // ------------------------------------------------------------------------------- launchers
-template <int D, int CAL, int MODE, typename TIn>
-static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
+// a.phase: 0 the whole forward in one launch; 1 and 2 its two halves (phase 1 is the same for every
+// reconstruction and is built once per calibration)
+template <int D, int CAL, int MODE, typename TIn, int PHASE>
+static hipError_t fwd_launch(const Problem& p, const FwdArgs& a, hipStream_t s) {
   const int nqt = (p.T + BN - 1) / BN;
   const size_t smem = fwd_smem_bytes<D, CAL, MODE, TIn>(p.K, p.lres);
   if constexpr (MODE == BINM) {
     if (p.K < BINM_SMALLB) {
-      hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_SMALLB>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+      hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_SMALLB, PHASE>), dim3(p.nheads * nqt), dim3(FWD_NT), smem,
+                         s, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAL, MODE, TIn, BINM_MAXB, PHASE>), dim3(p.nheads * nqt), dim3(FWD_NT), smem, s, a);
   return hipGetLastError();
+}
+template <int D, int CAL, int MODE, typename TIn>
+static hipError_t fwd_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
+  constexpr int MODE1 = CAL == EXPB ? EXP32 : LERP;
+  if (a.phase == 1) return fwd_launch<D, CAL, MODE1, TIn, 1>(p, a, s);
+  if (a.phase == 2) return fwd_launch<D, CAL, MODE, TIn, 2>(p, a, s);
+  return fwd_launch<D, CAL, MODE, TIn, 0>(p, a, s);
 }
 template <int D, int CAL, int MODE>
 static hipError_t fwd_dt(const Problem& p, const FwdArgs& a, hipStream_t s) {

@@ -54,6 +54,7 @@ struct RowRec {
   int32_t* nC;
   float* WN;
   float* WL;
+  float* E;   // the rigorous error bound of the row's stored scores (pass 1 for pass 2)
   float* OL;  // [N, D]: Nearest + Prob-STE O^L, BF16-exp O's residual (else nullptr)
   float* S;   // stored score tiles: per head, tiles_per_head tiles of 1024 floats
   int nt;     // number of 32-row tiles along T
@@ -85,6 +86,7 @@ struct FwdArgs {
   double scale;  // score scale, applied in double to the exact scores
   int lres;      // FWM_RES: grid levels below the window in the table
   int res_far;   // FWM_RES: keys below the table need computed grid values
+  int phase;     // 0: the whole forward; 1: pass 1 and the exact extrema; 2: the rest
 };
 
 struct BwdArgs {

@@ -200,6 +200,34 @@ def test_full_and_detached_forward_bitwise_identical(kb):
         assert ratio > 1e-3
 
 
+@pytest.mark.parametrize("var", [("minmax", "lerp", "prob", "full", 4, 8.0, "zero"),
+                                 ("minmax", "nearest", "prob", "full", 4, 8.0, "zero"),
+                                 ("fwm", "nearest", "weight", "full", 4, 8.0, "zero"),
+                                 ("fwm", "lerp", "prob", "full", 16, 8.0, "resolved"),
+                                 ("minmax", "binmean", "prob", "full", 8, 8.0, "zero"),
+                                 ("fwm", "exp_bf16", "prob", "full", 4, 8.0, "zero"),
+                                 ("fwm", "softmax", "prob", "full", 4, 8.0, "zero")],
+                         ids=lambda v: f"{v[0]}-{v[1]}-{v[3]}-{v[6]}")
+def test_split_forward_stages_match(kb, var):
+    """kia_forward_scores then kia_forward_weights write the same bits as kia_forward (O and the whole
+    row record, stored scores included), on the gpt2-shaped workload."""
+    import torch
+    from quantized_softmax_attention_kia_amd.inputs import Variant
+    wl = WORKLOADS["gpt2"]
+    q, k, v, do = inputs("gpt2")
+    v_ = Variant(*var)
+    say(f"[split forward] gpt2 {v_.name}")
+    qt, kt, vt = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    o, rowrec, p = kb.forward(kb.Config.of(v_), qt, kt, vt)
+    o2 = torch.full_like(o, float("nan"))
+    rowrec2 = torch.zeros_like(rowrec)
+    kb.kia_forward_scores(p, qt, kt, vt, rowrec2)
+    kb.kia_forward_weights(p, qt, kt, vt, o2, rowrec2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    assert torch.equal(rowrec, rowrec2)
+
+
 def test_split_backward_stages_match(kb):
     import torch
     wl = WORKLOADS["gpt2"]

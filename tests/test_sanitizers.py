@@ -88,6 +88,8 @@ for kw in bad:
     assert lib.kia_backward_noalloc(ctypes.byref(p), *([None] * 10)) != 0
     assert lib.kia_debug_bins(ctypes.byref(p), None, None, None) != 0
     assert lib.kia_flash_forward(ctypes.byref(p), None, None, None, None, None, None) != 0
+    assert lib.kia_forward_scores(ctypes.byref(p), None, None, None, None, None) != 0
+    assert lib.kia_forward_weights(ctypes.byref(p), None, None, None, None, None, None) != 0
     assert lib.kia_flash_backward(ctypes.byref(p), *([None] * 10)) != 0
     lib.kia_last_error()
 # the one-pass kernels compute softmax only; null buffers are rejected
