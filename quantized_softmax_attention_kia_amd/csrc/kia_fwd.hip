@@ -83,9 +83,15 @@ struct FwdSmem {
   double sL[FWD_NW][BN], sN[FWD_NW][BN];
   float rowW[BN], rowWL[BN];
   double rowWd[BN], rowWLd[BN];  // the row sums in double: O's normalizer, and W^L
-  // heavy keys retaken after pass 2: per lane up to HMAX (key, change of the continuous weight)
-  int hn[FWD_NW][64], hk[FWD_NW][64][HMAX];
+  // heavy keys retaken after pass 2: per lane up to HMAX keys with their stored scores (batched)
+  // or their weight changes (one at a time); per row the sum of the weight changes (batched) or
+  // per lane the number of keys (one at a time)
+  int hk[FWD_NW][64][HMAX];
   float hd[FWD_NW][64][HMAX];
+  union {
+    double hs[FWD_NW][BN];
+    int hn[FWD_NW][64];
+  };
   // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
 };
 
@@ -768,8 +774,185 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // weight (w^L, or softmax's e^z) for the output.  Bin mean sums its bins before pass 2 and keeps
   // its faster scores; the rounded exponentials (BF16-exp, FP8) have taken every weight exactly.
   constexpr bool HEAVY = MODE != BINM && MODE != EXPBF && MODE != EXPF8;
-  int nh_any = 0;
-  if constexpr (HEAVY) {
+  // whether a heavy key's weight change reaches the output (the continuous weight: w^L, or e^z)
+  constexpr bool HCORR = MODE == LERP || MODE == EXP32 || MODE == NEAREST_P;
+  // fp32 inputs take the heavy keys in batches: found first, then their exact scores with every
+  // load of a batch in flight, then their weight changes applied four keys at a time.  bfloat16
+  // inputs take them one key at a time (a key's exact score and correction before the next).
+  constexpr bool HBATCH = std::is_same_v<TIn, float>;
+  double hsum = 0.0;  // batched: the weight changes of this lane's heavy keys (all in its own row)
+  int nh_any = 0;     // one at a time: whether this lane retook a heavy key
+  if constexpr (HEAVY && HBATCH) {
+    __syncthreads();
+    double WLr = 0.0, WNr = 0.0;
+#pragma unroll
+    for (int u = 0; u < FWD_NW; ++u) {
+      WLr += sm.sL[u][c];
+      WNr += sm.sN[u][c];
+    }
+    const double Wmin = is_nearest(MODE) ? fmin(WLr, WNr) : WLr;
+    const bool maybe = qvalid && Wmin <= HEAVY_INV;
+    const double hgrid = CAL == EXPB ? 0.0 : 1.0 / rc.inv_h;
+    const float s_thr = maybe ? (float)((double)M + log(Wmin / HEAVY_INV) - hgrid) - Erow : INFINITY;
+    if (__any(maybe)) {
+      // (a) the heavy keys, found on the stored scores (the next tile's scores are in flight while
+      // one is tested); up to HMAX per lane, with their stored scores
+      int nh = 0;
+      float sc[16], sn[16];
+      auto load16 = [&](float(&dst)[16], int kt) {
+        const float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[v] = St[v * 64];
+      };
+      if (w < ntiles) load16(sc, w);
+      for (int kt = w; kt < ntiles; kt += FWD_NW) {
+        const bool more = kt + FWD_NW < ntiles;
+        if (more) load16(sn, kt + FWD_NW);
+        const int k0 = kt * BN;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + crow(v, g);
+          const bool ok = maybe & (key < T) & (!a.causal | (key <= qi));
+          // the extremum keys' stored scores are exact already
+          bits |= (ok && sc[v] >= s_thr && sc[v] != M) ? (1u << v) : 0u;
+        }
+        while (__any(bits != 0u)) {
+          const int j = bits ? __builtin_ctz(bits) : 0;
+          if (bits) {
+            bits &= bits - 1u;
+            float old = sc[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) old = v == j ? sc[v] : old;
+            // the key's probability under either normalizer, from its faster score (a margin of
+            // 1e-3 for that score's error)
+            bool heavy;
+            if constexpr (CAL == EXPB) {
+              heavy = (double)__expf(old - M) * (HEAVY_INV * (1.0 + 1e-3)) >= WLr;
+            } else {
+              constexpr int ST = CAL == MINMAX ? BN : 1;
+              const Weights w0 = weights_cal<CAL, ST>(decide<CAL>(old, rc, K, a.tau), trow, a.lres, a.res_far != 0,
+                                                       K, a.tau);
+              heavy = (double)w0.wL * (HEAVY_INV * (1.0 + 1e-3)) >= WLr ||
+                      (is_nearest(MODE) && (double)w0.wN * (HEAVY_INV * (1.0 + 1e-3)) >= WNr);
+            }
+            if (heavy && nh < HMAX) {
+              sm.hk[w][l][nh] = k0 + crow(j, g);
+              sm.hd[w][l][nh] = old;
+              ++nh;
+            }
+          }
+        }
+        if (more) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[v] = sn[v];
+        }
+      }
+      // the wave's heavy keys as one list in its LDS region (V^T is no longer read): lane order
+      int incl = nh;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (l >= d) incl += t;
+      }
+      const int off = incl - nh;
+      const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+      int* fk = reinterpret_cast<int*>(sm.wave[w]);  // key
+      int* fr = fk + 64 * HMAX;                       // query row in the tile
+      float* fx = reinterpret_cast<float*>(fr + 64 * HMAX);  // exact score, then weight change
+      for (int x = 0; x < nh; ++x) {
+        fk[off + x] = sm.hk[w][l][x];
+        fr[off + x] = c;
+      }
+      wave_lds_sync();
+      // (b) their exact scores (double products and sums, double scale, one rounding), LPK lanes
+      // to a key: each lane sums 16 products, then the lanes' sums are added across the group;
+      // every load of a batch of 64 / LPK keys is in flight at once
+      constexpr int LPK = D / 16;
+      const TIn* Qh = reinterpret_cast<const TIn*>(a.q) + hb;
+      for (int e0 = 0; e0 < total; e0 += 64 / LPK) {
+        const int e = e0 + l / LPK, part = l % LPK;
+        const int ee = e < total ? e : e0;  // a spare lane repeats a listed key (in bounds)
+        const TIn* qp = Qh + (size_t)(q0 + fr[ee]) * D + 16 * part;
+        const TIn* kp = Kp + (size_t)fk[ee] * D + 16 * part;
+        f4v xq[4], yk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xq[i] = Ld<TIn>::four(qp + 4 * i);
+          yk[i] = Ld<TIn>::four(kp + 4 * i);
+        }
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc = fma((double)xq[i][k], (double)yk[i][k], acc);
+#pragma unroll
+        for (int s = LPK / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
+        if (e < total && part == 0) fx[e] = (float)(a.scale * acc);
+      }
+      wave_lds_sync();
+      // (c) each lane patches its keys' exact scores into the tiles it stored (for the backward)
+      // and takes the change of each continuous weight: pass 2 weighed the key with the float
+      // decision on its stored score (the decision itself is the same: pass 2 settled it against
+      // the bound)
+      for (int x = 0; x < nh; ++x) {
+        const float xe = fx[off + x], old = sm.hd[w][l][x];
+        float dw = 0.f;
+        if (xe != old) {
+          const int key = fk[off + x];
+          Sh[stored_at(key)] = xe;
+          if constexpr (MODE == EXP32) {
+            dw = __expf(xe - M) - __expf(old - M);
+          } else if constexpr (MODE == LERP || MODE == NEAREST_P) {
+            constexpr int ST = CAL == MINMAX ? BN : 1;
+            const Decision d0 = decide_fast<CAL>(old, rc, K, a.tau), d1 = decide<CAL>(xe, rc, K, a.tau);
+            const bool keep = CAL == FWM_FLOOR || !d0.tail;
+            dw = keep ? weights_cal<CAL, ST>(d1, trow, a.lres, a.res_far != 0, K, a.tau).wL -
+                            weights_cal<CAL, ST>(d0, trow, a.lres, a.res_far != 0, K, a.tau).wL
+                      : 0.f;
+          }
+        }
+        fx[off + x] = dw;
+        hsum += (double)dw;
+      }
+      if constexpr (HCORR) {
+        // (d) the weight changes into this wave's output rows (O, or O^L under Nearest with
+        // Prob-STE), in list order; four keys' V rows are loaded together.  Lane (c, g) holds
+        // row crow(v, g) of the tile at columns 32 nb + c.
+        wave_lds_sync();
+        f16v(&acc)[D / 32] = MODE == NEAREST_P ? ol : o;  // DRUN: od
+        for (int e0 = 0; e0 < total; e0 += 4) {
+          float vv[4][D / 32], dws[4];
+          int rs[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = e0 + j < total ? e0 + j : e0;
+            dws[j] = e0 + j < total ? fx[e] : 0.f;  // (a spare slot repeats a listed key with no change)
+            rs[j] = fr[e];
+            const TIn* vp = Vp + (size_t)fk[e] * D + c;
+#pragma unroll
+            for (int nb = 0; nb < D / 32; ++nb) vv[j][nb] = Ld<TIn>::one(vp + 32 * nb);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = rs[j], vr_ = 4 * (r >> 3) + (r & 3);  // crow(vr_, (r >> 2) & 1) == r
+            const float xdw = g == ((r >> 2) & 1) ? dws[j] : 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float f = v == vr_ ? xdw : 0.f;
+#pragma unroll
+              for (int nb = 0; nb < D / 32; ++nb) {
+                if constexpr (DRUN) od[nb][v] = fma((double)f, (double)vv[j][nb], od[nb][v]);
+                else acc[nb][v] = fmaf(f, vv[j][nb], acc[nb][v]);
+              }
+            }
+          }
+        }
+      }
+    }
+    hsum += __shfl_xor(hsum, 32);
+    if (g == 0) sm.hs[w][c] = hsum;
+  } else if constexpr (HEAVY) {
     __syncthreads();
     double WLr = 0.0, WNr = 0.0;
 #pragma unroll
@@ -863,8 +1046,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
     }
   };
-  // whether any lane of the workgroup retook a heavy key (a barrier, which also orders the slots)
-  const bool anyheavy = HEAVY && __syncthreads_or(nh_any);
+  // one key at a time: whether any lane of the workgroup retook a heavy key (a barrier, which also
+  // orders the slots)
+  bool anyheavy = false;
+  if constexpr (HEAVY && !HBATCH) anyheavy = __syncthreads_or(nh_any);
   if constexpr (F64) {
     double* pd = reinterpret_cast<double*>(sm.wave[w]);
     __syncthreads();
@@ -922,7 +1107,11 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
     sumL += sm.sL[u][c];
     sumN += sm.sN[u][c];
   }
-  if (HEAVY && (MODE == LERP || MODE == EXP32 || MODE == NEAREST_P) && anyheavy) {
+  if constexpr (HEAVY && HBATCH) {
+#pragma unroll
+    for (int u = 0; u < FWD_NW; ++u) sumL += sm.hs[u][c];  // the heavy keys' weight changes (W^L, softmax's W)
+  }
+  if (HEAVY && !HBATCH && HCORR && anyheavy) {
     // the heavy keys' weight changes, in a fixed order (waves, lanes, slots): into the continuous
     // row sum (W^L, softmax's W) and into the output rows (O, or O^L under Nearest with Prob-STE).
     // Lane (c, g) holds output row crow(v, g) of the tile at columns 32 nb + c.
@@ -1024,6 +1213,7 @@ size_t fwd_smem_bytes(int K, int lres) {
 }
 static_assert(sizeof(float) * 2 * BINM_MAXB * BN * FWD_NW <= FWD_NW * fwd_wave_bytes<64, 1, false>(),
               "bin-mean partial sums fit the V^T staging area");
+static_assert(3 * 64 * HMAX * 4 <= fwd_wave_bytes<64, 1, false>(), "a wave's heavy-key list fits its staging area");
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
 template <int CAL, int MODE>
