@@ -64,6 +64,24 @@ def read_traffic(kernel: str):
     return None
 
 
+def read_issue(kernel: str):
+    """SQ counters of the kernel (profiles/sq_counters_gpt2_fwd_bwd.md): the VALU's and the matrix
+    pipe's busy shares of SIMD time and the waves' share of time waiting, or None when the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "sq_counters_gpt2_fwd_bwd.md")
+    if not os.path.exists(path):
+        return None
+    digest = sources_digest()
+    for line in open(path):
+        parts = line.split()
+        # machine-readable lines:  issue <kernel> <valu_busy> <mfma_busy> <wait_any> <sources_digest>
+        if len(parts) == 6 and parts[0] == "issue" and parts[1] == kernel and parts[5] == digest:
+            valu, mfma, wait = (float(x) for x in parts[2:5])
+            return {"limiter": "valu" if valu > mfma else "mfma", "valu_busy": valu, "mfma_busy": mfma,
+                    "wait_any": wait}
+    return None
+
+
 def cpu_baseline(variants, q, k, v, do, budget_s: float, grad: str = "full"):
     """The oracle, as it stands, on a bounded sample: heads in order, every variant, until the budget."""
     import dataclasses
@@ -275,6 +293,7 @@ def main() -> int:
     headline = (args.grad == "full" and args.tail == "zero" and not args.baselines and not args.binmean
                 and not args.split_forward)
     traffic = read_traffic(kernel_key) if headline else None
+    issue = read_issue(kernel_key) if headline else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "
@@ -305,7 +324,7 @@ def main() -> int:
         },
         "roofline": {"bound": "mfma", "kernel": kernel_key, "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "issue": issue},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -798,6 +798,44 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       // (a) the heavy keys, found on the stored scores (the next tile's scores are in flight while
       // one is tested); up to HMAX per lane, with their stored scores
       int nh = 0;
+      // The lowest stored score that the heavy test below can accept.  The bound above holds on
+      // every grid; where the weight threshold falls inside the grid, the grid inverted at it gives
+      // a tighter one (the weights rise with u; a margin of 1e-3 interval widths, or 1e-3 of a
+      // score unit for softmax, covers the roundings of the inversion and of the float decisions).
+      float s_cand = s_thr;
+      if (maybe) {
+        const double thrL = WLr / (HEAVY_INV * (1.0 + 1e-3)), thrN = WNr / (HEAVY_INV * (1.0 + 1e-3));
+        if constexpr (CAL == EXPB) {
+          s_cand = fmaxf(s_thr, (float)((double)M + log(thrL) - 1e-3));
+        } else if constexpr (CAL == MINMAX || CAL == FWM || CAL == FWM_FLOOR) {
+          constexpr int ST = CAL == MINMAX ? BN : 1;
+          // interval r with E_r < thr <= E_{r+1} (E rises with r), or -1 (thr <= E_0), or K (thr > E_K)
+          auto interval = [&](double thr) {
+            if (thr <= (double)trow[0]) return -1;
+            if (thr > (double)trow[K * ST]) return K;
+            int lo = 0, hi = K;
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if ((double)trow[mid * ST] < thr) lo = mid;
+              else hi = mid;
+            }
+            return lo;
+          };
+          // LERP: the u at which the interpolated weight reaches the threshold
+          const int rL = interval(thrL);
+          double ustar = rL < 0 ? -1.0
+                         : rL >= K ? (double)K + 1.0
+                                   : rL + (thrL - (double)trow[rL * ST]) /
+                                              ((double)trow[(rL + 1) * ST] - (double)trow[rL * ST]);
+          if (is_nearest(MODE)) {  // Nearest: a weight E_rho with E_rho >= thr from u >= rho - 1/2
+            const int rN = interval(thrN);
+            ustar = fmin(ustar, rN < 0 ? -1.0 : rN + 0.5);
+          }
+          const bool regular = CAL != MINMAX || rc.kappa != 0.f;
+          if (regular && ustar >= 0.0)
+            s_cand = fmaxf(s_thr, (float)((double)M - ((double)K - ustar + 1e-3) * hgrid));
+        }
+      }
       float sc[16], sn[16];
       auto load16 = [&](float(&dst)[16], int kt) {
         const float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
@@ -810,12 +848,18 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
         if (more) load16(sn, kt + FWD_NW);
         const int k0 = kt * BN;
         uint32_t bits = 0u;
+        // candidates (a lane without a possible heavy key has s_cand = infinity); the extremum
+        // keys' stored scores are exact already
+        if (full_tile(kt)) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + crow(v, g);
-          const bool ok = maybe & (key < T) & (!a.causal | (key <= qi));
-          // the extremum keys' stored scores are exact already
-          bits |= (ok && sc[v] >= s_thr && sc[v] != M) ? (1u << v) : 0u;
+          for (int v = 0; v < 16; ++v) bits |= (sc[v] >= s_cand && sc[v] != M) ? (1u << v) : 0u;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + crow(v, g);
+            const bool ok = (key < T) & (!a.causal | (key <= qi));
+            bits |= (ok && sc[v] >= s_cand && sc[v] != M) ? (1u << v) : 0u;
+          }
         }
         while (__any(bits != 0u)) {
           const int j = bits ? __builtin_ctz(bits) : 0;
