@@ -910,24 +910,24 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
       wave_lds_sync();
       // (b) their exact scores (double products and sums, double scale, one rounding), LPK lanes
-      // to a key: each lane sums 16 products, then the lanes' sums are added across the group;
+      // to a key: each lane sums 32 products, then the lanes' sums are added across the group;
       // every load of a batch of 64 / LPK keys is in flight at once
-      constexpr int LPK = D / 16;
+      constexpr int LPK = D / 32;
       const TIn* Qh = reinterpret_cast<const TIn*>(a.q) + hb;
       for (int e0 = 0; e0 < total; e0 += 64 / LPK) {
         const int e = e0 + l / LPK, part = l % LPK;
         const int ee = e < total ? e : e0;  // a spare lane repeats a listed key (in bounds)
-        const TIn* qp = Qh + (size_t)(q0 + fr[ee]) * D + 16 * part;
-        const TIn* kp = Kp + (size_t)fk[ee] * D + 16 * part;
-        f4v xq[4], yk[4];
+        const TIn* qp = Qh + (size_t)(q0 + fr[ee]) * D + 32 * part;
+        const TIn* kp = Kp + (size_t)fk[ee] * D + 32 * part;
+        f4v xq[8], yk[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
           xq[i] = Ld<TIn>::four(qp + 4 * i);
           yk[i] = Ld<TIn>::four(kp + 4 * i);
         }
         double acc = 0.0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
           for (int k = 0; k < 4; ++k) acc = fma((double)xq[i][k], (double)yk[i][k], acc);
 #pragma unroll
@@ -961,35 +961,42 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       }
       if constexpr (HCORR) {
         // (d) the weight changes into this wave's output rows (O, or O^L under Nearest with
-        // Prob-STE), in list order; four keys' V rows are loaded together.  Lane (c, g) holds
-        // row crow(v, g) of the tile at columns 32 nb + c.
+        // Prob-STE): summed per row in an LDS tile in list order (lane l takes columns l + 64 i;
+        // the V rows of eight keys are loaded together), then added to the accumulators once.
+        // Lane (c, g) holds row crow(v, g) of the tile at columns 32 nb + c.
+        constexpr int DS = D + 4;  // row stride of the correction tile
+        float* dO = fx + 64 * HMAX;
+#pragma unroll
+        for (int i = 4 * l; i < 32 * DS; i += 256) *reinterpret_cast<f4v*>(dO + i) = f4v{0.f, 0.f, 0.f, 0.f};
         wave_lds_sync();
-        f16v(&acc)[D / 32] = MODE == NEAREST_P ? ol : o;  // DRUN: od
-        for (int e0 = 0; e0 < total; e0 += 4) {
-          float vv[4][D / 32], dws[4];
-          int rs[4];
+        constexpr int EB = 8;
+        for (int e0 = 0; e0 < total; e0 += EB) {
+          float vv[EB][D / 64];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = e0 + j < total ? e0 + j : e0;
-            dws[j] = e0 + j < total ? fx[e] : 0.f;  // (a spare slot repeats a listed key with no change)
-            rs[j] = fr[e];
-            const TIn* vp = Vp + (size_t)fk[e] * D + c;
+          for (int j = 0; j < EB; ++j) {
+            const TIn* vp = Vp + (size_t)fk[e0 + j < total ? e0 + j : e0] * D + l;
 #pragma unroll
-            for (int nb = 0; nb < D / 32; ++nb) vv[j][nb] = Ld<TIn>::one(vp + 32 * nb);
+            for (int i = 0; i < D / 64; ++i) vv[j][i] = Ld<TIn>::one(vp + 64 * i);
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = rs[j], vr_ = 4 * (r >> 3) + (r & 3);  // crow(vr_, (r >> 2) & 1) == r
-            const float xdw = g == ((r >> 2) & 1) ? dws[j] : 0.f;
+          for (int j = 0; j < EB; ++j) {
+            if (e0 + j < total) {
+              const float dw = fx[e0 + j];
+              float* row = dO + fr[e0 + j] * DS + l;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float f = v == vr_ ? xdw : 0.f;
-#pragma unroll
-              for (int nb = 0; nb < D / 32; ++nb) {
-                if constexpr (DRUN) od[nb][v] = fma((double)f, (double)vv[j][nb], od[nb][v]);
-                else acc[nb][v] = fmaf(f, vv[j][nb], acc[nb][v]);
-              }
+              for (int i = 0; i < D / 64; ++i) row[64 * i] = fmaf(dw, vv[j][i], row[64 * i]);
             }
+          }
+        }
+        wave_lds_sync();
+        f16v(&acc)[D / 32] = MODE == NEAREST_P ? ol : o;  // DRUN: od
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float* row = dO + crow(v, g) * DS + c;
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) {
+            if constexpr (DRUN) od[nb][v] += (double)row[32 * nb];
+            else acc[nb][v] += row[32 * nb];
           }
         }
       }
@@ -1257,7 +1264,9 @@ size_t fwd_smem_bytes(int K, int lres) {
 }
 static_assert(sizeof(float) * 2 * BINM_MAXB * BN * FWD_NW <= FWD_NW * fwd_wave_bytes<64, 1, false>(),
               "bin-mean partial sums fit the V^T staging area");
-static_assert(3 * 64 * HMAX * 4 <= fwd_wave_bytes<64, 1, false>(), "a wave's heavy-key list fits its staging area");
+static_assert(3 * 64 * HMAX * 4 + 32 * (64 + 4) * 4 <= fwd_wave_bytes<64, 3, false>() &&
+                  3 * 64 * HMAX * 4 + 32 * (128 + 4) * 4 <= fwd_wave_bytes<128, 3, false>(),
+              "a wave's heavy-key list and correction tile fit its staging area (fp32 inputs)");
 
 // Test hook: the bin decision of every (query, key) pair, from the stored scores and row record.
 template <int CAL, int MODE>
