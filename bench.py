@@ -290,8 +290,9 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    headline = (args.grad == "full" and args.tail == "zero" and not args.baselines and not args.binmean
-                and not args.split_forward)
+    # the committed counters are of the default gpt2 step
+    headline = (args.workload == "gpt2" and args.grad == "full" and args.tail == "zero" and not args.baselines
+                and not args.binmean and not args.split_forward)
     traffic = read_traffic(kernel_key) if headline else None
     issue = read_issue(kernel_key) if headline else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
