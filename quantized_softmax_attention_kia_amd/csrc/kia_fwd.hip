@@ -45,6 +45,7 @@ namespace kia {
 constexpr int FWD_NW = 2;            // waves per workgroup, splitting the key tiles of a query tile
 constexpr int FWD_NT = 64 * FWD_NW;
 constexpr int BN = 32;               // keys per tile, query rows per workgroup
+constexpr int FWD_EARLY = 4;         // causal: query tiles dispatched before the heaviest-first order
 // A key that carries P >= 1/HEAVY_INV of its row is heavy: its score is recomputed exactly after
 // pass 2 and its weight corrected, up to HMAX keys per lane
 constexpr double HEAVY_INV = 16.0;
@@ -201,7 +202,11 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   const int T = a.T, K = a.K, nt = a.rec.nt;
   int head, rank;
   block_work(a.nheads, head, rank);
-  const int qt = a.causal ? nt - 1 - rank : rank;  // rank 0: the latest query tile, the most keys
+  // causal order: the FWD_EARLY earliest query tiles first (short rows, where the heavy-key stage
+  // has the most keys to retake: at the end of the launch their latency was its tail), then the
+  // rest heaviest first (rank FWD_EARLY: the latest query tile, the most keys)
+  const int early = nt < FWD_EARLY ? nt : FWD_EARLY;
+  const int qt = a.causal ? (rank < early ? rank : nt - 1 - (rank - early)) : rank;
   const size_t hb = (size_t)head * T * D;
   const TIn* Kp = reinterpret_cast<const TIn*>(a.k) + hb;
   const TIn* Vp = reinterpret_cast<const TIn*>(a.v) + hb;
