@@ -782,8 +782,9 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   // whether a heavy key's weight change reaches the output (the continuous weight: w^L, or e^z)
   constexpr bool HCORR = MODE == LERP || MODE == EXP32 || MODE == NEAREST_P;
   // fp32 inputs take the heavy keys in batches: found first, then their exact scores with every
-  // load of a batch in flight, then their weight changes applied four keys at a time.  bfloat16
-  // inputs take them one key at a time (a key's exact score and correction before the next).
+  // load of a batch in flight, then their weight changes summed per output row in LDS and added to
+  // the accumulators once.  bfloat16 inputs take them one key at a time (a key's exact score and
+  // correction before the next).
   constexpr bool HBATCH = std::is_same_v<TIn, float>;
   double hsum = 0.0;  // batched: the weight changes of this lane's heavy keys (all in its own row)
   int nh_any = 0;     // one at a time: whether this lane retook a heavy key
