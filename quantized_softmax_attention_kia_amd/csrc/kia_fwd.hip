@@ -93,6 +93,10 @@ struct FwdSmem {
     double hs[FWD_NW][BN];
     int hn[FWD_NW][64];
   };
+  // long rows: per wave, the key tiles pass 2 flagged for the heavy-key stage (tile iteration i:
+  // bit i % 32 of word i / 32), and per row the lowest score that can be heavy for any row sum
+  uint32_t tflag[FWD_NW][4];
+  float sflag[BN];
   // followed in dynamic LDS by the grid table: BN rows x (K + 1) floats
 };
 
@@ -518,6 +522,57 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
   }
   __syncthreads();
 
+  // The lowest stored score whose weight can reach thrL (w^L) or thrN (w^N, Nearest), or `loose`
+  // where the grid cannot tell (a bound that holds on every grid).  The weights rise with u, so
+  // the grid inverted at the threshold gives it; a margin of 1e-3 interval widths, or 1e-3 of a
+  // score unit for softmax, covers the roundings of the inversion and of the float decisions.
+  const double hgrid = CAL == EXPB ? 0.0 : 1.0 / rc.inv_h;
+  auto lowest_score = [&](double thrL, double thrN, float loose) -> float {
+    if constexpr (CAL == EXPB) {
+      return fmaxf(loose, (float)((double)M + log(thrL) - 1e-3));
+    } else if constexpr (CAL == MINMAX || CAL == FWM || CAL == FWM_FLOOR) {
+      constexpr int ST = CAL == MINMAX ? BN : 1;
+      // interval r with E_r < thr <= E_{r+1} (E rises with r), or -1 (thr <= E_0), or K (thr > E_K)
+      auto interval = [&](double thr) {
+        if (thr <= (double)trow[0]) return -1;
+        if (thr > (double)trow[K * ST]) return K;
+        int lo = 0, hi = K;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if ((double)trow[mid * ST] < thr) lo = mid;
+          else hi = mid;
+        }
+        return lo;
+      };
+      // LERP: the u at which the interpolated weight reaches the threshold
+      const int rL = interval(thrL);
+      double ustar = rL < 0 ? -1.0
+                     : rL >= K ? (double)K + 1.0
+                               : rL + (thrL - (double)trow[rL * ST]) /
+                                          ((double)trow[(rL + 1) * ST] - (double)trow[rL * ST]);
+      if (is_nearest(MODE)) {  // Nearest: a weight E_rho with E_rho >= thr from u >= rho - 1/2
+        const int rN = interval(thrN);
+        ustar = fmin(ustar, rN < 0 ? -1.0 : rN + 0.5);
+      }
+      const bool regular = CAL != MINMAX || rc.kappa != 0.f;
+      return regular && ustar >= 0.0 ? fmaxf(loose, (float)((double)M - ((double)K - ustar + 1e-3) * hgrid)) : loose;
+    } else {
+      return loose;
+    }
+  };
+  // Long rows (fp32 inputs): pass 2 flags, per wave, the key tiles holding a key that can be heavy
+  // for any row sum (W >= 1: the maximum weighs 1), so that the heavy-key stage reads only those
+  constexpr bool HFLAG = MODE != BINM && MODE != EXPBF && MODE != EXPF8 && std::is_same_v<TIn, float>;
+  const bool track = HFLAG && ntiles > 2 * 32;
+  if (track) {
+    if (w == 0 && g == 0)
+      sm.sflag[c] = qvalid ? lowest_score(1.0 / (HEAVY_INV * (1.0 + 1e-3)), 1.0 / (HEAVY_INV * (1.0 + 1e-3)),
+                                          (float)((double)M - log(HEAVY_INV * (1.0 + 1e-3)) - hgrid) - Erow)
+                           : INFINITY;
+    if (l < 4) sm.tflag[w][l] = 0u;
+    __syncthreads();
+  }
+
   // ---- pass 2: reconstruct, normalize, multiply by V
   double sumL = 0.0, sumN = 0.0;  // row sums of positive weights: double, no absorption of small terms
   f16v o[D / 32], ol[D / 32];
@@ -694,6 +749,13 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) ot[nb] = mfma_split<NS>(ps, vb[nb], ot[nb]);
     }
+    if (track) {  // (before the next tile's scores replace this one's)
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+      const int it = (kt - w) / FWD_NW;
+      if (__ballot(mx >= sm.sflag[c]) != 0ull && it < 128 && l == 0) sm.tflag[w][it >> 5] |= 1u << (it & 31);
+    }
     if constexpr (F64) {
       // O += P V in double: A = the weights (query l%16 of the block, key 4 s4 + l/16), B = V
       wave_lds_sync();
@@ -797,9 +859,10 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       WNr += sm.sN[u][c];
     }
     const double Wmin = is_nearest(MODE) ? fmin(WLr, WNr) : WLr;
-    const bool maybe = qvalid && Wmin <= HEAVY_INV;
-    const double hgrid = CAL == EXPB ? 0.0 : 1.0 / rc.inv_h;
-    const float s_thr = maybe ? (float)((double)M + log(Wmin / HEAVY_INV) - hgrid) - Erow : INFINITY;
+    const bool maybe = qvalid && Wmin <= HEAVY_INV * (1.0 + 1e-3);
+    // (the same margin as the heavy test below)
+    const float s_thr =
+        maybe ? (float)((double)M + log(Wmin / (HEAVY_INV * (1.0 + 1e-3))) - hgrid) - Erow : INFINITY;
     if (__any(maybe)) {
       // (a) the heavy keys, found on the stored scores (the next tile's scores are in flight while
       // one is tested); up to HMAX per lane, with their stored scores
@@ -808,50 +871,30 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
       // every grid; where the weight threshold falls inside the grid, the grid inverted at it gives
       // a tighter one (the weights rise with u; a margin of 1e-3 interval widths, or 1e-3 of a
       // score unit for softmax, covers the roundings of the inversion and of the float decisions).
-      float s_cand = s_thr;
-      if (maybe) {
-        const double thrL = WLr / (HEAVY_INV * (1.0 + 1e-3)), thrN = WNr / (HEAVY_INV * (1.0 + 1e-3));
-        if constexpr (CAL == EXPB) {
-          s_cand = fmaxf(s_thr, (float)((double)M + log(thrL) - 1e-3));
-        } else if constexpr (CAL == MINMAX || CAL == FWM || CAL == FWM_FLOOR) {
-          constexpr int ST = CAL == MINMAX ? BN : 1;
-          // interval r with E_r < thr <= E_{r+1} (E rises with r), or -1 (thr <= E_0), or K (thr > E_K)
-          auto interval = [&](double thr) {
-            if (thr <= (double)trow[0]) return -1;
-            if (thr > (double)trow[K * ST]) return K;
-            int lo = 0, hi = K;
-            while (hi - lo > 1) {
-              const int mid = (lo + hi) >> 1;
-              if ((double)trow[mid * ST] < thr) lo = mid;
-              else hi = mid;
-            }
-            return lo;
-          };
-          // LERP: the u at which the interpolated weight reaches the threshold
-          const int rL = interval(thrL);
-          double ustar = rL < 0 ? -1.0
-                         : rL >= K ? (double)K + 1.0
-                                   : rL + (thrL - (double)trow[rL * ST]) /
-                                              ((double)trow[(rL + 1) * ST] - (double)trow[rL * ST]);
-          if (is_nearest(MODE)) {  // Nearest: a weight E_rho with E_rho >= thr from u >= rho - 1/2
-            const int rN = interval(thrN);
-            ustar = fmin(ustar, rN < 0 ? -1.0 : rN + 0.5);
-          }
-          const bool regular = CAL != MINMAX || rc.kappa != 0.f;
-          if (regular && ustar >= 0.0)
-            s_cand = fmaxf(s_thr, (float)((double)M - ((double)K - ustar + 1e-3) * hgrid));
-        }
-      }
+      const float s_cand =
+          maybe ? lowest_score(WLr / (HEAVY_INV * (1.0 + 1e-3)), WNr / (HEAVY_INV * (1.0 + 1e-3)), s_thr) : INFINITY;
       float sc[16], sn[16];
       auto load16 = [&](float(&dst)[16], int kt) {
         const float* St = Sh + tile_index(qt, kt, nt, a.causal) * 1024 + l;
 #pragma unroll
         for (int v = 0; v < 16; ++v) dst[v] = St[v * 64];
       };
-      if (w < ntiles) load16(sc, w);
-      for (int kt = w; kt < ntiles; kt += FWD_NW) {
-        const bool more = kt + FWD_NW < ntiles;
-        if (more) load16(sn, kt + FWD_NW);
+      // the wave's tiles that pass 2 flagged (every tile where it flagged none)
+      auto visit = [&](int kt) {
+        const int it = (kt - w) / FWD_NW;
+        return !track || it >= 128 || ((sm.tflag[w][it >> 5] >> (it & 31)) & 1u) != 0u;
+      };
+      auto next_visit = [&](int kt) {
+        for (kt += FWD_NW; kt < ntiles && !visit(kt); kt += FWD_NW) {
+        }
+        return kt;
+      };
+      int kt = w < ntiles && visit(w) ? w : next_visit(w);
+      if (kt < ntiles) load16(sc, kt);
+      while (kt < ntiles) {
+        const int kn = next_visit(kt);
+        const bool more = kn < ntiles;
+        if (more) load16(sn, kn);
         const int k0 = kt * BN;
         uint32_t bits = 0u;
         // candidates (a lane without a possible heavy key has s_cand = infinity); the extremum
@@ -897,6 +940,7 @@ __global__ __launch_bounds__(FWD_NT) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
           for (int v = 0; v < 16; ++v) sc[v] = sn[v];
         }
+        kt = kn;
       }
       // the wave's heavy keys as one list in its LDS region (V^T is no longer read): lane order
       int incl = nh;
