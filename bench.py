@@ -82,11 +82,12 @@ def read_issue(kernel: str):
     return None
 
 
-def cpu_baseline(variants, q, k, v, do, budget_s: float, grad: str = "full"):
-    """The oracle, as it stands, on a bounded sample: heads in order, every variant, until the budget."""
+def cpu_baseline(variants, q, k, v, do, budget_s: float, grad: str = "full", threads: int = 0):
+    """The oracle, as it stands, on a bounded sample: heads in order, every variant, until the budget
+    (on `threads` host threads; 0: all of them)."""
     import dataclasses
     from oracle import oracle as ORC
-    threads = ORC.default_threads()
+    threads = threads or ORC.default_threads()
     B, H, T, D = q.shape
     pairs = T * (T + 1) // 2
     done_heads, flops = 0, 0.0
@@ -303,7 +304,11 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample ...")
-        cpu = cpu_baseline([x for x in variants if not isinstance(x, str)], q, k, v, do, args.cpu_seconds, args.grad)
+        kv = [x for x in variants if not isinstance(x, str)]
+        cpu = cpu_baseline(kv, q, k, v, do, args.cpu_seconds, args.grad)
+        # the same oracle on one host thread, over a shorter sample
+        one = cpu_baseline(kv, q, k, v, do, max(1.0, args.cpu_seconds / 4), args.grad, threads=1)
+        cpu["one_core"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
         log(f"cpu baseline {cpu}")
 
     line = {
@@ -318,6 +323,9 @@ def main() -> int:
             "B": wl.B, "H": wl.H, "T": wl.T, "D": wl.D, "causal": True,
             "alg_flops_per_step": step_flops,
             "frac_of_mfma_peak": round(value / peak, 4),
+            # the same step priced by the FlashAttention convention, 14 D flops per causal pair (4 D
+            # forward; 10 D backward, the recomputed Q K^T included), for comparison with such figures
+            "flash_convention_tflops": round(value * 14.0 / 12.0, 3),
             "slowest_variant": {"name": slowest, "tflops": round(slowest_tflops, 3),
                                 "ms": round(sum(per[slowest].values()), 4)},
             "kernel_ms": {n: {k2: round(x, 4) for k2, x in d.items()} for n, d in per.items()},
