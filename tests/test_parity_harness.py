@@ -156,3 +156,58 @@ def test_scores_are_correctly_rounded_fp32():
     r2 = ORC.head(cfg, q2, k2, np.ones((2, 4)), None, scale=1.0, flips=np.array([(1, 1, ORC.FLIP_SCORE)]),
                   scores=True)
     assert r2["scores"][1, 1] == 1.0 + 2.0 ** -23
+
+
+@pytest.mark.parametrize("calib,recon,tail,K", [("minmax", "lerp", "zero", 4), ("minmax", "nearest", "zero", 16),
+                                               ("fwm", "nearest", "zero", 4), ("fwm", "lerp", "resolved", 8)])
+def test_decision_flags_are_the_positions_within_the_guard(calib, recon, tail, K):
+    """The flag list holds exactly the visible positions whose u lies within the guard of a
+    decision boundary (§3: interior interval boundaries 1..K-1, every integer below K on the
+    resolved grid; the Nearest midpoints k + 1/2; the FWM window edge z = -tau), found here by
+    brute force over every pair from the fp32 scores and the row extrema.  A wider or narrower
+    band, a missed boundary or a spurious one fails; positions within 1e-9 of the guard's edge are
+    left out (either answer is the definition's)."""
+    T, guard = 200, 2e-3
+    q, k, v, do = make_inputs(1, 1, T, 64, 11, q_scale=3.0)
+    q, k, v, do = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    cfg = ORC.OracleConfig(calib, recon, "prob", "full", K, 6.0, tail=tail)
+    ref = ORC.head(cfg, q, k, v, do, guard=guard, flag_cap=1 << 20, scores=True)
+    kinds = ORC.FLIP_INTERVAL | ORC.FLIP_NEAREST | ORC.FLIP_TAIL
+    got = {(int(i), int(j), int(kd)) for i, j, kd in ref["flags"] if kd & kinds}
+    S, M, m = ref["scores"], ref["rowd"]["M"], ref["rowd"]["m"]
+    want, edge = set(), set()
+    nearest = recon == "nearest"
+    for i in range(T):
+        for j in range(i + 1):
+            s = S[i, j]
+            if calib == "minmax":
+                if M[i] - m[i] <= 1e-12:
+                    continue                          # degenerate row: no boundary
+                h = (M[i] - m[i]) / K
+                u = (s - m[i]) / h
+            else:
+                h = 6.0 / K
+                z = min(s - M[i], 0.0)
+                u = ((z if tail == "resolved" else max(z, -6.0)) + 6.0) / h
+                if tail != "resolved":
+                    dt = abs(z + 6.0) / h             # distance from the window edge
+                    if dt < guard:
+                        want.add((i, j, ORC.FLIP_TAIL))
+                    if abs(dt - guard) < 1e-9:
+                        edge.add((i, j, ORC.FLIP_TAIL))
+            ki = np.floor(u + 0.5)
+            if (tail == "resolved" or ki >= 1) and ki <= K - 1:
+                di = abs(u - ki)
+                if di < guard:
+                    want.add((i, j, ORC.FLIP_INTERVAL))
+                if abs(di - guard) < 1e-9:
+                    edge.add((i, j, ORC.FLIP_INTERVAL))
+            kh = np.floor(u) + 0.5
+            if nearest and kh < K:
+                dh = abs(u - kh)
+                if dh < guard:
+                    want.add((i, j, ORC.FLIP_NEAREST))
+                if abs(dh - guard) < 1e-9:
+                    edge.add((i, j, ORC.FLIP_NEAREST))
+    assert len(want) > 20, "the guard is wide enough that this head has flagged positions"
+    assert got - edge == want - edge
