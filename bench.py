@@ -49,10 +49,10 @@ def sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic_gpt2_fwd_bwd.md), or None
-    when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2_fwd_bwd.md")
+def read_traffic(kernel: str, workload: str = "gpt2"):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic_<workload>_fwd_bwd.md),
+    or None when there are none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_fwd_bwd.md")
     if not os.path.exists(path):
         return None
     digest = sources_digest()
@@ -64,11 +64,11 @@ def read_traffic(kernel: str):
     return None
 
 
-def read_issue(kernel: str):
-    """SQ counters of the kernel (profiles/sq_counters_gpt2_fwd_bwd.md): the VALU's and the matrix
-    pipe's busy shares of SIMD time and the waves' share of time waiting, or None when the kernel
-    sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "sq_counters_gpt2_fwd_bwd.md")
+def read_issue(kernel: str, workload: str = "gpt2"):
+    """SQ counters of the kernel (profiles/sq_counters_<workload>_fwd_bwd.md): the VALU's and the
+    matrix pipe's busy shares of SIMD time and the waves' share of time waiting, or None when there
+    are none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{workload}_fwd_bwd.md")
     if not os.path.exists(path):
         return None
     digest = sources_digest()
@@ -291,11 +291,11 @@ def main() -> int:
     dom_alg = ALG_PER_PAIR[dom_stage] * wl.D * pairs
     achieved = dom_alg / (dom_ms * 1e-3) / 1e12
     kernel_key = f"{dom_stage}:{dom_var}"
-    # the committed counters are of the default gpt2 step
-    headline = (args.workload == "gpt2" and args.grad == "full" and args.tail == "zero" and not args.baselines
-                and not args.binmean and not args.split_forward)
-    traffic = read_traffic(kernel_key) if headline else None
-    issue = read_issue(kernel_key) if headline else None
+    # the committed counters are of each workload's default step
+    default_step = (args.grad == "full" and args.tail == "zero" and not args.baselines
+                    and not args.binmean and not args.split_forward)
+    traffic = read_traffic(kernel_key, args.workload) if default_step else None
+    issue = read_issue(kernel_key, args.workload) if default_step else None
     slowest = max(per, key=lambda n: sum(per[n].values()))
     slowest_tflops = alg_flops_variant / (sum(per[slowest].values()) * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms; {value:.1f} TFLOP/s = {100 * value / peak:.1f}% of {peak} TFLOP/s; "
